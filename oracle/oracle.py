@@ -1,0 +1,137 @@
+"""ctypes wrapper and build step for the fp64 oracle in ``mfa_oracle.c``.
+
+Test infrastructure only (see the header of ``mfa_oracle.c``).  Inputs are
+float32 arrays holding the already-rounded input tensors exactly (bf16 and
+fp16 widen to float32 without loss); results come back as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import numpy as np
+
+ORACLE_DIR = os.path.dirname(os.path.abspath(__file__))
+ORACLE_SRC = os.path.join(ORACLE_DIR, "mfa_oracle.c")
+ORACLE_LIB = os.path.join(ORACLE_DIR, "libmfa_oracle.so")
+
+
+def build_oracle(out_path: str = ORACLE_LIB, mutant: int = 0) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math).  ``mutant`` > 0 plants
+    the numbered deliberate mistake (used only by the mutation test)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared", "-pthread",
+           f"-DORACLE_MUTANT={int(mutant)}", ORACLE_SRC, "-o", out_path + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+def _f32(x):
+    """float32, C-contiguous numpy view of a torch tensor or array (exact for
+    fp32/bf16/fp16 inputs)."""
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float32).contiguous().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+_fp = ctypes.POINTER(ctypes.c_float)
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int64)
+
+
+def _ptr(a, t):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+class Oracle:
+    """One loaded build of the oracle library."""
+
+    def __init__(self, path: str = ORACLE_LIB):
+        if not os.path.exists(path):
+            build_oracle(path)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.mfa_oracle_rows.restype = ctypes.c_int
+        lib.mfa_oracle_rows.argtypes = [_fp, _fp, _fp, _fp] + [ctypes.c_int64] * 6 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            _ip, ctypes.c_int64, _dp, _dp, _ip, ctypes.c_int]
+        lib.mfa_oracle_visible_counts.restype = ctypes.c_int64
+        lib.mfa_oracle_visible_counts.argtypes = [_fp] + [ctypes.c_int64] * 3 + [
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, _ip]
+        lib.mfa_oracle_key_range.restype = None
+        lib.mfa_oracle_key_range.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                             ctypes.c_int64, _ip, _ip]
+        lib.mfa_oracle_mutant.restype = ctypes.c_int
+        self.lib = lib
+        self.mutant = lib.mfa_oracle_mutant()
+
+    def key_range(self, aq: int, Lk: int, causal: bool, window: int):
+        lo, hi = ctypes.c_int64(), ctypes.c_int64()
+        self.lib.mfa_oracle_key_range(aq, Lk, int(bool(causal)), window,
+                                      ctypes.byref(lo), ctypes.byref(hi))
+        return lo.value, hi.value
+
+    def rows(self, q, k, v, rows, *, scale, causal=False, window=0, q_offset=None,
+             softcap=0.0, key_mask=None, nthreads=1):
+        """Evaluate the rows given as an (n, 3) array of (b, hq, i).
+
+        q is [B, Lq, Hq, D]; k, v are [B, Lk, Hkv, D]; key_mask is [B, Lk] or
+        None.  Returns (out [n, D] float64, lse [n] float64, nvis [n] int64).
+        """
+        q, k, v, m = _f32(q), _f32(k), _f32(v), _f32(key_mask)
+        B, Lq, Hq, D = q.shape
+        Lk, Hkv = k.shape[1], k.shape[2]
+        assert k.shape == (B, Lk, Hkv, D) and v.shape == k.shape
+        if m is not None:
+            assert m.shape == (B, Lk)
+        if q_offset is None:
+            q_offset = Lk - Lq
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        n = rows.shape[0]
+        out = np.zeros((n, D), np.float64)
+        lse = np.zeros(n, np.float64)
+        nvis = np.zeros(n, np.int64)
+        rc = self.lib.mfa_oracle_rows(
+            _ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), _ptr(m, _fp),
+            B, Lq, Lk, Hq, Hkv, D, float(scale), int(bool(causal)), int(window), int(q_offset),
+            float(softcap), _ptr(rows, _ip), n, _ptr(out, _dp), _ptr(lse, _dp), _ptr(nvis, _ip),
+            int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return out, lse, nvis
+
+    def full(self, q, k, v, **kw):
+        """Every row: returns O [B, Lq, Hq, D] and LSE [B, Hq, Lq] (float64)."""
+        q = _f32(q)
+        B, Lq, Hq, D = q.shape
+        b, h, i = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(Lq), indexing="ij")
+        rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
+        out, lse, nvis = self.rows(q, k, v, rows, **kw)
+        O = out.reshape(B, Hq, Lq, D).transpose(0, 2, 1, 3).copy()
+        return O, lse.reshape(B, Hq, Lq), nvis.reshape(B, Hq, Lq)
+
+    def visible_counts(self, B, Lq, Lk, *, causal=False, window=0, q_offset=None, key_mask=None):
+        """Visible-key count of every row, [B, Lq] int64, and the total."""
+        m = _f32(key_mask)
+        if q_offset is None:
+            q_offset = Lk - Lq
+        counts = np.zeros((B, Lq), np.int64)
+        total = self.lib.mfa_oracle_visible_counts(_ptr(m, _fp), B, Lq, Lk, int(bool(causal)),
+                                                   int(window), int(q_offset), _ptr(counts, _ip))
+        return counts, int(total)
+
+
+_default = None
+
+
+def default_oracle() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,445 @@
+"""Pins for the fp64 oracle: checks against facts other than the oracle itself.
+
+Each ``pin_*`` function takes a loaded ``oracle.Oracle`` and raises
+AssertionError when the oracle disagrees with what the pages or the
+mathematics fix.  The checks use independent formulations: the window rules as
+other functions on the pages state them, torch's float64 attention (a library
+special case), a dense NumPy/SciPy formulation, closed forms (Q = 0, V = 1,
+V = I, single visible key) and invariants (GQA head grouping, decode as the
+last prefill row, mask tail as a shorter key axis, window limits, perturbation
+of invisible keys).  ``ALL_PINS`` lists them for the mutation test.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+from scipy.special import logsumexp
+
+TIGHT = 1e-12
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(rng, shape, std=1.0):
+    return (rng.standard_normal(shape) * std).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# independent statements of the visibility rule
+# ---------------------------------------------------------------------------
+
+def vis_causal_p1(aq, j, w):
+    """ferrotensor attention.rs, AttentionOptions: a key is visible when it is
+    not after the query and, with a window, closer than ``w`` positions."""
+    return j <= aq and (w <= 0 or abs(aq - j) < w)
+
+
+def vis_causal_p4(i, j, w):
+    """forge attention.metal forward kernel (no offset): keys from
+    i+1-w (when i+1 > w and w > 0) up to i."""
+    jmax = i
+    jmin = i + 1 - w if (w > 0 and i + 1 > w) else 0
+    return jmin <= j <= jmax
+
+
+def vis_bidir_packed(aq, j, w):
+    """brotensor flash_attention.h, packed-QKV forward: with a window, keys
+    within window/2 (integer halving) of the row; without one, every key."""
+    return w <= 0 or abs(aq - j) <= w // 2
+
+
+def dense_visibility(Lq, Lk, causal, window, q_offset, mask_b=None):
+    """[Lq, Lk] boolean visibility from the statements above."""
+    vis = np.zeros((Lq, Lk), bool)
+    for i in range(Lq):
+        aq = i + q_offset
+        for j in range(Lk):
+            ok = vis_causal_p1(aq, j, window) if causal else vis_bidir_packed(aq, j, window)
+            if mask_b is not None and not (mask_b[j] > 0.5):
+                ok = False
+            vis[i, j] = ok
+    return vis
+
+
+# ---------------------------------------------------------------------------
+# dense formulation (full score matrix, additive -inf mask, SciPy logsumexp)
+# ---------------------------------------------------------------------------
+
+def dense_reference(q, k, v, *, scale, causal, window, q_offset, softcap=0.0, key_mask=None):
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    kr = np.repeat(k, g, axis=2)          # head h uses kv head h // g
+    vr = np.repeat(v, g, axis=2)
+    O = np.zeros((B, Lq, Hq, D))
+    L = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        vis = dense_visibility(Lq, Lk, causal, window, q_offset,
+                               None if key_mask is None else np.asarray(key_mask)[b])
+        for h in range(Hq):
+            s = scale * (q[b, :, h, :] @ kr[b, :, h, :].T)
+            if softcap > 0:
+                s = softcap * np.tanh(s / softcap)
+            s = np.where(vis, s, -np.inf)
+            lse = logsumexp(s, axis=1)
+            empty = ~vis.any(1)
+            lse[empty] = -np.inf
+            p = np.where(vis, np.exp(s - np.where(empty, 0.0, lse)[:, None]), 0.0)
+            O[b, :, h, :] = p @ vr[b, :, h, :]
+            L[b, h, :] = lse
+    return O, L
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), f"{what}: finiteness differs"
+    assert np.array_equal(a[~fin], b[~fin]), f"{what}: infinities differ"
+    if fin.any():
+        err = np.max(np.abs(a[fin] - b[fin]))
+        assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+def pin_range_causal_matches_ferrotensor_rule(orc):
+    for Lk in range(1, 26):
+        for aq in range(Lk):
+            for w in range(-1, Lk + 3):
+                lo, hi = orc.key_range(aq, Lk, True, w)
+                got = {j for j in range(Lk) if lo <= j <= hi}
+                want = {j for j in range(Lk) if vis_causal_p1(aq, j, w)}
+                assert got == want, ("causal range", Lk, aq, w, got, want)
+
+
+def pin_range_causal_matches_forge_rule(orc):
+    for T in range(1, 26):
+        for i in range(T):
+            for w in range(0, T + 3):
+                lo, hi = orc.key_range(i, T, True, w)
+                got = {j for j in range(T) if lo <= j <= hi}
+                want = {j for j in range(T) if vis_causal_p4(i, j, w)}
+                assert got == want, ("forge causal range", T, i, w)
+
+
+def pin_range_bidirectional_matches_packed_rule(orc):
+    for Lk in range(1, 26):
+        for aq in range(Lk):
+            for w in range(-1, 2 * Lk + 3):
+                lo, hi = orc.key_range(aq, Lk, False, w)
+                got = {j for j in range(Lk) if lo <= j <= hi}
+                want = {j for j in range(Lk) if vis_bidir_packed(aq, j, w)}
+                assert got == want, ("bidirectional range", Lk, aq, w)
+
+
+def pin_golden_visibility_tables(orc):
+    """Hand-worked visibility tables under tests/golden (see the file)."""
+    path = os.path.join(GOLDEN, "visibility_tables.txt")
+    cases = _parse_tables(path)
+    assert len(cases) >= 4
+    for hdr, table in cases:
+        B, Lq, Lk = 1, hdr["Lq"], hdr["Lk"]
+        mask = None
+        if "masked" in hdr:
+            mask = np.ones((1, Lk), np.float32)
+            mask[0, hdr["masked"]] = 0.0
+        counts, _ = orc.visible_counts(B, Lq, Lk, causal=hdr["causal"], window=hdr["window"],
+                                       q_offset=hdr["q_offset"], key_mask=mask)
+        # V = I and Q = 0 reveal the exact visible set of each row
+        D = max(Lk, 1)
+        q = np.zeros((1, Lq, 1, D), np.float32)
+        k = np.zeros((1, Lk, 1, D), np.float32)
+        v = np.eye(Lk, D, dtype=np.float32).reshape(1, Lk, 1, D)
+        O, _, _ = orc.full(q, k, v, scale=1.0, causal=hdr["causal"], window=hdr["window"],
+                           q_offset=hdr["q_offset"], key_mask=mask)
+        for i, keys in table.items():
+            assert counts[0, i] == len(keys), (hdr, i, counts[0, i], keys)
+            got = set(np.nonzero(O[0, i, 0, :Lk] > 0)[0].tolist())
+            assert got == set(keys), (hdr, i, got, keys)
+
+
+def _parse_tables(path):
+    cases, hdr, table = [], None, None
+    with open(path) as f:
+        for raw in f:
+            line = raw.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("case"):
+                if hdr is not None:
+                    cases.append((hdr, table))
+                hdr, table = {}, {}
+                for tok in line.split()[1:]:
+                    key, val = tok.split("=")
+                    if key == "causal":
+                        hdr[key] = val == "1"
+                    elif key == "masked":
+                        hdr[key] = [int(x) for x in val.split(",") if x]
+                    else:
+                        hdr[key] = int(val)
+                continue
+            row, keys = line.split(":")
+            table[int(row)] = [int(x) for x in keys.split()]
+    if hdr is not None:
+        cases.append((hdr, table))
+    return cases
+
+
+def pin_visible_counts_match_predicates(orc):
+    rng = _rng(1)
+    for causal in (True, False):
+        for window in (-1, 0, 1, 2, 5, 8, 40):
+            B, Lq, Lk = 3, 7, 19
+            for q_offset in (0, 5, Lk - Lq):
+                mask = (rng.random((B, Lk)) > 0.3).astype(np.float32)
+                counts, total = orc.visible_counts(B, Lq, Lk, causal=causal, window=window,
+                                                   q_offset=q_offset, key_mask=mask)
+                want = np.stack([dense_visibility(Lq, Lk, causal, window, q_offset, mask[b]).sum(1)
+                                 for b in range(B)])
+                assert np.array_equal(counts, want), (causal, window, q_offset)
+                assert total == int(want.sum())
+
+
+def pin_matches_torch_sdpa_float64(orc):
+    """No window, mask or soft-cap and Hq = Hkv: torch's float64 math-path
+    attention is the same definition."""
+    rng = _rng(2)
+    for (B, Lq, Lk, H, D, causal) in [(2, 9, 9, 3, 16, True), (1, 13, 13, 2, 8, False),
+                                      (2, 5, 11, 2, 8, False), (1, 4, 10, 3, 8, True)]:
+        q, k, v = _rand(rng, (B, Lq, H, D)), _rand(rng, (B, Lk, H, D)), _rand(rng, (B, Lk, H, D))
+        scale = 1.0 / math.sqrt(D) * 1.3
+        O, L, _ = orc.full(q, k, v, scale=scale, causal=causal, window=0, q_offset=Lk - Lq)
+        tq, tk, tv = (torch.from_numpy(x).double().permute(0, 2, 1, 3) for x in (q, k, v))
+        if causal:
+            # queries sit at the last Lq positions of the key axis
+            allowed = torch.ones(Lq, Lk, dtype=torch.bool).tril(diagonal=Lk - Lq)
+        else:
+            allowed = torch.ones(Lq, Lk, dtype=torch.bool)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed,
+                                                               scale=scale)
+        _close(O, ref.permute(0, 2, 1, 3).numpy(), TIGHT, "sdpa O")
+        s = (tq @ tk.transpose(-1, -2)) * scale
+        s = s.masked_fill(~allowed, float("-inf"))
+        _close(L, torch.logsumexp(s, dim=-1).numpy(), TIGHT, "sdpa LSE")
+
+
+def pin_matches_dense_bruteforce(orc):
+    rng = _rng(3)
+    cases = [
+        dict(B=2, Lq=12, Lk=12, Hq=4, Hkv=2, D=8, causal=True, window=5, softcap=0.0, mask=True),
+        dict(B=1, Lq=10, Lk=10, Hq=3, Hkv=1, D=16, causal=False, window=6, softcap=0.0, mask=True),
+        dict(B=2, Lq=3, Lk=14, Hq=4, Hkv=4, D=8, causal=True, window=0, softcap=1.5, mask=False),
+        dict(B=1, Lq=6, Lk=15, Hq=2, Hkv=1, D=8, causal=False, window=7, softcap=2.0, mask=True),
+        dict(B=2, Lq=8, Lk=8, Hq=2, Hkv=2, D=8, causal=True, window=3, softcap=0.7, mask=True),
+    ]
+    for c in cases:
+        B, Lq, Lk, Hq, Hkv, D = c["B"], c["Lq"], c["Lk"], c["Hq"], c["Hkv"], c["D"]
+        q, k, v = _rand(rng, (B, Lq, Hq, D), 2.0), _rand(rng, (B, Lk, Hkv, D), 2.0), _rand(rng, (B, Lk, Hkv, D))
+        mask = (rng.random((B, Lk)) > 0.25).astype(np.float32) if c["mask"] else None
+        kw = dict(scale=0.4, causal=c["causal"], window=c["window"], q_offset=Lk - Lq,
+                  softcap=c["softcap"], key_mask=mask)
+        O, L, _ = orc.full(q, k, v, **kw)
+        Od, Ld = dense_reference(q, k, v, **kw)
+        _close(O, Od, TIGHT, f"dense O {c}")
+        _close(L, Ld, TIGHT, f"dense LSE {c}")
+
+
+def pin_zero_query_closed_form(orc):
+    """Q = 0 makes every visible score 0 (soft-capped or not): each row is the
+    plain mean of its visible V rows and LSE = ln(count)."""
+    rng = _rng(4)
+    for causal, window, softcap in [(True, 0, 0.0), (True, 4, 3.0), (False, 6, 0.0), (False, 0, 1.0)]:
+        B, Lq, Lk, Hq, Hkv, D = 2, 7, 11, 4, 2, 8
+        q = np.zeros((B, Lq, Hq, D), np.float32)
+        k, v = _rand(rng, (B, Lk, Hkv, D)), _rand(rng, (B, Lk, Hkv, D))
+        mask = (rng.random((B, Lk)) > 0.3).astype(np.float32)
+        O, L, n = orc.full(q, k, v, scale=0.5, causal=causal, window=window, q_offset=Lk - Lq,
+                           softcap=softcap, key_mask=mask)
+        for b in range(B):
+            vis = dense_visibility(Lq, Lk, causal, window, Lk - Lq, mask[b])
+            for h in range(Hq):
+                for i in range(Lq):
+                    cnt = int(vis[i].sum())
+                    assert n[b, h, i] == cnt
+                    if cnt == 0:
+                        assert np.all(O[b, i, h] == 0) and L[b, h, i] == -np.inf
+                        continue
+                    mean = v[b, vis[i], h // (Hq // Hkv), :].astype(np.float64).mean(0)
+                    assert np.max(np.abs(O[b, i, h] - mean)) <= TIGHT
+                    assert abs(L[b, h, i] - math.log(cnt)) <= TIGHT
+
+
+def pin_rows_sum_to_one(orc):
+    """V = 1 everywhere: O = sum_j P_ij must be 1 for every non-empty row."""
+    rng = _rng(5)
+    B, Lq, Lk, Hq, Hkv, D = 2, 9, 9, 2, 1, 8
+    q, k = _rand(rng, (B, Lq, Hq, D), 3.0), _rand(rng, (B, Lk, Hkv, D), 3.0)
+    v = np.ones((B, Lk, Hkv, D), np.float32)
+    for causal, window in [(True, 0), (False, 4), (True, 3)]:
+        O, _, n = orc.full(q, k, v, scale=1.0, causal=causal, window=window, q_offset=0)
+        assert np.all(n > 0)
+        assert np.max(np.abs(O - 1.0)) <= TIGHT
+
+
+def pin_single_visible_key(orc):
+    """A causal window of one key: row i sees only key i, so O_i = V_i and
+    LSE_i is that single (scaled) score."""
+    rng = _rng(6)
+    B, L, H, D = 2, 6, 2, 8
+    q, k, v = _rand(rng, (B, L, H, D)), _rand(rng, (B, L, H, D)), _rand(rng, (B, L, H, D))
+    O, Lse, n = orc.full(q, k, v, scale=0.25, causal=True, window=1, q_offset=0)
+    assert np.all(n == 1)
+    _close(O, v.astype(np.float64), 0.0, "single key O")
+    s = 0.25 * np.einsum("blhd,blhd->bhl", q.astype(np.float64), k.astype(np.float64))
+    _close(Lse, s, TIGHT, "single key LSE")
+
+
+def pin_gqa_equals_mha_on_repeated_kv(orc):
+    rng = _rng(7)
+    B, Lq, Lk, Hq, Hkv, D = 2, 6, 9, 6, 2, 8
+    q, k, v = _rand(rng, (B, Lq, Hq, D)), _rand(rng, (B, Lk, Hkv, D)), _rand(rng, (B, Lk, Hkv, D))
+    kw = dict(scale=0.3, causal=True, window=4, q_offset=Lk - Lq)
+    Og, Lg, _ = orc.full(q, k, v, **kw)
+    g = Hq // Hkv
+    kt = torch.from_numpy(k).repeat_interleave(g, dim=2).numpy()
+    vt = torch.from_numpy(v).repeat_interleave(g, dim=2).numpy()
+    Om, Lm, _ = orc.full(q, kt, vt, **kw)
+    _close(Og, Om, 0.0, "GQA vs MHA O")
+    _close(Lg, Lm, 0.0, "GQA vs MHA LSE")
+
+
+def pin_window_limits(orc):
+    """window <= 0 is the unwindowed form; a causal window of at least Lk
+    keys, or a bidirectional one of at least 2*Lk, changes nothing."""
+    rng = _rng(8)
+    B, L, H, D = 1, 10, 2, 8
+    q, k, v = _rand(rng, (B, L, H, D)), _rand(rng, (B, L, H, D)), _rand(rng, (B, L, H, D))
+    for causal, big in [(True, L), (True, L + 5), (False, 2 * L), (False, 2 * L + 3)]:
+        base = orc.full(q, k, v, scale=0.5, causal=causal, window=0, q_offset=0)
+        for w in (-3, -1, big):
+            other = orc.full(q, k, v, scale=0.5, causal=causal, window=w, q_offset=0)
+            _close(other[0], base[0], 0.0, f"window {w}")
+            _close(other[1], base[1], 0.0, f"window {w}")
+
+
+def pin_decode_rows_are_prefill_rows(orc):
+    """A query block at the end of the key axis (q_offset = Lk - Lq) equals the
+    same rows of the full causal prefill; Lq = 1 is the last row."""
+    rng = _rng(9)
+    B, L, Hq, Hkv, D = 2, 12, 4, 2, 8
+    q, k, v = _rand(rng, (B, L, Hq, D)), _rand(rng, (B, L, Hkv, D)), _rand(rng, (B, L, Hkv, D))
+    for window in (0, 5):
+        Op, Lp, _ = orc.full(q, k, v, scale=0.35, causal=True, window=window, q_offset=0)
+        for Lq in (1, 3):
+            Od, Ld, _ = orc.full(q[:, L - Lq:], k, v, scale=0.35, causal=True, window=window,
+                                 q_offset=L - Lq)
+            _close(Od, Op[:, L - Lq:], 0.0, "decode O")
+            _close(Ld, Lp[:, :, L - Lq:], 0.0, "decode LSE")
+
+
+def pin_mask_tail_is_shorter_key_axis(orc):
+    rng = _rng(10)
+    B, Lq, Lk, H, D, V = 1, 5, 14, 2, 8, 9
+    q, k, v = _rand(rng, (B, Lq, H, D)), _rand(rng, (B, Lk, H, D)), _rand(rng, (B, Lk, H, D))
+    mask = np.ones((B, Lk), np.float32)
+    mask[:, V:] = 0.0
+    Om, Lm, _ = orc.full(q, k, v, scale=0.5, causal=False, window=0, q_offset=0, key_mask=mask)
+    Os, Ls, _ = orc.full(q, k[:, :V], v[:, :V], scale=0.5, causal=False, window=0, q_offset=0)
+    _close(Om, Os, 0.0, "mask tail O")
+    _close(Lm, Ls, 0.0, "mask tail LSE")
+    ones = np.ones((B, Lk), np.float32)
+    Oa, La, _ = orc.full(q, k, v, scale=0.5, causal=True, window=4, q_offset=3, key_mask=ones)
+    On, Ln, _ = orc.full(q, k, v, scale=0.5, causal=True, window=4, q_offset=3)
+    _close(Oa, On, 0.0, "all-ones mask O")
+    _close(La, Ln, 0.0, "all-ones mask LSE")
+
+
+def pin_softcap_limits(orc):
+    """A huge cap is the uncapped score to within its cubic term; a small cap
+    c bounds every score by c, so LSE lies within [ln n - c, ln n + c]."""
+    rng = _rng(11)
+    B, L, H, D = 1, 8, 2, 8
+    q, k, v = _rand(rng, (B, L, H, D), 2.0), _rand(rng, (B, L, H, D), 2.0), _rand(rng, (B, L, H, D))
+    O0, L0, _ = orc.full(q, k, v, scale=0.5, causal=True, q_offset=0)
+    Ob, Lb, _ = orc.full(q, k, v, scale=0.5, causal=True, q_offset=0, softcap=1e6)
+    _close(Ob, O0, 1e-9, "huge cap O")
+    _close(Lb, L0, 1e-9, "huge cap LSE")
+    c = 0.25
+    Oc, Lc, n = orc.full(q, k, v, scale=0.5, causal=True, q_offset=0, softcap=c)
+    lnn = np.log(n.astype(np.float64))
+    assert np.all(Lc <= lnn + c + TIGHT) and np.all(Lc >= lnn - c - TIGHT)
+    # capped scores sit in (-c, c), so each weight is within e^{+-2c} of uniform
+    Oz, _, _ = orc.full(np.zeros_like(q), k, v, scale=0.5, causal=True, q_offset=0, softcap=c)
+    assert np.max(np.abs(Oc - Oz)) <= (math.exp(2 * c) - 1) * np.max(np.abs(v)) + TIGHT
+
+
+def pin_invisible_keys_have_no_influence(orc):
+    """Keys a row cannot see may hold anything finite without changing it."""
+    rng = _rng(12)
+    B, L, Hq, Hkv, D = 1, 16, 2, 1, 8
+    q, k, v = _rand(rng, (B, L, Hq, D)), _rand(rng, (B, L, Hkv, D)), _rand(rng, (B, L, Hkv, D))
+    mask = np.ones((B, L), np.float32)
+    mask[0, [3, 11]] = 0.0
+    kw = dict(scale=0.5, causal=True, window=5, q_offset=0, key_mask=mask)
+    O, Lse, _ = orc.full(q, k, v, **kw)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, [3, 11]] = 1e4
+    v2[0, [3, 11]] = -1e4
+    O2, L2, _ = orc.full(q, k2, v2, **kw)
+    _close(O2, O, 0.0, "masked keys perturbed")
+    _close(L2, Lse, 0.0, "masked keys perturbed LSE")
+    # rows 0..7 cannot see keys 8.. (causal) -- perturb those too
+    k3, v3 = k.copy(), v.copy()
+    k3[0, 8:] = -1e4
+    v3[0, 8:] = 1e4
+    O3, L3, _ = orc.full(q, k3, v3, **kw)
+    _close(O3[:, :8], O[:, :8], 0.0, "future keys perturbed")
+    _close(L3[:, :, :8], Lse[:, :, :8], 0.0, "future keys perturbed LSE")
+
+
+def pin_empty_rows(orc):
+    """Rows with no visible key: O = 0 and LSE = -inf (reading for a case the
+    pages leave open; brotensor's decode_len writes zeros for length 0)."""
+    rng = _rng(13)
+    B, L, H, D = 2, 5, 1, 8
+    q, k, v = _rand(rng, (B, L, H, D)), _rand(rng, (B, L, H, D)), _rand(rng, (B, L, H, D))
+    mask = np.zeros((B, L), np.float32)
+    mask[1, 4] = 1.0
+    O, Lse, n = orc.full(q, k, v, scale=0.5, causal=False, window=0, q_offset=0, key_mask=mask)
+    assert np.all(n[0] == 0) and np.all(O[0] == 0) and np.all(Lse[0] == -np.inf)
+    assert np.all(n[1] == 1)
+    _close(O[1], np.broadcast_to(v[1, 4], (L, H, D)).astype(np.float64), 0.0, "one key")
+
+
+ALL_PINS = [
+    pin_range_causal_matches_ferrotensor_rule,
+    pin_range_causal_matches_forge_rule,
+    pin_range_bidirectional_matches_packed_rule,
+    pin_golden_visibility_tables,
+    pin_visible_counts_match_predicates,
+    pin_matches_torch_sdpa_float64,
+    pin_matches_dense_bruteforce,
+    pin_zero_query_closed_form,
+    pin_rows_sum_to_one,
+    pin_single_visible_key,
+    pin_gqa_equals_mha_on_repeated_kv,
+    pin_window_limits,
+    pin_decode_rows_are_prefill_rows,
+    pin_mask_tail_is_shorter_key_axis,
+    pin_softcap_limits,
+    pin_invisible_keys_have_no_influence,
+    pin_empty_rows,
+]

@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module draws random tensors and key masks and nothing else: it holds none
+of the attention arithmetic, so both the HIP path and the fp64 oracle can take
+their inputs from it.
+
+Recipe (the same for every workload): one torch generator on the target
+device, seeded with ``seed``, draws Q, then K, then V as float32 standard
+normals times ``std``, each then rounded to nearest-even into the workload's
+dtype.  The key mask, when there is one, comes from a separate CPU generator
+seeded with ``seed`` so that it is identical on every device.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "f32" | "f16" | "bf16"
+    B: int
+    Lq: int
+    Lk: int
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+    window: int = 0       # <= 0: no window
+    softcap: float = 0.0  # <= 0: off
+    mask: Optional[str] = None   # None | "pad_tail" | "random_frac"
+    pad_max: int = 0      # pad_tail: per-batch padding drawn from [0, pad_max)
+    mask_frac: float = 0.0  # random_frac: floor(frac * Lk) keys zeroed per batch
+    std: float = 1.0
+
+    @property
+    def q_offset(self) -> int:
+        return self.Lk - self.Lq
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    def describe(self) -> dict:
+        d = dataclasses.asdict(self)
+        d["q_offset"] = self.q_offset
+        d["scale"] = self.scale
+        return d
+
+
+# The five workloads of the method's feature set, named by what they are.
+SINGLE_HEAD_CAUSAL_FP32 = Workload("single_head_causal_fp32_L128_D64", "f32", 1, 128, 128, 1, 1, 64, True)
+GQA_CAUSAL_PREFILL_BF16 = Workload("gqa_causal_prefill_bf16_B4_L2048_H32_KV8_D128", "bf16",
+                                   4, 2048, 2048, 32, 8, 128, True)
+BIDIR_WINDOW_ENCODER_FP16 = Workload("bidir_window128_encoder_fp16_B8_L8192_H12_D64_padmask", "f16",
+                                     8, 8192, 8192, 12, 12, 64, False, window=128,
+                                     mask="pad_tail", pad_max=2048)
+LONG_CACHE_DECODE_BF16 = Workload("long_cache_decode_bf16_B64_Lk32768_H32_KV8_D128", "bf16",
+                                  64, 1, 32768, 32, 8, 128, True)
+CAUSAL_WINDOW_SOFTCAP_BF16 = Workload("causal_window4096_softcap50_bf16_B2_L16384_H16_KV4_D128_mask5pct",
+                                      "bf16", 2, 16384, 16384, 16, 4, 128, True, window=4096,
+                                      softcap=50.0, mask="random_frac", mask_frac=0.05, std=2.0)
+
+ALL = [SINGLE_HEAD_CAUSAL_FP32, GQA_CAUSAL_PREFILL_BF16, BIDIR_WINDOW_ENCODER_FP16,
+       LONG_CACHE_DECODE_BF16, CAUSAL_WINDOW_SOFTCAP_BF16]
+BY_NAME = {w.name: w for w in ALL}
+
+
+def make_key_mask(w: Workload, seed: int = 0) -> Optional[torch.Tensor]:
+    """[B, Lk] float32 key mask on the CPU (1 = keep, 0 = drop), or None."""
+    if w.mask is None:
+        return None
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    m = torch.ones(w.B, w.Lk, dtype=torch.float32)
+    if w.mask == "pad_tail":
+        pads = torch.randint(0, max(w.pad_max, 1), (w.B,), generator=g)
+        for b in range(w.B):
+            p = int(pads[b])
+            if p > 0:
+                m[b, w.Lk - p:] = 0.0
+    elif w.mask == "random_frac":
+        n = int(math.floor(w.mask_frac * w.Lk))
+        for b in range(w.B):
+            perm = torch.randperm(w.Lk, generator=g)
+            m[b, perm[:n]] = 0.0
+    else:
+        raise ValueError(f"unknown mask kind {w.mask!r}")
+    return m
+
+
+def make_inputs(w: Workload, device="cpu", seed: int = 0):
+    """Q [B,Lq,Hq,D], K and V [B,Lk,Hkv,D] in the workload's dtype on
+    ``device``, and the key mask [B,Lk] float32 (or None) on ``device``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = w.torch_dtype
+    out = []
+    for shape in ((w.B, w.Lq, w.Hq, w.D), (w.B, w.Lk, w.Hkv, w.D), (w.B, w.Lk, w.Hkv, w.D)):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if w.std != 1.0:
+            x.mul_(w.std)
+        out.append(x.to(dt))
+        del x
+    m = make_key_mask(w, seed)
+    if m is not None:
+        m = m.to(device)
+    return out[0], out[1], out[2], m
