@@ -1,0 +1,141 @@
+/*
+ * mfa.h -- C ABI of libmfa, a fused attention forward for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * One operation:  O = softmax(scale * Q K^T + masks) V,  with the per-row
+ * natural-log log-sum-exp LSE saved alongside.  It is computed tile by tile
+ * with an online softmax, so the Lq x Lk score matrix never exists in memory
+ * (vision_rs flash_attn2.rs, module doc and forward kernel; brotensor
+ * flash_attention.h, flash_attention_forward: tiled online softmax with fp32
+ * accumulation).
+ *
+ * Feature set (brotensor flash_attention.h; ferrotensor attention.rs):
+ *   - grouped-query heads: Hkv divides Hq and q head h reads kv head
+ *     h / (Hq / Hkv) (flash_attention_gqa_forward, flash_attention_decode);
+ *   - queries sit at absolute positions aq = i + q_offset of the key axis
+ *     (flash_attention_windowed_forward; AttentionOptions::causal_offset);
+ *   - causal: key j visible only when j <= aq; with window > 0 also
+ *     j >= aq - window + 1 (flash_attention_windowed_forward, causal form);
+ *   - bidirectional (causal = 0) with window > 0: keys aq - window/2 through
+ *     aq + window/2, integer halving, clipped to [0, Lk) (same function,
+ *     bidirectional form); window <= 0 means no window in either form;
+ *   - key mask: key j of batch b is dropped unless key_mask[b*Lk + j] > 0.5
+ *     (flash_attention_forward mask description; flash_attention_backward
+ *     threshold);
+ *   - soft-cap > 0: each scaled score s becomes softcap * tanh(s / softcap)
+ *     before masking and the softmax (flash_attention_decode);
+ *   - Lq = 1 decode over a long cache runs as a split over the keys plus a
+ *     combine pass (flash_attention_decode_len: the work divides the valid
+ *     keys and split points only change rounding).
+ *
+ * Layouts (row-major, contiguous, all in device memory):
+ *   q, out     [B, Lq, Hq, D]   element type `dtype`
+ *   k, v       [B, Lk, Hkv, D]  element type `dtype`
+ *   lse        [B, Hq, Lq]      float32, may be NULL (then not written)
+ *   key_mask   [B, Lk]          float32, may be NULL (no mask)
+ * q, k, v and out must be 16-byte aligned; lse and key_mask 4-byte aligned.
+ *
+ * A row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Ownership: every pointer is caller-owned device memory.  The library keeps
+ * no reference after a call returns and writes only out, lse and (for the
+ * _ws / _ex forms) the workspace.
+ *
+ * Streams: every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ * null stream) and never synchronises the device.  A fault in a kernel shows
+ * at the caller's next synchronisation.
+ *
+ * Errors: arguments are checked on the host before any device work; on a
+ * non-zero return nothing has been launched and nothing written.
+ * mfa_last_error() then holds a description (per host thread).
+ */
+#ifndef MFA_H
+#define MFA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out. */
+typedef enum { MFA_F32 = 0, MFA_F16 = 1, MFA_BF16 = 2 } mfa_dtype;
+
+typedef enum {
+    MFA_SUCCESS = 0,
+    /* a null pointer, a misaligned pointer, a dimension < 0 (or Hq, Hkv, D,
+     * Lk = 0), Hq % Hkv != 0, q_offset < 0, q_offset + Lq > Lk, a non-finite
+     * scale or softcap, or a workspace that is too small */
+    MFA_ERROR_INVALID_VALUE = 1,
+    /* D not in {64, 128}, an unknown dtype, or a forced path that cannot
+     * serve the arguments */
+    MFA_ERROR_NOT_SUPPORTED = 2,
+    /* a HIP runtime call or kernel launch failed */
+    MFA_ERROR_HIP = 3,
+    /* the workspace pool could not provide device memory */
+    MFA_ERROR_OUT_OF_MEMORY = 4
+} mfa_status;
+
+/* Kernel path selection for mfa_fwd_ex. */
+typedef enum {
+    MFA_PATH_AUTO = 0,        /* what mfa_fwd chooses */
+    MFA_PATH_GENERIC = 1,     /* fp32-arithmetic tiled kernel, every dtype */
+    MFA_PATH_MFMA = 2,        /* bf16/fp16 MFMA prefill kernel */
+    MFA_PATH_SPLIT_DECODE = 3 /* Lq = 1 split-over-keys kernel + combine */
+} mfa_path;
+
+/*
+ * Attention forward.  B = 0 or Lq = 0 is an empty call that succeeds without
+ * launching anything.  `scale` is used as given (the conventional value is
+ * 1/sqrt(D)).  Any workspace the chosen kernels need comes from the device's
+ * stream-ordered memory pool and is released in stream order.
+ */
+int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+            int B, int Lq, int Lk, int Hq, int Hkv, int D,
+            float scale, int causal, int window, int q_offset, float softcap,
+            const float* key_mask, int dtype, void* stream);
+
+/* Workspace bytes that mfa_fwd_ws needs for these sizes (0 if none); the
+ * figure covers every flag combination. */
+size_t mfa_fwd_workspace_size(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype);
+
+/* mfa_fwd with a caller-owned device workspace of ws_bytes bytes (256-byte
+ * aligned, at least mfa_fwd_workspace_size).  The workspace must not be used
+ * by other work until this call's kernels finish on `stream`. */
+int mfa_fwd_ws(const void* q, const void* k, const void* v, void* out, float* lse,
+               int B, int Lq, int Lk, int Hq, int Hkv, int D,
+               float scale, int causal, int window, int q_offset, float softcap,
+               const float* key_mask, int dtype,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * mfa_fwd_ws with the kernel path forced (`path`, an mfa_path) and, for the
+ * split decode, the number of key splits (`splits` <= 0 chooses).  Returns
+ * MFA_ERROR_NOT_SUPPORTED when the forced path cannot serve the arguments.
+ * Paths differ only in rounding; the test suite uses this to compare them.
+ * workspace may be NULL when ws_bytes is 0, in which case the pool is used.
+ */
+int mfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+               int B, int Lq, int Lk, int Hq, int Hkv, int D,
+               float scale, int causal, int window, int q_offset, float softcap,
+               const float* key_mask, int dtype, int path, int splits,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/* The path mfa_fwd would take for these arguments (an mfa_path value), and
+ * the split count it would use (through *splits, may be NULL). */
+int mfa_fwd_plan(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype, int* splits);
+
+/* Static text for a status code. */
+const char* mfa_status_string(int status);
+
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* mfa_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFA_H */

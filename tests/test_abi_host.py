@@ -1,0 +1,110 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mfa.h declares, and rejects bad arguments on the host before any
+device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_mfa_fwd_amd as mfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mfa.h")
+
+# Distinct, 256-byte aligned fake addresses: never dereferenced, because every
+# call below fails validation (or is empty) before any HIP call.
+FAKE = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mfa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_api():
+    names = declared_functions()
+    assert set(names) == set(mfa.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mfa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", mfa.LIB_PATH], capture_output=True, text=True)
+    if nm.returncode == 0:
+        exported = {line.split()[-1] for line in nm.stdout.splitlines() if line.strip()}
+        for name in declared_functions():
+            assert name in exported, name
+
+
+def call(**over):
+    lib = mfa.load_library()
+    a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], lse=FAKE[4], B=2, Lq=16, Lk=16, Hq=4,
+             Hkv=2, D=64, scale=0.125, causal=1, window=0, q_offset=0, softcap=0.0, key_mask=None,
+             dtype=2)
+    a.update(over)
+    return lib.mfa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                       a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["window"],
+                       a["q_offset"], a["softcap"], a["key_mask"], a["dtype"], None)
+
+
+INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(out=None),
+    dict(B=-1), dict(Lq=-1), dict(Lk=0), dict(Hq=0), dict(Hkv=0), dict(D=0),
+    dict(Hq=6, Hkv=4), dict(q_offset=-1), dict(Lq=16, Lk=16, q_offset=1), dict(Lq=17, Lk=16),
+    dict(scale=float("nan")), dict(scale=float("inf")), dict(softcap=float("inf")),
+    dict(softcap=float("nan")), dict(q=ctypes.c_void_p(0x10008)), dict(out=ctypes.c_void_p(0x10004)),
+    dict(lse=ctypes.c_void_p(0x10002)), dict(key_mask=ctypes.c_void_p(0x10001)),
+]
+
+
+@pytest.mark.parametrize("over", INVALID, ids=lambda d: ",".join(f"{k}" for k in d))
+def test_invalid_arguments_rejected(over):
+    st = call(**over)
+    assert st == 1, (over, st)
+    msg = mfa.load_library().mfa_last_error().decode()
+    assert msg
+
+
+@pytest.mark.parametrize("over", [dict(D=96), dict(D=32), dict(D=256), dict(dtype=7), dict(dtype=-1)])
+def test_unsupported_rejected(over):
+    assert call(**over) == 2
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(Lq=0)])
+def test_empty_call_succeeds_without_work(over):
+    assert call(**over) == 0
+
+
+def test_status_strings():
+    lib = mfa.load_library()
+    for s, text in [(0, "success"), (1, "invalid value"), (2, "not supported"), (3, "HIP error"),
+                    (4, "out of memory")]:
+        assert lib.mfa_status_string(s).decode() == text
+    assert lib.mfa_status_string(99).decode() == "unknown status"
+
+
+def test_forced_path_rejection():
+    lib = mfa.load_library()
+    # split decode needs Lq == 1; fp32 cannot take the MFMA path
+    st = lib.mfa_fwd_ex(FAKE[0], FAKE[1], FAKE[2], FAKE[3], None, 1, 4, 16, 2, 1, 64, 0.125, 1, 0, 12,
+                        0.0, None, 2, mfa.PATH_SPLIT_DECODE, 0, None, 0, None)
+    assert st == 2
+    st = lib.mfa_fwd_ex(FAKE[0], FAKE[1], FAKE[2], FAKE[3], None, 1, 4, 16, 2, 1, 64, 0.125, 1, 0, 12,
+                        0.0, None, 0, mfa.PATH_MFMA, 0, None, 0, None)
+    assert st == 2
+    st = lib.mfa_fwd_ex(FAKE[0], FAKE[1], FAKE[2], FAKE[3], None, 1, 4, 16, 2, 1, 64, 0.125, 1, 0, 12,
+                        0.0, None, 2, 9, 0, None, 0, None)
+    assert st == 2
+
+
+def test_workspace_size_and_plan():
+    import torch
+    assert mfa.workspace_size(4, 2048, 2048, 32, 8, 128, torch.bfloat16) >= 4 * 32 * 8
+    path, splits = mfa.plan(64, 1, 32768, 32, 8, 128, torch.bfloat16)
+    assert path in ("split_decode", "generic", "mfma")
+    p32, _ = mfa.plan(1, 128, 128, 1, 1, 64, torch.float32)
+    assert p32 == "generic"

@@ -1,0 +1,227 @@
+"""GPU parity: libmfa (through its C ABI) against the fp64 oracle.
+
+Small shapes are compared on every row; they span several tiles with ragged
+tails.  The full-size workloads are compared on sampled rows, and every row of
+them is checked for the exact visible-key count through Q = 0.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_mfa_fwd_amd as mfa
+from oracle import default_oracle
+from tests import parity_util as pu
+from transformer_mfa_fwd_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+PATHS = {"generic": mfa.PATH_GENERIC, "mfma": mfa.PATH_MFMA, "split_decode": mfa.PATH_SPLIT_DECODE}
+
+
+def say(msg):
+    print(f"\n[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def path_available(path, w):
+    """Probe whether a forced path serves these arguments (host-side check)."""
+    if path == "generic":
+        return True
+    if path == "split_decode" and w.Lq != 1:
+        return False
+    # a tiny call through the forced path tells whether it is built
+    q = torch.zeros((1, 1, w.Hq, w.D), dtype=w.torch_dtype, device=DEV)
+    k = torch.zeros((1, 4, w.Hkv, w.D), dtype=w.torch_dtype, device=DEV)
+    try:
+        mfa.fwd(q, k, k, path=PATHS[path], causal=True)
+        torch.cuda.synchronize()
+        return True
+    except mfa.MFAError as e:
+        if e.status == 2:
+            return False
+        raise
+
+
+def run_case(w, path="auto", seed=0, rows=None, q_zero=False):
+    q, k, v, m = wl.make_inputs(w, DEV, seed)
+    if q_zero:
+        q = torch.zeros_like(q)
+    say(f"{w.name} path={path} seed={seed}")
+    out, lse = mfa.fwd(q, k, v, causal=w.causal, window=w.window, q_offset=w.q_offset,
+                       softcap=w.softcap, key_mask=m, scale=w.scale,
+                       path=PATHS.get(path, mfa.PATH_AUTO))
+    torch.cuda.synchronize()
+    return q, k, v, m, out, lse
+
+
+def check_all_rows(w, path="auto", seed=0):
+    q, k, v, m, out, lse = run_case(w, path, seed)
+    O, L, _ = default_oracle().full(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
+                                    q_offset=w.q_offset, softcap=w.softcap, key_mask=m,
+                                    nthreads=pu.ORACLE_THREADS)
+    # row form: O as [B, Hq, Lq, D] so that it lines up with LSE [B, Hq, Lq]
+    og = out.double().cpu().numpy().transpose(0, 2, 1, 3)
+    return pu.compare(w.dtype, og, lse.double().cpu().numpy(), O.transpose(0, 2, 1, 3), L,
+                      f"{w.name}/{path}")
+
+
+# --- small shapes: several tiles, ragged tails, every flag -------------------
+
+SMALL = []
+for dtype in ("f32", "f16", "bf16"):
+    for D in (64, 128):
+        SMALL += [
+            wl.Workload(f"causal_gqa_{dtype}_D{D}", dtype, 2, 200, 200, 4, 2, D, True),
+            wl.Workload(f"bidir_{dtype}_D{D}", dtype, 1, 150, 150, 2, 2, D, False),
+            wl.Workload(f"causal_win37_mask_{dtype}_D{D}", dtype, 2, 190, 190, 4, 1, D, True, window=37,
+                        mask="random_frac", mask_frac=0.3),
+            wl.Workload(f"bidir_win100_pad_{dtype}_D{D}", dtype, 2, 260, 260, 3, 3, D, False, window=100,
+                        mask="pad_tail", pad_max=120),
+            wl.Workload(f"decode_block_softcap_{dtype}_D{D}", dtype, 2, 70, 333, 8, 2, D, True, window=0,
+                        softcap=5.0, std=2.0),
+            wl.Workload(f"decode1_{dtype}_D{D}", dtype, 3, 1, 517, 8, 2, D, True, window=0),
+            wl.Workload(f"decode1_win_mask_cap_{dtype}_D{D}", dtype, 2, 1, 700, 16, 1, D, True, window=300,
+                        softcap=20.0, mask="random_frac", mask_frac=0.5),
+        ]
+
+
+@pytest.mark.parametrize("path", ["generic", "mfma", "split_decode", "auto"])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_all_rows(w, path):
+    if path != "auto" and not path_available(path, w):
+        pytest.skip(f"path {path} does not serve {w.name}")
+    if path == "mfma" and w.dtype == "f32":
+        pytest.skip("MFMA path is fp16/bf16 only")
+    check_all_rows(w, path)
+
+
+# --- edge cases ---------------------------------------------------------------
+
+EDGE = [
+    wl.Workload("single_key_bf16", "bf16", 1, 1, 1, 2, 1, 64, True),
+    wl.Workload("window1_f16", "f16", 1, 130, 130, 2, 2, 128, True, window=1),
+    wl.Workload("all_masked_tail_bf16", "bf16", 2, 100, 100, 2, 1, 64, False, mask="pad_tail", pad_max=100),
+    wl.Workload("short_lk_many_heads_bf16", "bf16", 1, 3, 5, 32, 8, 128, False),
+    wl.Workload("lq_lt_lk_causal_f32", "f32", 2, 65, 129, 2, 1, 64, True),
+    wl.Workload("big_bidir_window_bf16", "bf16", 1, 96, 96, 1, 1, 128, False, window=1000),
+    wl.Workload("mqa_g16_f16", "f16", 1, 80, 80, 16, 1, 64, True),
+    wl.Workload("mqa_g32_decode_bf16", "bf16", 2, 1, 300, 32, 1, 128, True),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
+def test_edge_cases(w):
+    check_all_rows(w)
+
+
+def test_fully_masked_batch_gives_zero_and_neg_inf():
+    w = wl.Workload("masked_batch", "bf16", 2, 70, 70, 2, 1, 64, False)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    m = torch.ones(2, 70, device=DEV)
+    m[0] = 0.0
+    for path in ("auto", "generic"):
+        out, lse = mfa.fwd(q, k, v, key_mask=m, path=PATHS.get(path, 0))
+        torch.cuda.synchronize()
+        assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+        assert torch.all(torch.isfinite(lse[1]))
+
+
+def test_deterministic_and_no_out_of_bounds_writes():
+    w = wl.Workload("canary", "bf16", 2, 190, 190, 4, 2, 128, True, window=50, mask="random_frac",
+                    mask_frac=0.2)
+    q, k, v, m = wl.make_inputs(w, DEV)
+    n = q.numel()
+    guard = 4096
+    for path in ("auto", "generic"):
+        outs = []
+        for rep in range(2):
+            obuf = torch.full((n + 2 * guard,), 7.0, dtype=q.dtype, device=DEV)
+            lbuf = torch.full((w.B * w.Hq * w.Lq + 2 * guard,), 7.0, dtype=torch.float32, device=DEV)
+            out = obuf[guard:guard + n].view(q.shape)
+            lse = lbuf[guard:guard + w.B * w.Hq * w.Lq].view(w.B, w.Hq, w.Lq)
+            mfa.fwd(q, k, v, causal=True, window=50, key_mask=m, out=out, lse=lse,
+                    path=PATHS.get(path, 0))
+            torch.cuda.synchronize()
+            assert torch.all(obuf[:guard] == 7.0) and torch.all(obuf[-guard:] == 7.0)
+            assert torch.all(lbuf[:guard] == 7.0) and torch.all(lbuf[-guard:] == 7.0)
+            outs.append((out.clone(), lse.clone()))
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    w = wl.Workload("gqa", "bf16", 2, 150, 150, 8, 2, 128, True, window=70)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    o1, l1 = mfa.fwd(q, k, v, causal=True, window=70)
+    o2, l2 = mfa.fwd(q, k.repeat_interleave(4, dim=2).contiguous(),
+                     v.repeat_interleave(4, dim=2).contiguous(), causal=True, window=70)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_workspace_entry_point_matches_pool_entry_point():
+    w = wl.Workload("ws", "bf16", 2, 1, 900, 8, 2, 128, True, mask="random_frac", mask_frac=0.1)
+    q, k, v, m = wl.make_inputs(w, DEV)
+    o1, l1 = mfa.fwd(q, k, v, causal=True, key_mask=m)
+    nbytes = mfa.workspace_size(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=DEV)
+    o2, l2 = mfa.fwd(q, k, v, causal=True, key_mask=m, workspace=ws[:nbytes] if nbytes else ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --- full-size workloads --------------------------------------------------------
+
+FULL = [wl.SINGLE_HEAD_CAUSAL_FP32, wl.GQA_CAUSAL_PREFILL_BF16, wl.BIDIR_WINDOW_ENCODER_FP16,
+        wl.LONG_CACHE_DECODE_BF16, wl.CAUSAL_WINDOW_SOFTCAP_BF16]
+
+
+def _full_rows(w, m):
+    if w.Lq * w.B * w.Hq <= 4096:
+        b, h, i = np.meshgrid(np.arange(w.B), np.arange(w.Hq), np.arange(w.Lq), indexing="ij")
+        return np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
+    rows = pu.sample_rows(w)
+    if w.mask == "pad_tail":
+        rows = np.concatenate([rows, pu.pad_boundary_rows(m.cpu(), w)])
+    return rows
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_workload_sampled_rows(w):
+    q, k, v, m, out, lse = run_case(w)
+    orc = default_oracle()
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, q_offset=w.q_offset, softcap=w.softcap)
+    if w.Lq == 1:
+        # decode: whole batches through the oracle, a seeded subset of batches
+        rng = np.random.default_rng(7)
+        bs = sorted({0, w.B - 1} | set(rng.choice(w.B, size=min(w.B, 6), replace=False).tolist()))
+        for b in bs:
+            rows = np.array([(0, h, 0) for h in range(w.Hq)], np.int64)
+            mb = None if m is None else m[b:b + 1]
+            O, L, _ = orc.rows(q[b:b + 1], k[b:b + 1], v[b:b + 1], rows, key_mask=mb,
+                               nthreads=pu.ORACLE_THREADS, **kw)
+            og, lg = pu.gather_rows(out[b:b + 1], lse[b:b + 1], rows)
+            pu.compare(w.dtype, og, lg, O, L, f"{w.name} batch {b}")
+        return
+    rows = _full_rows(w, m)
+    say(f"oracle on {len(rows)} rows")
+    O, L, _ = orc.rows(q, k, v, rows, key_mask=m, nthreads=pu.ORACLE_THREADS, **kw)
+    og, lg = pu.gather_rows(out, lse, rows)
+    pu.compare(w.dtype, og, lg, O, L, w.name)
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_workload_exact_visible_counts(w):
+    """Q = 0: every visible score is 0, so exp(LSE) is the visible-key count."""
+    q, k, v, m, out, lse = run_case(w, q_zero=True)
+    counts, _ = default_oracle().visible_counts(w.B, w.Lq, w.Lk, causal=w.causal, window=w.window,
+                                                q_offset=w.q_offset,
+                                                key_mask=None if m is None else m.cpu())
+    got = torch.exp(lse.double()).round().to(torch.int64).cpu().numpy()   # [B, Hq, Lq]
+    want = np.broadcast_to(counts[:, None, :], got.shape)
+    empty = want == 0
+    assert np.array_equal(got[~empty], want[~empty])
+    assert torch.all(torch.isneginf(lse.cpu()[torch.from_numpy(np.ascontiguousarray(empty))]))

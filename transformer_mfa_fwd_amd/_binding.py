@@ -1,0 +1,166 @@
+"""ctypes binding of libmfa (include/mfa.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed to
+the C ABI, and a non-zero status raises MFAError.  Every step of the attention
+forward runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmfa.so")
+
+MFA_F32, MFA_F16, MFA_BF16 = 0, 1, 2
+PATH_AUTO, PATH_GENERIC, PATH_MFMA, PATH_SPLIT_DECODE = 0, 1, 2, 3
+PATH_NAMES = {PATH_AUTO: "auto", PATH_GENERIC: "generic", PATH_MFMA: "mfma",
+              PATH_SPLIT_DECODE: "split_decode"}
+_DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: MFA_BF16}
+
+EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
+            "mfa_status_string", "mfa_last_error", "mfa_version")
+
+
+class MFAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+_I = ctypes.c_int
+_P = ctypes.c_void_p
+_F = ctypes.c_float
+_FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F, _P, _I]
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmfa.so (built in-tree by transformer_mfa_fwd_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libmfa.so not found at {path}; build it with "
+                          "`python transformer_mfa_fwd_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    lib.mfa_fwd.restype = _I
+    lib.mfa_fwd.argtypes = _FWD_ARGS + [_P]
+    lib.mfa_fwd_ws.restype = _I
+    lib.mfa_fwd_ws.argtypes = _FWD_ARGS + [_P, ctypes.c_size_t, _P]
+    lib.mfa_fwd_ex.restype = _I
+    lib.mfa_fwd_ex.argtypes = _FWD_ARGS + [_I, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.mfa_fwd_workspace_size.argtypes = [_I] * 7
+    lib.mfa_fwd_plan.restype = _I
+    lib.mfa_fwd_plan.argtypes = [_I] * 7 + [ctypes.POINTER(_I)]
+    lib.mfa_status_string.restype = ctypes.c_char_p
+    lib.mfa_status_string.argtypes = [_I]
+    lib.mfa_last_error.restype = ctypes.c_char_p
+    lib.mfa_last_error.argtypes = []
+    lib.mfa_version.restype = _I
+    lib.mfa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise MFAError(status, f"libmfa: {lib.mfa_status_string(status).decode()}: "
+                               f"{lib.mfa_last_error().decode()}")
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, Lq, Hq, D]; k and v [B, Lk, Hkv, D]")
+    B, Lq, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    return B, Lq, k.shape[1], Hq, k.shape[2], D
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+        window: int = 0, q_offset: Optional[int] = None, softcap: float = 0.0,
+        key_mask: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        return_lse: bool = True, path: int = PATH_AUTO, splits: int = 0,
+        workspace: Optional[torch.Tensor] = None, stream=None
+        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention forward through libmfa.
+
+    q [B, Lq, Hq, D]; k, v [B, Lk, Hkv, D] (same dtype, contiguous, on one
+    GPU); key_mask [B, Lk] float32 or None.  q_offset defaults to Lk - Lq and
+    scale to 1/sqrt(D).  Returns (out [B, Lq, Hq, D], lse [B, Hq, Lq] float32
+    or None).  ``path``/``splits`` force a kernel path (mfa_fwd_ex);
+    ``workspace`` is a caller-owned uint8 device tensor (mfa_fwd_ws).
+    """
+    lib = load_library()
+    B, Lq, Lk, Hq, Hkv, D = _dims(q, k, v)
+    if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"dtypes must match and be one of float32/float16/bfloat16 "
+                        f"(got {q.dtype}, {k.dtype}, {v.dtype})")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if key_mask is not None:
+        if key_mask.dtype != torch.float32 or tuple(key_mask.shape) != (B, Lk) or \
+                not key_mask.is_cuda or not key_mask.is_contiguous():
+            raise ValueError("key_mask must be a contiguous float32 GPU tensor of shape [B, Lk]")
+    if q_offset is None:
+        q_offset = Lk - Lq
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous and match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, Hq, Lq]")
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Lq, Lk, Hq, Hkv, D,
+            float(scale), int(bool(causal)), int(window), int(q_offset), float(softcap),
+            _ptr(key_mask), _DTYPE_CODES[q.dtype]]
+    with torch.cuda.device(q.device):
+        s = _stream(stream)
+        ws_ptr = _ptr(workspace)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        if path != PATH_AUTO or splits:
+            _check(lib.mfa_fwd_ex(*args, int(path), int(splits), ws_ptr, ws_bytes, s))
+        elif workspace is not None:
+            _check(lib.mfa_fwd_ws(*args, ws_ptr, ws_bytes, s))
+        else:
+            _check(lib.mfa_fwd(*args, s))
+    return out, lse
+
+
+def workspace_size(B, Lq, Lk, Hq, Hkv, D, dtype: torch.dtype) -> int:
+    return int(load_library().mfa_fwd_workspace_size(B, Lq, Lk, Hq, Hkv, D, _DTYPE_CODES[dtype]))
+
+
+def plan(B, Lq, Lk, Hq, Hkv, D, dtype: torch.dtype):
+    """(path name, split count) that mfa_fwd would use."""
+    s = ctypes.c_int(0)
+    p = load_library().mfa_fwd_plan(B, Lq, Lk, Hq, Hkv, D, _DTYPE_CODES[dtype], ctypes.byref(s))
+    return PATH_NAMES.get(p, str(p)), s.value
+
+
+def version() -> int:
+    return int(load_library().mfa_version())

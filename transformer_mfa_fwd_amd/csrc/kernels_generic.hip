@@ -1,0 +1,203 @@
+// kernels_generic.hip -- fp32-arithmetic attention forward for every dtype,
+// plus the key-mask bit-packing prepass.
+//
+// The generic kernel is the straightforward tiled form of the method (vision_rs
+// flash_attn2.rs, forward kernel: running max, rescaled running sum and
+// accumulator per query row, LSE = max + log(sum) at the end), written for
+// clarity rather than speed.  It serves fp32 inputs (whose 1e-4 tolerance rules
+// out 16-bit MFMA operands) and any shape the MFMA kernels decline.
+//
+// Work decomposition: one 256-thread workgroup per (64-query tile, q head,
+// batch); each of its four waves owns 16 query rows.  K and V tiles of 64 keys
+// are converted to fp32 in LDS.  For the scores, lane j of a wave owns key j of
+// the tile; for P.V, lane c owns output columns c and c+64.
+#include "mfa_internal.h"
+
+#include <math.h>
+
+namespace mfa {
+namespace {
+
+constexpr int GBM = 64;  // query rows per workgroup
+constexpr int GBN = 64;  // keys per tile
+constexpr int ROWS_PER_WAVE = 16;
+
+template <typename T>
+__device__ inline float to_f32(T x) { return static_cast<float>(x); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
+    __shared__ float sQ[GBM][D + 4];
+    __shared__ float sK[GBN][D + 4];
+    __shared__ float sV[GBN][D];
+    __shared__ float sP[4][ROWS_PER_WAVE][GBN];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int i0 = blockIdx.x * GBM;
+    const int hq = blockIdx.y;
+    const int b = blockIdx.z;
+    const int kvh = hq / a.group;
+    const int i_end = min(i0 + GBM, a.Lq);
+
+    const T* __restrict__ q = static_cast<const T*>(a.q);
+    const T* __restrict__ k = static_cast<const T*>(a.k);
+    const T* __restrict__ v = static_cast<const T*>(a.v);
+    T* __restrict__ out = static_cast<T*>(a.out);
+    const int64_t q_row_stride = (int64_t)a.Hq * D;
+    const int64_t kv_row_stride = (int64_t)a.Hkv * D;
+
+    for (int x = tid; x < GBM * D; x += 256) {
+        const int r = x / D, d = x % D;
+        const int i = i0 + r;
+        sQ[r][d] = i < a.Lq ? to_f32(q[((int64_t)b * a.Lq + i) * q_row_stride + (int64_t)hq * D + d])
+                            : 0.0f;
+    }
+
+    // keys any row of this tile can see
+    int lo_first, hi_first, lo_last, hi_last;
+    key_range(i0 + a.q_offset, a.Lk, a.causal, a.window, lo_first, hi_first);
+    key_range(i_end - 1 + a.q_offset, a.Lk, a.causal, a.window, lo_last, hi_last);
+    const int klo = lo_first, khi = hi_last;
+
+    int rlo[ROWS_PER_WAVE], rhi[ROWS_PER_WAVE];
+    float m[ROWS_PER_WAVE], l[ROWS_PER_WAVE], acc[ROWS_PER_WAVE][D / 64];
+#pragma unroll
+    for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+        const int i = i0 + wave * ROWS_PER_WAVE + rr;
+        key_range(i + a.q_offset, a.Lk, a.causal, a.window, rlo[rr], rhi[rr]);
+        if (i >= a.Lq) { rlo[rr] = 1; rhi[rr] = 0; }
+        m[rr] = -INFINITY;
+        l[rr] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) acc[rr][c] = 0.0f;
+    }
+
+    if (klo <= khi) {
+        for (int kt = klo / GBN; kt <= khi / GBN; ++kt) {
+            __syncthreads();  // previous tile fully consumed (and sQ written)
+            for (int x = tid; x < GBN * D; x += 256) {
+                const int j = x / D, d = x % D;
+                const int key = kt * GBN + j;
+                float kv = 0.0f, vv = 0.0f;
+                if (key < a.Lk) {
+                    const int64_t off = ((int64_t)b * a.Lk + key) * kv_row_stride + (int64_t)kvh * D + d;
+                    kv = to_f32(k[off]);
+                    vv = to_f32(v[off]);
+                }
+                sK[j][d] = kv;
+                sV[j][d] = vv;
+            }
+            __syncthreads();
+
+            const int key = kt * GBN + lane;
+            bool key_ok = key < a.Lk;
+            if (key_ok && a.key_mask) key_ok = a.key_mask[(int64_t)b * a.Lk + key] > 0.5f;
+
+            float s[ROWS_PER_WAVE];
+#pragma unroll
+            for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) s[rr] = 0.0f;
+            for (int d = 0; d < D; d += 4) {
+                const float4 kk = *reinterpret_cast<const float4*>(&sK[lane][d]);
+#pragma unroll
+                for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+                    const float4 qq = *reinterpret_cast<const float4*>(&sQ[wave * ROWS_PER_WAVE + rr][d]);
+                    s[rr] = fmaf(qq.x, kk.x, s[rr]);
+                    s[rr] = fmaf(qq.y, kk.y, s[rr]);
+                    s[rr] = fmaf(qq.z, kk.z, s[rr]);
+                    s[rr] = fmaf(qq.w, kk.w, s[rr]);
+                }
+            }
+
+#pragma unroll
+            for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+                float x = s[rr] * a.scale;
+                if (a.softcap > 0.0f) x = a.softcap * tanhf(x / a.softcap);
+                const bool vis = key_ok && key >= rlo[rr] && key <= rhi[rr];
+                x = vis ? x : -INFINITY;
+
+                float mx = x;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+                const float m_new = fmaxf(m[rr], mx);
+                const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+                const float alpha = expf(m[rr] - m_use);
+                const float p = expf(x - m_use);
+                l[rr] = l[rr] * alpha + p;
+                m[rr] = m_new;
+                sP[wave][rr][lane] = p;
+#pragma unroll
+                for (int c = 0; c < D / 64; ++c) acc[rr][c] *= alpha;
+            }
+            __syncthreads();
+
+            for (int j = 0; j < GBN; ++j) {
+                float vv[D / 64];
+#pragma unroll
+                for (int c = 0; c < D / 64; ++c) vv[c] = sV[j][lane + 64 * c];
+#pragma unroll
+                for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+                    const float p = sP[wave][rr][j];
+#pragma unroll
+                    for (int c = 0; c < D / 64; ++c) acc[rr][c] = fmaf(p, vv[c], acc[rr][c]);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+        const int i = i0 + wave * ROWS_PER_WAVE + rr;
+        float lt = l[rr];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
+        if (i >= a.Lq) continue;
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        T* orow = out + ((int64_t)b * a.Lq + i) * q_row_stride + (int64_t)hq * D;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) orow[lane + 64 * c] = static_cast<T>(acc[rr][c] * inv);
+        if (a.lse && lane == 0)
+            a.lse[((int64_t)b * a.Hq + hq) * a.Lq + i] = lt > 0.0f ? m[rr] + logf(lt) : -INFINITY;
+    }
+}
+
+// words[b * W + w], bit t: key 64*w + t exists and its mask is > 0.5.
+__global__ __launch_bounds__(64) void mask_words_kernel(const float* __restrict__ mask, int Lk, int W,
+                                                        uint64_t* __restrict__ words) {
+    const int w = blockIdx.x, b = blockIdx.y;
+    const int key = w * 64 + threadIdx.x;
+    const bool keep = key < Lk && mask[(int64_t)b * Lk + key] > 0.5f;
+    const uint64_t bits = __ballot(keep);
+    if (threadIdx.x == 0) words[(int64_t)b * W + w] = bits;
+}
+
+template <typename T>
+hipError_t launch_generic_t(const FwdArgs& a, hipStream_t s) {
+    dim3 grid((a.Lq + GBM - 1) / GBM, a.Hq, a.B);
+    if (a.D == 64)
+        hipLaunchKernelGGL((generic_fwd_kernel<T, 64>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((generic_fwd_kernel<T, 128>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_generic(const FwdArgs& a, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case kF32: return launch_generic_t<float>(a, s);
+        case kF16: return launch_generic_t<_Float16>(a, s);
+        case kBF16: return launch_generic_t<__bf16>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s) {
+    dim3 grid(a.words_per_batch, a.B);
+    hipLaunchKernelGGL(mask_words_kernel, grid, dim3(64), 0, s, a.key_mask, a.Lk, a.words_per_batch,
+                       words);
+    return hipGetLastError();
+}
+
+}  // namespace mfa

@@ -1,0 +1,275 @@
+// mfa_api.cpp -- the C ABI of libmfa: argument checks, kernel choice,
+// workspace handling and launches.  Declarations and semantics: include/mfa.h.
+#include "mfa.h"
+#include "mfa_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+struct Call {
+    const void *q, *k, *v;
+    void* out;
+    float* lse;
+    int B, Lq, Lk, Hq, Hkv, D;
+    float scale;
+    int causal, window, q_offset;
+    float softcap;
+    const float* key_mask;
+    int dtype;
+};
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Host-side checks; no HIP call happens here.
+int validate(const Call& c) {
+    if (!c.q || !c.k || !c.v || !c.out)
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k, v and out must be non-null");
+    if (c.B < 0 || c.Lq < 0 || c.Lk <= 0 || c.Hq <= 0 || c.Hkv <= 0 || c.D <= 0)
+        return fail(MFA_ERROR_INVALID_VALUE,
+                    "bad dimensions B=%d Lq=%d Lk=%d Hq=%d Hkv=%d D=%d (B, Lq >= 0; others > 0)",
+                    c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D);
+    if (c.Hq % c.Hkv != 0)
+        return fail(MFA_ERROR_INVALID_VALUE, "Hkv=%d does not divide Hq=%d", c.Hkv, c.Hq);
+    if (c.q_offset < 0 || (int64_t)c.q_offset + c.Lq > c.Lk)
+        return fail(MFA_ERROR_INVALID_VALUE, "need 0 <= q_offset and q_offset + Lq <= Lk (q_offset=%d Lq=%d Lk=%d)",
+                    c.q_offset, c.Lq, c.Lk);
+    if (!std::isfinite(c.scale) || !std::isfinite(c.softcap))
+        return fail(MFA_ERROR_INVALID_VALUE, "scale and softcap must be finite");
+    if (c.dtype != MFA_F32 && c.dtype != MFA_F16 && c.dtype != MFA_BF16)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "unknown dtype %d", c.dtype);
+    if (c.D != 64 && c.D != 128)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "head dim %d not supported (64 or 128)", c.D);
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.out, 16))
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k, v and out must be 16-byte aligned");
+    if (!aligned(c.lse, 4) || !aligned(c.key_mask, 4))
+        return fail(MFA_ERROR_INVALID_VALUE, "lse and key_mask must be 4-byte aligned");
+    // sizes must fit the kernels' 64-bit element offsets and 32-bit row indices
+    const int64_t q_elems = (int64_t)c.B * c.Lq * c.Hq * c.D;
+    const int64_t kv_elems = (int64_t)c.B * c.Lk * c.Hkv * c.D;
+    if (q_elems < 0 || kv_elems < 0 || (int64_t)c.B * c.Hq > (int64_t)1 << 30)
+        return fail(MFA_ERROR_INVALID_VALUE, "problem too large");
+    return MFA_SUCCESS;
+}
+
+int auto_path(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype) {
+    (void)B; (void)Lk;
+    const int group = Hq / Hkv;
+    if (Lq == 1 && mfa::split_decode_supported(dtype, D, Lq, group)) return MFA_PATH_SPLIT_DECODE;
+    if (mfa::mfma_prefill_supported(dtype, D)) return MFA_PATH_MFMA;
+    return MFA_PATH_GENERIC;
+}
+
+int words_per_batch(int Lk) { return (Lk + 63) / 64; }
+
+size_t mask_words_bytes(int B, int Lk) { return align256((size_t)B * words_per_batch(Lk) * 8); }
+
+size_t workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype, int path, int splits) {
+    size_t ws = mask_words_bytes(B, Lk);
+    if (path == MFA_PATH_SPLIT_DECODE) {
+        (void)Lq; (void)dtype;
+        ws += align256(mfa::split_decode_workspace_bytes(B, Hq, D, splits));
+    }
+    (void)Hkv;
+    return ws;
+}
+
+std::once_flag g_pool_once[64];
+
+// Keep freed workspace in the device's default pool instead of returning it
+// to the driver after every call.
+void prepare_pool(int dev) {
+    if (dev < 0 || dev >= 64) return;
+    std::call_once(g_pool_once[dev], [dev]() {
+        hipMemPool_t pool;
+        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t thr = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        }
+    });
+}
+
+int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    int st = validate(c);
+    if (st != MFA_SUCCESS) return st;
+    if (c.B == 0 || c.Lq == 0) return MFA_SUCCESS;
+
+    const int group = c.Hq / c.Hkv;
+    if (path == MFA_PATH_AUTO) path = auto_path(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D, c.dtype);
+    switch (path) {
+        case MFA_PATH_GENERIC: break;
+        case MFA_PATH_MFMA:
+            if (!mfa::mfma_prefill_supported(c.dtype, c.D))
+                return fail(MFA_ERROR_NOT_SUPPORTED, "MFMA path needs fp16/bf16 and D in {64,128}");
+            break;
+        case MFA_PATH_SPLIT_DECODE:
+            if (!mfa::split_decode_supported(c.dtype, c.D, c.Lq, group))
+                return fail(MFA_ERROR_NOT_SUPPORTED,
+                            "split decode needs Lq = 1, fp16/bf16, D in {64,128} and Hq/Hkv <= 16");
+            if (splits <= 0) splits = mfa::split_decode_default_splits(c.B, c.Hkv, c.Lk, group);
+            if (splits > c.Lk) splits = c.Lk;
+            break;
+        default: return fail(MFA_ERROR_NOT_SUPPORTED, "unknown path %d", path);
+    }
+
+    const size_t need = workspace_bytes(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D, c.dtype, path, splits);
+    const bool use_pool = workspace == nullptr && ws_bytes == 0;
+    if (!use_pool) {
+        if (!workspace) return fail(MFA_ERROR_INVALID_VALUE, "workspace is null but ws_bytes > 0");
+        if (!aligned(workspace, 256)) return fail(MFA_ERROR_INVALID_VALUE, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(MFA_ERROR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    }
+
+    mfa::FwdArgs a{};
+    a.q = c.q; a.k = c.k; a.v = c.v; a.out = c.out; a.lse = c.lse;
+    a.key_mask = c.key_mask;
+    a.B = c.B; a.Lq = c.Lq; a.Lk = c.Lk; a.Hq = c.Hq; a.Hkv = c.Hkv; a.D = c.D;
+    a.group = group;
+    a.causal = c.causal ? 1 : 0;
+    a.window = c.window > 0 ? c.window : 0;
+    a.q_offset = c.q_offset;
+    a.words_per_batch = words_per_batch(c.Lk);
+    a.scale = c.scale;
+    a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
+    const float log2e = 1.4426950408889634f;
+    a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * c.scale;
+
+    const bool needs_ws = c.key_mask != nullptr || path == MFA_PATH_SPLIT_DECODE;
+    void* ws = workspace;
+    if (needs_ws && use_pool) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
+        prepare_pool(dev);
+        hipError_t e = hipMallocAsync(&ws, need, stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
+                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
+        }
+    }
+    char* wsb = static_cast<char*>(ws);
+    hipError_t e = hipSuccess;
+    if (c.key_mask) {
+        a.mask_words = reinterpret_cast<const uint64_t*>(wsb);
+        e = mfa::launch_mask_words(a, reinterpret_cast<uint64_t*>(wsb), stream);
+    }
+    if (e == hipSuccess) {
+        switch (path) {
+            case MFA_PATH_GENERIC: e = mfa::launch_generic(a, c.dtype, stream); break;
+            case MFA_PATH_MFMA: e = mfa::launch_mfma_prefill(a, c.dtype, stream); break;
+            case MFA_PATH_SPLIT_DECODE:
+                e = mfa::launch_split_decode(a, c.dtype, splits,
+                                             reinterpret_cast<float*>(wsb + mask_words_bytes(c.B, c.Lk)),
+                                             stream);
+                break;
+        }
+    }
+    if (needs_ws && use_pool) {
+        hipError_t e2 = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return MFA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+            int B, int Lq, int Lk, int Hq, int Hkv, int D,
+            float scale, int causal, int window, int q_offset, float softcap,
+            const float* key_mask, int dtype, void* stream) {
+    g_last_error.clear();
+    Call c{q, k, v, out, lse, B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap, key_mask, dtype};
+    return run(c, MFA_PATH_AUTO, 0, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+size_t mfa_fwd_workspace_size(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype) {
+    if (B <= 0 || Lq <= 0 || Lk <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return 0;
+    const int path = auto_path(B, Lq, Lk, Hq, Hkv, D, dtype);
+    const int splits = path == MFA_PATH_SPLIT_DECODE
+                           ? mfa::split_decode_default_splits(B, Hkv, Lk, Hq / Hkv) : 0;
+    return workspace_bytes(B, Lq, Lk, Hq, Hkv, D, dtype, path, splits > Lk ? Lk : splits);
+}
+
+int mfa_fwd_ws(const void* q, const void* k, const void* v, void* out, float* lse,
+               int B, int Lq, int Lk, int Hq, int Hkv, int D,
+               float scale, int causal, int window, int q_offset, float softcap,
+               const float* key_mask, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    Call c{q, k, v, out, lse, B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap, key_mask, dtype};
+    if (!workspace && ws_bytes == 0) {
+        // nothing given: valid only when the plan needs no workspace
+        if (mfa_fwd_workspace_size(B, Lq, Lk, Hq, Hkv, D, dtype) > 0 &&
+            (key_mask || auto_path(B, Lq, Lk, Hq, Hkv, D, dtype) == MFA_PATH_SPLIT_DECODE))
+            return fail(MFA_ERROR_INVALID_VALUE, "this call needs a workspace");
+    }
+    return run(c, MFA_PATH_AUTO, 0, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int mfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+               int B, int Lq, int Lk, int Hq, int Hkv, int D,
+               float scale, int causal, int window, int q_offset, float softcap,
+               const float* key_mask, int dtype, int path, int splits,
+               void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    Call c{q, k, v, out, lse, B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap, key_mask, dtype};
+    return run(c, path, splits, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int mfa_fwd_plan(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype, int* splits) {
+    int s = 0;
+    int path = MFA_PATH_GENERIC;
+    if (Hkv > 0 && Hq > 0 && Hq % Hkv == 0) {
+        path = auto_path(B, Lq, Lk, Hq, Hkv, D, dtype);
+        if (path == MFA_PATH_SPLIT_DECODE) {
+            s = mfa::split_decode_default_splits(B, Hkv, Lk, Hq / Hkv);
+            if (s > Lk) s = Lk;
+        }
+    }
+    if (splits) *splits = s;
+    return path;
+}
+
+const char* mfa_status_string(int status) {
+    switch (status) {
+        case MFA_SUCCESS: return "success";
+        case MFA_ERROR_INVALID_VALUE: return "invalid value";
+        case MFA_ERROR_NOT_SUPPORTED: return "not supported";
+        case MFA_ERROR_HIP: return "HIP error";
+        case MFA_ERROR_OUT_OF_MEMORY: return "out of memory";
+    }
+    return "unknown status";
+}
+
+const char* mfa_last_error(void) { return g_last_error.c_str(); }
+
+int mfa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// mfa_internal.h -- kernel arguments, key-range arithmetic and launchers
+// shared by the libmfa host code and its HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfa {
+
+enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Everything a forward kernel needs, passed by value as one kernel argument.
+struct FwdArgs {
+    const void* q;            // [B, Lq, Hq, D]
+    const void* k;            // [B, Lk, Hkv, D]
+    const void* v;            // [B, Lk, Hkv, D]
+    void* out;                // [B, Lq, Hq, D]
+    float* lse;               // [B, Hq, Lq] or null
+    const float* key_mask;    // [B, Lk] or null
+    const uint64_t* mask_words;  // [B, words_per_batch]: bit t of word w = key 64w+t kept
+    int B, Lq, Lk, Hq, Hkv, D;
+    int group;                // Hq / Hkv
+    int causal, window, q_offset;
+    int words_per_batch;      // ceil(Lk / 64)
+    float scale;              // applied to Q.K
+    float softcap;            // <= 0: off
+    float score_to_log2;      // log2(e) * scale when the cap is off, log2(e) otherwise
+};
+
+// Keys [lo, hi] (inclusive) in range for a query at absolute position aq,
+// before the key mask.  Causal: keys up to aq and, with a window, no earlier
+// than aq - window + 1.  Bidirectional with a window: window/2 keys on either
+// side.  window <= 0: no window.  Both bounds are nondecreasing in aq, so the
+// range of a block of consecutive queries is [lo(first), hi(last)].
+__host__ __device__ inline void key_range(int aq, int Lk, int causal, int window,
+                                          int& lo, int& hi) {
+    if (causal) {
+        hi = aq;
+        lo = window > 0 ? aq - window + 1 : 0;
+    } else if (window > 0) {
+        lo = aq - window / 2;
+        hi = aq + window / 2;
+    } else {
+        lo = 0;
+        hi = Lk - 1;
+    }
+    if (lo < 0) lo = 0;
+    if (hi > Lk - 1) hi = Lk - 1;
+}
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s);
+hipError_t launch_generic(const FwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s);
+bool mfma_prefill_supported(int dtype, int D);
+hipError_t launch_split_decode(const FwdArgs& a, int dtype, int splits, float* partials,
+                               hipStream_t s);
+bool split_decode_supported(int dtype, int D, int Lq, int group);
+int split_decode_default_splits(int B, int Hkv, int Lk, int group);
+size_t split_decode_workspace_bytes(int B, int Hq, int D, int splits);
+
+}  // namespace mfa
