@@ -1,0 +1,94 @@
+// mfa_device.h -- device-side helpers shared by the MFMA kernels: vector
+// types, MFMA wrappers, conversions, LDS swizzles and the soft-cap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
+// 16 raw bytes as a native vector (kept in registers; HIP's uint4 struct is not)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Element-type traits: storage type, 8-wide MFMA operand type and the MFMAs.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+    typedef bf16x8_t v8;
+    static __device__ inline f32x4_t mma16(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ inline f32x16_t mma32(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mfma<_Float16> {
+    typedef f16x8_t v8;
+    static __device__ inline f32x4_t mma16(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ inline f32x16_t mma32(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename V, typename S>
+__device__ inline V bitcast(S s) {
+    static_assert(sizeof(V) == sizeof(S), "size mismatch");
+    V v;
+    __builtin_memcpy(&v, &s, sizeof(V));
+    return v;
+}
+
+// Eight fp32 values rounded to nearest-even into one MFMA operand.
+template <typename T>
+__device__ inline typename Mfma<T>::v8 pack8(const float* x) {
+    typename Mfma<T>::v8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = static_cast<T>(x[e]);
+    return r;
+}
+
+// Transposing LDS read: within each group of 16 lanes, source lane j supplies
+// the address of 4 consecutive 16-bit elements; result lane i element e is
+// element (i % 4) of source lane 4e + i/4.  With source lane j pointing at
+// row (j / 4), columns 4 (j % 4) .. +3 of a row-major block, lane i receives
+// column i of the 4 rows.
+__device__ inline i16x4_t lds_read_tr16(const void* lds_ptr) {
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// c * tanh(s / c) through tanh(y) = 1 - 2 / (exp(2y) + 1), with the hardware
+// base-2 exponential.  Saturates correctly at both ends (exp2 -> inf or 0).
+__device__ inline float softcap_apply(float s, float cap, float two_log2e_over_cap) {
+    const float e = fast_exp2(s * two_log2e_over_cap);
+    return cap - 2.0f * cap * fast_rcp(e + 1.0f);
+}
+
+// LDS swizzles for a [rows][D] tile of 16-bit elements stored as 16-byte
+// chunks (D/8 chunks per row).  The chunk index is XOR-ed with a function of
+// the row so that the access patterns of the kernels hit distinct banks.
+//  - K-style (16 consecutive rows, same chunk): chunk ^ row-bits.
+//  - V-style (transposing reads of 2 adjacent chunks from 8 rows): chunk pairs
+//    permuted by row-bits.
+template <int D>
+__device__ inline int swz_k(int row, int chunk) {
+    return D == 128 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
+}
+template <int D>
+__device__ inline int swz_v(int row, int chunk) {
+    return D == 128 ? (chunk ^ ((row & 7) << 1)) : (chunk ^ (((row >> 1) & 3) << 1));
+}
+
+}  // namespace mfa
