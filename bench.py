@@ -1,0 +1,279 @@
+"""Benchmark of the fused attention forward (libmfa) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-decode] [--no-cpu-baseline]
+
+A step is one mfa_fwd call over one batch of synthetic input already resident
+in HBM: the whole forward (tile ranges, Q/K/V staging, Q.K^T, soft-cap and
+masks, online softmax, P.V, normalisation and LSE) for the workload.  The
+default workload is the causal GQA prefill (B=4, L=2048, Hq=32, Hkv=8,
+D=128, bf16); FLOPs count 4*D per visible (query, key) pair and query head.
+The long-cache decode (B=64, Lk=32768, Hq=32, Hkv=8, D=128, bf16; split over
+keys plus combine) is timed in the same run and reported under "decode" in
+HBM GB/s of compulsory traffic.
+
+Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
+average duration comes from HIP events recorded on the launch stream around
+every timed call, and "traffic" is read from the committed rocprofv3 counter
+summary in profiles/ (null when the kernel sources changed since).
+"cpu_baseline" times the fp64 CPU oracle on a bounded row sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (visible pairs) prefill + decode HBM GB/s, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "transformer_mfa_fwd_amd", "csrc")
+
+
+# ---------------------------------------------------------------------------
+# work accounting
+# ---------------------------------------------------------------------------
+
+def visible_pairs(w, key_mask_cpu) -> int:
+    """Visible (query row, key) pairs summed over batches and query heads,
+    from the key-range bounds and prefix sums of the key mask."""
+    i = np.arange(w.Lq, dtype=np.int64)
+    aq = i + w.q_offset
+    if w.causal:
+        hi = aq.copy()
+        lo = aq - w.window + 1 if w.window > 0 else np.zeros_like(aq)
+    elif w.window > 0:
+        lo, hi = aq - w.window // 2, aq + w.window // 2
+    else:
+        lo, hi = np.zeros_like(aq), np.full_like(aq, w.Lk - 1)
+    lo = np.clip(lo, 0, None)
+    hi = np.clip(hi, None, w.Lk - 1)
+    total = 0
+    for b in range(w.B):
+        if key_mask_cpu is None:
+            cnt = np.clip(hi - lo + 1, 0, None)
+        else:
+            keep = (key_mask_cpu[b].numpy() > 0.5).astype(np.int64)
+            pre = np.concatenate([[0], np.cumsum(keep)])
+            cnt = np.where(hi >= lo, pre[np.clip(hi + 1, 0, w.Lk)] - pre[np.clip(lo, 0, w.Lk)], 0)
+        total += int(cnt.sum())
+    return total * w.Hq
+
+
+def algorithmic_bytes(w, q) -> int:
+    """Compulsory HBM traffic: read Q, K, V (and the mask), write O and LSE."""
+    es = q.element_size()
+    n = (w.B * w.Lq * w.Hq * w.D * 2 + w.B * w.Lk * w.Hkv * w.D * 2) * es + w.B * w.Hq * w.Lq * 4
+    if w.mask is not None:
+        n += w.B * w.Lk * 4
+    return n
+
+
+def kernel_source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["kernels_mfma.hip", "mfa_device.h", "mfa_internal.h"]
+DECODE_SOURCES = ["kernels_decode.hip", "mfa_device.h", "mfa_internal.h"]
+
+
+def measured_traffic(name: str, sources) -> tuple:
+    """Per-launch HBM bytes from the committed counter summary, if it was taken
+    on the current kernel sources; else (None, reason)."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(sources):
+        return None, "kernel changed since counters were taken"
+    return rec.get("traffic_bytes_per_launch"), rec.get("note", "")
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def time_workload(w, steps: int, warmup: int, seed: int = 0):
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    q, k, v, m = wl.make_inputs(w, "cuda", seed)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=q.device)
+    kw = dict(causal=w.causal, window=w.window, q_offset=w.q_offset, softcap=w.softcap,
+              key_mask=m, scale=w.scale, out=out, lse=lse)
+    for _ in range(warmup):
+        mfa.fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        mfa.fwd(q, k, v, **kw)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per_call = [s.elapsed_time(e) for s, e in ev]
+    res = dict(wall_ms=wall_ms, event_ms_avg=float(np.mean(per_call)),
+               event_ms_min=float(np.min(per_call)), event_ms_median=float(np.median(per_call)),
+               path=mfa.plan(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)[0],
+               pairs=visible_pairs(w, None if m is None else m.cpu()),
+               bytes=algorithmic_bytes(w, q))
+    return res, (q, k, v, m)
+
+
+def cpu_baseline(w, tensors, target_s: float = 12.0, seed: int = 0):
+    """Time the fp64 oracle on a seeded sample of query rows of the workload."""
+    from oracle import default_oracle
+    q, k, v, m = tensors
+    orc = default_oracle()
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    qc, kc, vc = (t.float().cpu() for t in (q, k, v))
+    mc = None if m is None else m.cpu()
+    rng = np.random.default_rng(seed)
+    b, h, i = np.meshgrid(np.arange(w.B), np.arange(w.Hq), np.arange(w.Lq), indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)[rng.permutation(w.B * w.Hq * w.Lq)]
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, q_offset=w.q_offset,
+              softcap=w.softcap, key_mask=mc, nthreads=cores)
+    # calibrate on a small prefix, then size the sample for ~target_s seconds
+    n_cal = min(len(rows), 64 * cores)
+    t0 = time.perf_counter()
+    _, _, nv = orc.rows(qc, kc, vc, rows[:n_cal], **kw)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(len(rows), max(n_cal, n_cal * target_s / dt)))
+    sample = rows[:n]
+    t0 = time.perf_counter()
+    _, _, nv = orc.rows(qc, kc, vc, sample, **kw)
+    dt = time.perf_counter() - t0
+    pairs = int(nv.sum())
+    return {"value": 4.0 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} of {len(rows)} query rows (seeded shuffle), {pairs} visible pairs, "
+                      f"{dt:.1f} s, fp64 C oracle with {cores} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_causal_prefill_bf16")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every call runs on one device); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": args.steps}))
+        return
+
+    match = [x for x in wl.ALL if x.name.startswith(args.workload)]
+    if not match:
+        raise SystemExit(f"unknown workload {args.workload}; choose from {[x.name for x in wl.ALL]}")
+    w = match[0]
+
+    res, tensors = time_workload(w, args.steps, args.warmup)
+    flops = 4.0 * w.D * res["pairs"]
+    tflops_wall = flops / (res["wall_ms"] * 1e-3) / 1e12
+    kern_ms = res["event_ms_avg"]
+    is_prefill = res["path"] in ("mfma", "generic")
+    traffic, tnote = measured_traffic(f"{'prefill' if is_prefill else 'decode'}_{w.name}.counters.json",
+                                      PREFILL_SOURCES if is_prefill else DECODE_SOURCES)
+    if is_prefill:
+        roof = {"bound": "mfma", "achieved": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(res["bytes"] / (kern_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic
+    roof["kernel"] = {"mfma": "prefill_kernel", "generic": "generic_fwd_kernel",
+                      "split_decode": "decode_split_kernel + decode_combine_kernel"}[res["path"]]
+    roof["kernel_ms_avg"] = round(kern_ms, 5)
+    roof["algorithmic_flops_per_launch"] = flops
+    roof["algorithmic_bytes_per_launch"] = res["bytes"]
+    if traffic is None:
+        roof["traffic_note"] = tnote
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops_wall if is_prefill else res["bytes"] / (res["wall_ms"] * 1e-3) / 1e9, 2),
+        "unit": "TFLOP/s" if is_prefill else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["wall_ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Lq": w.Lq, "Lk": w.Lk, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "causal": w.causal, "window": w.window, "softcap": w.softcap,
+                   "key_mask": w.mask, "path": res["path"], "visible_pairs": res["pairs"]},
+        "roofline": roof,
+    }
+
+    if not args.no_decode and w is not wl.LONG_CACHE_DECODE_BF16:
+        del tensors
+        torch.cuda.empty_cache()
+        wd = wl.LONG_CACHE_DECODE_BF16
+        rd, td = time_workload(wd, max(10, args.steps // 2), max(3, args.warmup // 2))
+        dtraffic, dnote = measured_traffic(f"decode_{wd.name}.counters.json", DECODE_SOURCES)
+        dk = rd["event_ms_avg"]
+        line["decode"] = {
+            "workload": wd.name, "path": rd["path"], "unit": "GB/s",
+            "value": round(rd["bytes"] / (rd["wall_ms"] * 1e-3) / 1e9, 1),
+            "ms_per_step": round(rd["wall_ms"], 5),
+            "roofline": {"bound": "hbm", "achieved": round(rd["bytes"] / (dk * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(rd["bytes"] / (dk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": dtraffic, "kernel_ms_avg": round(dk, 5),
+                         "algorithmic_bytes_per_launch": rd["bytes"]},
+        }
+        if dtraffic is None:
+            line["decode"]["roofline"]["traffic_note"] = dnote
+        del td
+        torch.cuda.empty_cache()
+        tensors = None
+
+    if not args.no_cpu_baseline:
+        if tensors is None:
+            _, tensors = time_workload(w, 1, 0)
+        line["cpu_baseline"] = cpu_baseline(w, tensors)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
