@@ -174,11 +174,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
                     v = vis ? v : -INFINITY;
                 }
                 x[blk * 4 + i] = v;
-                tmax = fmaxf(tmax, v);
+                tmax = fmax_fast(tmax, v);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = fmax_fast(tmax, __shfl_xor(tmax, 16));
+        tmax = fmax_fast(tmax, __shfl_xor(tmax, 32));
         const float m_new = fmaxf(m, tmax);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         const float alpha = fast_exp2(m - m_use);

@@ -38,16 +38,20 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
 
-// swizzle of a [BN][D] tile for the K pattern (32 rows, same chunk) and the
-// V pattern (transposing reads of 4 rows x 4 chunks per half wave)
-template <int D>
-__device__ inline int pf_swz_k(int row, int chunk) {
-    return D == 128 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
-}
-template <int D>
-__device__ inline int pf_swz_v(int row, int chunk) {
-    return D == 128 ? (chunk ^ ((row & 3) << 2)) : (chunk ^ (((row >> 1) & 1) << 2));
-}
+// Padded LDS rows.  K rows are D*2 + 16 bytes apart: the 32 lanes that read
+// one 16-byte chunk from 32 consecutive rows start 4 banks apart, so each
+// group of 16 rows covers all 64 banks once.  V rows are D*2 + 64 bytes apart:
+// a transposing read takes 64 bytes from each of 4 consecutive rows per half
+// wave, and those rows start 16 banks apart.  With padding (instead of an XOR
+// swizzle) every LDS read is a per-lane base plus a compile-time offset.
+template <int D> struct PfLds {
+    static constexpr int KS = D * 2 + 16;         // K row stride, bytes
+    static constexpr int VS = D * 2 + 64;         // V row stride, bytes
+    static constexpr int KT = BN * KS;            // one K tile
+    static constexpr int VT = BN * VS;            // one V tile
+    static constexpr int BUF = KT + VT;           // one stage
+    static constexpr int BYTES = 2 * BUF;         // double buffered
+};
 
 __device__ inline int remap_xcd(int p, int n) {
     const int per = n / 8;
@@ -64,12 +68,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
     typedef typename Mfma<T>::v8 v8;
     constexpr float LOG2E = 1.4426950408889634f;
 
-    __shared__ u32x4_t sK[2][BN * CPR];
-    __shared__ u32x4_t sV[2][BN * CPR];
+    typedef PfLds<D> L;
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lq = lane & 31;               // query row within the wave
     const int h2 = lane >> 5;               // lane half
 
@@ -127,156 +131,184 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
     float m = -INFINITY;   // running max (base 2) of this lane's row
     float l = 0.0f;        // this lane's half of the running sum
 
-    const float c_log2 = a.score_to_log2;
-    const float two_log2e_over_cap = CAP ? 2.0f * LOG2E / a.softcap : 0.0f;
+    const float c_log2 = a.score_to_log2;                       // scale * log2(e)
+    const float cap_arg = CAP ? 2.0f * LOG2E * a.scale / a.softcap : 0.0f;
+    const float cap_l2 = CAP ? a.softcap * LOG2E : 0.0f;
+    const float two_cap_l2 = 2.0f * cap_l2;
 
     int kt_lo = 0, kt_hi = -1;
     if (lo_blk <= hi_blk) { kt_lo = lo_blk / BN; kt_hi = hi_blk / BN; }
+
+    // per-thread offsets of its LPT (row, chunk) pieces of a tile: in global
+    // memory (elements, relative to the tile's first row) and in LDS (bytes)
+    int ld_off[LPT], ld_row[LPT], st_k[LPT], st_v[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+        const int idx = tid + 256 * i;
+        const int r = idx / CPR, c = idx % CPR;
+        ld_row[i] = r;
+        ld_off[i] = r * (int)kv_stride + c * 8;
+        st_k[i] = r * L::KS + c * 16;
+        st_v[i] = L::KT + r * L::VS + c * 16;
+    }
+    // per-lane LDS read bases (bytes within a stage)
+    //  K (A operand): row 32 kb + lq, chunk 2 ks + h2
+    const int rd_k = lq * L::KS + h2 * 16;
+    //  V (transposing read): rows 32 kb + 16 hh + 4 h2 + j/4 (+8), 16 d-columns
+    //  32 db + 16 (group & 1) + 4 (j & 3) .. +3
+    const int grp16 = lane >> 4, j16 = lane & 15;
+    const int rd_v = L::KT + (h2 * 4 + (j16 >> 2)) * L::VS + (grp16 & 1) * 32 + (j16 & 3) * 8;
 
     u32x4_t kreg[LPT], vreg[LPT];
     int t = kt_lo;
     if (MASK) while (t <= kt_hi && words[t] == 0ull) ++t;
 
-    // prologue: first tile into buffer 0
     if (t <= kt_hi) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            int key = t * BN + r;
-            key = key < a.Lk ? key : a.Lk - 1;
-            const int64_t off = (int64_t)key * kv_stride + c * 8;
-            kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-            vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
-        }
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / CPR, c = idx % CPR;
-            sK[0][r * CPR + pf_swz_k<D>(r, c)] = kreg[i];
-            sV[0][r * CPR + pf_swz_v<D>(r, c)] = vreg[i];
-        }
-    }
-    __syncthreads();
-
-    int cur = 0;
-    while (t <= kt_hi) {
-        int tn = t + 1;
-        if (MASK) while (tn <= kt_hi && words[tn] == 0ull) ++tn;
-        const bool more = tn <= kt_hi;
-        if (more) {
+        // prologue: first tile into stage 0
+        {
+            const int64_t tb = (int64_t)t * BN * kv_stride;
+            const bool full = t * BN + BN <= a.Lk;
 #pragma unroll
             for (int i = 0; i < LPT; ++i) {
-                const int idx = tid + 256 * i;
-                const int r = idx / CPR, c = idx % CPR;
-                int key = tn * BN + r;
-                key = key < a.Lk ? key : a.Lk - 1;
-                const int64_t off = (int64_t)key * kv_stride + c * 8;
-                kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-                vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+                int off = ld_off[i];
+                if (!full && t * BN + ld_row[i] >= a.Lk) off -= (t * BN + ld_row[i] - (a.Lk - 1)) * (int)kv_stride;
+                kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + tb + off);
+                vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + tb + off);
             }
-        }
-
-        const int k0 = t * BN;
-        const uint64_t word = MASK ? words[t] : ~0ull;
-        const bool interior = k0 >= wlo_last && k0 + BN - 1 <= whi_first && (!MASK || word == ~0ull);
-
-        // ---- S^T = K Q^T for two 32-key blocks
-        f32x16_t sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
-            const int r = kb * 32 + lq;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const v8 kop = bitcast<v8>(sK[cur][r * CPR + pf_swz_k<D>(r, ks * 2 + h2)]);
-                sacc[kb] = Mfma<T>::mma32(kop, qop[ks], sacc[kb]);
-            }
-        }
-
-        // ---- scores -> base-2 logits, masking, running max
-        // sacc[kb][4 j + i] is key k0 + 32 kb + 8 j + 4 h2 + i of row qrow
-        float x[32];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float v = sacc[kb][e];
-                if (CAP) v = softcap_apply(v * a.scale, a.softcap, two_log2e_over_cap) * LOG2E;
-                else v = v * c_log2;
-                if (!interior) {
-                    const int kk = kb * 32 + (e >> 2) * 8 + h2 * 4 + (e & 3);
-                    const int key = k0 + kk;
-                    bool vis = key >= rlo && key <= rhi;
-                    if (MASK) vis = vis && ((word >> kk) & 1ull);
-                    v = vis ? v : -INFINITY;
-                }
-                x[kb * 16 + e] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        m = m_new;
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            x[e] = fast_exp2(x[e] - m_use);
-            psum += x[e];
-        }
-        l = l * alpha + psum;
-        // rescale the accumulator only when some row's max moved
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-        }
-
-        // ---- O^T += V^T P^T, four 16-key steps
-        const int grp16 = lane >> 4;        // 16-lane group
-        const int j16 = lane & 15;          // source lane within the group
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int kb = st >> 1, hh = st & 1;
-            float pv[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pv[i] = x[kb * 16 + (2 * hh) * 4 + i];
-                pv[4 + i] = x[kb * 16 + (2 * hh + 1) * 4 + i];
-            }
-            const v8 pop = pack8<T>(pv);
-            const int r0 = kb * 32 + hh * 16 + h2 * 4 + (j16 >> 2);
-            const int r1 = r0 + 8;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int chunk = db * 4 + (grp16 & 1) * 2 + ((j16 & 3) >> 1);
-                const int half = (j16 & 1) * 8;
-                const char* p0 = reinterpret_cast<const char*>(&sV[cur][r0 * CPR + pf_swz_v<D>(r0, chunk)]) + half;
-                const char* p1 = reinterpret_cast<const char*>(&sV[cur][r1 * CPR + pf_swz_v<D>(r1, chunk)]) + half;
-                const i16x4_t lo4 = lds_read_tr16(p0);
-                const i16x4_t hi4 = lds_read_tr16(p1);
-                const i16x8_t vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                oacc[db] = Mfma<T>::mma32(bitcast<v8>(vv), pop, oacc[db]);
-            }
-        }
-
-        if (more) {
 #pragma unroll
             for (int i = 0; i < LPT; ++i) {
-                const int idx = tid + 256 * i;
-                const int r = idx / CPR, c = idx % CPR;
-                sK[cur ^ 1][r * CPR + pf_swz_k<D>(r, c)] = kreg[i];
-                sV[cur ^ 1][r * CPR + pf_swz_v<D>(r, c)] = vreg[i];
+                *reinterpret_cast<u32x4_t*>(smem + st_k[i]) = kreg[i];
+                *reinterpret_cast<u32x4_t*>(smem + st_v[i]) = vreg[i];
             }
         }
         __syncthreads();
-        cur ^= 1;
-        t = tn;
+
+        int cur = 0;
+        while (true) {
+            int tn = t + 1;
+            if (MASK) while (tn <= kt_hi && words[tn] == 0ull) ++tn;
+            const bool more = tn <= kt_hi;
+            if (more) {
+                const int64_t tb = (int64_t)tn * BN * kv_stride;
+                const bool full = tn * BN + BN <= a.Lk;
+#pragma unroll
+                for (int i = 0; i < LPT; ++i) {
+                    int off = ld_off[i];
+                    if (!full && tn * BN + ld_row[i] >= a.Lk)
+                        off -= (tn * BN + ld_row[i] - (a.Lk - 1)) * (int)kv_stride;  // clamp; masked below
+                    kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + tb + off);
+                    vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + tb + off);
+                }
+            }
+            const char* stage = smem + cur * L::BUF;
+
+            const int k0 = t * BN;
+            const uint64_t word = MASK ? words[t] : ~0ull;
+            // uniform across the wave: every row of the wave sees every key of the tile
+            const bool interior = __builtin_amdgcn_readfirstlane(
+                (k0 >= wlo_last && k0 + BN - 1 <= whi_first && (!MASK || word == ~0ull)) ? 1 : 0);
+
+            // ---- S^T = K Q^T for two 32-key blocks
+            f32x16_t sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const v8 kop = bitcast<v8>(
+                        *reinterpret_cast<const u32x4_t*>(stage + rd_k + kb * 32 * L::KS + ks * 32));
+                    sacc[kb] = Mfma<T>::mma32(kop, qop[ks], sacc[kb]);
+                }
+            }
+
+            // ---- scores: sacc[kb][4 j + i] is key k0 + 32 kb + 8 j + 4 h2 + i of row qrow.
+            // Without a cap the base-2 logit is s * c_log2, folded into the exponent below;
+            // with a cap it is cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1).
+            float x[32];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float v = sacc[kb][e];
+                    if (CAP) v = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(v * cap_arg) + 1.0f);
+                    x[kb * 16 + e] = v;
+                }
+            if (!interior) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int kk = kb * 32 + (e >> 2) * 8 + h2 * 4 + (e & 3);
+                        const int key = k0 + kk;
+                        bool vis = key >= rlo && key <= rhi;
+                        if (MASK) vis = vis && ((word >> kk) & 1ull);
+                        x[kb * 16 + e] = vis ? x[kb * 16 + e] : -INFINITY;
+                    }
+            }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 32; e += 2) tmax = fmax_fast(fmax_fast(tmax, x[e]), x[e + 1]);
+            tmax = fmax_fast(tmax, __shfl_xor(tmax, 32));
+            const float tmax_l2 = CAP ? tmax : tmax * c_log2;   // base-2 logit units
+
+            // Lazy rescale: the running max only moves when a tile's max exceeds
+            // it by more than 8 (base 2), so every weight 2^(x - m) stays <= 256
+            // and the accumulator is rescaled rarely.  Exact after O = acc / l.
+            const bool grow = tmax_l2 > m + 8.0f;
+            if (__any(grow)) {
+                // rows that do not grow keep alpha = 1 (m may still be -inf there)
+                const float alpha = grow ? fast_exp2(m - tmax_l2) : 1.0f;   // 0 when m = -inf
+                m = grow ? tmax_l2 : m;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            }
+            const float m_use = m == -INFINITY ? 0.0f : m;
+            float psum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                x[e] = CAP ? fast_exp2(x[e] - m_use) : fast_exp2(fmaf(x[e], c_log2, -m_use));
+                psum += x[e];
+            }
+            l += psum;
+
+            // ---- O^T += V^T P^T, four 16-key steps
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int kb = st >> 1, hh = st & 1;
+                float pv[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pv[i] = x[kb * 16 + (2 * hh) * 4 + i];
+                    pv[4 + i] = x[kb * 16 + (2 * hh + 1) * 4 + i];
+                }
+                const v8 pop = pack8<T>(pv);
+                const char* vb = stage + rd_v + (kb * 32 + hh * 16) * L::VS;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const i16x4_t lo4 = lds_read_tr16(vb + db * 64);
+                    const i16x4_t hi4 = lds_read_tr16(vb + 8 * L::VS + db * 64);
+                    const i16x8_t vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                    oacc[db] = Mfma<T>::mma32(bitcast<v8>(vv), pop, oacc[db]);
+                }
+            }
+
+            if (more) {
+                char* nstage = smem + (cur ^ 1) * L::BUF;
+#pragma unroll
+                for (int i = 0; i < LPT; ++i) {
+                    *reinterpret_cast<u32x4_t*>(nstage + st_k[i]) = kreg[i];
+                    *reinterpret_cast<u32x4_t*>(nstage + st_v[i]) = vreg[i];
+                }
+            }
+            __syncthreads();
+            if (!more) break;
+            cur ^= 1;
+            t = tn;
+        }
     }
 
     // ---- epilogue: normalise, round, store; LSE in natural log

@@ -67,6 +67,9 @@ __device__ inline i16x4_t lds_read_tr16(const void* lds_ptr) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// IEEE maximum (gfx950 v_maximum3_f32 for chains); unlike fmaxf it needs no
+// canonicalisation of its operands.  Scores are finite or -inf.
+__device__ inline float fmax_fast(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // c * tanh(s / c) through tanh(y) = 1 - 2 / (exp(2y) + 1), with the hardware
