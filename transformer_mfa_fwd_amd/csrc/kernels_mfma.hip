@@ -9,14 +9,17 @@
 //
 // Work decomposition.  One 256-thread workgroup owns 128 query rows of one
 // query head; its four waves own 32 rows each.  64-key tiles of K and V are
-// staged, double buffered, in XOR-swizzled LDS through coalesced 16-byte
-// loads.  Per wave and tile:
+// copied straight from HBM into XOR-swizzled LDS (global_load_lds_dwordx4, no
+// register staging), two stages each.  Per wave and tile:
 //   S^T[32 keys x 32 q] = K . Q^T            v_mfma_f32_32x32x16, Q^T in VGPRs
 //     -> lane l holds 16 keys of query row (l % 32): the row max is an in-lane
 //        max plus one exchange with lane l ^ 32
 //   O^T[32 d x 32 q] += V^T . P^T            v_mfma_f32_32x32x16; P^T is the
 //        score accumulator (rounded to the input type), V^T comes from the
 //        transposing LDS read, so no score ever leaves the registers.
+// The next tile's copy is in flight while the current one is computed; the
+// two workgroups resident per CU interleave softmax (VALU) with MFMA work.
+//
 // Only tiles that intersect the key range of the workgroup's rows are visited
 // (causal and window bounds), tiles whose key-mask word is zero are skipped
 // without loading K or V, and per-element masking runs only on tiles that are
@@ -38,19 +41,23 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
 
-// Padded LDS rows.  K rows are D*2 + 16 bytes apart: the 32 lanes that read
-// one 16-byte chunk from 32 consecutive rows start 4 banks apart, so each
-// group of 16 rows covers all 64 banks once.  V rows are D*2 + 64 bytes apart:
-// a transposing read takes 64 bytes from each of 4 consecutive rows per half
-// wave, and those rows start 16 banks apart.  With padding (instead of an XOR
-// swizzle) every LDS read is a per-lane base plus a compile-time offset.
+// LDS layout of one stage: K tile then V tile, each [BN rows][D] of 16-bit
+// elements stored as 16-byte chunks, row-major without padding (a direct
+// global->LDS load writes 1 KiB contiguously per wave instruction).  The
+// chunk index is XOR-swizzled with row bits:
+//  - K: 32 lanes read one chunk from 32 consecutive rows; XOR with the row's
+//    low bits spreads 16 rows over all 64 banks.
+//  - V: a transposing read takes 64 bytes from each of 4 consecutive rows per
+//    half wave; XOR moves those rows into different 64-byte bank groups.
 template <int D> struct PfLds {
-    static constexpr int KS = D * 2 + 16;         // K row stride, bytes
-    static constexpr int VS = D * 2 + 64;         // V row stride, bytes
-    static constexpr int KT = BN * KS;            // one K tile
-    static constexpr int VT = BN * VS;            // one V tile
-    static constexpr int BUF = KT + VT;           // one stage
-    static constexpr int BYTES = 2 * BUF;         // double buffered
+    static constexpr int CPR = D / 8;             // chunks per row
+    static constexpr int RS = D * 2;              // row bytes
+    static constexpr int TILE = BN * RS;          // one K or V tile
+    static constexpr int KST = 0;                 // K stage s at KST + s * TILE
+    static constexpr int VST = 2 * TILE;          // V stage s at VST + s * TILE
+    static constexpr int BYTES = 4 * TILE;
+    static __device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+    static __device__ inline int swz_v(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 };
 
 __device__ inline int remap_xcd(int p, int n) {
@@ -59,23 +66,48 @@ __device__ inline int remap_xcd(int p, int n) {
     return p;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int QK_LA = 4;  // K fragment reads in flight ahead of the MFMA
+
+// fragment f = (key block f / nks, k-step f % nks); compile-time f after unrolling
+template <int RS, int NKS>
+__device__ inline void mfa_qk_issue(u32x4_t (&kf)[2 * NKS], const uint32_t (&ka)[NKS], int f) {
+    const int kb = f / NKS, ks = f % NKS;
+    if (kb == 0) lds_read_b128_asm<0>(kf[f], ka[ks]);
+    else lds_read_b128_asm<32 * RS>(kf[f], ka[ks]);
+}
+template <int LA, int NF>
+__device__ inline void mfa_qk_wait(u32x4_t (&kf)[NF], int f) {
+    // reads issued so far: min(NF, f + LA); those after f may stay in flight
+    const int after = (f + LA < NF ? f + LA : NF) - f - 1;
+    switch (after) {
+        case 0: lds_wait_b128<0>(kf[f]); break;
+        case 1: lds_wait_b128<1>(kf[f]); break;
+        case 2: lds_wait_b128<2>(kf[f]); break;
+        default: lds_wait_b128<3>(kf[f]); break;
+    }
+}
+
 template <typename T, int D, bool CAP, bool MASK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
-    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    typedef PfLds<D> L;
+    constexpr int CPR = L::CPR;
     constexpr int NKS = D / 16;             // k-steps of Q.K^T
     constexpr int NDB = D / 32;             // 32-wide d blocks of O
-    constexpr int LPT = BN * CPR / 256;     // 16-byte loads per thread per tensor
+    constexpr int RPI = 64 / CPR;           // tile rows per DMA instruction
+    constexpr int IPW = BN / RPI / 4;       // DMA instructions per wave per tile
     typedef typename Mfma<T>::v8 v8;
     constexpr float LOG2E = 1.4426950408889634f;
 
-    typedef PfLds<D> L;
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lq = lane & 31;               // query row within the wave
     const int h2 = lane >> 5;               // lane half
+    const int grp16 = lane >> 4, j16 = lane & 15;
 
     // ---- block -> (batch, kv head, q tile, q head)
     const int n = remap_xcd(blockIdx.x, gridDim.x);
@@ -123,6 +155,35 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
         for (int ks = 0; ks < NKS; ++ks) qop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(qp + ks * 16));
     }
 
+    // ---- DMA: instruction i of this wave fills tile rows R..R+RPI-1,
+    // R = (wave * IPW + i) * RPI; lane -> physical (row, chunk), fetching the
+    // logical chunk that the swizzle stores there.
+    int dma_row[IPW], dma_koff[IPW], dma_voff[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int r = (wave * IPW + i) * RPI + lane / CPR;
+        const int pc = lane % CPR;
+        dma_row[i] = r;
+        dma_koff[i] = r * (int)kv_stride + (pc ^ L::swz_k(r)) * 8;
+        dma_voff[i] = r * (int)kv_stride + (pc ^ L::swz_v(r)) * 8;
+    }
+    // per-lane LDS read offsets (bytes, within a K or V tile)
+    //  K (A operand): row 32 kb + lq, logical chunk 2 ks + h2
+    int rd_k[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = lq * L::RS + (((2 * ks + h2) ^ L::swz_k(lq)) * 16);
+    //  V (transposing read): rows 32 kb + 16 hh + 4 h2 + j/4 (and +8),
+    //  d columns 32 db + 16 (group & 1) + 4 (j & 3) .. +3
+    int rd_v[NDB];
+    {
+        const int r0 = h2 * 4 + (j16 >> 2);  // row within the 16-row step (low bits fix the swizzle)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int chunk = db * 4 + (grp16 & 1) * 2 + ((j16 & 3) >> 1);
+            rd_v[db] = r0 * L::RS + ((chunk ^ L::swz_v(r0)) * 16) + (j16 & 1) * 8;
+        }
+    }
+
     f32x16_t oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -139,98 +200,90 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
     int kt_lo = 0, kt_hi = -1;
     if (lo_blk <= hi_blk) { kt_lo = lo_blk / BN; kt_hi = hi_blk / BN; }
 
-    // per-thread offsets of its LPT (row, chunk) pieces of a tile: in global
-    // memory (elements, relative to the tile's first row) and in LDS (bytes)
-    int ld_off[LPT], ld_row[LPT], st_k[LPT], st_v[LPT];
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int idx = tid + 256 * i;
-        const int r = idx / CPR, c = idx % CPR;
-        ld_row[i] = r;
-        ld_off[i] = r * (int)kv_stride + c * 8;
-        st_k[i] = r * L::KS + c * 16;
-        st_v[i] = L::KT + r * L::VS + c * 16;
-    }
-    // per-lane LDS read bases (bytes within a stage)
-    //  K (A operand): row 32 kb + lq, chunk 2 ks + h2
-    const int rd_k = lq * L::KS + h2 * 16;
-    //  V (transposing read): rows 32 kb + 16 hh + 4 h2 + j/4 (+8), 16 d-columns
-    //  32 db + 16 (group & 1) + 4 (j & 3) .. +3
-    const int grp16 = lane >> 4, j16 = lane & 15;
-    const int rd_v = L::KT + (h2 * 4 + (j16 >> 2)) * L::VS + (grp16 & 1) * 32 + (j16 & 3) * 8;
+// next tile at or after x that has a visible key
+#define MFA_NEXT_TILE(x) ({ int _t = (x); if (MASK) while (_t <= kt_hi && words[_t] == 0ull) ++_t; _t; })
 
-    u32x4_t kreg[LPT], vreg[LPT];
-    int t = kt_lo;
-    if (MASK) while (t <= kt_hi && words[t] == 0ull) ++t;
+// copy K (and/or V) rows of tile TT into stage STG with direct global->LDS loads
+#define MFA_DMA(TT, STG, DO_K, DO_V)                                                         \
+    do {                                                                                     \
+        const int _t = (TT);                                                                 \
+        const int64_t _tb = (int64_t)_t * BN * kv_stride;                                    \
+        const bool _full = _t * BN + BN <= a.Lk;                                             \
+        _Pragma("unroll") for (int i = 0; i < IPW; ++i) {                                    \
+            int _clamp = 0;                                                                  \
+            if (!_full && _t * BN + dma_row[i] >= a.Lk)                                      \
+                _clamp = (_t * BN + dma_row[i] - (a.Lk - 1)) * (int)kv_stride;               \
+            char* _dst = smem + (wave * IPW + i) * 1024;                                     \
+            if (DO_K)                                                                        \
+                __builtin_amdgcn_global_load_lds((const void*)(kbase + _tb + dma_koff[i] - _clamp), \
+                    (lds_void_t*)(_dst + L::KST + (STG) * L::TILE), 16, 0, 0);               \
+            if (DO_V)                                                                        \
+                __builtin_amdgcn_global_load_lds((const void*)(vbase + _tb + dma_voff[i] - _clamp), \
+                    (lds_void_t*)(_dst + L::VST + (STG) * L::TILE), 16, 0, 0);               \
+        }                                                                                    \
+    } while (0)
 
-    if (t <= kt_hi) {
-        // prologue: first tile into stage 0
-        {
-            const int64_t tb = (int64_t)t * BN * kv_stride;
-            const bool full = t * BN + BN <= a.Lk;
-#pragma unroll
-            for (int i = 0; i < LPT; ++i) {
-                int off = ld_off[i];
-                if (!full && t * BN + ld_row[i] >= a.Lk) off -= (t * BN + ld_row[i] - (a.Lk - 1)) * (int)kv_stride;
-                kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + tb + off);
-                vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + tb + off);
-            }
-#pragma unroll
-            for (int i = 0; i < LPT; ++i) {
-                *reinterpret_cast<u32x4_t*>(smem + st_k[i]) = kreg[i];
-                *reinterpret_cast<u32x4_t*>(smem + st_v[i]) = vreg[i];
-            }
-        }
+// S^T = K Q^T for the two 32-key blocks of the K tile in stage STG.  The
+// 2*NKS K fragments are read through a rolling window of QK_LA reads in
+// flight, each MFMA waiting only for its own fragment.
+#define MFA_QK(SACC, STG)                                                                    \
+    do {                                                                                     \
+        uint32_t _ka[NKS];                                                                   \
+        _Pragma("unroll") for (int ks = 0; ks < NKS; ++ks)                                   \
+            _ka[ks] = lds_base + L::KST + (STG) * L::TILE + rd_k[ks];                        \
+        u32x4_t _kf[2 * NKS];                                                                \
+        _Pragma("unroll") for (int f = 0; f < QK_LA; ++f) mfa_qk_issue<L::RS, NKS>(_kf, _ka, f); \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
+            _Pragma("unroll") for (int e = 0; e < 16; ++e) SACC[kb][e] = 0.0f;              \
+        _Pragma("unroll") for (int f = 0; f < 2 * NKS; ++f) {                                \
+            mfa_qk_wait<QK_LA, 2 * NKS>(_kf, f);                                             \
+            if (f + QK_LA < 2 * NKS) mfa_qk_issue<L::RS, NKS>(_kf, _ka, f + QK_LA);         \
+            SACC[f / NKS] = Mfma<T>::mma32(bitcast<v8>(_kf[f]), qop[f % NKS], SACC[f / NKS]); \
+        }                                                                                    \
+    } while (0)
+
+// transposing reads of V for 16-key step S (rows 16 S .. 16 S + 15 of the tile)
+#define MFA_TR_ISSUE(S, LO, HI)                                                              \
+    do {                                                                                     \
+        if constexpr (NDB == 4)                                                              \
+            lds_read_tr16_pair4<(S) * 16 * L::RS, (S) * 16 * L::RS + 8 * L::RS>(vaddr, LO, HI); \
+        else                                                                                 \
+            lds_read_tr16_pair2<(S) * 16 * L::RS, (S) * 16 * L::RS + 8 * L::RS>(vaddr, LO, HI); \
+    } while (0)
+
+    const uint32_t lds_base = lds_offset(smem);
+    int tcur = MFA_NEXT_TILE(kt_lo);
+    if (tcur <= kt_hi) {
+        // prologue: K,V of the first tile into stage 0
+        MFA_DMA(tcur, 0, true, true);
         __syncthreads();
 
-        int cur = 0;
+        int st = 0;       // stage of tile tcur
         while (true) {
-            int tn = t + 1;
-            if (MASK) while (tn <= kt_hi && words[tn] == 0ull) ++tn;
-            const bool more = tn <= kt_hi;
-            if (more) {
-                const int64_t tb = (int64_t)tn * BN * kv_stride;
-                const bool full = tn * BN + BN <= a.Lk;
-#pragma unroll
-                for (int i = 0; i < LPT; ++i) {
-                    int off = ld_off[i];
-                    if (!full && tn * BN + ld_row[i] >= a.Lk)
-                        off -= (tn * BN + ld_row[i] - (a.Lk - 1)) * (int)kv_stride;  // clamp; masked below
-                    kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + tb + off);
-                    vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + tb + off);
-                }
-            }
-            const char* stage = smem + cur * L::BUF;
+            const int tnext = MFA_NEXT_TILE(tcur + 1);
+            const bool more = tnext <= kt_hi;
+            // DMA: K,V of the next tile into the other stage (read two steps ago)
+            if (more) MFA_DMA(tnext, st ^ 1, true, true);
 
-            const int k0 = t * BN;
-            const uint64_t word = MASK ? words[t] : ~0ull;
-            // uniform across the wave: every row of the wave sees every key of the tile
+            f32x16_t scur[2];
+            MFA_QK(scur, st);
+
+            // ---- scores -> weights (VALU)
+            const int k0 = tcur * BN;
+            const uint64_t word = MASK ? words[tcur] : ~0ull;
             const bool interior = __builtin_amdgcn_readfirstlane(
                 (k0 >= wlo_last && k0 + BN - 1 <= whi_first && (!MASK || word == ~0ull)) ? 1 : 0);
 
-            // ---- S^T = K Q^T for two 32-key blocks
-            f32x16_t sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const v8 kop = bitcast<v8>(
-                        *reinterpret_cast<const u32x4_t*>(stage + rd_k + kb * 32 * L::KS + ks * 32));
-                    sacc[kb] = Mfma<T>::mma32(kop, qop[ks], sacc[kb]);
-                }
-            }
-
-            // ---- scores: sacc[kb][4 j + i] is key k0 + 32 kb + 8 j + 4 h2 + i of row qrow.
-            // Without a cap the base-2 logit is s * c_log2, folded into the exponent below;
-            // with a cap it is cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1).
+            // scur[kb][4 j + i] is key k0 + 32 kb + 8 j + 4 h2 + i of row qrow.
+            // Without a cap the base-2 logit is s * c_log2, folded into the
+            // exponent below; with a cap it is
+            // cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1).
             float x[32];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    float v = sacc[kb][e];
+                    float v = scur[kb][e];
                     if (CAP) v = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(v * cap_arg) + 1.0f);
                     x[kb * 16 + e] = v;
                 }
@@ -275,41 +328,48 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
             }
             l += psum;
 
-            // ---- O^T += V^T P^T, four 16-key steps
+            // ---- O^T += V^T P^T, four 16-key steps over V stage st.  The
+            // transposing reads of step s+1 are in flight while step s runs on
+            // the matrix cores.
+            {
+                uint32_t vaddr[NDB];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int kb = st >> 1, hh = st & 1;
-                float pv[8];
+                for (int db = 0; db < NDB; ++db) vaddr[db] = lds_base + L::VST + st * L::TILE + rd_v[db];
+                i16x4_t vlo[2][NDB], vhi[2][NDB];
+                MFA_TR_ISSUE(0, vlo[0], vhi[0]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[i] = x[kb * 16 + (2 * hh) * 4 + i];
-                    pv[4 + i] = x[kb * 16 + (2 * hh + 1) * 4 + i];
-                }
-                const v8 pop = pack8<T>(pv);
-                const char* vb = stage + rd_v + (kb * 32 + hh * 16) * L::VS;
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int kb = s4 >> 1, hh = s4 & 1;
+                    float pv[8];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const i16x4_t lo4 = lds_read_tr16(vb + db * 64);
-                    const i16x4_t hi4 = lds_read_tr16(vb + 8 * L::VS + db * 64);
-                    const i16x8_t vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                    oacc[db] = Mfma<T>::mma32(bitcast<v8>(vv), pop, oacc[db]);
+                    for (int i = 0; i < 4; ++i) {
+                        pv[i] = x[kb * 16 + (2 * hh) * 4 + i];
+                        pv[4 + i] = x[kb * 16 + (2 * hh + 1) * 4 + i];
+                    }
+                    const v8 pop = pack8<T>(pv);
+                    lds_wait<NDB>(vlo[s4 & 1], vhi[s4 & 1]);
+                    if (s4 == 0) MFA_TR_ISSUE(1, vlo[1], vhi[1]);
+                    if (s4 == 1) MFA_TR_ISSUE(2, vlo[0], vhi[0]);
+                    if (s4 == 2) MFA_TR_ISSUE(3, vlo[1], vhi[1]);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const i16x4_t lo4 = vlo[s4 & 1][db], hi4 = vhi[s4 & 1][db];
+                        const i16x8_t vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                        oacc[db] = Mfma<T>::mma32(bitcast<v8>(vv), pop, oacc[db]);
+                    }
                 }
             }
 
-            if (more) {
-                char* nstage = smem + (cur ^ 1) * L::BUF;
-#pragma unroll
-                for (int i = 0; i < LPT; ++i) {
-                    *reinterpret_cast<u32x4_t*>(nstage + st_k[i]) = kreg[i];
-                    *reinterpret_cast<u32x4_t*>(nstage + st_v[i]) = vreg[i];
-                }
-            }
-            __syncthreads();
+            __syncthreads();  // DMA of this step landed; stage st free for reuse
             if (!more) break;
-            cur ^= 1;
-            t = tn;
+            tcur = tnext;
+            st ^= 1;
         }
     }
+#undef MFA_NEXT_TILE
+#undef MFA_DMA
+#undef MFA_QK
+#undef MFA_TR_ISSUE
 
     // ---- epilogue: normalise, round, store; LSE in natural log
     l += __shfl_xor(l, 32);

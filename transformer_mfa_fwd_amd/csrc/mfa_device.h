@@ -66,6 +66,63 @@ __device__ inline i16x4_t lds_read_tr16(const void* lds_ptr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
 }
 
+// The same transposing read issued through inline assembly, for code that
+// keeps direct global->LDS copies in flight: the compiler waits for every
+// outstanding copy before the intrinsic form, since it cannot tell which LDS
+// bytes the intrinsic reads.  The caller must wait (lds_wait) before using
+// the result; lds_wait ties the registers so no consumer is hoisted above it.
+// Issues N reads at immediate byte offsets OFF0/OFF1 from addr[k].
+template <int OFF0, int OFF1>
+__device__ inline void lds_read_tr16_pair4(const uint32_t (&addr)[4], i16x4_t (&lo)[4], i16x4_t (&hi)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]),
+          "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFF0), "i"(OFF1));
+}
+template <int OFF0, int OFF1>
+__device__ inline void lds_read_tr16_pair2(const uint32_t (&addr)[2], i16x4_t (&lo)[2], i16x4_t (&hi)[2]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7"
+        : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+        : "v"(addr[0]), "v"(addr[1]), "i"(OFF0), "i"(OFF1));
+}
+template <int N>
+__device__ inline void lds_wait(i16x4_t (&lo)[N], i16x4_t (&hi)[N]) {
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]),
+                       "+v"(lo[2]), "+v"(hi[2]), "+v"(lo[3]), "+v"(hi[3]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]));
+}
+// 16-byte LDS read at an immediate offset, and a wait until at most N LDS
+// reads are outstanding that ties the result register (LDS reads of one wave
+// complete in order, so N counts the reads issued after the one awaited).
+template <int OFF>
+__device__ inline void lds_read_b128_asm(u32x4_t& dst, uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+}
+template <int N>
+__device__ inline void lds_wait_b128(u32x4_t& r) {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+
+// LDS byte offset of a pointer into __shared__ memory
+__device__ inline uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // IEEE maximum (gfx950 v_maximum3_f32 for chains); unlike fmaxf it needs no
 // canonicalisation of its operands.  Scores are finite or -inf.
