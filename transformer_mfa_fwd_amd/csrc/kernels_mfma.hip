@@ -17,8 +17,15 @@
 //   O^T[32 d x 32 q] += V^T . P^T            v_mfma_f32_32x32x16; P^T is the
 //        score accumulator (rounded to the input type), V^T comes from the
 //        transposing LDS read, so no score ever leaves the registers.
-// The next tile's copy is in flight while the current one is computed; the
-// two workgroups resident per CU interleave softmax (VALU) with MFMA work.
+//
+// Software pipeline.  Iteration j of a wave issues the Q.K^T MFMAs of tile
+// j+1 and, between them, the softmax of tile j (masking, row max, rescale,
+// the first half of the exponentials); then the P.V MFMAs of tile j and,
+// between them, the rest of tile j's exponentials and its row sum.  Each MFMA
+// (32 cycles on the matrix core) thus has independent VALU work behind it,
+// and the matrix core is never idle while the softmax runs.  The copies of
+// K(j+2) and V(j+1) are in flight during iteration j; one barrier per
+// iteration hands the stages over.
 //
 // Only tiles that intersect the key range of the workgroup's rows are visited
 // (causal and window bounds), tiles whose key-mask word is zero are skipped
@@ -41,7 +48,7 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
 
-// LDS layout of one stage: K tile then V tile, each [BN rows][D] of 16-bit
+// LDS layout: two K stages then two V stages, each [BN rows][D] of 16-bit
 // elements stored as 16-byte chunks, row-major without padding (a direct
 // global->LDS load writes 1 KiB contiguously per wave instruction).  The
 // chunk index is XOR-swizzled with row bits:
@@ -60,6 +67,12 @@ template <int D> struct PfLds {
     static __device__ inline int swz_v(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 };
 
+// source of one K or V tile: first row and byte range up to key Lk - 1
+struct TileSrc {
+    const void* p;
+    int n;
+};
+
 __device__ inline int remap_xcd(int p, int n) {
     const int per = n / 8;
     if (p < per * 8) return (p % 8) * per + p / 8;
@@ -70,23 +83,42 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int QK_LA = 4;  // K fragment reads in flight ahead of the MFMA
 
-// fragment f = (key block f / nks, k-step f % nks); compile-time f after unrolling
-template <int RS, int NKS>
-__device__ inline void mfa_qk_issue(u32x4_t (&kf)[2 * NKS], const uint32_t (&ka)[NKS], int f) {
-    const int kb = f / NKS, ks = f % NKS;
-    if (kb == 0) lds_read_b128_asm<0>(kf[f], ka[ks]);
-    else lds_read_b128_asm<32 * RS>(kf[f], ka[ks]);
+// K fragment f = (key block f & 1, k-step f >> 1): consecutive MFMAs alternate
+// between the two score accumulators.  f is a compile-time constant after
+// unrolling.
+template <int RS, int BASE>
+__device__ inline void mfa_qk_issue(u32x4_t* kf, const uint32_t* rd_k, int f) {
+    if ((f & 1) == 0) lds_read_b128_asm<BASE>(kf[f], rd_k[f >> 1]);
+    else lds_read_b128_asm<BASE + 32 * RS>(kf[f], rd_k[f >> 1]);
 }
-template <int LA, int NF>
-__device__ inline void mfa_qk_wait(u32x4_t (&kf)[NF], int f) {
-    // reads issued so far: min(NF, f + LA); those after f may stay in flight
-    const int after = (f + LA < NF ? f + LA : NF) - f - 1;
+// Wait for K fragment f.  Reads issued after it may stay in flight: the K
+// reads up to f + LA and, once f > XF, the XN reads issued behind K read
+// XF + LA (LDS reads of a wave complete in order).
+template <int LA, int NF, int XF, int XN>
+__device__ inline void mfa_qk_wait(u32x4_t* kf, int f) {
+    const int after = (f + LA < NF ? f + LA : NF) - f - 1 + (f > XF ? XN : 0);
     switch (after) {
         case 0: lds_wait_b128<0>(kf[f]); break;
         case 1: lds_wait_b128<1>(kf[f]); break;
         case 2: lds_wait_b128<2>(kf[f]); break;
-        default: lds_wait_b128<3>(kf[f]); break;
+        case 3: lds_wait_b128<3>(kf[f]); break;
+        case 4: lds_wait_b128<4>(kf[f]); break;
+        case 5: lds_wait_b128<5>(kf[f]); break;
+        case 6: lds_wait_b128<6>(kf[f]); break;
+        case 7: lds_wait_b128<7>(kf[f]); break;
+        case 8: lds_wait_b128<8>(kf[f]); break;
+        case 9: lds_wait_b128<9>(kf[f]); break;
+        case 10: lds_wait_b128<10>(kf[f]); break;
+        default: lds_wait_b128<11>(kf[f]); break;
     }
+}
+
+// Bits lo..hi (clipped to 0..63) set; zero when the range is empty.
+__device__ inline uint64_t range_bits64(int lo, int hi) {
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 63 ? 63 : hi;
+    if (lo > hi) return 0ull;
+    return (~0ull << lo) & (~0ull >> (63 - hi));
 }
 
 template <typename T, int D, bool CAP, bool MASK>
@@ -94,9 +126,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
     typedef PfLds<D> L;
     constexpr int CPR = L::CPR;
     constexpr int NKS = D / 16;             // k-steps of Q.K^T
+    constexpr int NQK = 2 * NKS;            // Q.K^T MFMAs per tile
     constexpr int NDB = D / 32;             // 32-wide d blocks of O
     constexpr int RPI = 64 / CPR;           // tile rows per DMA instruction
     constexpr int IPW = BN / RPI / 4;       // DMA instructions per wave per tile
+    constexpr int NSA = CAP ? 17 : 13;      // softmax steps run beside Q.K^T
+    constexpr int TRS = NQK - QK_LA;        // slot issuing the first V reads
+    static_assert(TRS > 0 && TRS + QK_LA == NQK, "V reads follow the last K read");
     typedef typename Mfma<T>::v8 v8;
     constexpr float LOG2E = 1.4426950408889634f;
 
@@ -157,30 +193,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
 
     // ---- DMA: instruction i of this wave fills tile rows R..R+RPI-1,
     // R = (wave * IPW + i) * RPI; lane -> physical (row, chunk), fetching the
-    // logical chunk that the swizzle stores there.
-    int dma_row[IPW], dma_koff[IPW], dma_voff[IPW];
+    // logical chunk that the swizzle stores there.  Source offsets are byte
+    // offsets within the tile, read through a buffer descriptor whose base is
+    // the tile's first row and whose range ends at key Lk - 1: rows of a
+    // partial last tile past it read as zero (and are masked anyway).
+    const int dma_r0 = wave * IPW * RPI + lane / CPR;   // tile row of copy 0
+    uint32_t dma_koff[IPW], dma_voff[IPW];
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-        const int r = (wave * IPW + i) * RPI + lane / CPR;
+        const int r = dma_r0 + i * RPI;
         const int pc = lane % CPR;
-        dma_row[i] = r;
-        dma_koff[i] = r * (int)kv_stride + (pc ^ L::swz_k(r)) * 8;
-        dma_voff[i] = r * (int)kv_stride + (pc ^ L::swz_v(r)) * 8;
+        dma_koff[i] = (uint32_t)(r * (int)kv_stride + (pc ^ L::swz_k(r)) * 8) * 2u;
+        dma_voff[i] = (uint32_t)(r * (int)kv_stride + (pc ^ L::swz_v(r)) * 8) * 2u;
     }
-    // per-lane LDS read offsets (bytes, within a K or V tile)
+    // per-lane LDS read addresses (bytes; stage offsets go in the immediate)
+    const uint32_t lds_base = lds_offset(smem);
     //  K (A operand): row 32 kb + lq, logical chunk 2 ks + h2
-    int rd_k[NKS];
+    uint32_t rd_k[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = lq * L::RS + (((2 * ks + h2) ^ L::swz_k(lq)) * 16);
+    for (int ks = 0; ks < NKS; ++ks) rd_k[ks] = lds_base + lq * L::RS + (((2 * ks + h2) ^ L::swz_k(lq)) * 16);
     //  V (transposing read): rows 32 kb + 16 hh + 4 h2 + j/4 (and +8),
     //  d columns 32 db + 16 (group & 1) + 4 (j & 3) .. +3
-    int rd_v[NDB];
+    uint32_t rd_v[NDB];
     {
         const int r0 = h2 * 4 + (j16 >> 2);  // row within the 16-row step (low bits fix the swizzle)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int chunk = db * 4 + (grp16 & 1) * 2 + ((j16 & 3) >> 1);
-            rd_v[db] = r0 * L::RS + ((chunk ^ L::swz_v(r0)) * 16) + (j16 & 1) * 8;
+            rd_v[db] = lds_base + r0 * L::RS + ((chunk ^ L::swz_v(r0)) * 16) + (j16 & 1) * 8;
         }
     }
 
@@ -203,176 +243,281 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
 // next tile at or after x that has a visible key
 #define MFA_NEXT_TILE(x) ({ int _t = (x); if (MASK) while (_t <= kt_hi && words[_t] == 0ull) ++_t; _t; })
 
-// copy K (and/or V) rows of tile TT into stage STG with direct global->LDS loads
+// source of tile TT of K or V (BASE): first row of the tile and the byte range
+// up to the end of key Lk - 1
+#define MFA_RSRC(BASE, TT)                                                                   \
+    ({                                                                                       \
+        const int _t = (TT);                                                                 \
+        const int _rows = min(BN, a.Lk - _t * BN);                                           \
+        TileSrc{(const void*)((BASE) + (int64_t)_t * BN * kv_stride),                        \
+                (_rows - 1) * (int)kv_stride * 2 + D * 2};                                   \
+    })
+// copy I (0 .. IPW-1) of a K or V tile (source RS, lane offsets OFF) into the
+// LDS tile at byte offset DST
+#define MFA_DMA1(RS, OFF, I, DST)                                                            \
+    buffer_copy16_to_lds((RS).p, (RS).n, smem + (wave * IPW + (I)) * 1024 + (DST), OFF[I])
+// copy K (and/or V) of tile TT into stage STG
 #define MFA_DMA(TT, STG, DO_K, DO_V)                                                         \
     do {                                                                                     \
-        const int _t = (TT);                                                                 \
-        const int64_t _tb = (int64_t)_t * BN * kv_stride;                                    \
-        const bool _full = _t * BN + BN <= a.Lk;                                             \
-        _Pragma("unroll") for (int i = 0; i < IPW; ++i) {                                    \
-            int _clamp = 0;                                                                  \
-            if (!_full && _t * BN + dma_row[i] >= a.Lk)                                      \
-                _clamp = (_t * BN + dma_row[i] - (a.Lk - 1)) * (int)kv_stride;               \
-            char* _dst = smem + (wave * IPW + i) * 1024;                                     \
-            if (DO_K)                                                                        \
-                __builtin_amdgcn_global_load_lds((const void*)(kbase + _tb + dma_koff[i] - _clamp), \
-                    (lds_void_t*)(_dst + L::KST + (STG) * L::TILE), 16, 0, 0);               \
-            if (DO_V)                                                                        \
-                __builtin_amdgcn_global_load_lds((const void*)(vbase + _tb + dma_voff[i] - _clamp), \
-                    (lds_void_t*)(_dst + L::VST + (STG) * L::TILE), 16, 0, 0);               \
+        if (DO_K) {                                                                          \
+            const auto _r = MFA_RSRC(kbase, TT);                                             \
+            _Pragma("unroll") for (int i = 0; i < IPW; ++i)                                  \
+                MFA_DMA1(_r, dma_koff, i, L::KST + (STG) * L::TILE);                         \
+        }                                                                                    \
+        if (DO_V) {                                                                          \
+            const auto _r = MFA_RSRC(vbase, TT);                                             \
+            _Pragma("unroll") for (int i = 0; i < IPW; ++i)                                  \
+                MFA_DMA1(_r, dma_voff, i, L::VST + (STG) * L::TILE);                         \
         }                                                                                    \
     } while (0)
 
-// S^T = K Q^T for the two 32-key blocks of the K tile in stage STG.  The
-// 2*NKS K fragments are read through a rolling window of QK_LA reads in
-// flight, each MFMA waiting only for its own fragment.
-#define MFA_QK(SACC, STG)                                                                    \
-    do {                                                                                     \
-        uint32_t _ka[NKS];                                                                   \
-        _Pragma("unroll") for (int ks = 0; ks < NKS; ++ks)                                   \
-            _ka[ks] = lds_base + L::KST + (STG) * L::TILE + rd_k[ks];                        \
-        u32x4_t _kf[2 * NKS];                                                                \
-        _Pragma("unroll") for (int f = 0; f < QK_LA; ++f) mfa_qk_issue<L::RS, NKS>(_kf, _ka, f); \
-        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
-            _Pragma("unroll") for (int e = 0; e < 16; ++e) SACC[kb][e] = 0.0f;              \
-        _Pragma("unroll") for (int f = 0; f < 2 * NKS; ++f) {                                \
-            mfa_qk_wait<QK_LA, 2 * NKS>(_kf, f);                                             \
-            if (f + QK_LA < 2 * NKS) mfa_qk_issue<L::RS, NKS>(_kf, _ka, f + QK_LA);         \
-            SACC[f / NKS] = Mfma<T>::mma32(bitcast<v8>(_kf[f]), qop[f % NKS], SACC[f / NKS]); \
-        }                                                                                    \
-    } while (0)
-
-// transposing reads of V for 16-key step S (rows 16 S .. 16 S + 15 of the tile)
+// transposing reads of V for 16-key step S (rows 16 S .. 16 S + 15 of the V
+// tile at LDS byte offset _vb)
 #define MFA_TR_ISSUE(S, LO, HI)                                                              \
     do {                                                                                     \
         if constexpr (NDB == 4)                                                              \
-            lds_read_tr16_pair4<(S) * 16 * L::RS, (S) * 16 * L::RS + 8 * L::RS>(vaddr, LO, HI); \
+            lds_read_tr16_pair4<_vb + (S) * 16 * L::RS, _vb + (S) * 16 * L::RS + 8 * L::RS>(rd_v, LO, HI); \
         else                                                                                 \
-            lds_read_tr16_pair2<(S) * 16 * L::RS, (S) * 16 * L::RS + 8 * L::RS>(vaddr, LO, HI); \
+            lds_read_tr16_pair2<_vb + (S) * 16 * L::RS, _vb + (S) * 16 * L::RS + 8 * L::RS>(rd_v, LO, HI); \
     } while (0)
 
-    const uint32_t lds_base = lds_offset(smem);
+// Score i (0..31) of this lane: key k0 + 32 (i / 16) + 8 ((i % 16) / 4) + 4 h2 + i % 4.
+#define MFA_X(SC, I) SC[(I) >> 4][(I) & 15]
+
+// Softmax step U (a constant, 0 .. NSA-1) of the tile whose raw scores are in
+// SC.  With a cap the base-2 logit is
+// cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1); without one it is
+// s * c_log2, folded into the exponent.  Steps: [cap x 4], mask, max x 3,
+// max finish + rescale, exponentials of scores 0..15 (two per step).
+#define MFA_SA(U, SC)                                                                        \
+    do {                                                                                     \
+        constexpr int _u = (U) - (CAP ? 4 : 0);                                              \
+        if constexpr (CAP && (U) < 4) {                                                      \
+            _Pragma("unroll") for (int _e = 0; _e < 8; ++_e) {                               \
+                const float _s = MFA_X(SC, 8 * (U) + _e);                                    \
+                MFA_X(SC, 8 * (U) + _e) = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(_s * cap_arg) + 1.0f); \
+            }                                                                                \
+        } else if constexpr (_u == 0) {                                                      \
+            if (!interior) {                                                                 \
+                /* bit c of _vis: key k0 + 4 h2 + c visible to this lane's row */           \
+                uint64_t _vis = range_bits64(rlo - k0 - 4 * h2, rhi - k0 - 4 * h2);          \
+                if (MASK) _vis &= word >> (4 * h2);                                          \
+                const uint32_t _vlo = (uint32_t)_vis, _vhi = (uint32_t)(_vis >> 32);         \
+                _Pragma("unroll") for (int _i = 0; _i < 32; ++_i) {                          \
+                    const int _c = (_i >> 4) * 32 + ((_i & 15) >> 2) * 8 + (_i & 3);          \
+                    const uint32_t _bit = ((_c < 32 ? _vlo : _vhi) >> (_c & 31)) & 1u;       \
+                    MFA_X(SC, _i) = _bit ? MFA_X(SC, _i) : -INFINITY;                        \
+                }                                                                            \
+            }                                                                                \
+        } else if constexpr (_u >= 1 && _u <= 3) {                                           \
+            _Pragma("unroll") for (int _d = 0; _d < 4; ++_d) {                               \
+                const int _p = 4 * (_u - 1) + _d;                                            \
+                if (_p < 10)                                                                 \
+                    pm[_p] = fmax_fast(fmax_fast(MFA_X(SC, 3 * _p), MFA_X(SC, 3 * _p + 1)), MFA_X(SC, 3 * _p + 2)); \
+            }                                                                                \
+            if (_u == 3) pm[10] = fmax_fast(MFA_X(SC, 30), MFA_X(SC, 31));                  \
+        } else if constexpr (_u == 4) {                                                      \
+            float _t = fmax_fast(fmax_fast(fmax_fast(pm[0], pm[1]), pm[2]),                  \
+                                 fmax_fast(fmax_fast(pm[3], pm[4]), pm[5]));                 \
+            _t = fmax_fast(_t, fmax_fast(fmax_fast(pm[6], pm[7]), pm[8]));                   \
+            _t = fmax_fast(fmax_fast(_t, pm[9]), pm[10]);                                    \
+            _t = xor32_max(_t);                                                              \
+            const float _tl2 = CAP ? _t : _t * c_log2;   /* base-2 logit units */           \
+            /* Lazy rescale: the running max only moves when a tile's max     */            \
+            /* exceeds it by more than 8 (base 2), so every weight 2^(x - m)  */            \
+            /* stays <= 256 and the accumulator is rescaled rarely.  Exact    */            \
+            /* after O = acc / l.  Rows that do not grow keep alpha = 1.      */            \
+            const bool _grow = _tl2 > m + 8.0f;                                              \
+            if (__any(_grow)) {                                                              \
+                const float _alpha = _grow ? fast_exp2(m - _tl2) : 1.0f;  /* 0 when m = -inf */ \
+                m = _grow ? _tl2 : m;                                                        \
+                l *= _alpha;                                                                 \
+                _Pragma("unroll") for (int _db = 0; _db < NDB; ++_db)                        \
+                    _Pragma("unroll") for (int _e = 0; _e < 16; ++_e) oacc[_db][_e] *= _alpha; \
+            }                                                                                \
+            neg_m = m == -INFINITY ? 0.0f : -m;                                              \
+        } else {                                                                             \
+            _Pragma("unroll") for (int _d = 0; _d < 2; ++_d) {                               \
+                const int _e = 2 * (_u - 5) + _d;                                            \
+                MFA_X(SC, _e) = CAP ? fast_exp2(MFA_X(SC, _e) + neg_m)                       \
+                                    : fast_exp2(fmaf(MFA_X(SC, _e), c_log2, neg_m));         \
+            }                                                                                \
+            psum0 += MFA_X(SC, 2 * (_u - 5));                                                \
+            psum1 += MFA_X(SC, 2 * (_u - 5) + 1);                                            \
+            if constexpr (_u == 8) pop[0] = pack8_at<T>(SC[0], 0);                           \
+            if constexpr (_u == 12) pop[1] = pack8_at<T>(SC[0], 8);                          \
+        }                                                                                    \
+    } while (0)
+
+// Softmax work beside the P.V MFMAs: quarter U of P.V step S4 (constants).
+// S4 = 0, 1: exponentials of scores 16..31, their operands and the row sum.
+#define MFA_SB(S4, U, SC)                                                                    \
+    do {                                                                                     \
+        if constexpr ((S4) < 2) {                                                            \
+            _Pragma("unroll") for (int _d = 0; _d < 2; ++_d) {                               \
+                const int _e = 16 + 8 * (S4) + 2 * (U) + _d;                                 \
+                MFA_X(SC, _e) = CAP ? fast_exp2(MFA_X(SC, _e) + neg_m)                       \
+                                    : fast_exp2(fmaf(MFA_X(SC, _e), c_log2, neg_m));         \
+            }                                                                                \
+            psum0 += MFA_X(SC, 16 + 8 * (S4) + 2 * (U));                                     \
+            psum1 += MFA_X(SC, 16 + 8 * (S4) + 2 * (U) + 1);                                 \
+            if constexpr ((U) == 3) pop[2 + (S4)] = pack8_at<T>(SC[1], 8 * (S4));           \
+            if constexpr ((S4) == 1 && (U) == 3) l += psum0 + psum1;                         \
+        }                                                                                    \
+    } while (0)
+
+// Slot F of the Q.K^T pass (a constant): wait for K fragment F, issue the read
+// QK_LA ahead, issue the MFMA, then the softmax steps of SC assigned to this
+// slot (SM).  Slot TRS, the first after the last K read is issued, also issues
+// the transposing V reads of the first P.V step (SM).
+#define MFA_SA_IF(U, F, SC) if constexpr ((U) < ((F) + 1) * NSA / NQK) MFA_SA(U, SC);
+// copy J of the iteration (K copies, then V copies) goes in slot J * NQK / (2 IPW)
+#define MFA_DMA_IF(F, J)                                                                     \
+    if constexpr ((J) < 2 * IPW && (F) == (J) * NQK / (2 * IPW)) {                           \
+        if constexpr ((J) < IPW) MFA_DMA1(_rk, dma_koff, (J), _dk_dst);                      \
+        else MFA_DMA1(_rv, dma_voff, (J) - IPW, _dv_dst);                                    \
+    }
+#define MFA_QK_SLOT(F, SC, SN, SM)                                                           \
+    if constexpr ((F) < NQK) {                                                               \
+        mfa_qk_wait<QK_LA, NQK, (SM) ? TRS : NQK, 2 * NDB>(_kf, (F));                        \
+        if constexpr ((F) + QK_LA < NQK) mfa_qk_issue<L::RS, _kb>(_kf, rd_k, (F) + QK_LA);  \
+        if constexpr ((SM) && (F) == TRS) MFA_TR_ISSUE(0, vlo[0], vhi[0]);                  \
+        if constexpr (SM) {                                                                  \
+            MFA_DMA_IF(F, 0) MFA_DMA_IF(F, 1) MFA_DMA_IF(F, 2) MFA_DMA_IF(F, 3)              \
+            MFA_DMA_IF(F, 4) MFA_DMA_IF(F, 5) MFA_DMA_IF(F, 6) MFA_DMA_IF(F, 7)              \
+        }                                                                                    \
+        SN[(F) & 1] = Mfma<T>::mma32(bitcast<v8>(_kf[F]), qop[(F) >> 1], SN[(F) & 1]);       \
+        if constexpr (SM) {                                                                  \
+            MFA_SA_IF((F) * NSA / NQK + 0, F, SC)                                            \
+            MFA_SA_IF((F) * NSA / NQK + 1, F, SC)                                            \
+            MFA_SA_IF((F) * NSA / NQK + 2, F, SC)                                            \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+    }
+
+// Q.K^T of the K tile in stage KSTG into SN, with the softmax steps of SC
+// spread over its MFMAs when SM.
+#define MFA_PART1(SC, SN, KSTG, SM)                                                          \
+    do {                                                                                     \
+        constexpr int _kb = L::KST + (KSTG) * L::TILE;                                       \
+        u32x4_t _kf[NQK];                                                                    \
+        _Pragma("unroll") for (int f = 0; f < QK_LA; ++f) mfa_qk_issue<L::RS, _kb>(_kf, rd_k, f); \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
+            _Pragma("unroll") for (int e = 0; e < 16; ++e) SN[kb][e] = 0.0f;                \
+        MFA_QK_SLOT(0, SC, SN, SM) MFA_QK_SLOT(1, SC, SN, SM)                                \
+        MFA_QK_SLOT(2, SC, SN, SM) MFA_QK_SLOT(3, SC, SN, SM)                                \
+        MFA_QK_SLOT(4, SC, SN, SM) MFA_QK_SLOT(5, SC, SN, SM)                                \
+        MFA_QK_SLOT(6, SC, SN, SM) MFA_QK_SLOT(7, SC, SN, SM)                                \
+        MFA_QK_SLOT(8, SC, SN, SM) MFA_QK_SLOT(9, SC, SN, SM)                                \
+        MFA_QK_SLOT(10, SC, SN, SM) MFA_QK_SLOT(11, SC, SN, SM)                              \
+        MFA_QK_SLOT(12, SC, SN, SM) MFA_QK_SLOT(13, SC, SN, SM)                              \
+        MFA_QK_SLOT(14, SC, SN, SM) MFA_QK_SLOT(15, SC, SN, SM)                              \
+    } while (0)
+
+// Slot (S4, DB) of the P.V pass (constants): at DB = 0 wait for the V
+// fragments of step S4 and issue those of S4 + 1; then the MFMA and the
+// softmax work assigned to the slot.
+#define MFA_SB_IF(S4, U, DB, SC) if constexpr ((U) < ((DB) + 1) * 4 / NDB) MFA_SB(S4, U, SC);
+#define MFA_PV_SLOT(S4, DB, SC)                                                              \
+    if constexpr ((DB) < NDB) {                                                              \
+        if constexpr ((DB) == 0) {                                                           \
+            lds_wait<NDB>(vlo[(S4) & 1], vhi[(S4) & 1]);                                     \
+            if constexpr ((S4) < 3) MFA_TR_ISSUE((S4) + 1, vlo[((S4) + 1) & 1], vhi[((S4) + 1) & 1]); \
+        }                                                                                    \
+        {                                                                                    \
+            const i16x4_t _lo4 = vlo[(S4) & 1][DB], _hi4 = vhi[(S4) & 1][DB];                \
+            const i16x8_t _vv = {_lo4[0], _lo4[1], _lo4[2], _lo4[3], _hi4[0], _hi4[1], _hi4[2], _hi4[3]}; \
+            oacc[DB] = Mfma<T>::mma32(bitcast<v8>(_vv), pop[S4], oacc[DB]);                 \
+        }                                                                                    \
+        MFA_SB_IF(S4, (DB) * 4 / NDB + 0, DB, SC)                                            \
+        MFA_SB_IF(S4, (DB) * 4 / NDB + 1, DB, SC)                                            \
+        MFA_SB_IF(S4, (DB) * 4 / NDB + 2, DB, SC)                                            \
+        MFA_SB_IF(S4, (DB) * 4 / NDB + 3, DB, SC)                                            \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+    }
+#define MFA_PV_STEP(S4, SC) MFA_PV_SLOT(S4, 0, SC) MFA_PV_SLOT(S4, 1, SC) MFA_PV_SLOT(S4, 2, SC) MFA_PV_SLOT(S4, 3, SC)
+
+// One pipeline iteration: tile tcur (scores in SC, V in stage ST) is finished
+// and the scores of tile tnxt (K in stage ST ^ 1) are computed into SN.
+#define MFA_ITER(SC, SN, ST)                                                                 \
+    do {                                                                                     \
+        has_nxt = tnxt <= kt_hi;                                                             \
+        tnx2 = has_nxt ? MFA_NEXT_TILE(tnxt + 1) : kt_hi + 1;                                \
+        /* copies spread over the Q.K^T slots: K(tnx2) into K(tcur)'s stage, V(tnxt)  */    \
+        /* into V(tcur-1)'s stage; near the end of the range tile tcur is re-copied   */    \
+        /* instead (harmless: those stages are not read again)                        */    \
+        const auto _rk = MFA_RSRC(kbase, tnx2 <= kt_hi ? tnx2 : tcur);                       \
+        const auto _rv = MFA_RSRC(vbase, has_nxt ? tnxt : tcur);                             \
+        constexpr int _dk_dst = L::KST + (ST) * L::TILE;                                     \
+        constexpr int _dv_dst = L::VST + ((ST) ^ 1) * L::TILE;                               \
+        const int k0 = tcur * BN;                                                            \
+        const uint64_t word = MASK ? words[tcur] : ~0ull;                                    \
+        const bool interior = __builtin_amdgcn_readfirstlane(                                \
+            (k0 >= wlo_last && k0 + BN - 1 <= whi_first && (!MASK || word == ~0ull)) ? 1 : 0); \
+        constexpr int _vb = L::VST + (ST) * L::TILE;                                         \
+        i16x4_t vlo[2][NDB], vhi[2][NDB];                                                    \
+        float pm[11];                                                                        \
+        float neg_m = 0.0f, psum0 = 0.0f, psum1 = 0.0f;                                      \
+        v8 pop[4];                                                                           \
+        /* stage ST ^ 1 holds K(tnxt); on the last tile its scores are discarded */         \
+        MFA_PART1(SC, SN, (ST) ^ 1, true);                                                   \
+        MFA_PV_STEP(0, SC) MFA_PV_STEP(1, SC) MFA_PV_STEP(2, SC) MFA_PV_STEP(3, SC)          \
+        __syncthreads();  /* copies of this iteration landed; stages handed over */         \
+    } while (0)
+
     int tcur = MFA_NEXT_TILE(kt_lo);
     if (tcur <= kt_hi) {
-        // prologue: K,V of the first tile into stage 0
+        int tnxt = MFA_NEXT_TILE(tcur + 1), tnx2;
+        bool has_nxt;
+        // prologue: K,V of the first tile into stage 0, K of the second into stage 1
         MFA_DMA(tcur, 0, true, true);
+        if (tnxt <= kt_hi) MFA_DMA(tnxt, 1, true, false);
         __syncthreads();
-
-        int st = 0;       // stage of tile tcur
+        f32x16_t sa[2], sb[2];
+        {
+            // scores of the first tile; no softmax and no V reads (names unused)
+            i16x4_t vlo[2][NDB], vhi[2][NDB];
+            float pm[11], neg_m, psum0, psum1;
+            v8 pop[4];
+            const int k0 = 0;
+            const uint64_t word = 0;
+            const bool interior = true;
+            constexpr int _vb = 0, _dk_dst = 0, _dv_dst = 0;
+            const auto _rk = MFA_RSRC(kbase, tcur);
+            const auto _rv = _rk;
+            (void)vlo; (void)vhi; (void)pm; (void)neg_m; (void)psum0; (void)psum1; (void)pop;
+            (void)k0; (void)word; (void)interior; (void)_vb; (void)_dk_dst; (void)_dv_dst;
+            (void)_rk; (void)_rv;
+            MFA_PART1(sa, sa, 0, false);
+        }
         while (true) {
-            const int tnext = MFA_NEXT_TILE(tcur + 1);
-            const bool more = tnext <= kt_hi;
-            // DMA: K,V of the next tile into the other stage (read two steps ago)
-            if (more) MFA_DMA(tnext, st ^ 1, true, true);
-
-            f32x16_t scur[2];
-            MFA_QK(scur, st);
-
-            // ---- scores -> weights (VALU)
-            const int k0 = tcur * BN;
-            const uint64_t word = MASK ? words[tcur] : ~0ull;
-            const bool interior = __builtin_amdgcn_readfirstlane(
-                (k0 >= wlo_last && k0 + BN - 1 <= whi_first && (!MASK || word == ~0ull)) ? 1 : 0);
-
-            // scur[kb][4 j + i] is key k0 + 32 kb + 8 j + 4 h2 + i of row qrow.
-            // Without a cap the base-2 logit is s * c_log2, folded into the
-            // exponent below; with a cap it is
-            // cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1).
-            float x[32];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float v = scur[kb][e];
-                    if (CAP) v = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(v * cap_arg) + 1.0f);
-                    x[kb * 16 + e] = v;
-                }
-            if (!interior) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int kk = kb * 32 + (e >> 2) * 8 + h2 * 4 + (e & 3);
-                        const int key = k0 + kk;
-                        bool vis = key >= rlo && key <= rhi;
-                        if (MASK) vis = vis && ((word >> kk) & 1ull);
-                        x[kb * 16 + e] = vis ? x[kb * 16 + e] : -INFINITY;
-                    }
-            }
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 32; e += 2) tmax = fmax_fast(fmax_fast(tmax, x[e]), x[e + 1]);
-            tmax = fmax_fast(tmax, __shfl_xor(tmax, 32));
-            const float tmax_l2 = CAP ? tmax : tmax * c_log2;   // base-2 logit units
-
-            // Lazy rescale: the running max only moves when a tile's max exceeds
-            // it by more than 8 (base 2), so every weight 2^(x - m) stays <= 256
-            // and the accumulator is rescaled rarely.  Exact after O = acc / l.
-            const bool grow = tmax_l2 > m + 8.0f;
-            if (__any(grow)) {
-                // rows that do not grow keep alpha = 1 (m may still be -inf there)
-                const float alpha = grow ? fast_exp2(m - tmax_l2) : 1.0f;   // 0 when m = -inf
-                m = grow ? tmax_l2 : m;
-                l *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-            }
-            const float m_use = m == -INFINITY ? 0.0f : m;
-            float psum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                x[e] = CAP ? fast_exp2(x[e] - m_use) : fast_exp2(fmaf(x[e], c_log2, -m_use));
-                psum += x[e];
-            }
-            l += psum;
-
-            // ---- O^T += V^T P^T, four 16-key steps over V stage st.  The
-            // transposing reads of step s+1 are in flight while step s runs on
-            // the matrix cores.
-            {
-                uint32_t vaddr[NDB];
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) vaddr[db] = lds_base + L::VST + st * L::TILE + rd_v[db];
-                i16x4_t vlo[2][NDB], vhi[2][NDB];
-                MFA_TR_ISSUE(0, vlo[0], vhi[0]);
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int kb = s4 >> 1, hh = s4 & 1;
-                    float pv[8];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pv[i] = x[kb * 16 + (2 * hh) * 4 + i];
-                        pv[4 + i] = x[kb * 16 + (2 * hh + 1) * 4 + i];
-                    }
-                    const v8 pop = pack8<T>(pv);
-                    lds_wait<NDB>(vlo[s4 & 1], vhi[s4 & 1]);
-                    if (s4 == 0) MFA_TR_ISSUE(1, vlo[1], vhi[1]);
-                    if (s4 == 1) MFA_TR_ISSUE(2, vlo[0], vhi[0]);
-                    if (s4 == 2) MFA_TR_ISSUE(3, vlo[1], vhi[1]);
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const i16x4_t lo4 = vlo[s4 & 1][db], hi4 = vhi[s4 & 1][db];
-                        const i16x8_t vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                        oacc[db] = Mfma<T>::mma32(bitcast<v8>(vv), pop, oacc[db]);
-                    }
-                }
-            }
-
-            __syncthreads();  // DMA of this step landed; stage st free for reuse
-            if (!more) break;
-            tcur = tnext;
-            st ^= 1;
+            MFA_ITER(sa, sb, 0);
+            if (!has_nxt) break;
+            tcur = tnxt; tnxt = tnx2;
+            MFA_ITER(sb, sa, 1);
+            if (!has_nxt) break;
+            tcur = tnxt; tnxt = tnx2;
         }
     }
 #undef MFA_NEXT_TILE
 #undef MFA_DMA
-#undef MFA_QK
+#undef MFA_DMA1
+#undef MFA_DMA_IF
+#undef MFA_RSRC
 #undef MFA_TR_ISSUE
+#undef MFA_X
+#undef MFA_SA
+#undef MFA_SB
+#undef MFA_SA_IF
+#undef MFA_SB_IF
+#undef MFA_QK_SLOT
+#undef MFA_PV_SLOT
+#undef MFA_PV_STEP
+#undef MFA_PART1
+#undef MFA_ITER
 
     // ---- epilogue: normalise, round, store; LSE in natural log
-    l += __shfl_xor(l, 32);
+    l = xor32_sum(l);
     if (qrow <= i_last) {
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
         T* orow = static_cast<T*>(a.out) + ((int64_t)b * a.Lq + qrow) * q_stride + (int64_t)hq * D;

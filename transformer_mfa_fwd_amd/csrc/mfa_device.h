@@ -56,6 +56,15 @@ __device__ inline typename Mfma<T>::v8 pack8(const float* x) {
     return r;
 }
 
+// Elements OFF .. OFF+7 of a 16-float accumulator, rounded into one operand.
+template <typename T>
+__device__ inline typename Mfma<T>::v8 pack8_at(const f32x16_t& x, int off) {
+    typename Mfma<T>::v8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = static_cast<T>(x[off + e]);
+    return r;
+}
+
 // Transposing LDS read: within each group of 16 lanes, source lane j supplies
 // the address of 4 consecutive 16-bit elements; result lane i element e is
 // element (i % 4) of source lane 4e + i/4.  With source lane j pointing at
@@ -118,6 +127,15 @@ __device__ inline void lds_wait_b128(u32x4_t& r) {
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
 }
 
+// Direct copy of 16 bytes per lane from global memory into LDS through a raw
+// buffer descriptor (base, range nbytes): lane l writes LDS bytes
+// lds + 16 l .. + 15 with the bytes at base + voffset, or zeros when voffset is
+// at or past nbytes.  lds must be wave-uniform.
+__device__ inline void buffer_copy16_to_lds(const void* base, int nbytes, void* lds, uint32_t voffset) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
+}
+
 // LDS byte offset of a pointer into __shared__ memory
 __device__ inline uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
@@ -128,6 +146,19 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // canonicalisation of its operands.  Scores are finite or -inf.
 __device__ inline float fmax_fast(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Max / sum of a value over lanes l and l ^ 32.  v_permlane32_swap exchanges
+// the upper half of its first operand with the lower half of its second, so
+// with both operands equal each lane ends up holding {v[l], v[l ^ 32]}; this
+// stays on the VALU (no LDS permute).
+__device__ inline float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmax_fast(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // c * tanh(s / c) through tanh(y) = 1 - 2 / (exp(2y) + 1), with the hardware
 // base-2 exponential.  Saturates correctly at both ends (exp2 -> inf or 0).
