@@ -516,11 +516,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
 #undef MFA_PART1
 #undef MFA_ITER
 
-    // ---- epilogue: normalise, round, store; LSE in natural log
+    // ---- epilogue: normalise, round, store; LSE in natural log.  O is staged
+    // through LDS (this wave's 32 rows, chunk-swizzled; every stage is free
+    // after the loop's last barrier) so that each store writes whole rows.
     l = xor32_sum(l);
-    if (qrow <= i_last) {
+    {
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        T* orow = static_cast<T*>(a.out) + ((int64_t)b * a.Lq + qrow) * q_stride + (int64_t)hq * D;
+        char* stg = smem + wave * 32 * L::RS;
+        char* wrow = stg + lq * L::RS;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -529,13 +532,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
                 T o4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o4[i] = static_cast<T>(oacc[db][4 * j + i] * inv);
-                *reinterpret_cast<uint2*>(orow + db * 32 + j * 8 + h2 * 4) = *reinterpret_cast<const uint2*>(o4);
+                const int c = 4 * db + j;
+                *reinterpret_cast<uint2*>(wrow + ((c ^ (lq & (CPR - 1))) * 16) + h2 * 8) =
+                    *reinterpret_cast<const uint2*>(o4);
             }
         }
-        if (a.lse && h2 == 0)
-            a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qrow] =
-                l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
+        T* obase = static_cast<T*>(a.out) + ((int64_t)b * a.Lq + w_first) * q_stride + (int64_t)hq * D;
+#pragma unroll
+        for (int s = 0; s < 32 * CPR / 64; ++s) {
+            const int r = s * (64 / CPR) + lane / CPR, c = lane % CPR;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * L::RS + ((c ^ (r & (CPR - 1))) * 16));
+            if (w_first + r <= i_last) *reinterpret_cast<u32x4_t*>(obase + (int64_t)r * q_stride + c * 8) = v;
+        }
     }
+    if (a.lse && h2 == 0 && qrow <= i_last)
+        a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qrow] = l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
 }
 
 template <typename T, int D, bool CAP, bool MASK>
