@@ -33,10 +33,11 @@
 // not fully visible to every row of the wave.
 //
 // Scheduling.  Blocks are ordered so that the Hq/Hkv heads sharing a kv head
-// and q tile are adjacent (they read the same K/V tiles together) and the
-// heaviest causal tiles go first; the block id is remapped so that each of the
-// 8 XCDs (round-robin dispatch, one L2 each) receives a contiguous range of
-// that order.
+// and q tile are adjacent (they read the same K/V tiles together) and, over
+// the up to 4 kv heads that one XCD serves at a time, the heaviest causal
+// tiles go first; the block id is remapped so that each of the 8 XCDs
+// (round-robin dispatch, one L2 each) receives a contiguous range of that
+// order.
 #include "mfa_device.h"
 #include "mfa_internal.h"
 
@@ -146,15 +147,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
     const int grp16 = lane >> 4, j16 = lane & 15;
 
     // ---- block -> (batch, kv head, q tile, q head)
+    // Blocks come in chunks of KG kv heads (all of one XCD's share when it
+    // holds up to 4); within a chunk the latest q tile (largest causal key
+    // range) of every head comes first.
     const int n = remap_xcd(blockIdx.x, gridDim.x);
     const int g = a.group;
     const int per_group = g * nqt;
-    const int bk = n / per_group;           // b * Hkv + kvh
-    const int rem = n - bk * per_group;
-    const int qt = nqt - 1 - rem / g;       // heaviest tile first
+    const int nbk = a.B * a.Hkv;
+    const int per_xcd = (nbk & 7) == 0 ? nbk >> 3 : 1;
+    const int KG = (per_xcd & 3) == 0 ? 4 : ((per_xcd & 1) == 0 ? 2 : 1);
+    const int chunk = n / (KG * per_group);
+    const int rem = n - chunk * KG * per_group;
+    const int lvl = rem / (KG * g);
+    const int rest = rem - lvl * KG * g;
+    const int bk = chunk * KG + rest / g;   // b * Hkv + kvh
+    const int qt = nqt - 1 - lvl;
     const int b = bk / a.Hkv;
     const int kvh = bk - b * a.Hkv;
-    const int hq = kvh * g + (rem % g);
+    const int hq = kvh * g + (rest % g);
 
     const int i0 = qt * BM;
     const int i_last = min(i0 + BM, a.Lq) - 1;
