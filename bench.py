@@ -110,7 +110,7 @@ def measured_traffic(name: str, sources) -> tuple:
 # timing
 # ---------------------------------------------------------------------------
 
-def time_workload(w, steps: int, warmup: int, seed: int = 0):
+def time_workload(w, steps: int, warmup: int, seed: int = 0, warmup_ms: float = 0.0):
     import torch
     import transformer_mfa_fwd_amd as mfa
     from transformer_mfa_fwd_amd import workloads as wl
@@ -120,8 +120,15 @@ def time_workload(w, steps: int, warmup: int, seed: int = 0):
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=q.device)
     kw = dict(causal=w.causal, window=w.window, q_offset=w.q_offset, softcap=w.softcap,
               key_mask=m, scale=w.scale, out=out, lse=lse)
-    for _ in range(warmup):
+    # W untimed steps, continued until warmup_ms has passed as well: the GPU
+    # clocks take a few hundred milliseconds of load to settle
+    n_warm = 0
+    t_w = time.perf_counter()
+    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
         mfa.fwd(q, k, v, **kw)
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -138,7 +145,7 @@ def time_workload(w, steps: int, warmup: int, seed: int = 0):
                event_ms_min=float(np.min(per_call)), event_ms_median=float(np.median(per_call)),
                path=mfa.plan(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)[0],
                pairs=visible_pairs(w, None if m is None else m.cpu()),
-               bytes=algorithmic_bytes(w, q))
+               bytes=algorithmic_bytes(w, q), warmup_steps=n_warm)
     return res, (q, k, v, m)
 
 
@@ -177,6 +184,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=300.0,
+                    help="keep warming up until this much time has passed (clock ramp)")
     ap.add_argument("--workload", default="gqa_causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -207,7 +216,7 @@ def main():
         raise SystemExit(f"unknown workload {args.workload}; choose from {[x.name for x in wl.ALL]}")
     w = match[0]
 
-    res, tensors = time_workload(w, args.steps, args.warmup)
+    res, tensors = time_workload(w, args.steps, args.warmup, warmup_ms=args.warmup_ms)
     flops = 4.0 * w.D * res["pairs"]
     tflops_wall = flops / (res["wall_ms"] * 1e-3) / 1e12
     kern_ms = res["event_ms_avg"]
@@ -234,7 +243,7 @@ def main():
         "metric": METRIC,
         "value": round(tflops_wall if is_prefill else res["bytes"] / (res["wall_ms"] * 1e-3) / 1e9, 2),
         "unit": "TFLOP/s" if is_prefill else "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": res["warmup_steps"],
         "ms_per_step": round(res["wall_ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
@@ -248,7 +257,8 @@ def main():
         del tensors
         torch.cuda.empty_cache()
         wd = wl.LONG_CACHE_DECODE_BF16
-        rd, td = time_workload(wd, max(10, args.steps // 2), max(3, args.warmup // 2))
+        rd, td = time_workload(wd, max(10, args.steps // 2), max(3, args.warmup // 2),
+                               warmup_ms=args.warmup_ms)
         dtraffic, dnote = measured_traffic(f"decode_{wd.name}.counters.json", DECODE_SOURCES)
         dk = rd["event_ms_avg"]
         line["decode"] = {
