@@ -20,7 +20,7 @@
 //
 // Software pipeline.  Iteration j of a wave issues the Q.K^T MFMAs of tile
 // j+1 and, between them, the softmax of tile j (masking, row max, rescale,
-// the first half of the exponentials); then the P.V MFMAs of tile j and,
+// the first quarter of the exponentials); then the P.V MFMAs of tile j and,
 // between them, the rest of tile j's exponentials and its row sum.  Each MFMA
 // (32 cycles on the matrix core) thus has independent VALU work behind it,
 // and the matrix core is never idle while the softmax runs.  The copies of
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
     constexpr int NDB = D / 32;             // 32-wide d blocks of O
     constexpr int RPI = 64 / CPR;           // tile rows per DMA instruction
     constexpr int IPW = BN / RPI / 4;       // DMA instructions per wave per tile
-    constexpr int NSA = CAP ? 17 : 13;      // softmax steps run beside Q.K^T
+    constexpr int NSA = CAP ? 13 : 9;       // softmax steps run beside Q.K^T
     constexpr int TRS = NQK - QK_LA;        // slot issuing the first V reads
     static_assert(TRS > 0 && TRS + QK_LA == NQK, "V reads follow the last K read");
     typedef typename Mfma<T>::v8 v8;
@@ -298,7 +298,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
 // SC.  With a cap the base-2 logit is
 // cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1); without one it is
 // s * c_log2, folded into the exponent.  Steps: [cap x 4], mask, max x 3,
-// max finish + rescale, exponentials of scores 0..15 (two per step).
+// max finish + rescale, exponentials of scores 0..7 (two per step).  The other
+// 24 exponentials run beside the P.V MFMAs, which leave the VALU idle.
 #define MFA_SA(U, SC)                                                                        \
     do {                                                                                     \
         constexpr int _u = (U) - (CAP ? 4 : 0);                                              \
@@ -312,11 +313,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
                 /* bit c of _vis: key k0 + 4 h2 + c visible to this lane's row */           \
                 uint64_t _vis = range_bits64(rlo - k0 - 4 * h2, rhi - k0 - 4 * h2);          \
                 if (MASK) _vis &= word >> (4 * h2);                                          \
-                const uint32_t _vlo = (uint32_t)_vis, _vhi = (uint32_t)(_vis >> 32);         \
+                const int _vlo = (int)(uint32_t)_vis, _vhi = (int)(uint32_t)(_vis >> 32);     \
                 _Pragma("unroll") for (int _i = 0; _i < 32; ++_i) {                          \
+                    /* all ones when visible (sign-extended bit), then a bit select */      \
                     const int _c = (_i >> 4) * 32 + ((_i & 15) >> 2) * 8 + (_i & 3);          \
-                    const uint32_t _bit = ((_c < 32 ? _vlo : _vhi) >> (_c & 31)) & 1u;       \
-                    MFA_X(SC, _i) = _bit ? MFA_X(SC, _i) : -INFINITY;                        \
+                    const uint32_t _mw = (uint32_t)__builtin_amdgcn_sbfe(_c < 32 ? _vlo : _vhi, _c & 31, 1); \
+                    MFA_X(SC, _i) = __uint_as_float((__float_as_uint(MFA_X(SC, _i)) & _mw) |  \
+                                                    (0xff800000u & ~_mw));                   \
                 }                                                                            \
             }                                                                                \
         } else if constexpr (_u >= 1 && _u <= 3) {                                           \
@@ -355,24 +358,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
             psum0 += MFA_X(SC, 2 * (_u - 5));                                                \
             psum1 += MFA_X(SC, 2 * (_u - 5) + 1);                                            \
             if constexpr (_u == 8) pop[0] = pack8_at<T>(SC[0], 0);                           \
-            if constexpr (_u == 12) pop[1] = pack8_at<T>(SC[0], 8);                          \
         }                                                                                    \
     } while (0)
 
 // Softmax work beside the P.V MFMAs: quarter U of P.V step S4 (constants).
-// S4 = 0, 1: exponentials of scores 16..31, their operands and the row sum.
+// S4 = 0, 1, 2: exponentials of scores 8 (S4 + 1) .. +7 and the operand of step
+// S4 + 1; the row sum is complete after step 2.
 #define MFA_SB(S4, U, SC)                                                                    \
     do {                                                                                     \
-        if constexpr ((S4) < 2) {                                                            \
+        if constexpr ((S4) < 3) {                                                            \
             _Pragma("unroll") for (int _d = 0; _d < 2; ++_d) {                               \
-                const int _e = 16 + 8 * (S4) + 2 * (U) + _d;                                 \
+                const int _e = 8 + 8 * (S4) + 2 * (U) + _d;                                  \
                 MFA_X(SC, _e) = CAP ? fast_exp2(MFA_X(SC, _e) + neg_m)                       \
                                     : fast_exp2(fmaf(MFA_X(SC, _e), c_log2, neg_m));         \
             }                                                                                \
-            psum0 += MFA_X(SC, 16 + 8 * (S4) + 2 * (U));                                     \
-            psum1 += MFA_X(SC, 16 + 8 * (S4) + 2 * (U) + 1);                                 \
-            if constexpr ((U) == 3) pop[2 + (S4)] = pack8_at<T>(SC[1], 8 * (S4));           \
-            if constexpr ((S4) == 1 && (U) == 3) l += psum0 + psum1;                         \
+            psum0 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U));                                      \
+            psum1 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U) + 1);                                  \
+            if constexpr ((U) == 3) pop[1 + (S4)] = pack8_at<T>(SC[(1 + (S4)) >> 1], 8 * ((1 + (S4)) & 1)); \
+            if constexpr ((S4) == 2 && (U) == 3) l += psum0 + psum1;                         \
         }                                                                                    \
     } while (0)
 
