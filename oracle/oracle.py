@@ -116,6 +116,35 @@ class Oracle:
         O = out.reshape(B, Hq, Lq, D).transpose(0, 2, 1, 3).copy()
         return O, lse.reshape(B, Hq, Lq), nvis.reshape(B, Hq, Lq)
 
+    def decode_len(self, q, k, v, lens, *, scale, softcap=0.0, nthreads=1):
+        """Decode over the first lens[b] keys of a fixed-capacity cache.
+
+        brotensor flash_attention.h, flash_attention_decode_len: the R query
+        rows of a batch are consecutive positions whose keys are the last R of
+        the valid ones, so row r attends causally to the first len - R + 1 + r
+        keys, and a length of 0 writes zeros.  That is the plain forward over
+        the valid prefix with the rows at positions len - R .. len - 1, which
+        is how it is evaluated here (rows before position 0 see no key).
+        q [B, R, Hq, D]; k, v [B, Lmax, Hkv, D]; lens [B] integers, clamped to
+        [0, Lmax].  Returns O [B, R, Hq, D], LSE [B, Hq, R] and the visible
+        counts [B, Hq, R].
+        """
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        B, R, Hq, D = q.shape
+        Lmax = k.shape[1]
+        O = np.zeros((B, R, Hq, D), np.float64)
+        L = np.full((B, Hq, R), -np.inf, np.float64)
+        N = np.zeros((B, Hq, R), np.int64)
+        lens = np.asarray(lens).reshape(-1)
+        for b in range(B):
+            n = min(max(int(lens[b]), 0), Lmax)
+            if n == 0:
+                continue
+            Ob, Lb, Nb = self.full(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n], scale=scale,
+                                   causal=True, window=0, q_offset=n - R, softcap=softcap)
+            O[b], L[b], N[b] = Ob[0], Lb[0], Nb[0]
+        return O, L, N
+
     def visible_counts(self, B, Lq, Lk, *, causal=False, window=0, q_offset=None, key_mask=None):
         """Visible-key count of every row, [B, Lq] int64, and the total."""
         m = _f32(key_mask)

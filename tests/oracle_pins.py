@@ -424,6 +424,96 @@ def pin_empty_rows(orc):
     _close(O[1], np.broadcast_to(v[1, 4], (L, H, D)).astype(np.float64), 0.0, "one key")
 
 
+# ---------------------------------------------------------------------------
+# decode over a device-held length (R query rows per batch)
+# ---------------------------------------------------------------------------
+
+def decode_len_visibility(R, Lmax, n):
+    """[R, Lmax] visibility as brotensor flash_attention.h states it for
+    flash_attention_decode_len: row r sees the first n - R + 1 + r keys."""
+    vis = np.zeros((R, Lmax), bool)
+    for r in range(R):
+        vis[r, :max(0, min(Lmax, n - R + 1 + r))] = True
+    return vis
+
+
+def dense_decode_len(q, k, v, lens, *, scale, softcap=0.0):
+    """Full score matrix over the whole capacity with the count-form mask."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    B, R, Hq, D = q.shape
+    Lmax, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    O = np.zeros((B, R, Hq, D))
+    L = np.zeros((B, Hq, R))
+    for b in range(B):
+        vis = decode_len_visibility(R, Lmax, min(max(int(lens[b]), 0), Lmax))
+        for h in range(Hq):
+            s = scale * (q[b, :, h, :] @ k[b, :, h // g, :].T)
+            if softcap > 0:
+                s = softcap * np.tanh(s / softcap)
+            s = np.where(vis, s, -np.inf)
+            empty = ~vis.any(1)
+            lse = np.where(empty, -np.inf, logsumexp(np.where(empty[:, None], 0.0, s), axis=1))
+            p = np.where(vis, np.exp(s - np.where(empty, 0.0, lse)[:, None]), 0.0)
+            O[b, :, h, :] = p @ v[b, :, h // g, :]
+            L[b, h, :] = lse
+    return O, L
+
+
+def pin_decode_len_matches_dense(orc):
+    """Against the dense count-form formulation, lengths 0 .. Lmax, R up to 4."""
+    rng = _rng(14)
+    for R, Hq, Hkv, softcap in [(1, 4, 2, 0.0), (3, 4, 1, 0.0), (4, 2, 2, 1.5)]:
+        B, Lmax, D = 7, 13, 8
+        lens = np.array([0, 1, R - 1, R, 6, 12, 13])
+        q, k, v = _rand(rng, (B, R, Hq, D), 2.0), _rand(rng, (B, Lmax, Hkv, D), 2.0), _rand(rng, (B, Lmax, Hkv, D))
+        O, L, n = orc.decode_len(q, k, v, lens, scale=0.45, softcap=softcap)
+        Od, Ld = dense_decode_len(q, k, v, lens, scale=0.45, softcap=softcap)
+        _close(O, Od, TIGHT, f"decode_len O R={R}")
+        _close(L, Ld, TIGHT, f"decode_len LSE R={R}")
+        for b in range(B):
+            cnt = decode_len_visibility(R, Lmax, int(lens[b])).sum(1)
+            assert np.array_equal(n[b], np.broadcast_to(cnt, (Hq, R))), (b, n[b], cnt)
+
+
+def pin_decode_len_zero_query_closed_form(orc):
+    """Q = 0: row r of a batch with length n is the mean of V rows
+    0 .. n - R + r, LSE = ln(n - R + 1 + r); a row with no key (n = 0, or
+    n < R for the first rows) is O = 0, LSE = -inf."""
+    rng = _rng(15)
+    B, R, Hq, Hkv, Lmax, D = 5, 3, 4, 2, 10, 8
+    lens = np.array([0, 2, 3, 7, 10])
+    q = np.zeros((B, R, Hq, D), np.float32)
+    k, v = _rand(rng, (B, Lmax, Hkv, D)), _rand(rng, (B, Lmax, Hkv, D))
+    O, L, _ = orc.decode_len(q, k, v, lens, scale=0.7, softcap=2.0)
+    for b in range(B):
+        for h in range(Hq):
+            for r in range(R):
+                cnt = int(lens[b]) - R + 1 + r
+                if cnt <= 0:
+                    assert np.all(O[b, r, h] == 0) and L[b, h, r] == -np.inf, (b, h, r)
+                    continue
+                mean = v[b, :cnt, h // (Hq // Hkv), :].astype(np.float64).mean(0)
+                assert np.max(np.abs(O[b, r, h] - mean)) <= TIGHT
+                assert abs(L[b, h, r] - math.log(cnt)) <= TIGHT
+
+
+def pin_decode_len_ignores_rows_past_length(orc):
+    """Cache rows at or past the length may hold anything finite."""
+    rng = _rng(16)
+    B, R, Hq, Hkv, Lmax, D = 3, 2, 2, 1, 12, 8
+    lens = np.array([5, 9, 12])
+    q, k, v = _rand(rng, (B, R, Hq, D)), _rand(rng, (B, Lmax, Hkv, D)), _rand(rng, (B, Lmax, Hkv, D))
+    O, L, _ = orc.decode_len(q, k, v, lens, scale=0.5)
+    k2, v2 = k.copy(), v.copy()
+    for b in range(B):
+        k2[b, lens[b]:] = 1e4
+        v2[b, lens[b]:] = -1e4
+    O2, L2, _ = orc.decode_len(q, k2, v2, lens, scale=0.5)
+    _close(O2, O, 0.0, "decode_len past-length rows perturbed")
+    _close(L2, L, 0.0, "decode_len past-length rows perturbed LSE")
+
+
 ALL_PINS = [
     pin_range_causal_matches_ferrotensor_rule,
     pin_range_causal_matches_forge_rule,
@@ -442,4 +532,7 @@ ALL_PINS = [
     pin_softcap_limits,
     pin_invisible_keys_have_no_influence,
     pin_empty_rows,
+    pin_decode_len_matches_dense,
+    pin_decode_len_zero_query_closed_form,
+    pin_decode_len_ignores_rows_past_length,
 ]
