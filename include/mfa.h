@@ -121,6 +121,44 @@ int mfa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* ls
                const float* key_mask, int dtype, int path, int splits,
                void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Decode over a fixed-capacity KV cache whose valid length is read on the
+ * device (brotensor flash_attention.h, flash_attention_decode_len).  Batch b
+ * holds R query rows, the last R positions of its first len_b = d_len[b] cache
+ * rows: row r attends causally to keys 0 .. len_b - R + r (the first
+ * len_b - R + 1 + r keys), with GQA and the optional soft-cap as in mfa_fwd.
+ * The launch shape depends only on the capacity Lmax, never on the lengths,
+ * so the call can be captured once in a HIP graph and replayed while the
+ * caller rewrites d_len between replays; the key splits divide each batch's
+ * valid keys, so rows past the length are neither read nor computed.
+ *
+ *   q, out             [B, R, Hq, D]     element type `dtype` (fp16 or bf16)
+ *   k_cache, v_cache   [B, Lmax, Hkv, D] element type `dtype`
+ *   lse                [B, Hq, R]        float32, may be NULL
+ *   d_len              [B]               int32 in device memory, read by the
+ *                                        kernels when they run; values are
+ *                                        clamped to [0, Lmax]
+ *
+ * A row that sees no key (len_b = 0, or len_b < R for the first rows) gets
+ * O = 0 and LSE = -inf.  Requires D in {64, 128} and R * Hq/Hkv <= 16
+ * (otherwise MFA_ERROR_NOT_SUPPORTED).  `splits` <= 0 chooses the split count
+ * from B, Hkv and Lmax.  The workspace is caller-owned (256-byte aligned, at
+ * least mfa_decode_len_workspace_size bytes, not used by other work until
+ * this call's kernels finish); workspace = NULL with ws_bytes = 0 takes it
+ * from the stream-ordered pool instead (not for graph capture).  q, k_cache,
+ * v_cache and out must be 16-byte aligned, lse and d_len 4-byte aligned.
+ * Errors, ownership and streams as for mfa_fwd.
+ */
+int mfa_decode_len(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                   const int* d_len, int B, int R, int Lmax, int Hq, int Hkv, int D,
+                   float scale, float softcap, int dtype, int splits,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes mfa_decode_len needs for these sizes and split count
+ * (`splits` <= 0: the count it would choose); 0 for unsupported arguments. */
+size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, int D, int dtype,
+                                     int splits);
+
 /* The path mfa_fwd would take for these arguments (an mfa_path value), and
  * the split count it would use (through *splits, may be NULL). */
 int mfa_fwd_plan(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype, int* splits);

@@ -108,3 +108,50 @@ def test_workspace_size_and_plan():
     assert path in ("split_decode", "generic", "mfma")
     p32, _ = mfa.plan(1, 128, 128, 1, 1, 64, torch.float32)
     assert p32 == "generic"
+
+
+def call_len(**over):
+    lib = mfa.load_library()
+    a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], lse=FAKE[4], d_len=FAKE[5], B=2, R=2,
+             Lmax=64, Hq=8, Hkv=2, D=128, scale=0.1, softcap=0.0, dtype=2, splits=0,
+             ws=None, ws_bytes=0)
+    a.update(over)
+    return lib.mfa_decode_len(a["q"], a["k"], a["v"], a["out"], a["lse"], a["d_len"], a["B"],
+                              a["R"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                              a["softcap"], a["dtype"], a["splits"], a["ws"], a["ws_bytes"], None)
+
+
+LEN_INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(out=None), dict(d_len=None),
+    dict(B=-1), dict(R=0), dict(Lmax=0), dict(Hq=0), dict(Hkv=0), dict(D=0), dict(Hq=6, Hkv=4),
+    dict(scale=float("nan")), dict(softcap=float("inf")),
+    dict(q=ctypes.c_void_p(0x10008)), dict(lse=ctypes.c_void_p(0x10002)),
+    dict(d_len=ctypes.c_void_p(0x10001)),
+    dict(ws=None, ws_bytes=1024), dict(ws=ctypes.c_void_p(0x10010), ws_bytes=1 << 30),
+    dict(ws=ctypes.c_void_p(0x10000), ws_bytes=256),
+]
+
+
+@pytest.mark.parametrize("over", LEN_INVALID, ids=lambda d: ",".join(f"{k}" for k in d))
+def test_decode_len_invalid_arguments_rejected(over):
+    assert call_len(**over) == 1, over
+    assert mfa.load_library().mfa_last_error().decode()
+
+
+@pytest.mark.parametrize("over", [dict(D=96), dict(dtype=0), dict(dtype=5), dict(R=5, Hq=8, Hkv=2),
+                                  dict(R=2, Hq=32, Hkv=2)])
+def test_decode_len_unsupported_rejected(over):
+    assert call_len(**over) == 2, over
+
+
+def test_decode_len_empty_batch_and_workspace_size():
+    import torch
+    assert call_len(B=0) == 0
+    n = mfa.decode_len_workspace_size(64, 4, 32768, 32, 8, 128, torch.bfloat16)
+    s = ctypes.c_int(0)
+    mfa.load_library().mfa_fwd_plan(64, 1, 32768, 32, 8, 128, 2, ctypes.byref(s))
+    # (m, l) and D partial sums for every (batch, row, head, split)
+    assert n >= 64 * 4 * 32 * s.value * (128 + 2) * 4
+    assert mfa.decode_len_workspace_size(64, 5, 32768, 32, 8, 128, torch.bfloat16) == 0
+    assert mfa.decode_len_workspace_size(2, 1, 64, 8, 2, 128, torch.bfloat16, splits=3) >= \
+        2 * 8 * 3 * (128 + 2) * 4

@@ -24,6 +24,7 @@ PATH_NAMES = {PATH_AUTO: "auto", PATH_GENERIC: "generic", PATH_MFMA: "mfma",
 _DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: MFA_BF16}
 
 EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
+            "mfa_decode_len", "mfa_decode_len_workspace_size",
             "mfa_status_string", "mfa_last_error", "mfa_version")
 
 
@@ -60,6 +61,10 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_fwd_workspace_size.argtypes = [_I] * 7
     lib.mfa_fwd_plan.restype = _I
     lib.mfa_fwd_plan.argtypes = [_I] * 7 + [ctypes.POINTER(_I)]
+    lib.mfa_decode_len.restype = _I
+    lib.mfa_decode_len.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_decode_len_workspace_size.restype = ctypes.c_size_t
+    lib.mfa_decode_len_workspace_size.argtypes = [_I] * 8
     lib.mfa_status_string.restype = ctypes.c_char_p
     lib.mfa_status_string.argtypes = [_I]
     lib.mfa_last_error.restype = ctypes.c_char_p
@@ -149,6 +154,59 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         else:
             _check(lib.mfa_fwd(*args, s))
     return out, lse
+
+
+def decode_len(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               d_len: torch.Tensor, *, softcap: float = 0.0, scale: Optional[float] = None,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               return_lse: bool = True, splits: int = 0,
+               workspace: Optional[torch.Tensor] = None, stream=None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Decode over the first d_len[b] rows of a fixed-capacity cache
+    (mfa_decode_len).
+
+    q [B, R, Hq, D]; k_cache, v_cache [B, Lmax, Hkv, D] (fp16 or bf16, one
+    dtype, contiguous, on one GPU); d_len int32 [B] on the same GPU, read by
+    the kernels when they run.  Row r of batch b attends to keys
+    0 .. d_len[b] - R + r.  Returns (out [B, R, Hq, D], lse [B, Hq, R] float32
+    or None).  ``workspace`` (a uint8 device tensor of at least
+    decode_len_workspace_size bytes) makes the call allocation-free, as graph
+    capture needs.
+    """
+    lib = load_library()
+    B, R, Lmax, Hq, Hkv, D = _dims(q, k_cache, v_cache)
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or \
+            v_cache.dtype != q.dtype:
+        raise TypeError(f"dtypes must match and be float16 or bfloat16 "
+                        f"(got {q.dtype}, {k_cache.dtype}, {v_cache.dtype})")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if d_len.dtype != torch.int32 or tuple(d_len.shape) != (B,) or not d_len.is_cuda or \
+            not d_len.is_contiguous():
+        raise ValueError("d_len must be a contiguous int32 GPU tensor of shape [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous and match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, R), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, Hq, R) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, Hq, R]")
+    with torch.cuda.device(q.device):
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.mfa_decode_len(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                  _ptr(d_len), B, R, Lmax, Hq, Hkv, D, float(scale), float(softcap),
+                                  _DTYPE_CODES[q.dtype], int(splits), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))
+    return out, lse
+
+
+def decode_len_workspace_size(B, R, Lmax, Hq, Hkv, D, dtype: torch.dtype, splits: int = 0) -> int:
+    return int(load_library().mfa_decode_len_workspace_size(B, R, Lmax, Hq, Hkv, D,
+                                                            _DTYPE_CODES[dtype], int(splits)))
 
 
 def workspace_size(B, Lq, Lk, Hq, Hkv, D, dtype: torch.dtype) -> int:

@@ -17,6 +17,13 @@
 //                                          transposing LDS reads
 // Query heads beyond Hq/Hkv (columns g..15) compute on zeros and are dropped.
 //
+// With a device-held length (same header, flash_attention_decode_len) the
+// kernel serves R query rows per batch, the columns being (row, head) pairs,
+// R * Hq/Hkv <= 16: row r attends causally to the first len - R + 1 + r keys
+// of the cache.  The length is read on the device and the splits divide its
+// tiles, so the launch shape depends on the cache capacity only and rows past
+// the length cost nothing.
+//
 // Each split writes (m, l, O_unnormalised[D]) in base-2 units; the combine
 // kernel merges them: M = max m_s, w_s = 2^(m_s - M), O = sum w_s O_s / sum
 // w_s l_s, LSE = (M + log2 sum w_s l_s) ln 2.  Empty splits carry m = -inf,
@@ -32,10 +39,11 @@ namespace {
 constexpr int DT = 32;  // keys per tile
 
 struct DecodeArgs {
-    FwdArgs f;
+    FwdArgs f;                // Lq = R query rows per batch; Lk = cache rows
+    const int* d_len;         // [B] valid lengths on the device, or null (Lq = 1, key_range)
     int splits;
-    float* part_ml;   // [B, Hq, S, 2]: m (base 2), l
-    float* part_o;    // [B, Hq, S, D]
+    float* part_ml;   // [B, R, Hq, S, 2]: m (base 2), l
+    float* part_o;    // [B, R, Hq, S, D]
 };
 
 // Visible-key bits of tile t (keys 32t .. 32t+31) from the packed mask.
@@ -64,10 +72,25 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
     const int g = a.group;
     const int col = lane & 15;          // query column of the MFMA tiles
     const int grp = lane >> 4;          // lane group 0..3
+    const int R = a.Lq;
+    const int crow = col / g;           // column -> (query row, head in the group)
+    const int chead = col - crow * g;
+    const bool real = crow < R;
 
-    // key range of the single query and this split's share of its tiles
-    int lo, hi;
-    key_range(a.q_offset, a.Lk, a.causal, a.window, lo, hi);
+    // Keys [lo, hi] of all columns, this column's last key hi_col and the last
+    // key every column sees (hi_min), then this split's share of the tiles.
+    int lo, hi, hi_col, hi_min;
+    if (da.d_len) {
+        int n = da.d_len[b];
+        n = n < 0 ? 0 : (n > a.Lk ? a.Lk : n);
+        lo = 0;
+        hi = n - 1;
+        hi_min = n - R;
+        hi_col = n - R + (real ? crow : R - 1);
+    } else {
+        key_range(a.q_offset, a.Lk, a.causal, a.window, lo, hi);
+        hi_col = hi_min = hi;
+    }
     int t_begin = 0, t_end = 0;
     if (lo <= hi) {
         const int t_lo = lo / DT, n_t = hi / DT - t_lo + 1;
@@ -76,13 +99,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
     }
     const uint64_t* words = MASK ? a.mask_words + (int64_t)b * a.words_per_batch : nullptr;
 
-    // Q^T operand: lane (col, grp) holds Q[head col][32 ks + 8 grp .. +7]
+    // Q^T operand: lane (col, grp) holds Q[row crow][head kvh*g + chead][32 ks + 8 grp .. +7]
     const T* __restrict__ qp = static_cast<const T*>(a.q);
     v8 qop[NKS];
     {
-        const int hq = kvh * g + col;
-        const bool real = col < g;
-        const T* qrow = qp + ((int64_t)b * a.Hq + (real ? hq : 0)) * D;  // Lq = 1
+        const int hq = kvh * g + chead;
+        const T* qrow = qp + (((int64_t)b * R + (real ? crow : 0)) * a.Hq + (real ? hq : 0)) * D;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qrow + ks * 32 + grp * 8);
@@ -157,7 +179,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
 
         // transform, mask, running max
         const uint32_t bits = MASK ? tile_mask_bits(words, t) : 0xffffffffu;
-        const bool interior = t * DT >= lo && t * DT + DT - 1 <= hi && (!MASK || bits == 0xffffffffu);
+        const bool interior = t * DT >= lo && t * DT + DT - 1 <= hi_min && (!MASK || bits == 0xffffffffu);
         float x[8];
         float tmax = -INFINITY;
 #pragma unroll
@@ -170,7 +192,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
                 if (!interior) {
                     const int kk = blk * 16 + grp * 4 + i;
                     const int key = t * DT + kk;
-                    const bool vis = key >= lo && key <= hi && ((bits >> kk) & 1u);
+                    const bool vis = key >= lo && key <= hi_col && ((bits >> kk) & 1u);
                     v = vis ? v : -INFINITY;
                 }
                 x[blk * 4 + i] = v;
@@ -215,9 +237,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
     // lane groups hold disjoint keys of the same query column: total the sum
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (col < g) {
-        const int hq = kvh * g + col;
-        const int64_t slot = ((int64_t)b * a.Hq + hq) * da.splits + split;
+    if (real) {
+        const int hq = kvh * g + chead;
+        const int64_t slot = (((int64_t)b * R + crow) * a.Hq + hq) * da.splits + split;
         if (grp == 0) {
             da.part_ml[slot * 2 + 0] = m;
             da.part_ml[slot * 2 + 1] = l;
@@ -233,7 +255,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs da) {
     const FwdArgs& a = da.f;
-    const int bh = blockIdx.x;          // b * Hq + hq
+    const int bh = blockIdx.x;          // (b * R + r) * Hq + hq
     const int lane = threadIdx.x;
     const int S = da.splits;
     const float* ml = da.part_ml + (int64_t)bh * S * 2;
@@ -252,11 +274,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs da) {
         for (int c = 0; c < D / 64; ++c) acc[c] += w * po[(int64_t)s * D + lane + 64 * c];
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    T* out = static_cast<T*>(a.out) + (int64_t)bh * D;   // Lq = 1: [B, 1, Hq, D]
+    T* out = static_cast<T*>(a.out) + (int64_t)bh * D;   // [B, R, Hq, D]
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) out[lane + 64 * c] = static_cast<T>(acc[c] * inv);
-    if (a.lse && lane == 0)
-        a.lse[bh] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+    if (a.lse && lane == 0) {
+        const int hq = bh % a.Hq, br = bh / a.Hq;          // LSE is [B, Hq, R]
+        const int r = br % a.Lq, b = br / a.Lq;
+        a.lse[((int64_t)b * a.Hq + hq) * a.Lq + r] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+    }
 }
 
 template <typename T, int D, bool CAP, bool MASK>
@@ -265,7 +290,7 @@ hipError_t launch_t(const DecodeArgs& da, hipStream_t s) {
     hipLaunchKernelGGL((decode_split_kernel<T, D, CAP, MASK>), dim3(da.splits, a.Hkv, a.B), dim3(64), 0, s, da);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Hq), dim3(64), 0, s, da);
+    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Lq * a.Hq), dim3(64), 0, s, da);
     return hipGetLastError();
 }
 
@@ -283,6 +308,11 @@ bool split_decode_supported(int dtype, int D, int Lq, int group) {
            group <= 16;
 }
 
+bool decode_len_supported(int dtype, int D, int R, int group) {
+    return (dtype == kBF16 || dtype == kF16) && (D == 64 || D == 128) && R >= 1 && group >= 1 &&
+           R * group <= 16;
+}
+
 // Enough (split, kv head, batch) waves to fill the chip several times over,
 // but at least 8 tiles (256 keys) per split.
 int split_decode_default_splits(int B, int Hkv, int Lk, int group) {
@@ -298,16 +328,18 @@ int split_decode_default_splits(int B, int Hkv, int Lk, int group) {
     return (int)s;
 }
 
-size_t split_decode_workspace_bytes(int B, int Hq, int D, int splits) {
-    const size_t slots = (size_t)B * Hq * splits;
+size_t split_decode_workspace_bytes(int B, int R, int Hq, int D, int splits) {
+    const size_t slots = (size_t)B * R * Hq * splits;
     return slots * 2 * sizeof(float) + 256 + slots * D * sizeof(float);
 }
 
-hipError_t launch_split_decode(const FwdArgs& a, int dtype, int splits, float* partials, hipStream_t s) {
+hipError_t launch_split_decode(const FwdArgs& a, const int* d_len, int dtype, int splits, float* partials,
+                               hipStream_t s) {
     DecodeArgs da;
     da.f = a;
+    da.d_len = d_len;
     da.splits = splits;
-    const size_t slots = (size_t)a.B * a.Hq * splits;
+    const size_t slots = (size_t)a.B * a.Lq * a.Hq * splits;
     da.part_ml = partials;
     const size_t ml_bytes = (slots * 2 * sizeof(float) + 255) & ~size_t(255);
     da.part_o = reinterpret_cast<float*>(reinterpret_cast<char*>(partials) + ml_bytes);

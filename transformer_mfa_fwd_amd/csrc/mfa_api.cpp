@@ -89,7 +89,7 @@ size_t workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype,
     size_t ws = mask_words_bytes(B, Lk);
     if (path == MFA_PATH_SPLIT_DECODE) {
         (void)Lq; (void)dtype;
-        ws += align256(mfa::split_decode_workspace_bytes(B, Hq, D, splits));
+        ws += align256(mfa::split_decode_workspace_bytes(B, 1, Hq, D, splits));
     }
     (void)Hkv;
     return ws;
@@ -180,7 +180,7 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
             case MFA_PATH_GENERIC: e = mfa::launch_generic(a, c.dtype, stream); break;
             case MFA_PATH_MFMA: e = mfa::launch_mfma_prefill(a, c.dtype, stream); break;
             case MFA_PATH_SPLIT_DECODE:
-                e = mfa::launch_split_decode(a, c.dtype, splits,
+                e = mfa::launch_split_decode(a, nullptr, c.dtype, splits,
                                              reinterpret_cast<float*>(wsb + mask_words_bytes(c.B, c.Lk)),
                                              stream);
                 break;
@@ -197,9 +197,117 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
     return MFA_SUCCESS;
 }
 
+struct LenCall {
+    const void *q, *k, *v;
+    void* out;
+    float* lse;
+    const int* d_len;
+    int B, R, Lmax, Hq, Hkv, D;
+    float scale, softcap;
+    int dtype;
+};
+
+int validate_len(const LenCall& c) {
+    if (!c.q || !c.k || !c.v || !c.out || !c.d_len)
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k_cache, v_cache, out and d_len must be non-null");
+    if (c.B < 0 || c.R <= 0 || c.Lmax <= 0 || c.Hq <= 0 || c.Hkv <= 0 || c.D <= 0)
+        return fail(MFA_ERROR_INVALID_VALUE,
+                    "bad dimensions B=%d R=%d Lmax=%d Hq=%d Hkv=%d D=%d (B >= 0; others > 0)",
+                    c.B, c.R, c.Lmax, c.Hq, c.Hkv, c.D);
+    if (c.Hq % c.Hkv != 0)
+        return fail(MFA_ERROR_INVALID_VALUE, "Hkv=%d does not divide Hq=%d", c.Hkv, c.Hq);
+    if (!std::isfinite(c.scale) || !std::isfinite(c.softcap))
+        return fail(MFA_ERROR_INVALID_VALUE, "scale and softcap must be finite");
+    if (c.dtype != MFA_F32 && c.dtype != MFA_F16 && c.dtype != MFA_BF16)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "unknown dtype %d", c.dtype);
+    if (!mfa::decode_len_supported(c.dtype, c.D, c.R, c.Hq / c.Hkv))
+        return fail(MFA_ERROR_NOT_SUPPORTED,
+                    "decode over a device length needs fp16/bf16, D in {64,128} and R * Hq/Hkv <= 16 "
+                    "(dtype=%d D=%d R=%d Hq/Hkv=%d)", c.dtype, c.D, c.R, c.Hq / c.Hkv);
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.out, 16))
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (!aligned(c.lse, 4) || !aligned(c.d_len, 4))
+        return fail(MFA_ERROR_INVALID_VALUE, "lse and d_len must be 4-byte aligned");
+    const int64_t q_elems = (int64_t)c.B * c.R * c.Hq * c.D;
+    const int64_t kv_elems = (int64_t)c.B * c.Lmax * c.Hkv * c.D;
+    if (q_elems < 0 || kv_elems < 0 || (int64_t)c.B * c.R * c.Hq > (int64_t)1 << 30)
+        return fail(MFA_ERROR_INVALID_VALUE, "problem too large");
+    return MFA_SUCCESS;
+}
+
+int len_splits(int B, int Hkv, int Lmax, int group, int splits) {
+    if (splits <= 0) splits = mfa::split_decode_default_splits(B, Hkv, Lmax, group);
+    return splits > Lmax ? Lmax : splits;
+}
+
+int run_len(const LenCall& c, int splits, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    int st = validate_len(c);
+    if (st != MFA_SUCCESS) return st;
+    if (c.B == 0) return MFA_SUCCESS;
+    const int group = c.Hq / c.Hkv;
+    splits = len_splits(c.B, c.Hkv, c.Lmax, group, splits);
+    const size_t need = align256(mfa::split_decode_workspace_bytes(c.B, c.R, c.Hq, c.D, splits));
+    const bool use_pool = workspace == nullptr && ws_bytes == 0;
+    if (!use_pool) {
+        if (!workspace) return fail(MFA_ERROR_INVALID_VALUE, "workspace is null but ws_bytes > 0");
+        if (!aligned(workspace, 256)) return fail(MFA_ERROR_INVALID_VALUE, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(MFA_ERROR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    }
+
+    mfa::FwdArgs a{};
+    a.q = c.q; a.k = c.k; a.v = c.v; a.out = c.out; a.lse = c.lse;
+    a.B = c.B; a.Lq = c.R; a.Lk = c.Lmax; a.Hq = c.Hq; a.Hkv = c.Hkv; a.D = c.D;
+    a.group = group;
+    a.causal = 1;
+    a.scale = c.scale;
+    a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
+    const float log2e = 1.4426950408889634f;
+    a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * c.scale;
+
+    void* ws = workspace;
+    if (use_pool) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
+        prepare_pool(dev);
+        hipError_t e = hipMallocAsync(&ws, need, stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
+                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
+        }
+    }
+    hipError_t e = mfa::launch_split_decode(a, c.d_len, c.dtype, splits, static_cast<float*>(ws), stream);
+    if (use_pool) {
+        hipError_t e2 = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return MFA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mfa_decode_len(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                   const int* d_len, int B, int R, int Lmax, int Hq, int Hkv, int D,
+                   float scale, float softcap, int dtype, int splits,
+                   void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    LenCall c{q, k_cache, v_cache, out, lse, d_len, B, R, Lmax, Hq, Hkv, D, scale, softcap, dtype};
+    return run_len(c, splits, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, int D, int dtype, int splits) {
+    if (B <= 0 || R <= 0 || Lmax <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return 0;
+    if (!mfa::decode_len_supported(dtype, D, R, Hq / Hkv)) return 0;
+    splits = len_splits(B, Hkv, Lmax, Hq / Hkv, splits);
+    return align256(mfa::split_decode_workspace_bytes(B, R, Hq, D, splits));
+}
 
 int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
             int B, int Lq, int Lk, int Hq, int Hkv, int D,
@@ -270,6 +378,6 @@ const char* mfa_status_string(int status) {
 
 const char* mfa_last_error(void) { return g_last_error.c_str(); }
 
-int mfa_version(void) { return 100; }
+int mfa_version(void) { return 200; }
 
 }  // extern "C"

@@ -53,10 +53,13 @@ hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s);
 hipError_t launch_generic(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s);
 bool mfma_prefill_supported(int dtype, int D);
-hipError_t launch_split_decode(const FwdArgs& a, int dtype, int splits, float* partials,
-                               hipStream_t s);
+// Split decode: a.Lq query rows per batch (1 unless d_len is given).  With
+// d_len (device [B]) the key range of batch b is its first d_len[b] keys.
+hipError_t launch_split_decode(const FwdArgs& a, const int* d_len, int dtype, int splits,
+                               float* partials, hipStream_t s);
 bool split_decode_supported(int dtype, int D, int Lq, int group);
+bool decode_len_supported(int dtype, int D, int R, int group);
 int split_decode_default_splits(int B, int Hkv, int Lk, int group);
-size_t split_decode_workspace_bytes(int B, int Hq, int D, int splits);
+size_t split_decode_workspace_bytes(int B, int R, int Hq, int D, int splits);
 
 }  // namespace mfa

@@ -78,6 +78,11 @@ ALL = [SINGLE_HEAD_CAUSAL_FP32, GQA_CAUSAL_PREFILL_BF16, BIDIR_WINDOW_ENCODER_FP
        LONG_CACHE_DECODE_BF16, CAUSAL_WINDOW_SOFTCAP_BF16]
 BY_NAME = {w.name: w for w in ALL}
 
+# Decode over a device-held length: Lq is the number R of query rows per batch
+# (a block of draft tokens) and Lk the cache capacity.
+DEVICE_LENGTH_DECODE_BF16 = Workload("device_length_decode_bf16_B64_R4_cap32768_H32_KV8_D128", "bf16",
+                                     64, 4, 32768, 32, 8, 128, True)
+
 
 def make_key_mask(w: Workload, seed: int = 0) -> Optional[torch.Tensor]:
     """[B, Lk] float32 key mask on the CPU (1 = keep, 0 = drop), or None."""
@@ -100,6 +105,21 @@ def make_key_mask(w: Workload, seed: int = 0) -> Optional[torch.Tensor]:
     else:
         raise ValueError(f"unknown mask kind {w.mask!r}")
     return m
+
+
+def make_cache_lengths(B: int, Lmax: int, R: int, seed: int = 0, edges: bool = True,
+                       low: int = 0) -> torch.Tensor:
+    """[B] int32 valid lengths on the CPU: with ``edges`` the first entries are
+    0, 1, R - 1, R, Lmax - 1 and Lmax (as many as fit, duplicates allowed),
+    the rest uniform in [low, Lmax] from a CPU generator seeded with ``seed``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    n = torch.randint(low, Lmax + 1, (B,), generator=g, dtype=torch.int64)
+    if edges:
+        fixed = [0, 1, max(R - 1, 0), R, Lmax - 1, Lmax]
+        for i, x in enumerate(fixed[:B]):
+            n[i] = min(max(x, 0), Lmax)
+    return n.to(torch.int32)
 
 
 def make_inputs(w: Workload, device="cpu", seed: int = 0):
