@@ -1,7 +1,7 @@
 """Benchmark of the fused attention forward (libmfa) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-decode] [--no-cpu-baseline]
+                    [--no-decode] [--no-decode-len] [--no-cpu-baseline]
 
 A step is one mfa_fwd call over one batch of synthetic input already resident
 in HBM: the whole forward (tile ranges, Q/K/V staging, Q.K^T, soft-cap and
@@ -10,7 +10,9 @@ default workload is the causal GQA prefill (B=4, L=2048, Hq=32, Hkv=8,
 D=128, bf16); FLOPs count 4*D per visible (query, key) pair and query head.
 The long-cache decode (B=64, Lk=32768, Hq=32, Hkv=8, D=128, bf16; split over
 keys plus combine) is timed in the same run and reported under "decode" in
-HBM GB/s of compulsory traffic.
+HBM GB/s of compulsory traffic, and so is the decode over a device-held length
+(mfa_decode_len: 4 draft rows per batch on the same cache, full and half-full)
+under "decode_len".
 
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
 average duration comes from HIP events recorded on the launch stream around
@@ -149,6 +151,47 @@ def time_workload(w, steps: int, warmup: int, seed: int = 0, warmup_ms: float = 
     return res, (q, k, v, m)
 
 
+def time_decode_len(w, lens_cpu, steps: int, warmup: int, warmup_ms: float = 0.0, seed: int = 0):
+    """mfa_decode_len on workload w (Lq = draft rows R, Lk = capacity) with the
+    given per-batch lengths, timed like time_workload.  Algorithmic bytes: Q and
+    O, the LSE, the lengths and the K and V rows below each length."""
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    q, k, v, _ = wl.make_inputs(w, "cuda", seed)
+    d_len = lens_cpu.to("cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=q.device)
+    nbytes = mfa.decode_len_workspace_size(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    n_warm = 0
+    t_w = time.perf_counter()
+    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
+        mfa.decode_len(q, k, v, d_len, out=out, lse=lse, workspace=ws)
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        s_.record(stream)
+        mfa.decode_len(q, k, v, d_len, out=out, lse=lse, workspace=ws)
+        e_.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    el = q.element_size()
+    valid = int(lens_cpu.clamp(0, w.Lk).sum())
+    nbytes_alg = (2 * q.numel() * el + lse.numel() * 4 + w.B * 4 + 2 * valid * w.Hkv * w.D * el)
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+    return dict(wall_ms=wall_ms, kernel_ms=kern_ms, bytes=nbytes_alg, valid_keys=valid)
+
+
 def cpu_baseline(w, tensors, target_s: float = 12.0, seed: int = 0):
     """Time the fp64 oracle on a seeded sample of query rows of the workload."""
     from oracle import default_oracle
@@ -188,6 +231,7 @@ def main():
                     help="keep warming up until this much time has passed (clock ramp)")
     ap.add_argument("--workload", default="gqa_causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode-len", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
@@ -276,6 +320,24 @@ def main():
         del td
         torch.cuda.empty_cache()
         tensors = None
+
+    if not args.no_decode_len:
+        del tensors
+        torch.cuda.empty_cache()
+        tensors = None
+        wl_len = wl.DEVICE_LENGTH_DECODE_BF16
+        dl = {"workload": wl_len.name, "api": "mfa_decode_len", "unit": "GB/s", "R": wl_len.Lq,
+              "capacity": wl_len.Lk, "peak": PEAK_HBM_GBS}
+        for tag, fill in (("full", 1.0), ("half", 0.5)):
+            lens = torch.full((wl_len.B,), int(wl_len.Lk * fill), dtype=torch.int32)
+            r = time_decode_len(wl_len, lens, max(10, args.steps // 2), max(3, args.warmup // 2),
+                                warmup_ms=args.warmup_ms)
+            dl[tag] = {"lengths": int(lens[0]), "value": round(r["bytes"] / (r["wall_ms"] * 1e-3) / 1e9, 1),
+                       "ms_per_step": round(r["wall_ms"], 5), "kernel_ms_avg": round(r["kernel_ms"], 5),
+                       "achieved": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                       "frac": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes_per_launch": r["bytes"]}
+        line["decode_len"] = dl
 
     if not args.no_cpu_baseline:
         if tensors is None:
