@@ -145,6 +145,44 @@ class Oracle:
             O[b], L[b], N[b] = Ob[0], Lb[0], Nb[0]
         return O, L, N
 
+    def packed_qkv(self, qkv, seq_bounds, num_heads, *, scale, window=0, softcap=0.0, nthreads=1):
+        """Bidirectional attention over sequences packed back to back in one
+        fused QKV tensor (brotensor flash_attention.h,
+        flash_attention_packed_qkv_forward): each row attends only inside its
+        own sequence, with the bidirectional window (|r - j| <= window/2) when
+        window > 0.  The sequences are independent problems, so each is the
+        plain forward on its own rows.  qkv [L, 3*H*D] (per row: query heads,
+        key heads, value heads); seq_bounds [L, 2].  Returns O [L, H, D],
+        LSE [H, L] and the visible counts [H, L].
+        """
+        x = _f32(qkv)
+        try:
+            import torch
+            if isinstance(seq_bounds, torch.Tensor):
+                seq_bounds = seq_bounds.detach().cpu().numpy()
+        except ImportError:  # pragma: no cover
+            pass
+        sb = np.asarray(seq_bounds, dtype=np.int64).reshape(-1, 2)
+        L = x.shape[0]
+        H = int(num_heads)
+        D = x.shape[1] // (3 * H)
+        q = x[:, :H * D].reshape(1, L, H, D)
+        k = x[:, H * D:2 * H * D].reshape(1, L, H, D)
+        v = x[:, 2 * H * D:].reshape(1, L, H, D)
+        O = np.zeros((L, H, D), np.float64)
+        LSE = np.full((H, L), -np.inf, np.float64)
+        N = np.zeros((H, L), np.int64)
+        r = 0
+        while r < L:
+            s0, s1 = int(sb[r, 0]), int(sb[r, 1])
+            if not (s0 == r and s1 > r and s1 <= L and np.all(sb[s0:s1] == (s0, s1))):
+                raise ValueError(f"row {r}: bounds ({s0}, {s1}) do not describe back-to-back sequences")
+            Os, Ls, Ns = self.full(q[:, s0:s1], k[:, s0:s1], v[:, s0:s1], scale=scale, causal=False,
+                                   window=window, q_offset=0, softcap=softcap, nthreads=nthreads)
+            O[s0:s1], LSE[:, s0:s1], N[:, s0:s1] = Os[0], Ls[0], Ns[0]
+            r = s1
+        return O, LSE, N
+
     def visible_counts(self, B, Lq, Lk, *, causal=False, window=0, q_offset=None, key_mask=None):
         """Visible-key count of every row, [B, Lq] int64, and the total."""
         m = _f32(key_mask)

@@ -514,6 +514,102 @@ def pin_decode_len_ignores_rows_past_length(orc):
     _close(L2, L, 0.0, "decode_len past-length rows perturbed LSE")
 
 
+# ---------------------------------------------------------------------------
+# sequences packed back to back in one fused QKV tensor
+# ---------------------------------------------------------------------------
+
+def packed_bounds(lengths):
+    rows, s = [], 0
+    for n in lengths:
+        rows += [(s, s + n)] * n
+        s += n
+    return np.array(rows, np.int64).reshape(-1, 2)
+
+
+def packed_visibility(sb, window):
+    """[L, L] visibility as brotensor flash_attention.h states it for the
+    packed-QKV forward: row r sees key j of its own sequence
+    [sb[r,0], sb[r,1]), and with a window only when |r - j| <= window/2."""
+    L = sb.shape[0]
+    vis = np.zeros((L, L), bool)
+    for r in range(L):
+        for j in range(L):
+            vis[r, j] = sb[r, 0] <= j < sb[r, 1] and (window <= 0 or abs(r - j) <= window // 2)
+    return vis
+
+
+def dense_packed(qkv, sb, H, *, scale, window, softcap=0.0):
+    x = np.asarray(qkv, np.float64)
+    L = x.shape[0]
+    D = x.shape[1] // (3 * H)
+    vis = packed_visibility(sb, window)
+    O = np.zeros((L, H, D))
+    LSE = np.zeros((H, L))
+    for h in range(H):
+        q = x[:, h * D:(h + 1) * D]
+        k = x[:, (H + h) * D:(H + h + 1) * D]
+        v = x[:, (2 * H + h) * D:(2 * H + h + 1) * D]
+        s = scale * (q @ k.T)
+        if softcap > 0:
+            s = softcap * np.tanh(s / softcap)
+        s = np.where(vis, s, -np.inf)
+        lse = logsumexp(s, axis=1)
+        O[:, h, :] = np.exp(s - lse[:, None]) @ v
+        LSE[h] = lse
+    return O, LSE
+
+
+def pin_packed_matches_dense(orc):
+    """Against the full packed score matrix with the pages' row rule."""
+    rng = _rng(17)
+    for lengths, H, window, softcap in [([5, 1, 9, 3], 2, 0, 0.0), ([7, 8], 1, 4, 0.0),
+                                        ([1, 1, 12], 3, 5, 2.0), ([16], 2, 6, 0.0)]:
+        D = 8
+        L = sum(lengths)
+        qkv = _rand(rng, (L, 3 * H * D), 2.0)
+        sb = packed_bounds(lengths)
+        O, LSE, N = orc.packed_qkv(qkv, sb, H, scale=0.4, window=window, softcap=softcap)
+        Od, Ld = dense_packed(qkv, sb, H, scale=0.4, window=window, softcap=softcap)
+        _close(O, Od, TIGHT, f"packed O {lengths}")
+        _close(LSE, Ld, TIGHT, f"packed LSE {lengths}")
+        assert np.array_equal(N, np.broadcast_to(packed_visibility(sb, window).sum(1), (H, L)))
+
+
+def pin_packed_zero_query_closed_form(orc):
+    """Q = 0: each row is the mean of the V rows of its sequence inside the
+    window, LSE = ln(count)."""
+    rng = _rng(18)
+    lengths, H, D, window = [4, 10, 1, 6], 2, 8, 6
+    L = sum(lengths)
+    qkv = _rand(rng, (L, 3 * H * D))
+    qkv[:, :H * D] = 0.0
+    sb = packed_bounds(lengths)
+    O, LSE, _ = orc.packed_qkv(qkv, sb, H, scale=0.9, window=window)
+    for r in range(L):
+        js = [j for j in range(sb[r, 0], sb[r, 1]) if abs(r - j) <= window // 2]
+        for h in range(H):
+            v = qkv[js, (2 * H + h) * D:(2 * H + h + 1) * D].astype(np.float64)
+            assert np.max(np.abs(O[r, h] - v.mean(0))) <= TIGHT
+            assert abs(LSE[h, r] - math.log(len(js))) <= TIGHT
+
+
+def pin_packed_sequences_are_independent(orc):
+    """Changing one sequence's rows (any of Q, K, V) leaves the others exactly
+    unchanged."""
+    rng = _rng(19)
+    lengths, H, D = [6, 9, 5], 2, 8
+    L = sum(lengths)
+    qkv = _rand(rng, (L, 3 * H * D))
+    sb = packed_bounds(lengths)
+    O, LSE, _ = orc.packed_qkv(qkv, sb, H, scale=0.5, window=0)
+    qkv2 = qkv.copy()
+    qkv2[6:15] = 1e3
+    O2, L2, _ = orc.packed_qkv(qkv2, sb, H, scale=0.5, window=0)
+    keep = np.r_[0:6, 15:20]
+    _close(O2[keep], O[keep], 0.0, "other sequences perturbed")
+    _close(L2[:, keep], LSE[:, keep], 0.0, "other sequences perturbed LSE")
+
+
 ALL_PINS = [
     pin_range_causal_matches_ferrotensor_rule,
     pin_range_causal_matches_forge_rule,
@@ -535,4 +631,7 @@ ALL_PINS = [
     pin_decode_len_matches_dense,
     pin_decode_len_zero_query_closed_form,
     pin_decode_len_ignores_rows_past_length,
+    pin_packed_matches_dense,
+    pin_packed_zero_query_closed_form,
+    pin_packed_sequences_are_independent,
 ]
