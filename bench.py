@@ -1,7 +1,8 @@
 """Benchmark of the fused attention forward (libmfa) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-decode] [--no-decode-len] [--no-cpu-baseline]
+                    [--no-decode] [--no-decode-len] [--no-packed]
+                    [--no-cpu-baseline]
 
 A step is one mfa_fwd call over one batch of synthetic input already resident
 in HBM: the whole forward (tile ranges, Q/K/V staging, Q.K^T, soft-cap and
@@ -12,7 +13,10 @@ The long-cache decode (B=64, Lk=32768, Hq=32, Hkv=8, D=128, bf16; split over
 keys plus combine) is timed in the same run and reported under "decode" in
 HBM GB/s of compulsory traffic, and so is the decode over a device-held length
 (mfa_decode_len: 4 draft rows per batch on the same cache, full and half-full)
-under "decode_len".
+under "decode_len".  "packed_encoder" times the bidirectional encoder workload
+(B=8, L=8192, H=12, D=64, fp16, window 128, tail padding) twice: padded with a
+key mask through mfa_fwd, and packed without its padding through
+mfa_packed_qkv_fwd.
 
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
 average duration comes from HIP events recorded on the launch stream around
@@ -192,6 +196,64 @@ def time_decode_len(w, lens_cpu, steps: int, warmup: int, warmup_ms: float = 0.0
     return dict(wall_ms=wall_ms, kernel_ms=kern_ms, bytes=nbytes_alg, valid_keys=valid)
 
 
+def time_calls(fn, steps: int, warmup: int, warmup_ms: float = 0.0):
+    """Average wall ms per call and average HIP-event ms per call of fn()."""
+    import torch
+    n_warm = 0
+    t_w = time.perf_counter()
+    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
+        fn()
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        s_.record(stream)
+        fn()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def packed_encoder(steps: int, warmup: int, warmup_ms: float):
+    """The padded encoder workload against its packed form, which carries no
+    padding rows (so it also drops the padding rows' pairs)."""
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    w = wl.BIDIR_WINDOW_ENCODER_FP16
+    res = {"workload": w.name, "unit": "TFLOP/s"}
+    q, k, v, m = wl.make_inputs(w, "cuda")
+    pairs = visible_pairs(w, m.cpu())
+    out = torch.empty_like(q)
+    wall, kern = time_calls(lambda: mfa.fwd(q, k, v, causal=False, window=w.window, key_mask=m,
+                                            out=out, return_lse=False), steps, warmup, warmup_ms)
+    res["padded"] = {"api": "mfa_fwd + key mask", "rows": w.B * w.Lq, "ms_per_step": round(wall, 5),
+                     "kernel_ms_avg": round(kern, 5),
+                     "visible_pairs": pairs, "value": round(4.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
+    del q, k, v, m, out
+    torch.cuda.empty_cache()
+    lengths = wl.encoder_packing_lengths(w)
+    qkv, sb = wl.make_packed_qkv(lengths, w.Hq, w.D, w.dtype, "cuda")
+    out = torch.empty((qkv.shape[0], w.Hq * w.D), dtype=qkv.dtype, device="cuda")
+    wall, kern = time_calls(lambda: mfa.packed_qkv_fwd(qkv, sb, w.Hq, window=w.window, out=out,
+                                                       return_lse=False), steps, warmup, warmup_ms)
+    half = w.window // 2
+    # the padded form also counts its padding rows' pairs with valid keys near the boundary
+    ppairs = w.Hq * sum(sum(min(n - 1, r + half) - max(0, r - half) + 1 for r in range(n)) for n in lengths)
+    res["packed"] = {"api": "mfa_packed_qkv_fwd", "rows": int(qkv.shape[0]), "ms_per_step": round(wall, 5),
+                     "kernel_ms_avg": round(kern, 5),
+                     "visible_pairs": ppairs, "value": round(4.0 * w.D * ppairs / (wall * 1e-3) / 1e12, 2)}
+    del qkv, sb, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, tensors, target_s: float = 12.0, seed: int = 0):
     """Time the fp64 oracle on a seeded sample of query rows of the workload."""
     from oracle import default_oracle
@@ -232,6 +294,7 @@ def main():
     ap.add_argument("--workload", default="gqa_causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-len", action="store_true")
+    ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
@@ -338,6 +401,12 @@ def main():
                        "frac": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                        "algorithmic_bytes_per_launch": r["bytes"]}
         line["decode_len"] = dl
+
+    if not args.no_packed:
+        tensors = None
+        torch.cuda.empty_cache()
+        line["packed_encoder"] = packed_encoder(max(10, args.steps // 2), max(3, args.warmup // 2),
+                                                args.warmup_ms)
 
     if not args.no_cpu_baseline:
         if tensors is None:

@@ -159,6 +159,35 @@ int mfa_decode_len(const void* q, const void* k_cache, const void* v_cache, void
 size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, int D, int dtype,
                                      int splits);
 
+/*
+ * Bidirectional self-attention over many independent sequences packed back to
+ * back in one fused QKV tensor, with no padding (brotensor flash_attention.h,
+ * flash_attention_packed_qkv_forward: the encoder-batching entry point).
+ *
+ *   qkv         [L, 3, H, D]  each row holds its H query heads, then its H key
+ *                             heads, then its H value heads (the output of one
+ *                             fused QKV projection); fp32, fp16 or bf16
+ *   seq_bounds  [L, 2] int32  row r belongs to the sequence of rows
+ *                             [seq_bounds[r][0], seq_bounds[r][1]), which must
+ *                             contain r; sequences lie back to back
+ *   out         [L, H, D]     element type `dtype`
+ *   lse         [H, L]        float32, natural log, may be NULL
+ *
+ * Row r attends to the keys j of its own sequence, and with window > 0 only
+ * to those with |r - j| <= window / 2 (integer halving; same header,
+ * flash_attention_windowed_forward, bidirectional form).  Scale and soft-cap
+ * as in mfa_fwd.  Which row belongs to which sequence is data read by the
+ * kernels: the launch shape depends on L only, so a graph captured for one L
+ * replays for any packing of it.  Bounds that do not describe back-to-back
+ * sequences containing their rows give unspecified results, but every access
+ * stays inside the L rows.  D in {64, 128}; qkv and out 16-byte aligned, lse
+ * and seq_bounds 4-byte aligned.  L = 0 succeeds without work.  Errors,
+ * ownership and streams as for mfa_fwd; no workspace is needed.
+ */
+int mfa_packed_qkv_fwd(const void* qkv, const int* seq_bounds, void* out, float* lse,
+                       int L, int H, int D, float scale, int window, float softcap, int dtype,
+                       void* stream);
+
 /* The path mfa_fwd would take for these arguments (an mfa_path value), and
  * the split count it would use (through *splits, may be NULL). */
 int mfa_fwd_plan(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype, int* splits);

@@ -155,3 +155,31 @@ def test_decode_len_empty_batch_and_workspace_size():
     assert mfa.decode_len_workspace_size(64, 5, 32768, 32, 8, 128, torch.bfloat16) == 0
     assert mfa.decode_len_workspace_size(2, 1, 64, 8, 2, 128, torch.bfloat16, splits=3) >= \
         2 * 8 * 3 * (128 + 2) * 4
+
+
+def call_packed(**over):
+    lib = mfa.load_library()
+    a = dict(qkv=FAKE[0], sb=FAKE[1], out=FAKE[2], lse=FAKE[3], L=100, H=4, D=64, scale=0.125,
+             window=0, softcap=0.0, dtype=2)
+    a.update(over)
+    return lib.mfa_packed_qkv_fwd(a["qkv"], a["sb"], a["out"], a["lse"], a["L"], a["H"], a["D"],
+                                  a["scale"], a["window"], a["softcap"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("over", [dict(qkv=None), dict(sb=None), dict(out=None), dict(L=-1), dict(H=0),
+                                  dict(D=0), dict(scale=float("nan")), dict(softcap=float("inf")),
+                                  dict(qkv=ctypes.c_void_p(0x10008)), dict(out=ctypes.c_void_p(0x10004)),
+                                  dict(lse=ctypes.c_void_p(0x10002)), dict(sb=ctypes.c_void_p(0x10001))],
+                         ids=lambda d: ",".join(d))
+def test_packed_invalid_arguments_rejected(over):
+    assert call_packed(**over) == 1, over
+    assert mfa.load_library().mfa_last_error().decode()
+
+
+@pytest.mark.parametrize("over", [dict(D=96), dict(D=256), dict(dtype=3)])
+def test_packed_unsupported_rejected(over):
+    assert call_packed(**over) == 2, over
+
+
+def test_packed_empty_call_succeeds():
+    assert call_packed(L=0) == 0

@@ -24,7 +24,7 @@ PATH_NAMES = {PATH_AUTO: "auto", PATH_GENERIC: "generic", PATH_MFMA: "mfma",
 _DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: MFA_BF16}
 
 EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
-            "mfa_decode_len", "mfa_decode_len_workspace_size",
+            "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_packed_qkv_fwd",
             "mfa_status_string", "mfa_last_error", "mfa_version")
 
 
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_fwd_plan.argtypes = [_I] * 7 + [ctypes.POINTER(_I)]
     lib.mfa_decode_len.restype = _I
     lib.mfa_decode_len.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_packed_qkv_fwd.restype = _I
+    lib.mfa_packed_qkv_fwd.argtypes = [_P] * 4 + [_I] * 3 + [_F, _I, _F, _I, _P]
     lib.mfa_decode_len_workspace_size.restype = ctypes.c_size_t
     lib.mfa_decode_len_workspace_size.argtypes = [_I] * 8
     lib.mfa_status_string.restype = ctypes.c_char_p
@@ -201,6 +203,49 @@ def decode_len(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                   _ptr(d_len), B, R, Lmax, Hq, Hkv, D, float(scale), float(softcap),
                                   _DTYPE_CODES[q.dtype], int(splits), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
+    return out, lse
+
+
+def packed_qkv_fwd(qkv: torch.Tensor, seq_bounds: torch.Tensor, num_heads: int, *,
+                   window: int = 0, softcap: float = 0.0, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   return_lse: bool = True, stream=None
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Bidirectional attention over sequences packed back to back in one fused
+    QKV tensor (mfa_packed_qkv_fwd).
+
+    qkv [L, 3 * num_heads * D] (per row: query heads, key heads, value heads;
+    fp32, fp16 or bf16, contiguous, on a GPU); seq_bounds int32 [L, 2] on the
+    same GPU, row r's sequence being rows [seq_bounds[r, 0], seq_bounds[r, 1]).
+    Returns (out [L, num_heads * D], lse [num_heads, L] float32 or None).
+    """
+    lib = load_library()
+    if qkv.dim() != 2 or qkv.shape[1] % (3 * num_heads) != 0:
+        raise ValueError("qkv must be [L, 3 * num_heads * head_dim]")
+    L = qkv.shape[0]
+    H = int(num_heads)
+    D = qkv.shape[1] // (3 * H)
+    if qkv.dtype not in _DTYPE_CODES:
+        raise TypeError(f"qkv dtype must be float32, float16 or bfloat16 (got {qkv.dtype})")
+    if not qkv.is_cuda or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous GPU tensor")
+    if seq_bounds.dtype != torch.int32 or tuple(seq_bounds.shape) != (L, 2) or \
+            not seq_bounds.is_cuda or not seq_bounds.is_contiguous():
+        raise ValueError("seq_bounds must be a contiguous int32 GPU tensor of shape [L, 2]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((L, H * D), dtype=qkv.dtype, device=qkv.device)
+    elif tuple(out.shape) != (L, H * D) or out.dtype != qkv.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous [L, num_heads * head_dim] in qkv's dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((H, L), dtype=torch.float32, device=qkv.device)
+    elif lse is not None and (tuple(lse.shape) != (H, L) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [num_heads, L]")
+    with torch.cuda.device(qkv.device):
+        _check(lib.mfa_packed_qkv_fwd(_ptr(qkv), _ptr(seq_bounds), _ptr(out), _ptr(lse), L, H, D,
+                                      float(scale), int(window), float(softcap),
+                                      _DTYPE_CODES[qkv.dtype], _stream(stream)))
     return out, lse
 
 

@@ -45,8 +45,8 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
     const T* __restrict__ k = static_cast<const T*>(a.k);
     const T* __restrict__ v = static_cast<const T*>(a.v);
     T* __restrict__ out = static_cast<T*>(a.out);
-    const int64_t q_row_stride = (int64_t)a.Hq * D;
-    const int64_t kv_row_stride = (int64_t)a.Hkv * D;
+    const int64_t q_row_stride = a.q_stride;
+    const int64_t kv_row_stride = a.kv_stride;
 
     for (int x = tid; x < GBM * D; x += 256) {
         const int r = x / D, d = x % D;
@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
 
     // keys any row of this tile can see
     int lo_first, hi_first, lo_last, hi_last;
-    key_range(i0 + a.q_offset, a.Lk, a.causal, a.window, lo_first, hi_first);
-    key_range(i_end - 1 + a.q_offset, a.Lk, a.causal, a.window, lo_last, hi_last);
+    row_key_range(a, i0, lo_first, hi_first);
+    row_key_range(a, i_end - 1, lo_last, hi_last);
     const int klo = lo_first, khi = hi_last;
 
     int rlo[ROWS_PER_WAVE], rhi[ROWS_PER_WAVE];
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
         const int i = i0 + wave * ROWS_PER_WAVE + rr;
-        key_range(i + a.q_offset, a.Lk, a.causal, a.window, rlo[rr], rhi[rr]);
-        if (i >= a.Lq) { rlo[rr] = 1; rhi[rr] = 0; }
+        if (i < a.Lq) row_key_range(a, i, rlo[rr], rhi[rr]);
+        else { rlo[rr] = 1; rhi[rr] = 0; }
         m[rr] = -INFINITY;
         l[rr] = 0.0f;
 #pragma unroll
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
         for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
         if (i >= a.Lq) continue;
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        T* orow = out + ((int64_t)b * a.Lq + i) * q_row_stride + (int64_t)hq * D;
+        T* orow = out + ((int64_t)b * a.Lq + i) * a.o_stride + (int64_t)hq * D;
 #pragma unroll
         for (int c = 0; c < D / 64; ++c) orow[lane + 64 * c] = static_cast<T>(acc[rr][c] * inv);
         if (a.lse && lane == 0)

@@ -174,19 +174,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
 
     // key ranges: workgroup (tiles to visit), wave (interior test), lane (mask)
     int lo_blk, hi_tmp, lo_tmp, hi_blk;
-    key_range(i0 + a.q_offset, a.Lk, a.causal, a.window, lo_blk, hi_tmp);
-    key_range(i_last + a.q_offset, a.Lk, a.causal, a.window, lo_tmp, hi_blk);
+    row_key_range(a, i0, lo_blk, hi_tmp);
+    row_key_range(a, i_last, lo_tmp, hi_blk);
     int wlo_last = a.Lk, whi_first = -1;
     if (w_first <= i_last) {
         int t0, t1;
-        key_range(w_first + a.q_offset, a.Lk, a.causal, a.window, t0, whi_first);
-        key_range(w_last + a.q_offset, a.Lk, a.causal, a.window, wlo_last, t1);
+        row_key_range(a, w_first, t0, whi_first);
+        row_key_range(a, w_last, wlo_last, t1);
     }
     int rlo = 1, rhi = 0;
-    if (qrow <= i_last) key_range(qrow + a.q_offset, a.Lk, a.causal, a.window, rlo, rhi);
+    if (qrow <= i_last) row_key_range(a, qrow, rlo, rhi);
 
-    const int64_t q_stride = (int64_t)a.Hq * D;
-    const int64_t kv_stride = (int64_t)a.Hkv * D;
+    const int64_t q_stride = a.q_stride;
+    const int64_t kv_stride = a.kv_stride;
     const T* __restrict__ qbase = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * q_stride + (int64_t)hq * D;
     const T* __restrict__ kbase = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * kv_stride + (int64_t)kvh * D;
     const T* __restrict__ vbase = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * kv_stride + (int64_t)kvh * D;
@@ -550,12 +550,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
                     *reinterpret_cast<const uint2*>(o4);
             }
         }
-        T* obase = static_cast<T*>(a.out) + ((int64_t)b * a.Lq + w_first) * q_stride + (int64_t)hq * D;
+        T* obase = static_cast<T*>(a.out) + ((int64_t)b * a.Lq + w_first) * a.o_stride + (int64_t)hq * D;
 #pragma unroll
         for (int s = 0; s < 32 * CPR / 64; ++s) {
             const int r = s * (64 / CPR) + lane / CPR, c = lane % CPR;
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * L::RS + ((c ^ (r & (CPR - 1))) * 16));
-            if (w_first + r <= i_last) *reinterpret_cast<u32x4_t*>(obase + (int64_t)r * q_stride + c * 8) = v;
+            if (w_first + r <= i_last) *reinterpret_cast<u32x4_t*>(obase + (int64_t)r * a.o_stride + c * 8) = v;
         }
     }
     if (a.lse && h2 == 0 && qrow <= i_last)

@@ -151,6 +151,10 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
     a.window = c.window > 0 ? c.window : 0;
     a.q_offset = c.q_offset;
     a.words_per_batch = words_per_batch(c.Lk);
+    a.q_stride = (int64_t)c.Hq * c.D;
+    a.kv_stride = (int64_t)c.Hkv * c.D;
+    a.o_stride = (int64_t)c.Hq * c.D;
+    a.seq_bounds = nullptr;
     a.scale = c.scale;
     a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
     const float log2e = 1.4426950408889634f;
@@ -260,6 +264,9 @@ int run_len(const LenCall& c, int splits, void* workspace, size_t ws_bytes, hipS
     a.B = c.B; a.Lq = c.R; a.Lk = c.Lmax; a.Hq = c.Hq; a.Hkv = c.Hkv; a.D = c.D;
     a.group = group;
     a.causal = 1;
+    a.q_stride = (int64_t)c.Hq * c.D;
+    a.kv_stride = (int64_t)c.Hkv * c.D;
+    a.o_stride = (int64_t)c.Hq * c.D;
     a.scale = c.scale;
     a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
     const float log2e = 1.4426950408889634f;
@@ -289,9 +296,66 @@ int run_len(const LenCall& c, int splits, void* workspace, size_t ws_bytes, hipS
     return MFA_SUCCESS;
 }
 
+int run_packed(const void* qkv, const int* seq_bounds, void* out, float* lse, int L, int H, int D,
+               float scale, int window, float softcap, int dtype, hipStream_t stream) {
+    if (!qkv || !seq_bounds || !out)
+        return fail(MFA_ERROR_INVALID_VALUE, "qkv, seq_bounds and out must be non-null");
+    if (L < 0 || H <= 0 || D <= 0)
+        return fail(MFA_ERROR_INVALID_VALUE, "bad dimensions L=%d H=%d D=%d (L >= 0; others > 0)", L, H, D);
+    if (!std::isfinite(scale) || !std::isfinite(softcap))
+        return fail(MFA_ERROR_INVALID_VALUE, "scale and softcap must be finite");
+    if (dtype != MFA_F32 && dtype != MFA_F16 && dtype != MFA_BF16)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "unknown dtype %d", dtype);
+    if (D != 64 && D != 128)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "head dim %d not supported (64 or 128)", D);
+    if (!aligned(qkv, 16) || !aligned(out, 16))
+        return fail(MFA_ERROR_INVALID_VALUE, "qkv and out must be 16-byte aligned");
+    if (!aligned(lse, 4) || !aligned(seq_bounds, 4))
+        return fail(MFA_ERROR_INVALID_VALUE, "lse and seq_bounds must be 4-byte aligned");
+    if ((int64_t)L * 3 * H * D < 0 || H > (1 << 20))
+        return fail(MFA_ERROR_INVALID_VALUE, "problem too large");
+    if (L == 0) return MFA_SUCCESS;
+
+    const size_t el = dtype == MFA_F32 ? 4 : 2;
+    const char* base = static_cast<const char*>(qkv);
+    mfa::FwdArgs a{};
+    a.q = base;
+    a.k = base + (size_t)H * D * el;
+    a.v = base + (size_t)2 * H * D * el;
+    a.out = out; a.lse = lse;
+    a.B = 1; a.Lq = L; a.Lk = L; a.Hq = H; a.Hkv = H; a.D = D;
+    a.group = 1;
+    a.causal = 0;
+    a.window = window > 0 ? window : 0;
+    a.q_offset = 0;
+    a.q_stride = (int64_t)3 * H * D;
+    a.kv_stride = (int64_t)3 * H * D;
+    a.o_stride = (int64_t)H * D;
+    a.seq_bounds = seq_bounds;
+    a.scale = scale;
+    a.softcap = softcap > 0.0f ? softcap : 0.0f;
+    const float log2e = 1.4426950408889634f;
+    a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * scale;
+    const hipError_t e = mfa::mfma_prefill_supported(dtype, D) ? mfa::launch_mfma_prefill(a, dtype, stream)
+                                                                : mfa::launch_generic(a, dtype, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return MFA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mfa_packed_qkv_fwd(const void* qkv, const int* seq_bounds, void* out, float* lse,
+                       int L, int H, int D, float scale, int window, float softcap, int dtype,
+                       void* stream) {
+    g_last_error.clear();
+    return run_packed(qkv, seq_bounds, out, lse, L, H, D, scale, window, softcap, dtype,
+                      static_cast<hipStream_t>(stream));
+}
 
 int mfa_decode_len(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
                    const int* d_len, int B, int R, int Lmax, int Hq, int Hkv, int D,

@@ -25,6 +25,10 @@ struct FwdArgs {
     float scale;              // applied to Q.K
     float softcap;            // <= 0: off
     float score_to_log2;      // log2(e) * scale when the cap is off, log2(e) otherwise
+    // elements from one row to the next: q, k/v and out (Hq*D, Hkv*D, Hq*D
+    // for separate tensors; 3*H*D, 3*H*D, H*D for a packed QKV tensor)
+    int64_t q_stride, kv_stride, o_stride;
+    const int* seq_bounds;    // [Lq, 2]: row i only sees keys in [s0, s1) of its own sequence, or null
 };
 
 // Keys [lo, hi] (inclusive) in range for a query at absolute position aq,
@@ -46,6 +50,18 @@ __host__ __device__ inline void key_range(int aq, int Lk, int causal, int window
     }
     if (lo < 0) lo = 0;
     if (hi > Lk - 1) hi = Lk - 1;
+}
+
+// Keys [lo, hi] of query row i: key_range at aq = i + q_offset, cut to the
+// row's own sequence [s0, s1) when per-row bounds are given.  For sequences
+// packed back to back both bounds stay nondecreasing in i.
+__device__ inline void row_key_range(const FwdArgs& a, int i, int& lo, int& hi) {
+    key_range(i + a.q_offset, a.Lk, a.causal, a.window, lo, hi);
+    if (a.seq_bounds) {
+        const int s0 = a.seq_bounds[2 * i], s1 = a.seq_bounds[2 * i + 1];
+        lo = lo > s0 ? lo : s0;
+        hi = hi < s1 - 1 ? hi : s1 - 1;
+    }
 }
 
 // Launchers (each returns the hipError_t of its launch).

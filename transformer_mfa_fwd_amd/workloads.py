@@ -122,6 +122,38 @@ def make_cache_lengths(B: int, Lmax: int, R: int, seed: int = 0, edges: bool = T
     return n.to(torch.int32)
 
 
+def seq_bounds_from_lengths(lengths) -> torch.Tensor:
+    """[L, 2] int32 on the CPU for sequences of the given lengths packed back to
+    back: row r of a sequence spanning rows [s, e) holds (s, e)."""
+    rows = []
+    s = 0
+    for n in [int(x) for x in lengths]:
+        rows += [(s, s + n)] * n
+        s += n
+    return torch.tensor(rows, dtype=torch.int32).reshape(-1, 2)
+
+
+def make_packed_qkv(lengths, H: int, D: int, dtype: str, device="cpu", seed: int = 0, std: float = 1.0):
+    """Fused QKV [L, 3*H*D] for sequences of the given lengths (L their sum):
+    one generator seeded with ``seed`` on ``device`` draws float32 standard
+    normals times ``std``, rounded to nearest-even into ``dtype``; plus the
+    [L, 2] int32 sequence bounds on ``device``."""
+    L = int(sum(int(x) for x in lengths))
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((L, 3 * H * D), generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(DTYPES[dtype]), seq_bounds_from_lengths(lengths).to(device)
+
+
+def encoder_packing_lengths(w: Workload, seed: int = 0):
+    """Valid lengths of the padded encoder workload w (pad_tail key mask): the
+    sequences the packed form carries without their padding."""
+    m = make_key_mask(w, seed)
+    return [int(x) for x in m.sum(1).to(torch.int64).tolist()]
+
+
 def make_inputs(w: Workload, device="cpu", seed: int = 0):
     """Q [B,Lq,Hq,D], K and V [B,Lk,Hkv,D] in the workload's dtype on
     ``device``, and the key mask [B,Lk] float32 (or None) on ``device``."""
