@@ -183,6 +183,35 @@ class Oracle:
             r = s1
         return O, LSE, N
 
+    def varlen(self, q, k, v, cu_q, cu_k, *, scale, causal=False, window=0, softcap=0.0, nthreads=1):
+        """Attention over sequences packed back to back with separate query
+        and key packings (brotensor flash_attention.h,
+        flash_attention_varlen_forward): sequence b owns query rows
+        [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]) and nothing
+        else; causal keeps key k for query q when k - cu_k[b] <= q - cu_q[b]
+        (positions counted from each sequence's start).  Each sequence is the
+        plain forward on its own rows with q_offset 0; rows of no sequence, and
+        sequences without keys, give O = 0 and LSE = -inf.
+        q [Tq, Hq, D]; k, v [Tk, Hkv, D]; cu_q, cu_k [batch + 1] prefix sums.
+        Returns O [Tq, Hq, D], LSE [Hq, Tq] and the visible counts [Hq, Tq].
+        """
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        cq = np.asarray(cu_q.cpu() if hasattr(cu_q, "cpu") else cu_q, dtype=np.int64).reshape(-1)
+        ck = np.asarray(cu_k.cpu() if hasattr(cu_k, "cpu") else cu_k, dtype=np.int64).reshape(-1)
+        Tq, Hq, D = q.shape
+        O = np.zeros((Tq, Hq, D), np.float64)
+        LSE = np.full((Hq, Tq), -np.inf, np.float64)
+        N = np.zeros((Hq, Tq), np.int64)
+        for b in range(len(cq) - 1):
+            q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+            if q1 <= q0 or k1 <= k0:
+                continue
+            Ob, Lb, Nb = self.full(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], scale=scale,
+                                   causal=causal, window=window, q_offset=0, softcap=softcap,
+                                   nthreads=nthreads)
+            O[q0:q1], LSE[:, q0:q1], N[:, q0:q1] = Ob[0], Lb[0], Nb[0]
+        return O, LSE, N
+
     def visible_counts(self, B, Lq, Lk, *, causal=False, window=0, q_offset=None, key_mask=None):
         """Visible-key count of every row, [B, Lq] int64, and the total."""
         m = _f32(key_mask)

@@ -610,6 +610,104 @@ def pin_packed_sequences_are_independent(orc):
     _close(L2[:, keep], LSE[:, keep], 0.0, "other sequences perturbed LSE")
 
 
+# ---------------------------------------------------------------------------
+# separate query and key packings with prefix sums (varlen)
+# ---------------------------------------------------------------------------
+
+def varlen_visibility(cq, ck, causal, window):
+    """[Tq, Tk] visibility as brotensor flash_attention.h states it for
+    flash_attention_varlen_forward: no cross-sequence attention, and causal
+    keeps key k for query q when k - cu_k[b] <= q - cu_q[b]; the window rules
+    are those of the windowed forward on the positions within the sequence."""
+    Tq, Tk = int(cq[-1]), int(ck[-1])
+    vis = np.zeros((Tq, Tk), bool)
+    for b in range(len(cq) - 1):
+        for qi in range(cq[b], cq[b + 1]):
+            for kj in range(ck[b], ck[b + 1]):
+                pq, pk = qi - cq[b], kj - ck[b]
+                ok = vis_causal_p1(pq, pk, window) if causal else vis_bidir_packed(pq, pk, window)
+                vis[qi, kj] = ok
+    return vis
+
+
+def dense_varlen(q, k, v, cq, ck, *, scale, causal, window, softcap=0.0):
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    Tq, Hq, D = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    vis = varlen_visibility(cq, ck, causal, window)
+    O = np.zeros((Tq, Hq, D))
+    LSE = np.zeros((Hq, Tq))
+    for h in range(Hq):
+        s = scale * (q[:, h, :] @ k[:, h // g, :].T)
+        if softcap > 0:
+            s = softcap * np.tanh(s / softcap)
+        s = np.where(vis, s, -np.inf)
+        empty = ~vis.any(1)
+        lse = np.where(empty, -np.inf, logsumexp(np.where(empty[:, None], 0.0, s), axis=1))
+        O[:, h, :] = np.where(vis, np.exp(s - np.where(empty, 0.0, lse)[:, None]), 0.0) @ v[:, h // g, :]
+        LSE[h] = lse
+    return O, LSE
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+
+
+def pin_varlen_matches_dense(orc):
+    rng = _rng(20)
+    for lq, lk, causal, window, Hq, Hkv, softcap in [
+            ([3, 7, 1, 5], [3, 7, 1, 5], True, 0, 4, 2, 0.0),
+            ([4, 6, 2], [9, 2, 5], False, 0, 2, 1, 0.0),
+            ([5, 0, 6], [5, 4, 0], True, 3, 2, 2, 1.5),
+            ([8, 3], [8, 3], False, 4, 3, 1, 0.0)]:
+        D = 8
+        cq, ck = _cu(lq), _cu(lk)
+        q = _rand(rng, (int(cq[-1]), Hq, D), 2.0)
+        k, v = _rand(rng, (int(ck[-1]), Hkv, D), 2.0), _rand(rng, (int(ck[-1]), Hkv, D))
+        kw = dict(scale=0.4, causal=causal, window=window, softcap=softcap)
+        O, L, N = orc.varlen(q, k, v, cq, ck, **kw)
+        Od, Ld = dense_varlen(q, k, v, cq, ck, **kw)
+        _close(O, Od, TIGHT, f"varlen O {lq} {lk}")
+        _close(L, Ld, TIGHT, f"varlen LSE {lq} {lk}")
+        assert np.array_equal(N, np.broadcast_to(varlen_visibility(cq, ck, causal, window).sum(1), N.shape))
+
+
+def pin_varlen_zero_query_closed_form(orc):
+    """Q = 0: each row is the mean of its sequence's visible V rows and
+    LSE = ln(count); the causal count of row q is min(q - cu_q + 1, len_k)."""
+    rng = _rng(21)
+    lq, lk = [4, 9, 3], [6, 5, 3]
+    cq, ck = _cu(lq), _cu(lk)
+    Hq, Hkv, D = 2, 1, 8
+    q = np.zeros((int(cq[-1]), Hq, D), np.float32)
+    k, v = _rand(rng, (int(ck[-1]), Hkv, D)), _rand(rng, (int(ck[-1]), Hkv, D))
+    O, L, _ = orc.varlen(q, k, v, cq, ck, scale=0.8, causal=True)
+    for b in range(3):
+        for qi in range(cq[b], cq[b + 1]):
+            cnt = min(qi - cq[b] + 1, lk[b])
+            mean = v[ck[b]:ck[b] + cnt, 0, :].astype(np.float64).mean(0)
+            for h in range(Hq):
+                assert np.max(np.abs(O[qi, h] - mean)) <= TIGHT
+                assert abs(L[h, qi] - math.log(cnt)) <= TIGHT
+
+
+def pin_varlen_sequences_are_independent(orc):
+    rng = _rng(22)
+    lq, lk = [5, 6, 4], [7, 6, 2]
+    cq, ck = _cu(lq), _cu(lk)
+    q = _rand(rng, (int(cq[-1]), 2, 8))
+    k, v = _rand(rng, (int(ck[-1]), 2, 8)), _rand(rng, (int(ck[-1]), 2, 8))
+    O, L, _ = orc.varlen(q, k, v, cq, ck, scale=0.5, causal=False)
+    k2, v2 = k.copy(), v.copy()
+    k2[7:13] = 1e3
+    v2[7:13] = -1e3
+    O2, L2, _ = orc.varlen(q, k2, v2, cq, ck, scale=0.5, causal=False)
+    keep = np.r_[0:5, 11:15]
+    _close(O2[keep], O[keep], 0.0, "other sequences' keys perturbed")
+    _close(L2[:, keep], L[:, keep], 0.0, "other sequences' keys perturbed LSE")
+
+
 ALL_PINS = [
     pin_range_causal_matches_ferrotensor_rule,
     pin_range_causal_matches_forge_rule,
@@ -634,4 +732,7 @@ ALL_PINS = [
     pin_packed_matches_dense,
     pin_packed_zero_query_closed_form,
     pin_packed_sequences_are_independent,
+    pin_varlen_matches_dense,
+    pin_varlen_zero_query_closed_form,
+    pin_varlen_sequences_are_independent,
 ]
