@@ -188,6 +188,42 @@ int mfa_packed_qkv_fwd(const void* qkv, const int* seq_bounds, void* out, float*
                        int L, int H, int D, float scale, int window, float softcap, int dtype,
                        void* stream);
 
+/*
+ * Attention over sequences packed back to back with separate query and key
+ * packings and no padding (brotensor flash_attention.h,
+ * flash_attention_varlen_forward).  Sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key/value rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); nothing attends across sequences.
+ * Positions count from each sequence's start: causal keeps key j for query i
+ * when j - cu_seqlens_k[b] <= i - cu_seqlens_q[b], and the window (causal or
+ * bidirectional, as in mfa_fwd) applies to those positions.  GQA, scale and
+ * soft-cap as in mfa_fwd.
+ *
+ *   q, out        [total_q, Hq, D]   element type `dtype`
+ *   k, v          [total_k, Hkv, D]  element type `dtype`
+ *   lse           [Hq, total_q]      float32, may be NULL
+ *   cu_seqlens_*  [batch + 1] int32 in device memory: prefix sums starting at
+ *                 0, nondecreasing, ending at total_q / total_k
+ *
+ * The prefix sums are read on the device, so the launch shape depends only on
+ * total_q: a graph captured once replays for any lengths with those totals.
+ * A row of a sequence without keys (or of no sequence) gets O = 0 and
+ * LSE = -inf.  Prefix sums that break the rules above give unspecified
+ * results, but every access stays inside the given tensors.  A first kernel
+ * turns the prefix sums into per-row positions and key bounds in the
+ * workspace: caller-owned (256-byte aligned, at least
+ * mfa_varlen_workspace_size(total_q) bytes), or NULL with ws_bytes = 0 for the
+ * stream-ordered pool.  batch >= 1 unless total_q = 0 (then nothing is done).
+ * D in {64, 128}; alignment, errors, ownership and streams as for mfa_fwd.
+ */
+int mfa_varlen_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                   int Hq, int Hkv, int D, float scale, int causal, int window, float softcap, int dtype,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes mfa_varlen_fwd needs (0 when total_q <= 0). */
+size_t mfa_varlen_workspace_size(int total_q);
+
 /* The path mfa_fwd would take for these arguments (an mfa_path value), and
  * the split count it would use (through *splits, may be NULL). */
 int mfa_fwd_plan(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype, int* splits);

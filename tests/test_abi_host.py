@@ -183,3 +183,39 @@ def test_packed_unsupported_rejected(over):
 
 def test_packed_empty_call_succeeds():
     assert call_packed(L=0) == 0
+
+
+def call_varlen(**over):
+    lib = mfa.load_library()
+    a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], lse=FAKE[4], cq=FAKE[5], ck=FAKE[6], batch=3,
+             Tq=100, Tk=120, Hq=4, Hkv=2, D=128, scale=0.1, causal=1, window=0, softcap=0.0, dtype=2,
+             ws=FAKE[7], ws_bytes=1 << 20)
+    a.update(over)
+    return lib.mfa_varlen_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cq"], a["ck"], a["batch"],
+                              a["Tq"], a["Tk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"],
+                              a["window"], a["softcap"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over", [dict(q=None), dict(k=None), dict(v=None), dict(out=None), dict(cq=None),
+                                  dict(ck=None), dict(batch=-1), dict(batch=0), dict(Tq=-1), dict(Tk=-1),
+                                  dict(Hq=0), dict(Hkv=0), dict(D=0), dict(Hq=6, Hkv=4),
+                                  dict(scale=float("nan")), dict(softcap=float("inf")),
+                                  dict(q=ctypes.c_void_p(0x10008)), dict(lse=ctypes.c_void_p(0x10002)),
+                                  dict(cq=ctypes.c_void_p(0x10001)), dict(ws=None, ws_bytes=64),
+                                  dict(ws=ctypes.c_void_p(0x10010)), dict(ws_bytes=16)],
+                         ids=lambda d: ",".join(d))
+def test_varlen_invalid_arguments_rejected(over):
+    assert call_varlen(**over) == 1, over
+    assert mfa.load_library().mfa_last_error().decode()
+
+
+@pytest.mark.parametrize("over", [dict(D=96), dict(dtype=4)])
+def test_varlen_unsupported_rejected(over):
+    assert call_varlen(**over) == 2, over
+
+
+def test_varlen_empty_and_workspace_size():
+    assert call_varlen(Tq=0) == 0
+    assert call_varlen(Tq=0, batch=0) == 0
+    assert mfa.varlen_workspace_size(0) == 0
+    assert mfa.varlen_workspace_size(1000) >= 1000 * 3 * 4

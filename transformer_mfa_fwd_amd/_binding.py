@@ -25,6 +25,7 @@ _DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: 
 
 EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
             "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_packed_qkv_fwd",
+            "mfa_varlen_fwd", "mfa_varlen_workspace_size",
             "mfa_status_string", "mfa_last_error", "mfa_version")
 
 
@@ -63,6 +64,10 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_fwd_plan.argtypes = [_I] * 7 + [ctypes.POINTER(_I)]
     lib.mfa_decode_len.restype = _I
     lib.mfa_decode_len.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_varlen_fwd.restype = _I
+    lib.mfa_varlen_fwd.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.mfa_varlen_workspace_size.argtypes = [_I]
     lib.mfa_packed_qkv_fwd.restype = _I
     lib.mfa_packed_qkv_fwd.argtypes = [_P] * 4 + [_I] * 3 + [_F, _I, _F, _I, _P]
     lib.mfa_decode_len_workspace_size.restype = ctypes.c_size_t
@@ -247,6 +252,58 @@ def packed_qkv_fwd(qkv: torch.Tensor, seq_bounds: torch.Tensor, num_heads: int, 
                                       float(scale), int(window), float(softcap),
                                       _DTYPE_CODES[qkv.dtype], _stream(stream)))
     return out, lse
+
+
+def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_k: torch.Tensor, *, causal: bool = False, window: int = 0,
+               softcap: float = 0.0, scale: Optional[float] = None,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               return_lse: bool = True, workspace: Optional[torch.Tensor] = None, stream=None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention over sequences packed with separate query and key packings
+    (mfa_varlen_fwd).
+
+    q [total_q, Hq, D]; k, v [total_k, Hkv, D] (one dtype, contiguous, on one
+    GPU); cu_seqlens_q / cu_seqlens_k int32 [batch + 1] prefix sums on the same
+    GPU.  Returns (out [total_q, Hq, D], lse [Hq, total_q] float32 or None).
+    """
+    lib = load_library()
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total_q, Hq, D]; k and v [total_k, Hkv, D]")
+    Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"dtypes must match and be one of float32/float16/bfloat16 "
+                        f"(got {q.dtype}, {k.dtype}, {v.dtype})")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    batch = cu_seqlens_q.numel() - 1
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != batch + 1 or not t.is_cuda or \
+                not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor of batch + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous and match q")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (tuple(lse.shape) != (Hq, Tq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [Hq, total_q]")
+    with torch.cuda.device(q.device):
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.mfa_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                  _ptr(cu_seqlens_k), batch, Tq, Tk, Hq, Hkv, D, float(scale),
+                                  int(bool(causal)), int(window), float(softcap), _DTYPE_CODES[q.dtype],
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def varlen_workspace_size(total_q: int) -> int:
+    return int(load_library().mfa_varlen_workspace_size(int(total_q)))
 
 
 def decode_len_workspace_size(B, R, Lmax, Hq, Hkv, D, dtype: torch.dtype, splits: int = 0) -> int:

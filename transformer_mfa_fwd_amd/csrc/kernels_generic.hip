@@ -172,6 +172,30 @@ __global__ __launch_bounds__(64) void mask_words_kernel(const float* __restrict_
     if (threadIdx.x == 0) words[(int64_t)b * W + w] = bits;
 }
 
+__device__ inline int clamp_to(int x, int hi) { return x < 0 ? 0 : (x > hi ? hi : x); }
+
+// One thread per query row: the last sequence whose first row is at or
+// before the row (binary search over the prefix sums), then its key bounds.
+__global__ __launch_bounds__(256) void varlen_rows_kernel(const int* __restrict__ cu_q,
+                                                          const int* __restrict__ cu_k, int batch, int Tq,
+                                                          int Tk, int* __restrict__ row_pos,
+                                                          int* __restrict__ seq_bounds) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= Tq) return;
+    int lo = 0, hi = batch - 1;   // largest b with cu_q[b] <= i
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (clamp_to(cu_q[mid], Tq) <= i) lo = mid; else hi = mid - 1;
+    }
+    const int q0 = clamp_to(cu_q[lo], Tq), q1 = clamp_to(cu_q[lo + 1], Tq);
+    int k0 = clamp_to(cu_k[lo], Tk), k1 = clamp_to(cu_k[lo + 1], Tk);
+    if (!(q0 <= i && i < q1)) k0 = k1 = Tk;   // the row belongs to no sequence
+    if (k1 < k0) k1 = k0;
+    row_pos[i] = k0 + (i - q0);
+    seq_bounds[2 * i] = k0;
+    seq_bounds[2 * i + 1] = k1;
+}
+
 template <typename T>
 hipError_t launch_generic_t(const FwdArgs& a, hipStream_t s) {
     dim3 grid((a.Lq + GBM - 1) / GBM, a.Hq, a.B);
@@ -191,6 +215,13 @@ hipError_t launch_generic(const FwdArgs& a, int dtype, hipStream_t s) {
         case kBF16: return launch_generic_t<__bf16>(a, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_varlen_rows(const int* cu_q, const int* cu_k, int batch, int Tq, int Tk, int* row_pos,
+                              int* seq_bounds, hipStream_t s) {
+    hipLaunchKernelGGL(varlen_rows_kernel, dim3((Tq + 255) / 256), dim3(256), 0, s, cu_q, cu_k, batch, Tq,
+                       Tk, row_pos, seq_bounds);
+    return hipGetLastError();
 }
 
 hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s) {

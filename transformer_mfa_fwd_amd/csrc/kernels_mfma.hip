@@ -122,8 +122,8 @@ __device__ inline uint64_t range_bits64(int lo, int hi) {
     return (~0ull << lo) & (~0ull >> (63 - hi));
 }
 
-template <typename T, int D, bool CAP, bool MASK>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
+template <typename T, int D, bool CAP, bool MASK, bool SEQ>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a, int nqt) {
     typedef PfLds<D> L;
     constexpr int CPR = L::CPR;
     constexpr int NKS = D / 16;             // k-steps of Q.K^T
@@ -174,16 +174,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
 
     // key ranges: workgroup (tiles to visit), wave (interior test), lane (mask)
     int lo_blk, hi_tmp, lo_tmp, hi_blk;
-    row_key_range(a, i0, lo_blk, hi_tmp);
-    row_key_range(a, i_last, lo_tmp, hi_blk);
+    row_key_range<SEQ>(a, i0, lo_blk, hi_tmp);
+    row_key_range<SEQ>(a, i_last, lo_tmp, hi_blk);
     int wlo_last = a.Lk, whi_first = -1;
     if (w_first <= i_last) {
         int t0, t1;
-        row_key_range(a, w_first, t0, whi_first);
-        row_key_range(a, w_last, wlo_last, t1);
+        row_key_range<SEQ>(a, w_first, t0, whi_first);
+        row_key_range<SEQ>(a, w_last, wlo_last, t1);
     }
     int rlo = 1, rhi = 0;
-    if (qrow <= i_last) row_key_range(a, qrow, rlo, rhi);
+    if (qrow <= i_last) row_key_range<SEQ>(a, qrow, rlo, rhi);
 
     const int64_t q_stride = a.q_stride;
     const int64_t kv_stride = a.kv_stride;
@@ -562,19 +562,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(FwdArgs a, int nqt) {
         a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qrow] = l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
 }
 
-template <typename T, int D, bool CAP, bool MASK>
+template <typename T, int D, bool CAP, bool MASK, bool SEQ>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int nqt = (a.Lq + BM - 1) / BM;
     const int64_t blocks = (int64_t)a.B * a.Hq * nqt;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK>), dim3((unsigned)blocks), dim3(256), 0, s, a, nqt);
+    hipLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK, SEQ>), dim3((unsigned)blocks), dim3(256), 0, s, a, nqt);
     return hipGetLastError();
 }
 
+// Packed inputs (per-row positions or sequence bounds) have their own
+// instantiations without the key mask, so plain batches keep the leaner code.
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     const bool cap = a.softcap > 0.0f, mask = a.key_mask != nullptr;
-    if (cap) return mask ? launch_t<T, D, true, true>(a, s) : launch_t<T, D, true, false>(a, s);
-    return mask ? launch_t<T, D, false, true>(a, s) : launch_t<T, D, false, false>(a, s);
+    if (a.seq_bounds || a.row_pos) {
+        if (mask) return hipErrorInvalidValue;
+        return cap ? launch_t<T, D, true, false, true>(a, s) : launch_t<T, D, false, false, true>(a, s);
+    }
+    if (cap) return mask ? launch_t<T, D, true, true, false>(a, s) : launch_t<T, D, true, false, false>(a, s);
+    return mask ? launch_t<T, D, false, true, false>(a, s) : launch_t<T, D, false, false, false>(a, s);
 }
 
 }  // namespace

@@ -345,9 +345,100 @@ int run_packed(const void* qkv, const int* seq_bounds, void* out, float* lse, in
     return MFA_SUCCESS;
 }
 
+size_t varlen_ws_bytes(int Tq) { return align256((size_t)Tq * 3 * sizeof(int)); }
+
+int run_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int* cu_q,
+               const int* cu_k, int batch, int Tq, int Tk, int Hq, int Hkv, int D, float scale, int causal,
+               int window, float softcap, int dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !out || !cu_q || !cu_k)
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must be non-null");
+    if (batch < 0 || Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (batch == 0 && Tq > 0))
+        return fail(MFA_ERROR_INVALID_VALUE,
+                    "bad dimensions batch=%d Tq=%d Tk=%d Hq=%d Hkv=%d D=%d (batch >= 1 when Tq > 0)",
+                    batch, Tq, Tk, Hq, Hkv, D);
+    if (Hq % Hkv != 0) return fail(MFA_ERROR_INVALID_VALUE, "Hkv=%d does not divide Hq=%d", Hkv, Hq);
+    if (!std::isfinite(scale) || !std::isfinite(softcap))
+        return fail(MFA_ERROR_INVALID_VALUE, "scale and softcap must be finite");
+    if (dtype != MFA_F32 && dtype != MFA_F16 && dtype != MFA_BF16)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "unknown dtype %d", dtype);
+    if (D != 64 && D != 128)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "head dim %d not supported (64 or 128)", D);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k, v and out must be 16-byte aligned");
+    if (!aligned(lse, 4) || !aligned(cu_q, 4) || !aligned(cu_k, 4))
+        return fail(MFA_ERROR_INVALID_VALUE, "lse and the prefix sums must be 4-byte aligned");
+    if ((int64_t)Tq * Hq * D < 0 || (int64_t)Tk * Hkv * D < 0 || Hq > (1 << 20))
+        return fail(MFA_ERROR_INVALID_VALUE, "problem too large");
+    if (Tq == 0) return MFA_SUCCESS;
+    const size_t need = varlen_ws_bytes(Tq);
+    const bool use_pool = workspace == nullptr && ws_bytes == 0;
+    if (!use_pool) {
+        if (!workspace) return fail(MFA_ERROR_INVALID_VALUE, "workspace is null but ws_bytes > 0");
+        if (!aligned(workspace, 256)) return fail(MFA_ERROR_INVALID_VALUE, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(MFA_ERROR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    }
+    void* ws = workspace;
+    if (use_pool) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
+        prepare_pool(dev);
+        hipError_t e = hipMallocAsync(&ws, need, stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
+                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
+        }
+    }
+    int* row_pos = static_cast<int*>(ws);
+    int* bounds = row_pos + Tq;
+
+    mfa::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.B = 1; a.Lq = Tq; a.Lk = Tk > 0 ? Tk : 1; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+    a.group = Hq / Hkv;
+    a.causal = causal ? 1 : 0;
+    a.window = window > 0 ? window : 0;
+    a.q_offset = 0;
+    a.q_stride = (int64_t)Hq * D;
+    a.kv_stride = (int64_t)Hkv * D;
+    a.o_stride = (int64_t)Hq * D;
+    a.seq_bounds = bounds;
+    a.row_pos = row_pos;
+    a.scale = scale;
+    a.softcap = softcap > 0.0f ? softcap : 0.0f;
+    const float log2e = 1.4426950408889634f;
+    a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * scale;
+    hipError_t e = mfa::launch_varlen_rows(cu_q, cu_k, batch, Tq, Tk, row_pos, bounds, stream);
+    if (e == hipSuccess)
+        e = mfa::mfma_prefill_supported(dtype, D) ? mfa::launch_mfma_prefill(a, dtype, stream)
+                                                   : mfa::launch_generic(a, dtype, stream);
+    if (use_pool) {
+        hipError_t e2 = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return MFA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+int mfa_varlen_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                   int Hq, int Hkv, int D, float scale, int causal, int window, float softcap, int dtype,
+                   void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    return run_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, Hq, Hkv, D,
+                      scale, causal, window, softcap, dtype, workspace, ws_bytes,
+                      static_cast<hipStream_t>(stream));
+}
+
+size_t mfa_varlen_workspace_size(int total_q) { return total_q > 0 ? varlen_ws_bytes(total_q) : 0; }
 
 int mfa_packed_qkv_fwd(const void* qkv, const int* seq_bounds, void* out, float* lse,
                        int L, int H, int D, float scale, int window, float softcap, int dtype,

@@ -29,6 +29,7 @@ struct FwdArgs {
     // for separate tensors; 3*H*D, 3*H*D, H*D for a packed QKV tensor)
     int64_t q_stride, kv_stride, o_stride;
     const int* seq_bounds;    // [Lq, 2]: row i only sees keys in [s0, s1) of its own sequence, or null
+    const int* row_pos;       // [Lq]: absolute key-axis position of row i, or null (i + q_offset)
 };
 
 // Keys [lo, hi] (inclusive) in range for a query at absolute position aq,
@@ -52,20 +53,32 @@ __host__ __device__ inline void key_range(int aq, int Lk, int causal, int window
     if (hi > Lk - 1) hi = Lk - 1;
 }
 
-// Keys [lo, hi] of query row i: key_range at aq = i + q_offset, cut to the
-// row's own sequence [s0, s1) when per-row bounds are given.  For sequences
-// packed back to back both bounds stay nondecreasing in i.
+// Keys [lo, hi] of query row i: key_range at its position aq (row_pos[i], or
+// i + q_offset), cut to the row's own sequence [s0, s1) when per-row bounds
+// are given.  A row left with no key gets the empty range [s1, s1 - 1], so
+// that for sequences packed back to back both bounds stay nondecreasing in i
+// (rows past a window's reach lie at the end of their sequence).
+// SEQ = false ignores row_pos and seq_bounds (kernels instantiated for
+// plain batches); SEQ = true reads whichever of them is given.
+template <bool SEQ = true>
 __device__ inline void row_key_range(const FwdArgs& a, int i, int& lo, int& hi) {
-    key_range(i + a.q_offset, a.Lk, a.causal, a.window, lo, hi);
-    if (a.seq_bounds) {
+    key_range(SEQ && a.row_pos ? a.row_pos[i] : i + a.q_offset, a.Lk, a.causal, a.window, lo, hi);
+    if (SEQ && a.seq_bounds) {
         const int s0 = a.seq_bounds[2 * i], s1 = a.seq_bounds[2 * i + 1];
         lo = lo > s0 ? lo : s0;
         hi = hi < s1 - 1 ? hi : s1 - 1;
+        if (lo > hi) { lo = s1; hi = s1 - 1; }
     }
 }
 
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s);
+// Per-row position and key bounds of a varlen packing: row i of sequence b
+// (cu_q[b] <= i < cu_q[b+1]) gets row_pos[i] = cu_k[b] + i - cu_q[b] and
+// bounds [cu_k[b], cu_k[b+1]); rows of no sequence get the empty [Tk, Tk).
+// Prefix sums are clamped to [0, Tq] and [0, Tk].
+hipError_t launch_varlen_rows(const int* cu_q, const int* cu_k, int batch, int Tq, int Tk, int* row_pos,
+                              int* seq_bounds, hipStream_t s);
 hipError_t launch_generic(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s);
 bool mfma_prefill_supported(int dtype, int D);
