@@ -47,7 +47,60 @@ typedef struct {
     int64_t window;
     int64_t q_offset;
     double softcap;
+    /* additive score bias, element (b, hq, i, j) at b*bs[0] + hq*bs[1] +
+     * i*bs[2] + j*bs[3] (stride 0 broadcasts a size-1 dimension), or NULL */
+    const float* bias;
+    int64_t bs[4];
+    /* attention dropout: drop probability p and the seed of its pattern */
+    double dropout_p;
+    uint64_t seed;
 } oracle_dims;
+
+/*
+ * Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011): ten rounds over a 256-bit counter with a
+ * 128-bit key.  Each round multiplies counter words 0 and 2 by the two
+ * round constants into 128-bit products, rebuilds the counter from the
+ * products' halves XOR-ed with words 1 and 3 and the key, and the key is
+ * bumped by the two Weyl constants between rounds.
+ */
+void mfa_oracle_philox4x64(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4])
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        const unsigned __int128 p0 = (unsigned __int128)M0 * c0;
+        const unsigned __int128 p1 = (unsigned __int128)M1 * c2;
+        const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += W0;
+        k1 += W1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/*
+ * Dropout decision of score (b, hq, i, j).  The pages fix only that a seed
+ * drives the pattern (ferrotensor attention.rs, AttentionOptions); this build
+ * reads it as: Philox4x64-10 with counter (j, i, hq, b) and key (seed, 0);
+ * the top 24 bits r of output word 0 keep the weight iff
+ * r >= round(p * 2^24).
+ */
+int mfa_oracle_dropout_keep(uint64_t seed, double p, int64_t b, int64_t hq, int64_t i, int64_t j)
+{
+    const uint64_t ctr[4] = {(uint64_t)j, (uint64_t)i, (uint64_t)hq, (uint64_t)b};
+    const uint64_t key[2] = {seed, 0};
+    uint64_t out[4];
+    mfa_oracle_philox4x64(ctr, key, out);
+    const uint64_t threshold = (uint64_t)llround(p * 16777216.0);
+    return (out[0] >> 40) >= threshold;
+}
 
 /*
  * Key range [lo, hi] (inclusive) visible to a query at absolute position aq,
@@ -192,13 +245,23 @@ static void oracle_row(const float* q, const float* k, const float* v, const flo
             s = d->softcap * tanh(s / d->softcap);
 #endif
         }
+        if (d->bias) {
+            /* additive mask with size-1 dimensions broadcast (ferrotensor
+             * attention.rs, flash_attention_v2 and mask_strides), added to
+             * the scaled (and capped) score */
+#if ORACLE_MUTANT == 15
+            s += d->bias[b * d->bs[0] + hq * d->bs[1] + j * d->bs[2] + i * d->bs[3]];  /* i, j swapped */
+#else
+            s += d->bias[b * d->bs[0] + hq * d->bs[1] + i * d->bs[2] + j * d->bs[3]];
+#endif
+        }
         scores[j] = s;
         if (s > m) m = s;
         ++n;
     }
     *nvis = n;
     for (int64_t e = 0; e < D; ++e) out[e] = 0.0;
-    if (n == 0) {
+    if (n == 0 || m == -INFINITY) {          /* no key, or a bias of -inf on every one */
         *lse = -INFINITY;
         return;
     }
@@ -216,6 +279,19 @@ static void oracle_row(const float* q, const float* k, const float* v, const flo
 #else
         scores[j] /= sum;
 #endif
+    }
+    /* attention dropout on the normalised weights: a dropped weight becomes
+     * 0 and a kept one is divided by 1 - p (ferrotensor attention.rs,
+     * flash_attention_v2: dropout_prob and seed); the LSE is not affected */
+    if (d->dropout_p > 0.0) {
+        for (int64_t j = 0; j < d->Lk; ++j) {
+            if (isnan(scores[j])) continue;
+#if ORACLE_MUTANT == 16
+            scores[j] = mfa_oracle_dropout_keep(d->seed, d->dropout_p, b, hq, j, i) ? scores[j] / (1.0 - d->dropout_p) : 0.0;
+#else
+            scores[j] = mfa_oracle_dropout_keep(d->seed, d->dropout_p, b, hq, i, j) ? scores[j] / (1.0 - d->dropout_p) : 0.0;
+#endif
+        }
     }
     /* O = P V */
     for (int64_t j = 0; j < d->Lk; ++j) {
@@ -267,15 +343,21 @@ static void* row_worker(void* arg)
  * POSIX threads; the arithmetic of each row is independent of the threading.
  * Returns 0 on success, -1 on bad arguments or allocation failure.
  */
-int mfa_oracle_rows(const float* q, const float* k, const float* v, const float* key_mask,
-                    int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
-                    double scale, int causal, int64_t window, int64_t q_offset, double softcap,
-                    const int64_t* rows, int64_t n_rows,
-                    double* out, double* lse, int64_t* nvis, int nthreads)
+int mfa_oracle_rows_ext(const float* q, const float* k, const float* v, const float* key_mask,
+                        int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
+                        double scale, int causal, int64_t window, int64_t q_offset, double softcap,
+                        const float* bias, const int64_t* bias_strides, double dropout_p, uint64_t seed,
+                        const int64_t* rows, int64_t n_rows,
+                        double* out, double* lse, int64_t* nvis, int nthreads)
 {
     if (!q || !k || !v || !rows || !out || !lse || !nvis) return -1;
     if (B <= 0 || Lq <= 0 || Lk <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return -1;
-    oracle_dims d = {B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap};
+    if (bias && !bias_strides) return -1;
+    if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return -1;
+    oracle_dims d = {B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap,
+                     bias, {0, 0, 0, 0}, dropout_p, seed};
+    if (bias)
+        for (int e = 0; e < 4; ++e) d.bs[e] = bias_strides[e];
     for (int64_t r = 0; r < n_rows; ++r) {
         const int64_t* t = rows + 3 * r;
         if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= Hq || t[2] < 0 || t[2] >= Lq) return -1;
@@ -298,6 +380,17 @@ int mfa_oracle_rows(const float* q, const float* k, const float* v, const float*
     return failed ? -1 : 0;
 }
 
+/* mfa_oracle_rows_ext without bias and dropout. */
+int mfa_oracle_rows(const float* q, const float* k, const float* v, const float* key_mask,
+                    int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
+                    double scale, int causal, int64_t window, int64_t q_offset, double softcap,
+                    const int64_t* rows, int64_t n_rows,
+                    double* out, double* lse, int64_t* nvis, int nthreads)
+{
+    return mfa_oracle_rows_ext(q, k, v, key_mask, B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset,
+                               softcap, NULL, NULL, 0.0, 0, rows, n_rows, out, lse, nvis, nthreads);
+}
+
 /*
  * Visible-key count of every query row: counts[b*Lq + i] for all b < B and
  * i < Lq (the count does not depend on the head).  Returns the total number of
@@ -307,7 +400,7 @@ int64_t mfa_oracle_visible_counts(const float* key_mask, int64_t B, int64_t Lq, 
                                   int causal, int64_t window, int64_t q_offset,
                                   int64_t* counts)
 {
-    oracle_dims d = {B, Lq, Lk, 1, 1, 1, 1.0, causal, window, q_offset, 0.0};
+    oracle_dims d = {B, Lq, Lk, 1, 1, 1, 1.0, causal, window, q_offset, 0.0, NULL, {0, 0, 0, 0}, 0.0, 0};
     int64_t total = 0;
     for (int64_t b = 0; b < B; ++b)
         for (int64_t i = 0; i < Lq; ++i) {

@@ -61,6 +61,16 @@ class Oracle:
         lib.mfa_oracle_rows.argtypes = [_fp, _fp, _fp, _fp] + [ctypes.c_int64] * 6 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
             _ip, ctypes.c_int64, _dp, _dp, _ip, ctypes.c_int]
+        lib.mfa_oracle_rows_ext.restype = ctypes.c_int
+        lib.mfa_oracle_rows_ext.argtypes = [_fp, _fp, _fp, _fp] + [ctypes.c_int64] * 6 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            _fp, _ip, ctypes.c_double, ctypes.c_uint64,
+            _ip, ctypes.c_int64, _dp, _dp, _ip, ctypes.c_int]
+        _u64p = ctypes.POINTER(ctypes.c_uint64)
+        lib.mfa_oracle_philox4x64.restype = None
+        lib.mfa_oracle_philox4x64.argtypes = [_u64p, _u64p, _u64p]
+        lib.mfa_oracle_dropout_keep.restype = ctypes.c_int
+        lib.mfa_oracle_dropout_keep.argtypes = [ctypes.c_uint64, ctypes.c_double] + [ctypes.c_int64] * 4
         lib.mfa_oracle_visible_counts.restype = ctypes.c_int64
         lib.mfa_oracle_visible_counts.argtypes = [_fp] + [ctypes.c_int64] * 3 + [
             ctypes.c_int, ctypes.c_int64, ctypes.c_int64, _ip]
@@ -77,14 +87,39 @@ class Oracle:
                                       ctypes.byref(lo), ctypes.byref(hi))
         return lo.value, hi.value
 
+    def philox4x64(self, ctr, key):
+        """Philox4x64-10 of a 4-word counter and 2-word key (four uint64)."""
+        c = (ctypes.c_uint64 * 4)(*[int(x) for x in ctr])
+        kk = (ctypes.c_uint64 * 2)(*[int(x) for x in key])
+        out = (ctypes.c_uint64 * 4)()
+        self.lib.mfa_oracle_philox4x64(c, kk, out)
+        return [int(x) for x in out]
+
+    def dropout_keep(self, seed, p, b, hq, i, j) -> bool:
+        return bool(self.lib.mfa_oracle_dropout_keep(int(seed), float(p), int(b), int(hq), int(i), int(j)))
+
     def rows(self, q, k, v, rows, *, scale, causal=False, window=0, q_offset=None,
-             softcap=0.0, key_mask=None, nthreads=1):
+             softcap=0.0, key_mask=None, bias=None, dropout_p=0.0, seed=0, nthreads=1):
         """Evaluate the rows given as an (n, 3) array of (b, hq, i).
 
         q is [B, Lq, Hq, D]; k, v are [B, Lk, Hkv, D]; key_mask is [B, Lk] or
-        None.  Returns (out [n, D] float64, lse [n] float64, nvis [n] int64).
+        None; bias is an additive score mask whose shape (bB, bH, bLq, bLk)
+        has each dimension 1 (broadcast) or B, Hq, Lq, Lk, or None;
+        dropout_p and seed drive attention dropout.  Returns (out [n, D]
+        float64, lse [n] float64, nvis [n] int64).
         """
         q, k, v, m = _f32(q), _f32(k), _f32(v), _f32(key_mask)
+        bias = _f32(bias)
+        strides = None
+        if bias is not None:
+            assert bias.ndim == 4
+            full = (q.shape[0], q.shape[2], q.shape[1], k.shape[1])
+            st = [int(x) for x in np.array(bias.strides) // bias.itemsize]
+            for e in range(4):
+                assert bias.shape[e] in (1, full[e]), (bias.shape, full)
+                if bias.shape[e] == 1:
+                    st[e] = 0
+            strides = np.array(st, np.int64)
         B, Lq, Hq, D = q.shape
         Lk, Hkv = k.shape[1], k.shape[2]
         assert k.shape == (B, Lk, Hkv, D) and v.shape == k.shape
@@ -97,10 +132,11 @@ class Oracle:
         out = np.zeros((n, D), np.float64)
         lse = np.zeros(n, np.float64)
         nvis = np.zeros(n, np.int64)
-        rc = self.lib.mfa_oracle_rows(
+        rc = self.lib.mfa_oracle_rows_ext(
             _ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), _ptr(m, _fp),
             B, Lq, Lk, Hq, Hkv, D, float(scale), int(bool(causal)), int(window), int(q_offset),
-            float(softcap), _ptr(rows, _ip), n, _ptr(out, _dp), _ptr(lse, _dp), _ptr(nvis, _ip),
+            float(softcap), _ptr(bias, _fp), _ptr(strides, _ip), float(dropout_p), int(seed),
+            _ptr(rows, _ip), n, _ptr(out, _dp), _ptr(lse, _dp), _ptr(nvis, _ip),
             int(nthreads))
         if rc != 0:
             raise ValueError("oracle rejected its arguments")

@@ -708,6 +708,126 @@ def pin_varlen_sequences_are_independent(orc):
     _close(L2[:, keep], L[:, keep], 0.0, "other sequences' keys perturbed LSE")
 
 
+# ---------------------------------------------------------------------------
+# additive score mask (broadcast) and attention dropout
+# ---------------------------------------------------------------------------
+
+def _numpy_philox_block(ctr, key):
+    """First output block of NumPy's Philox (4x64-10) bit generator for the
+    given 256-bit counter: NumPy advances the counter once before its first
+    block, so it is started one below."""
+    c = [int(x) for x in ctr]
+    for w in range(4):                       # 256-bit decrement
+        if c[w] > 0:
+            c[w] -= 1
+            break
+        c[w] = (1 << 64) - 1
+    bg = np.random.Philox(key=np.array(key, np.uint64), counter=np.array(c, np.uint64))
+    return [int(x) for x in bg.random_raw(4)]
+
+
+def pin_philox_matches_numpy(orc):
+    """The oracle's Philox4x64-10 against NumPy's implementation of it."""
+    rng = _rng(23)
+    cases = [([0, 0, 0, 0], [0, 0]), ([1, 0, 0, 0], [5, 7]), ([2**64 - 1] * 4, [2**64 - 1] * 2)]
+    for _ in range(20):
+        cases.append((rng.integers(0, 2**63, 4, dtype=np.uint64).tolist(),
+                      rng.integers(0, 2**63, 2, dtype=np.uint64).tolist()))
+    for ctr, key in cases:
+        assert orc.philox4x64(ctr, key) == _numpy_philox_block(ctr, key), (ctr, key)
+
+
+def dense_bias_dropout(q, k, v, *, scale, causal, window, q_offset, softcap=0.0, key_mask=None,
+                       bias=None, dropout_p=0.0, seed=0):
+    """Full score matrix, bias broadcast by NumPy, dropout pattern from NumPy's
+    Philox with counter (j, i, hq, b) and key (seed, 0)."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    bb = None if bias is None else np.broadcast_to(np.asarray(bias, np.float64), (B, Hq, Lq, Lk))
+    thr = int(round(dropout_p * 2 ** 24))
+    O = np.zeros((B, Lq, Hq, D))
+    L = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        vis = dense_visibility(Lq, Lk, causal, window, q_offset,
+                               None if key_mask is None else np.asarray(key_mask)[b])
+        for h in range(Hq):
+            s = scale * (q[b, :, h, :] @ k[b, :, h // g, :].T)
+            if softcap > 0:
+                s = softcap * np.tanh(s / softcap)
+            if bb is not None:
+                s = s + bb[b, h]
+            s = np.where(vis, s, -np.inf)
+            empty = ~np.isfinite(s).any(1)
+            lse = np.where(empty, -np.inf, logsumexp(np.where(empty[:, None], 0.0, s), axis=1))
+            p = np.where(vis & ~empty[:, None], np.exp(s - np.where(empty, 0.0, lse)[:, None]), 0.0)
+            if dropout_p > 0:
+                keep = np.zeros((Lq, Lk), bool)
+                for i in range(Lq):
+                    for j in range(Lk):
+                        keep[i, j] = (_numpy_philox_block([j, i, h, b], [seed, 0])[0] >> 40) >= thr
+                p = np.where(keep, p / (1.0 - dropout_p), 0.0)
+            O[b, :, h, :] = p @ v[b, :, h // g, :]
+            L[b, h, :] = lse
+    return O, L
+
+
+def pin_bias_matches_dense(orc):
+    rng = _rng(24)
+    B, Lq, Lk, Hq, Hkv, D = 2, 7, 9, 4, 2, 8
+    q, k, v = _rand(rng, (B, Lq, Hq, D), 2.0), _rand(rng, (B, Lk, Hkv, D), 2.0), _rand(rng, (B, Lk, Hkv, D))
+    mask = (rng.random((B, Lk)) > 0.2).astype(np.float32)
+    for shape, causal, window, softcap in [((B, Hq, Lq, Lk), True, 0, 0.0), ((B, 1, 1, Lk), False, 6, 0.0),
+                                           ((1, Hq, Lq, Lk), True, 4, 2.0), ((1, 1, Lq, Lk), False, 0, 0.0),
+                                           ((B, 1, Lq, 1), True, 0, 0.0)]:
+        bias = _rand(rng, shape, 1.5)
+        kw = dict(scale=0.45, causal=causal, window=window, q_offset=Lk - Lq, softcap=softcap,
+                  key_mask=mask, bias=bias)
+        O, L, _ = orc.full(q, k, v, **kw)
+        Od, Ld = dense_bias_dropout(q, k, v, **kw)
+        _close(O, Od, TIGHT, f"bias O {shape}")
+        _close(L, Ld, TIGHT, f"bias LSE {shape}")
+
+
+def pin_bias_row_shift_and_neg_inf(orc):
+    """A bias constant along each row moves only the LSE (softmax shift
+    invariance); a bias of -inf on a key is the key mask."""
+    rng = _rng(25)
+    B, L, Hq, Hkv, D = 2, 8, 2, 1, 8
+    q, k, v = _rand(rng, (B, L, Hq, D)), _rand(rng, (B, L, Hkv, D)), _rand(rng, (B, L, Hkv, D))
+    O0, L0, _ = orc.full(q, k, v, scale=0.5, causal=True, q_offset=0)
+    c = _rand(rng, (B, Hq, L, 1), 3.0)
+    O1, L1, _ = orc.full(q, k, v, scale=0.5, causal=True, q_offset=0, bias=c)
+    _close(O1, O0, 1e-12, "row-constant bias O")
+    _close(L1, L0 + c[..., 0].astype(np.float64), 1e-12, "row-constant bias LSE")
+    mask = (rng.random((B, L)) > 0.4).astype(np.float32)
+    mask[:, 0] = 1.0
+    neg = np.where(mask > 0.5, 0.0, -np.inf).astype(np.float32)[:, None, None, :]
+    O2, L2, _ = orc.full(q, k, v, scale=0.5, causal=False, q_offset=0, bias=neg)
+    O3, L3, _ = orc.full(q, k, v, scale=0.5, causal=False, q_offset=0, key_mask=mask)
+    _close(O2, O3, 1e-12, "-inf bias vs key mask O")
+    _close(L2, L3, 1e-12, "-inf bias vs key mask LSE")
+
+
+def pin_dropout_matches_dense(orc):
+    """Dropout against the dense form with NumPy's Philox drawing the pattern;
+    the LSE ignores dropout and p = 0 is no dropout."""
+    rng = _rng(26)
+    B, Lq, Lk, Hq, Hkv, D = 2, 6, 8, 2, 1, 8
+    q, k, v = _rand(rng, (B, Lq, Hq, D), 2.0), _rand(rng, (B, Lk, Hkv, D), 2.0), _rand(rng, (B, Lk, Hkv, D))
+    for p, seed, causal in [(0.1, 1234, True), (0.5, 2**40 + 7, False), (0.9, 3, True)]:
+        kw = dict(scale=0.5, causal=causal, window=0, q_offset=Lk - Lq, dropout_p=p, seed=seed)
+        O, L, _ = orc.full(q, k, v, **kw)
+        Od, Ld = dense_bias_dropout(q, k, v, **kw)
+        _close(O, Od, TIGHT, f"dropout O p={p}")
+        _close(L, Ld, TIGHT, f"dropout LSE p={p}")
+    O0, L0, _ = orc.full(q, k, v, scale=0.5, causal=True, q_offset=Lk - Lq)
+    O1, L1, _ = orc.full(q, k, v, scale=0.5, causal=True, q_offset=Lk - Lq, dropout_p=0.0, seed=99)
+    _close(O1, O0, 0.0, "p = 0")
+    _close(L1, L0, 0.0, "p = 0 LSE")
+
+
 ALL_PINS = [
     pin_range_causal_matches_ferrotensor_rule,
     pin_range_causal_matches_forge_rule,
@@ -735,4 +855,8 @@ ALL_PINS = [
     pin_varlen_matches_dense,
     pin_varlen_zero_query_closed_form,
     pin_varlen_sequences_are_independent,
+    pin_philox_matches_numpy,
+    pin_bias_matches_dense,
+    pin_bias_row_shift_and_neg_inf,
+    pin_dropout_matches_dense,
 ]

@@ -25,6 +25,8 @@ MUTANTS = {
     12: "Q indexed as [B, H, L, D]",
     13: "batch 0's key mask used for every batch",
     14: "soft-cap applied before the scale",
+    15: "additive mask indexed with query and key swapped",
+    16: "dropout pattern drawn with query and key swapped",
 }
 
 
