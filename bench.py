@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-decode] [--no-decode-len] [--no-packed]
-                    [--no-cpu-baseline]
+                    [--no-bias-dropout] [--no-cpu-baseline]
 
 A step is one mfa_fwd call over one batch of synthetic input already resident
 in HBM: the whole forward (tile ranges, Q/K/V staging, Q.K^T, soft-cap and
@@ -16,7 +16,9 @@ HBM GB/s of compulsory traffic, and so is the decode over a device-held length
 under "decode_len".  "packed_encoder" times the bidirectional encoder workload
 (B=8, L=8192, H=12, D=64, fp16, window 128, tail padding) twice: padded with a
 key mask through mfa_fwd, and packed without its padding through
-mfa_packed_qkv_fwd.
+mfa_packed_qkv_fwd.  "bias_dropout" times the causal GQA prefill with a
+[1, 1, L, L] float32 additive mask and dropout 0.1 (mfa_fwd_bias_dropout, on
+the fp32-arithmetic generic kernel).
 
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
 average duration comes from HIP events recorded on the launch stream around
@@ -254,6 +256,29 @@ def packed_encoder(steps: int, warmup: int, warmup_ms: float):
     return res
 
 
+def bias_dropout(steps: int, warmup: int, warmup_ms: float):
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    w = wl.GQA_CAUSAL_PREFILL_BF16
+    q, k, v, _ = wl.make_inputs(w, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    bias = torch.randn((1, 1, w.Lq, w.Lk), generator=g, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
+    wall, kern = time_calls(lambda: mfa.fwd(q, k, v, causal=True, bias=bias, dropout_p=0.1, seed=5,
+                                            out=out, lse=lse), steps, warmup, warmup_ms)
+    pairs = visible_pairs(w, None)
+    res = {"workload": w.name, "api": "mfa_fwd_bias_dropout", "bias_shape": [1, 1, w.Lq, w.Lk],
+           "dropout_p": 0.1, "path": "generic", "unit": "TFLOP/s", "ms_per_step": round(wall, 5),
+           "kernel_ms_avg": round(kern, 5), "value": round(4.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
+    del q, k, v, bias, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, tensors, target_s: float = 12.0, seed: int = 0):
     """Time the fp64 oracle on a seeded sample of query rows of the workload."""
     from oracle import default_oracle
@@ -295,6 +320,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-len", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
+    ap.add_argument("--no-bias-dropout", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
@@ -407,6 +433,11 @@ def main():
         torch.cuda.empty_cache()
         line["packed_encoder"] = packed_encoder(max(10, args.steps // 2), max(3, args.warmup // 2),
                                                 args.warmup_ms)
+
+    if not args.no_bias_dropout:
+        tensors = None
+        torch.cuda.empty_cache()
+        line["bias_dropout"] = bias_dropout(5, 2, args.warmup_ms)
 
     if not args.no_cpu_baseline:
         if tensors is None:

@@ -95,6 +95,34 @@ int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
             float scale, int causal, int window, int q_offset, float softcap,
             const float* key_mask, int dtype, void* stream);
 
+/*
+ * mfa_fwd with two more of the pages' forward features (ferrotensor
+ * attention.rs, flash_attention_v2: an additive mask whose size-1 dimensions
+ * broadcast, and attention dropout driven by a seed).
+ *
+ *   bias        float32, contiguous [bias_B, bias_H, bias_Lq, bias_Lk], each
+ *               dimension 1 (broadcast) or B, Hq, Lq, Lk; added to the
+ *               scaled (and soft-capped) score before the causal, window and
+ *               key masks; may be NULL; finite values or -inf
+ *   dropout_p   in [0, 1): each normalised weight is dropped with this
+ *               probability and a kept one divided by 1 - p; the saved LSE
+ *               is the undropped one.  Weight (b, hq, i, j) is kept iff the
+ *               top 24 bits of word 0 of Philox4x64-10 (counter (j, i, hq, b),
+ *               key (seed, 0)) are at least round(p * 2^24), so a pattern is
+ *               reproducible from the seed alone.
+ *
+ * A row whose every visible key has a bias of -inf gets O = 0, LSE = -inf.
+ * These features run on the fp32-arithmetic kernel (MFA_PATH_GENERIC) for
+ * every dtype.  Other arguments, errors and streams as for mfa_fwd; a bias
+ * dimension other than 1 or full size, or p outside [0, 1), is
+ * MFA_ERROR_INVALID_VALUE.
+ */
+int mfa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Lq, int Lk, int Hq, int Hkv, int D,
+                         float scale, int causal, int window, int q_offset, float softcap,
+                         const float* key_mask, const float* bias, int bias_B, int bias_H, int bias_Lq,
+                         int bias_Lk, float dropout_p, unsigned long long seed, int dtype, void* stream);
+
 /* Workspace bytes that mfa_fwd_ws needs for these sizes (0 if none); the
  * figure covers every flag combination. */
 size_t mfa_fwd_workspace_size(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype);

@@ -219,3 +219,30 @@ def test_varlen_empty_and_workspace_size():
     assert call_varlen(Tq=0, batch=0) == 0
     assert mfa.varlen_workspace_size(0) == 0
     assert mfa.varlen_workspace_size(1000) >= 1000 * 3 * 4
+
+
+def call_bd(**over):
+    lib = mfa.load_library()
+    a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], lse=FAKE[4], B=2, Lq=16, Lk=20, Hq=4, Hkv=2,
+             D=64, scale=0.125, causal=1, window=0, q_offset=4, softcap=0.0, key_mask=None, bias=FAKE[5],
+             bB=1, bH=4, bQ=16, bK=20, p=0.1, seed=5, dtype=2)
+    a.update(over)
+    return lib.mfa_fwd_bias_dropout(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                                    a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["window"],
+                                    a["q_offset"], a["softcap"], a["key_mask"], a["bias"], a["bB"], a["bH"],
+                                    a["bQ"], a["bK"], a["p"], a["seed"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("over", [dict(q=None), dict(bB=3), dict(bH=2), dict(bQ=8), dict(bK=0), dict(p=1.0),
+                                  dict(p=-0.1), dict(p=float("nan")), dict(bias=ctypes.c_void_p(0x10002)),
+                                  dict(Hq=6, Hkv=4), dict(q_offset=5)],
+                         ids=lambda d: ",".join(d))
+def test_bias_dropout_invalid_arguments_rejected(over):
+    assert call_bd(**over) == 1, over
+    assert mfa.load_library().mfa_last_error().decode()
+
+
+def test_bias_dropout_unsupported_and_empty():
+    assert call_bd(D=96) == 2
+    assert call_bd(B=0) == 0
+    assert call_bd(Lq=0, bQ=1) == 0

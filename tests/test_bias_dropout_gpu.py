@@ -1,0 +1,89 @@
+"""GPU parity of the additive score mask and attention dropout
+(mfa_fwd_bias_dropout, generic kernel) against the fp64 oracle on every row:
+broadcast bias shapes, dropout probabilities and seeds, together with the
+causal/window/key-mask/soft-cap features, every dtype and head size."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_mfa_fwd_amd as mfa
+from oracle import default_oracle
+from tests import parity_util as pu
+from transformer_mfa_fwd_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"\n[bias_dropout] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bias_tensor(shape, seed, std=1.5, neg_inf_frac=0.0):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g) * std
+    if neg_inf_frac > 0:
+        x[torch.rand(shape, generator=g) < neg_inf_frac] = -float("inf")
+    return x.contiguous()
+
+
+def run_and_check(w, bias_shape, p, seed, neg_inf_frac=0.0):
+    q, k, v, m = wl.make_inputs(w, DEV)
+    full = (w.B, w.Hq, w.Lq, w.Lk)
+    shape = tuple(full[e] if bias_shape[e] else 1 for e in range(4)) if bias_shape else None
+    bias = None if shape is None else bias_tensor(shape, seed=17, neg_inf_frac=neg_inf_frac)
+    say(f"{w.name} bias={shape} p={p} seed={seed}")
+    out, lse = mfa.fwd(q, k, v, causal=w.causal, window=w.window, q_offset=w.q_offset, softcap=w.softcap,
+                       key_mask=m, scale=w.scale, bias=None if bias is None else bias.to(DEV),
+                       dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    O, L, _ = default_oracle().full(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
+                                    q_offset=w.q_offset, softcap=w.softcap, key_mask=m, bias=bias,
+                                    dropout_p=p, seed=seed, nthreads=pu.ORACLE_THREADS)
+    og = out.double().cpu().numpy().transpose(0, 2, 1, 3)
+    return pu.compare(w.dtype, og, lse.double().cpu().numpy(), O.transpose(0, 2, 1, 3), L,
+                      f"{w.name} bias={shape} p={p}")
+
+
+BASE = []
+for dtype in ("f32", "f16", "bf16"):
+    for D in (64, 128):
+        BASE.append(wl.Workload(f"bd_causal_gqa_{dtype}_D{D}", dtype, 2, 90, 130, 4, 2, D, True, window=60,
+                                mask="random_frac", mask_frac=0.2))
+        BASE.append(wl.Workload(f"bd_bidir_cap_{dtype}_D{D}", dtype, 2, 70, 70, 2, 2, D, False, softcap=8.0,
+                                std=2.0))
+
+SHAPES = [(1, 1, 1, 1), (1, 0, 0, 1), (0, 1, 1, 1), (0, 0, 1, 1), (1, 0, 1, 0)]
+
+
+@pytest.mark.parametrize("p,seed", [(0.0, 0), (0.1, 7), (0.5, 2**40 + 3)])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "".join(map(str, s)))
+@pytest.mark.parametrize("w", BASE, ids=lambda w: w.name)
+def test_bias_dropout_all_rows(w, shape, p, seed):
+    run_and_check(w, shape, p, seed)
+
+
+def test_dropout_without_bias_and_neg_inf_bias():
+    w = wl.Workload("bd_neginf", "bf16", 2, 64, 64, 2, 1, 128, True)
+    run_and_check(w, None, 0.3, 11)
+    run_and_check(w, (1, 1, 1, 1), 0.0, 0, neg_inf_frac=0.3)
+
+
+def test_all_neg_inf_row_is_empty_and_seeds_differ():
+    w = wl.Workload("bd_rows", "f16", 1, 40, 40, 2, 2, 64, False)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    bias = torch.zeros((1, 1, w.Lq, w.Lk), device=DEV)
+    bias[0, 0, 5] = -float("inf")
+    out, lse = mfa.fwd(q, k, v, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.all(out[0, 5] == 0) and torch.all(torch.isneginf(lse[0, :, 5]))
+    o1, _ = mfa.fwd(q, k, v, dropout_p=0.5, seed=1)
+    o2, _ = mfa.fwd(q, k, v, dropout_p=0.5, seed=1)
+    o3, _ = mfa.fwd(q, k, v, dropout_p=0.5, seed=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and not torch.equal(o1, o3)

@@ -25,7 +25,7 @@ _DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: 
 
 EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
             "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_packed_qkv_fwd",
-            "mfa_varlen_fwd", "mfa_varlen_workspace_size",
+            "mfa_varlen_fwd", "mfa_varlen_workspace_size", "mfa_fwd_bias_dropout",
             "mfa_status_string", "mfa_last_error", "mfa_version")
 
 
@@ -64,6 +64,8 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_fwd_plan.argtypes = [_I] * 7 + [ctypes.POINTER(_I)]
     lib.mfa_decode_len.restype = _I
     lib.mfa_decode_len.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_fwd_bias_dropout.restype = _I
+    lib.mfa_fwd_bias_dropout.argtypes = _FWD_ARGS[:-1] + [_P, _I, _I, _I, _I, _F, ctypes.c_ulonglong, _I, _P]
     lib.mfa_varlen_fwd.restype = _I
     lib.mfa_varlen_fwd.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]
     lib.mfa_varlen_workspace_size.restype = ctypes.c_size_t
@@ -113,7 +115,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         key_mask: Optional[torch.Tensor] = None, scale: Optional[float] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         return_lse: bool = True, path: int = PATH_AUTO, splits: int = 0,
-        workspace: Optional[torch.Tensor] = None, stream=None
+        workspace: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+        dropout_p: float = 0.0, seed: int = 0, stream=None
         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Attention forward through libmfa.
 
@@ -122,6 +125,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     scale to 1/sqrt(D).  Returns (out [B, Lq, Hq, D], lse [B, Hq, Lq] float32
     or None).  ``path``/``splits`` force a kernel path (mfa_fwd_ex);
     ``workspace`` is a caller-owned uint8 device tensor (mfa_fwd_ws).
+    ``bias`` (a contiguous float32 GPU tensor [bB, bH, bLq, bLk], each 1 or
+    B, Hq, Lq, Lk) and ``dropout_p``/``seed`` select mfa_fwd_bias_dropout.
     """
     lib = load_library()
     B, Lq, Lk, Hq, Hkv, D = _dims(q, k, v)
@@ -150,6 +155,20 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Lq, Lk, Hq, Hkv, D,
             float(scale), int(bool(causal)), int(window), int(q_offset), float(softcap),
             _ptr(key_mask), _DTYPE_CODES[q.dtype]]
+    if bias is not None or dropout_p > 0.0:
+        if path != PATH_AUTO or splits or workspace is not None:
+            raise ValueError("bias and dropout take neither a forced path nor a workspace")
+        dims = [1, 1, 1, 1]
+        if bias is not None:
+            if bias.dim() != 4 or bias.dtype != torch.float32 or not bias.is_cuda or \
+                    not bias.is_contiguous():
+                raise ValueError("bias must be a contiguous float32 GPU tensor [bB, bH, bLq, bLk]")
+            dims = [int(x) for x in bias.shape]
+        with torch.cuda.device(q.device):
+            _check(lib.mfa_fwd_bias_dropout(*args[:-1], _ptr(bias), *dims, float(dropout_p),
+                                            ctypes.c_ulonglong(int(seed) & (2 ** 64 - 1)), args[-1],
+                                            _stream(stream)))
+        return out, lse
     with torch.cuda.device(q.device):
         s = _stream(stream)
         ws_ptr = _ptr(workspace)

@@ -25,6 +25,26 @@ constexpr int ROWS_PER_WAVE = 16;
 template <typename T>
 __device__ inline float to_f32(T x) { return static_cast<float>(x); }
 
+// Word 0 of Philox4x64-10 (Salmon et al., SC 2011): ten rounds of two
+// 64x64 -> 128-bit products with the round constants, the halves mixed with
+// the other counter words and the key, the key bumped by the Weyl constants.
+__device__ inline uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                            uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += 0x9E3779B97F4A7C15ull;
+        k1 += 0xBB67AE8584CAA73Bull;
+    }
+    return c0;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
     __shared__ float sQ[GBM][D + 4];
@@ -112,9 +132,13 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
 
 #pragma unroll
             for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+                const int i = i0 + wave * ROWS_PER_WAVE + rr;
                 float x = s[rr] * a.scale;
                 if (a.softcap > 0.0f) x = a.softcap * tanhf(x / a.softcap);
                 const bool vis = key_ok && key >= rlo[rr] && key <= rhi[rr];
+                if (vis && a.bias)
+                    x += a.bias[b * a.bias_stride[0] + hq * a.bias_stride[1] + i * a.bias_stride[2] +
+                                key * a.bias_stride[3]];
                 x = vis ? x : -INFINITY;
 
                 float mx = x;
@@ -126,7 +150,13 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
                 const float p = expf(x - m_use);
                 l[rr] = l[rr] * alpha + p;
                 m[rr] = m_new;
-                sP[wave][rr][lane] = p;
+                float pv = p;   // the weight that multiplies V: after dropout, the sum stays undropped
+                if (a.drop_scale > 0.0f && p > 0.0f) {
+                    const uint64_t w = philox4x64_word0((uint64_t)key, (uint64_t)i, (uint64_t)hq, (uint64_t)b,
+                                                        a.drop_seed, 0);
+                    pv = (uint32_t)(w >> 40) >= a.drop_threshold ? p * a.drop_scale : 0.0f;
+                }
+                sP[wave][rr][lane] = pv;
 #pragma unroll
                 for (int c = 0; c < D / 64; ++c) acc[rr][c] *= alpha;
             }

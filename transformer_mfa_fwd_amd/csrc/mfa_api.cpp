@@ -36,6 +36,10 @@ struct Call {
     float softcap;
     const float* key_mask;
     int dtype;
+    const float* bias = nullptr;     // additive score mask [bias_dims] or null
+    int bias_dims[4] = {1, 1, 1, 1};
+    float dropout_p = 0.0f;
+    uint64_t seed = 0;
 };
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -65,6 +69,16 @@ int validate(const Call& c) {
         return fail(MFA_ERROR_INVALID_VALUE, "q, k, v and out must be 16-byte aligned");
     if (!aligned(c.lse, 4) || !aligned(c.key_mask, 4))
         return fail(MFA_ERROR_INVALID_VALUE, "lse and key_mask must be 4-byte aligned");
+    if (c.bias) {
+        const int full[4] = {c.B, c.Hq, c.Lq, c.Lk};
+        for (int e = 0; e < 4; ++e)
+            if (c.bias_dims[e] != 1 && c.bias_dims[e] != full[e])
+                return fail(MFA_ERROR_INVALID_VALUE, "bias dimension %d is %d: must be 1 or %d", e,
+                            c.bias_dims[e], full[e]);
+        if (!aligned(c.bias, 4)) return fail(MFA_ERROR_INVALID_VALUE, "bias must be 4-byte aligned");
+    }
+    if (!(c.dropout_p >= 0.0f && c.dropout_p < 1.0f))
+        return fail(MFA_ERROR_INVALID_VALUE, "dropout probability %g not in [0, 1)", (double)c.dropout_p);
     // sizes must fit the kernels' 64-bit element offsets and 32-bit row indices
     const int64_t q_elems = (int64_t)c.B * c.Lq * c.Hq * c.D;
     const int64_t kv_elems = (int64_t)c.B * c.Lk * c.Hkv * c.D;
@@ -116,7 +130,11 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
     if (c.B == 0 || c.Lq == 0) return MFA_SUCCESS;
 
     const int group = c.Hq / c.Hkv;
-    if (path == MFA_PATH_AUTO) path = auto_path(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D, c.dtype);
+    const bool extras = c.bias != nullptr || c.dropout_p > 0.0f;   // only the generic kernel has them
+    if (path == MFA_PATH_AUTO)
+        path = extras ? MFA_PATH_GENERIC : auto_path(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D, c.dtype);
+    if (extras && path != MFA_PATH_GENERIC)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "an additive mask or dropout needs the generic path");
     switch (path) {
         case MFA_PATH_GENERIC: break;
         case MFA_PATH_MFMA:
@@ -155,6 +173,19 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
     a.kv_stride = (int64_t)c.Hkv * c.D;
     a.o_stride = (int64_t)c.Hq * c.D;
     a.seq_bounds = nullptr;
+    if (c.bias) {
+        a.bias = c.bias;
+        const int64_t n3 = c.bias_dims[3], n2 = c.bias_dims[2] * n3, n1 = c.bias_dims[1] * n2;
+        a.bias_stride[0] = c.bias_dims[0] > 1 ? n1 : 0;
+        a.bias_stride[1] = c.bias_dims[1] > 1 ? n2 : 0;
+        a.bias_stride[2] = c.bias_dims[2] > 1 ? n3 : 0;
+        a.bias_stride[3] = c.bias_dims[3] > 1 ? 1 : 0;
+    }
+    if (c.dropout_p > 0.0f) {
+        a.drop_threshold = (uint32_t)std::llround((double)c.dropout_p * 16777216.0);
+        a.drop_scale = 1.0f / (1.0f - c.dropout_p);
+        a.drop_seed = c.seed;
+    }
     a.scale = c.scale;
     a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
     const float log2e = 1.4426950408889634f;
@@ -470,6 +501,20 @@ int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
             const float* key_mask, int dtype, void* stream) {
     g_last_error.clear();
     Call c{q, k, v, out, lse, B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap, key_mask, dtype};
+    return run(c, MFA_PATH_AUTO, 0, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+int mfa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Lq, int Lk, int Hq, int Hkv, int D,
+                         float scale, int causal, int window, int q_offset, float softcap,
+                         const float* key_mask, const float* bias, int bias_B, int bias_H, int bias_Lq,
+                         int bias_Lk, float dropout_p, unsigned long long seed, int dtype, void* stream) {
+    g_last_error.clear();
+    Call c{q, k, v, out, lse, B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap, key_mask, dtype};
+    c.bias = bias;
+    c.bias_dims[0] = bias_B; c.bias_dims[1] = bias_H; c.bias_dims[2] = bias_Lq; c.bias_dims[3] = bias_Lk;
+    c.dropout_p = dropout_p;
+    c.seed = seed;
     return run(c, MFA_PATH_AUTO, 0, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 

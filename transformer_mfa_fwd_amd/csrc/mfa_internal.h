@@ -30,6 +30,17 @@ struct FwdArgs {
     int64_t q_stride, kv_stride, o_stride;
     const int* seq_bounds;    // [Lq, 2]: row i only sees keys in [s0, s1) of its own sequence, or null
     const int* row_pos;       // [Lq]: absolute key-axis position of row i, or null (i + q_offset)
+    // additive score mask: element (b, hq, i, j) at the dot product of
+    // (b, hq, i, j) with bias_stride (0 for a broadcast dimension), or null
+    const float* bias;
+    int64_t bias_stride[4];
+    // attention dropout: a weight is kept iff the top 24 bits of word 0 of
+    // Philox4x64-10(counter (j, i, hq, b), key (drop_seed, 0)) are at least
+    // drop_threshold, and a kept weight is multiplied by drop_scale (> 0
+    // turns dropout on)
+    uint32_t drop_threshold;
+    float drop_scale;
+    uint64_t drop_seed;
 };
 
 // Keys [lo, hi] (inclusive) in range for a query at absolute position aq,
