@@ -411,5 +411,148 @@ int64_t mfa_oracle_visible_counts(const float* key_mask, int64_t B, int64_t Lq, 
     return total;
 }
 
+/*
+ * Gradients of the forward with respect to Q, K and V for an upstream
+ * gradient dO, from the definition: with P the row's softmax weights, Z the
+ * dropout factors (keep / (1 - p), or 1) and O = sum_j P_j Z_j V_j,
+ *     dV_j += P_j Z_j dO,      dP_j = Z_j <dO, V_j>,
+ *     dS_j  = P_j (dP_j - sum_l P_l dP_l)            (softmax derivative),
+ *     g_j   = dS_j * d s_j / d <Q, K_j>  = dS_j * scale * (1 - tanh^2) or scale,
+ *     dQ   += g_j K_j,         dK_j += g_j Q.
+ * (vision_rs flash_attn2.rs, backward kernels: D = rowsum(O * dO) and
+ * dS = P (dO . V - D); the additive mask takes no gradient, ferrotensor
+ * attention.rs backward.)  Masked keys contribute nothing.  Each (batch, kv
+ * head) is one job, so dK/dV sums run in a fixed order.
+ */
+typedef struct {
+    const float *q, *k, *v, *dout, *key_mask;
+    const oracle_dims* d;
+    double *dq, *dk, *dv;
+    int64_t first, step;
+    int failed;
+} bwd_job;
+
+static void bwd_group(const bwd_job* job, int64_t b, int64_t kvh, double* P, double* Z, double* dP, double* dl)
+{
+    const oracle_dims* d = job->d;
+    const int64_t D = d->D, g = d->Hq / d->Hkv, Lk = d->Lk;
+    for (int64_t hq = kvh * g; hq < (kvh + 1) * g; ++hq) {
+        for (int64_t i = 0; i < d->Lq; ++i) {
+            const float* qrow = job->q + ((b * d->Lq + i) * d->Hq + hq) * D;
+            const float* grow = job->dout + ((b * d->Lq + i) * d->Hq + hq) * D;
+            double* dqrow = job->dq + ((b * d->Lq + i) * d->Hq + hq) * D;
+            int64_t lo, hi;
+            mfa_oracle_key_range(query_position(d, i), Lk, d->causal, d->window, &lo, &hi);
+            /* scores of the visible keys (NaN marks the others) and d s / d <Q, K> */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < Lk; ++j) {
+                P[j] = NAN;
+                if (!(j >= lo && j <= hi && key_mask_keeps(job->key_mask, Lk, b, j))) continue;
+                const float* krow = job->k + ((b * Lk + j) * d->Hkv + kvh) * D;
+                double dot = 0.0;
+                for (int64_t e = 0; e < D; ++e) dot += (double)qrow[e] * (double)krow[e];
+                const double t = d->scale * dot;
+                double x = t;
+                dl[j] = d->scale;
+                if (d->softcap > 0.0) {
+                    const double th = tanh(t / d->softcap);
+                    x = d->softcap * th;
+                    dl[j] = d->scale * (1.0 - th * th);
+                }
+                if (d->bias) x += d->bias[b * d->bs[0] + hq * d->bs[1] + i * d->bs[2] + j * d->bs[3]];
+                P[j] = x;
+                if (x > m) m = x;
+            }
+            if (m == -INFINITY) continue;            /* no weight: no gradient */
+            /* softmax weights P, dropout factors Z, dP = Z <dO, V_j>, and sum P dP */
+            double sum = 0.0;
+            for (int64_t j = 0; j < Lk; ++j)
+                if (!isnan(P[j])) { P[j] = exp(P[j] - m); sum += P[j]; }
+            double pdp = 0.0;
+            for (int64_t j = 0; j < Lk; ++j) {
+                if (isnan(P[j])) continue;
+                P[j] /= sum;
+                Z[j] = 1.0;
+                if (d->dropout_p > 0.0)
+                    Z[j] = mfa_oracle_dropout_keep(d->seed, d->dropout_p, b, hq, i, j) ? 1.0 / (1.0 - d->dropout_p) : 0.0;
+                const float* vrow = job->v + ((b * Lk + j) * d->Hkv + kvh) * D;
+                double dov = 0.0;
+                for (int64_t e = 0; e < D; ++e) dov += (double)grow[e] * (double)vrow[e];
+                dP[j] = Z[j] * dov;
+                pdp += P[j] * dP[j];
+            }
+            for (int64_t j = 0; j < Lk; ++j) {
+                if (isnan(P[j])) continue;
+#if ORACLE_MUTANT == 17
+                const double gj = P[j] * (dP[j] - pdp);                 /* logit derivative dropped */
+#else
+                const double gj = P[j] * (dP[j] - pdp) * dl[j];
+#endif
+                const float* krow = job->k + ((b * Lk + j) * d->Hkv + kvh) * D;
+                double* dkrow = job->dk + ((b * Lk + j) * d->Hkv + kvh) * D;
+                double* dvrow = job->dv + ((b * Lk + j) * d->Hkv + kvh) * D;
+                for (int64_t e = 0; e < D; ++e) {
+                    dqrow[e] += gj * (double)krow[e];
+                    dkrow[e] += gj * (double)qrow[e];
+                    dvrow[e] += P[j] * Z[j] * (double)grow[e];
+                }
+            }
+        }
+    }
+}
+
+static void* bwd_worker(void* arg)
+{
+    bwd_job* job = (bwd_job*)arg;
+    const oracle_dims* d = job->d;
+    const size_t n = (size_t)(d->Lk > 0 ? d->Lk : 1);
+    double* buf = (double*)malloc(sizeof(double) * 4 * n);
+    if (!buf) { job->failed = 1; return NULL; }
+    for (int64_t t = job->first; t < d->B * d->Hkv; t += job->step)
+        bwd_group(job, t / d->Hkv, t % d->Hkv, buf, buf + n, buf + 2 * n, buf + 3 * n);
+    free(buf);
+    return NULL;
+}
+
+/*
+ * dQ [B, Lq, Hq, D] and dK, dV [B, Lk, Hkv, D] (fp64, overwritten) for the
+ * upstream gradient dout [B, Lq, Hq, D]; other arguments as for
+ * mfa_oracle_rows_ext.  Returns 0, or -1 on bad arguments.
+ */
+int mfa_oracle_bwd(const float* q, const float* k, const float* v, const float* dout, const float* key_mask,
+                   int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
+                   double scale, int causal, int64_t window, int64_t q_offset, double softcap,
+                   const float* bias, const int64_t* bias_strides, double dropout_p, uint64_t seed,
+                   double* dq, double* dk, double* dv, int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    if (B <= 0 || Lq <= 0 || Lk <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return -1;
+    if (bias && !bias_strides) return -1;
+    if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return -1;
+    oracle_dims d = {B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap,
+                     bias, {0, 0, 0, 0}, dropout_p, seed};
+    if (bias)
+        for (int e = 0; e < 4; ++e) d.bs[e] = bias_strides[e];
+    memset(dq, 0, sizeof(double) * (size_t)(B * Lq * Hq * D));
+    memset(dk, 0, sizeof(double) * (size_t)(B * Lk * Hkv * D));
+    memset(dv, 0, sizeof(double) * (size_t)(B * Lk * Hkv * D));
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    bwd_job jobs[256];
+    pthread_t tids[256];
+    int created[256];
+    int failed = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (bwd_job){q, k, v, dout, key_mask, &d, dq, dk, dv, t, nthreads, 0};
+        created[t] = nthreads > 1 && pthread_create(&tids[t], NULL, bwd_worker, &jobs[t]) == 0;
+        if (!created[t]) bwd_worker(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        if (created[t]) pthread_join(tids[t], NULL);
+        failed |= jobs[t].failed;
+    }
+    return failed ? -1 : 0;
+}
+
 /* Which mistake (0 = none) this build carries; the mutation test reads it. */
 int mfa_oracle_mutant(void) { return ORACLE_MUTANT; }

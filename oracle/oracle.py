@@ -71,6 +71,10 @@ class Oracle:
         lib.mfa_oracle_philox4x64.argtypes = [_u64p, _u64p, _u64p]
         lib.mfa_oracle_dropout_keep.restype = ctypes.c_int
         lib.mfa_oracle_dropout_keep.argtypes = [ctypes.c_uint64, ctypes.c_double] + [ctypes.c_int64] * 4
+        lib.mfa_oracle_bwd.restype = ctypes.c_int
+        lib.mfa_oracle_bwd.argtypes = [_fp] * 5 + [ctypes.c_int64] * 6 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            _fp, _ip, ctypes.c_double, ctypes.c_uint64, _dp, _dp, _dp, ctypes.c_int]
         lib.mfa_oracle_visible_counts.restype = ctypes.c_int64
         lib.mfa_oracle_visible_counts.argtypes = [_fp] + [ctypes.c_int64] * 3 + [
             ctypes.c_int, ctypes.c_int64, ctypes.c_int64, _ip]
@@ -141,6 +145,40 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
         return out, lse, nvis
+
+    @staticmethod
+    def _bias_strides(bias, q, k):
+        if bias is None:
+            return None, None
+        full = (q.shape[0], q.shape[2], q.shape[1], k.shape[1])
+        st = [int(x) for x in np.array(bias.strides) // bias.itemsize]
+        for e in range(4):
+            assert bias.shape[e] in (1, full[e]), (bias.shape, full)
+            if bias.shape[e] == 1:
+                st[e] = 0
+        return bias, np.array(st, np.int64)
+
+    def bwd(self, q, k, v, dout, *, scale, causal=False, window=0, q_offset=None, softcap=0.0,
+            key_mask=None, bias=None, dropout_p=0.0, seed=0, nthreads=1):
+        """Gradients (dq [B,Lq,Hq,D], dk, dv [B,Lk,Hkv,D], float64) of the
+        forward with the same arguments for the upstream gradient dout."""
+        q, k, v, g, m = _f32(q), _f32(k), _f32(v), _f32(dout), _f32(key_mask)
+        bias, strides = self._bias_strides(_f32(bias), q, k)
+        B, Lq, Hq, D = q.shape
+        Lk, Hkv = k.shape[1], k.shape[2]
+        if q_offset is None:
+            q_offset = Lk - Lq
+        dq = np.zeros(q.shape, np.float64)
+        dk = np.zeros(k.shape, np.float64)
+        dv = np.zeros(k.shape, np.float64)
+        rc = self.lib.mfa_oracle_bwd(
+            _ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), _ptr(g, _fp), _ptr(m, _fp),
+            B, Lq, Lk, Hq, Hkv, D, float(scale), int(bool(causal)), int(window), int(q_offset),
+            float(softcap), _ptr(bias, _fp), _ptr(strides, _ip), float(dropout_p), int(seed),
+            _ptr(dq, _dp), _ptr(dk, _dp), _ptr(dv, _dp), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return dq, dk, dv
 
     def full(self, q, k, v, **kw):
         """Every row: returns O [B, Lq, Hq, D] and LSE [B, Hq, Lq] (float64)."""

@@ -828,6 +828,95 @@ def pin_dropout_matches_dense(orc):
     _close(L1, L0, 0.0, "p = 0 LSE")
 
 
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def _grid(rng, shape, step=2.0 ** -6, spread=64):
+    """Values on a coarse binary grid, so that +-h perturbations with a
+    power-of-two h stay exact in float32."""
+    return (rng.integers(-spread, spread + 1, shape) * step).astype(np.float32)
+
+
+def pin_bwd_matches_finite_differences(orc):
+    """dL/dX for L = sum(O * G) against central differences of the oracle's
+    own forward (exact inputs on a binary grid, h = 2^-12)."""
+    rng = _rng(27)
+    B, Lq, Lk, Hq, Hkv, D = 1, 5, 7, 2, 1, 4
+    for kw in [dict(causal=True, window=0, softcap=0.0), dict(causal=False, window=4, softcap=1.5),
+               dict(causal=True, window=3, softcap=0.0, dropout_p=0.3, seed=9)]:
+        q, k, v = _grid(rng, (B, Lq, Hq, D)), _grid(rng, (B, Lk, Hkv, D)), _grid(rng, (B, Lk, Hkv, D))
+        G = _rand(rng, (B, Lq, Hq, D))
+        mask = np.ones((B, Lk), np.float32)
+        mask[0, 2] = 0.0
+        bias = _grid(rng, (1, Hq, Lq, Lk), 2.0 ** -4, 16)
+        args = dict(scale=0.7, q_offset=Lk - Lq, key_mask=mask, bias=bias, **kw)
+        dq, dk, dv = orc.bwd(q, k, v, G, **args)
+        h = 2.0 ** -12
+
+        def loss(q_, k_, v_):
+            O, _, _ = orc.full(q_, k_, v_, **args)
+            return float(np.sum(O * G))
+        for name, X, dX in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for idx in [tuple(rng.integers(0, n) for n in X.shape) for _ in range(6)]:
+                Xp, Xm = X.copy(), X.copy()
+                Xp[idx] += h
+                Xm[idx] -= h
+                if name == "q":
+                    fd = (loss(Xp, k, v) - loss(Xm, k, v)) / (2 * h)
+                elif name == "k":
+                    fd = (loss(q, Xp, v) - loss(q, Xm, v)) / (2 * h)
+                else:
+                    fd = (loss(q, k, Xp) - loss(q, k, Xm)) / (2 * h)
+                assert abs(fd - dX[idx]) <= 1e-6 * (1 + abs(fd)), (name, idx, kw, fd, dX[idx])
+
+
+def pin_bwd_matches_torch_autograd(orc):
+    """Against torch float64 autograd through a dense formulation of the same
+    forward (scale, soft-cap, additive mask, masks as -inf, softmax, dropout
+    factors from NumPy's Philox, GQA by repeating K and V)."""
+    rng = _rng(28)
+    B, Lq, Lk, Hq, Hkv, D = 2, 6, 8, 4, 2, 8
+    for kw in [dict(causal=True, window=0, softcap=0.0, bias=False, dropout_p=0.0),
+               dict(causal=False, window=6, softcap=2.0, bias=True, dropout_p=0.0),
+               dict(causal=True, window=4, softcap=0.0, bias=True, dropout_p=0.4)]:
+        q, k, v = _rand(rng, (B, Lq, Hq, D)), _rand(rng, (B, Lk, Hkv, D)), _rand(rng, (B, Lk, Hkv, D))
+        G = _rand(rng, (B, Lq, Hq, D))
+        mask = (rng.random((B, Lk)) > 0.2).astype(np.float32)
+        bias = _rand(rng, (B, 1, Lq, Lk)) if kw["bias"] else None
+        seed = 77
+        args = dict(scale=0.5, causal=kw["causal"], window=kw["window"], q_offset=Lk - Lq,
+                    softcap=kw["softcap"], key_mask=mask, bias=bias, dropout_p=kw["dropout_p"], seed=seed)
+        dq, dk, dv = orc.bwd(q, k, v, G, **args)
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        g = Hq // Hkv
+        kr = tk.repeat_interleave(g, dim=2)
+        vr = tv.repeat_interleave(g, dim=2)
+        S = 0.5 * torch.einsum("bihd,bjhd->bhij", tq, kr)
+        if kw["softcap"] > 0:
+            S = kw["softcap"] * torch.tanh(S / kw["softcap"])
+        if bias is not None:
+            S = S + torch.tensor(bias, dtype=torch.float64)
+        vis = np.stack([dense_visibility(Lq, Lk, kw["causal"], kw["window"], Lk - Lq, mask[b_]) for b_ in range(B)])
+        S = S.masked_fill(~torch.tensor(vis)[:, None], -float("inf"))
+        P = torch.softmax(S, dim=-1)
+        if kw["dropout_p"] > 0:
+            thr = int(round(kw["dropout_p"] * 2 ** 24))
+            Z = np.zeros((B, Hq, Lq, Lk))
+            for b_ in range(B):
+                for h_ in range(Hq):
+                    for i in range(Lq):
+                        for j in range(Lk):
+                            keep = (_numpy_philox_block([j, i, h_, b_], [seed, 0])[0] >> 40) >= thr
+                            Z[b_, h_, i, j] = 1.0 / (1.0 - kw["dropout_p"]) if keep else 0.0
+            P = P * torch.tensor(Z)
+        O = torch.einsum("bhij,bjhd->bihd", P, vr)
+        (O * torch.tensor(G, dtype=torch.float64)).sum().backward()
+        _close(dq, tq.grad.numpy(), 1e-12, f"dq {kw}")
+        _close(dk, tk.grad.numpy(), 1e-12, f"dk {kw}")
+        _close(dv, tv.grad.numpy(), 1e-12, f"dv {kw}")
+
+
 ALL_PINS = [
     pin_range_causal_matches_ferrotensor_rule,
     pin_range_causal_matches_forge_rule,
@@ -859,4 +948,6 @@ ALL_PINS = [
     pin_bias_matches_dense,
     pin_bias_row_shift_and_neg_inf,
     pin_dropout_matches_dense,
+    pin_bwd_matches_finite_differences,
+    pin_bwd_matches_torch_autograd,
 ]

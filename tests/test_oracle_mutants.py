@@ -27,6 +27,7 @@ MUTANTS = {
     14: "soft-cap applied before the scale",
     15: "additive mask indexed with query and key swapped",
     16: "dropout pattern drawn with query and key swapped",
+    17: "backward without the derivative of the scale and soft-cap",
 }
 
 
