@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-decode] [--no-decode-len] [--no-packed]
-                    [--no-bias-dropout] [--no-cpu-baseline]
+                    [--no-bias-dropout] [--no-backward]
+                    [--no-cpu-baseline]
 
 A step is one mfa_fwd call over one batch of synthetic input already resident
 in HBM: the whole forward (tile ranges, Q/K/V staging, Q.K^T, soft-cap and
@@ -18,7 +19,8 @@ under "decode_len".  "packed_encoder" times the bidirectional encoder workload
 key mask through mfa_fwd, and packed without its padding through
 mfa_packed_qkv_fwd.  "bias_dropout" times the causal GQA prefill with a
 [1, 1, L, L] float32 additive mask and dropout 0.1 (mfa_fwd_bias_dropout, on
-the fp32-arithmetic generic kernel).
+the fp32-arithmetic generic kernel).  "backward" times mfa_bwd (dQ, dK, dV) on
+the causal GQA prefill shape.
 
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
 average duration comes from HIP events recorded on the launch stream around
@@ -279,6 +281,27 @@ def bias_dropout(steps: int, warmup: int, warmup_ms: float):
     return res
 
 
+def backward(steps: int, warmup: int, warmup_ms: float):
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    w = wl.GQA_CAUSAL_PREFILL_BF16
+    q, k, v, _ = wl.make_inputs(w, "cuda")
+    out, lse = mfa.fwd(q, k, v, causal=True)
+    dout = torch.randn(q.shape, device="cuda").to(q.dtype)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wall, kern = time_calls(lambda: mfa.bwd(q, k, v, out, dout, lse, causal=True, dq=dq, dk=dk, dv=dv),
+                            steps, warmup, warmup_ms)
+    pairs = visible_pairs(w, None)
+    res = {"workload": w.name, "api": "mfa_bwd", "path": "generic", "unit": "TFLOP/s",
+           "flops_per_pair": 10 * w.D, "ms_per_step": round(wall, 5), "kernel_ms_avg": round(kern, 5),
+           "value": round(10.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
+    del q, k, v, out, lse, dout, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, tensors, target_s: float = 12.0, seed: int = 0):
     """Time the fp64 oracle on a seeded sample of query rows of the workload."""
     from oracle import default_oracle
@@ -321,6 +344,7 @@ def main():
     ap.add_argument("--no-decode-len", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--no-bias-dropout", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
@@ -438,6 +462,11 @@ def main():
         tensors = None
         torch.cuda.empty_cache()
         line["bias_dropout"] = bias_dropout(5, 2, args.warmup_ms)
+
+    if not args.no_backward:
+        tensors = None
+        torch.cuda.empty_cache()
+        line["backward"] = backward(5, 2, args.warmup_ms)
 
     if not args.no_cpu_baseline:
         if tensors is None:

@@ -123,6 +123,38 @@ int mfa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* out,
                          const float* key_mask, const float* bias, int bias_B, int bias_H, int bias_Lq,
                          int bias_Lk, float dropout_p, unsigned long long seed, int dtype, void* stream);
 
+/*
+ * Backward of mfa_fwd / mfa_fwd_bias_dropout: the gradients dQ, dK, dV of a
+ * loss for its gradient dout with respect to the output (vision_rs
+ * flash_attn2.rs, backward kernels; ferrotensor attention.rs,
+ * flash_attention_v2_backward_with: the same options and mask as the forward,
+ * dropout regenerated from the seed, no gradient for the additive mask).
+ *
+ *   out, dout     [B, Lq, Hq, D]   the forward's output and its gradient
+ *   lse           [B, Hq, Lq]      float32, the forward's saved LSE
+ *   dq            [B, Lq, Hq, D]   written, element type `dtype`
+ *   dk, dv        [B, Lk, Hkv, D]  written (summed over the Hq/Hkv query
+ *                                  heads that share each kv head)
+ * Every other argument must repeat the forward call's.  The weights are
+ * recomputed from q, k and lse (P = exp(s - LSE)); with Delta = <dO, O> per
+ * row, dS = P (Z <dO, V> - Delta) and the chain rule through the scale and
+ * soft-cap.  Each gradient element is written by one workgroup, with no
+ * atomics, so a call is deterministic.  fp32 arithmetic on every dtype (not
+ * tuned for speed).  The workspace holds Delta: caller-owned (256-byte
+ * aligned, at least mfa_bwd_workspace_size bytes) or NULL with ws_bytes = 0
+ * for the stream-ordered pool.  B = 0 does nothing; Lq = 0 writes zero dK,
+ * dV.  Errors as for mfa_fwd_bias_dropout, plus null or misaligned
+ * out/dout/lse/dq/dk/dv.
+ */
+int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+            void* dq, void* dk, void* dv, int B, int Lq, int Lk, int Hq, int Hkv, int D,
+            float scale, int causal, int window, int q_offset, float softcap,
+            const float* key_mask, const float* bias, int bias_B, int bias_H, int bias_Lq, int bias_Lk,
+            float dropout_p, unsigned long long seed, int dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes mfa_bwd needs (0 when B, Lq or Hq is 0). */
+size_t mfa_bwd_workspace_size(int B, int Lq, int Hq);
+
 /* Workspace bytes that mfa_fwd_ws needs for these sizes (0 if none); the
  * figure covers every flag combination. */
 size_t mfa_fwd_workspace_size(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype);

@@ -246,3 +246,34 @@ def test_bias_dropout_unsupported_and_empty():
     assert call_bd(D=96) == 2
     assert call_bd(B=0) == 0
     assert call_bd(Lq=0, bQ=1) == 0
+
+
+def call_bwd(**over):
+    lib = mfa.load_library()
+    a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], dout=FAKE[4], lse=FAKE[5], dq=FAKE[6], dk=FAKE[7],
+             dv=ctypes.c_void_p(0x90000), B=2, Lq=16, Lk=20, Hq=4, Hkv=2, D=64, scale=0.1, causal=1, window=0,
+             q_offset=4, softcap=0.0, key_mask=None, bias=None, bB=1, bH=1, bQ=1, bK=1, p=0.0, seed=0, dtype=2,
+             ws=None, ws_bytes=0)
+    a.update(over)
+    return lib.mfa_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                       a["Lq"], a["Lk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["window"],
+                       a["q_offset"], a["softcap"], a["key_mask"], a["bias"], a["bB"], a["bH"], a["bQ"], a["bK"],
+                       a["p"], a["seed"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over", [dict(q=None), dict(out=None), dict(dout=None), dict(lse=None), dict(dq=None),
+                                  dict(dk=None), dict(dv=None), dict(dout=ctypes.c_void_p(0x10008)),
+                                  dict(dv=ctypes.c_void_p(0x10004)), dict(Hq=6, Hkv=4), dict(q_offset=5),
+                                  dict(bias=FAKE[5], bQ=3), dict(p=1.0), dict(ws=None, ws_bytes=8),
+                                  dict(ws=ctypes.c_void_p(0x10010), ws_bytes=1 << 20)],
+                         ids=lambda d: ",".join(d))
+def test_bwd_invalid_arguments_rejected(over):
+    assert call_bwd(**over) == 1, over
+    assert mfa.load_library().mfa_last_error().decode()
+
+
+def test_bwd_unsupported_empty_and_workspace():
+    assert call_bwd(D=96) == 2
+    assert call_bwd(B=0) == 0
+    assert mfa.bwd_workspace_size(2, 16, 4) >= 2 * 16 * 4 * 4
+    assert mfa.bwd_workspace_size(0, 16, 4) == 0

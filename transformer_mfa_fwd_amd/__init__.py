@@ -4,12 +4,13 @@
 see ``_binding.fwd`` for the arguments.  ``decode_len`` is the decode over a
 device-held cache length (``_binding.decode_len``), ``packed_qkv_fwd`` the
 bidirectional forward over sequences packed in one fused QKV tensor, and
-``varlen_fwd`` the forward over separate query and key packings.  The package holds the HIP sources
+``varlen_fwd`` the forward over separate query and key packings, ``bwd`` the
+gradients of the forward.  The package holds the HIP sources
 (csrc/), their build step (build.py), the ctypes binding and the seeded input
 generators (workloads.py).
 """
 from ._binding import (  # noqa: F401
     EXPORTED, LIB_PATH, MFAError, PATH_AUTO, PATH_GENERIC, PATH_MFMA, PATH_NAMES,
-    PATH_SPLIT_DECODE, decode_len, decode_len_workspace_size, fwd, load_library, packed_qkv_fwd, plan,
+    PATH_SPLIT_DECODE, bwd, bwd_workspace_size, decode_len, decode_len_workspace_size, fwd, load_library, packed_qkv_fwd, plan,
     varlen_fwd, varlen_workspace_size, version, workspace_size,
 )

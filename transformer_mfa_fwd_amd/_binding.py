@@ -26,6 +26,7 @@ _DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: 
 EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
             "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_packed_qkv_fwd",
             "mfa_varlen_fwd", "mfa_varlen_workspace_size", "mfa_fwd_bias_dropout",
+            "mfa_bwd", "mfa_bwd_workspace_size",
             "mfa_status_string", "mfa_last_error", "mfa_version")
 
 
@@ -66,6 +67,11 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_decode_len.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P, ctypes.c_size_t, _P]
     lib.mfa_fwd_bias_dropout.restype = _I
     lib.mfa_fwd_bias_dropout.argtypes = _FWD_ARGS[:-1] + [_P, _I, _I, _I, _I, _F, ctypes.c_ulonglong, _I, _P]
+    lib.mfa_bwd.restype = _I
+    lib.mfa_bwd.argtypes = [_P] * 9 + [_I] * 6 + [_F, _I, _I, _I, _F, _P, _P, _I, _I, _I, _I, _F,
+                                                  ctypes.c_ulonglong, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mfa_bwd_workspace_size.argtypes = [_I] * 3
     lib.mfa_varlen_fwd.restype = _I
     lib.mfa_varlen_fwd.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]
     lib.mfa_varlen_workspace_size.restype = ctypes.c_size_t
@@ -319,6 +325,57 @@ def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
                                   int(bool(causal)), int(window), float(softcap), _DTYPE_CODES[q.dtype],
                                   _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+        lse: torch.Tensor, *, causal: bool = False, window: int = 0, q_offset: Optional[int] = None,
+        softcap: float = 0.0, key_mask: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+        bias: Optional[torch.Tensor] = None, dropout_p: float = 0.0, seed: int = 0,
+        dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+        dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) of the forward for the output gradient dout
+    (mfa_bwd).  out and lse are the forward's results; every option must
+    repeat the forward call's."""
+    lib = load_library()
+    B, Lq, Lk, Hq, Hkv, D = _dims(q, k, v)
+    if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one of float32/float16/bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out.shape != q.shape or dout.shape != q.shape or out.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("out and dout must match q")
+    if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, Lq]")
+    if key_mask is not None and (key_mask.dtype != torch.float32 or tuple(key_mask.shape) != (B, Lk)):
+        raise ValueError("key_mask must be float32 [B, Lk]")
+    dims = [1, 1, 1, 1]
+    if bias is not None:
+        if bias.dim() != 4 or bias.dtype != torch.float32 or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous float32 tensor [bB, bH, bLq, bLk]")
+        dims = [int(x) for x in bias.shape]
+    if q_offset is None:
+        q_offset = Lk - Lq
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous and match its input")
+    with torch.cuda.device(q.device):
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.mfa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                           _ptr(dv), B, Lq, Lk, Hq, Hkv, D, float(scale), int(bool(causal)), int(window),
+                           int(q_offset), float(softcap), _ptr(key_mask), _ptr(bias), *dims, float(dropout_p),
+                           ctypes.c_ulonglong(int(seed) & (2 ** 64 - 1)), _DTYPE_CODES[q.dtype],
+                           _ptr(workspace), ws_bytes, _stream(stream)))
+    return dq, dk, dv
+
+
+def bwd_workspace_size(B: int, Lq: int, Hq: int) -> int:
+    return int(load_library().mfa_bwd_workspace_size(B, Lq, Hq))
 
 
 def varlen_workspace_size(total_q: int) -> int:

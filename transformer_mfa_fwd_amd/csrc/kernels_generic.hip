@@ -25,26 +25,6 @@ constexpr int ROWS_PER_WAVE = 16;
 template <typename T>
 __device__ inline float to_f32(T x) { return static_cast<float>(x); }
 
-// Word 0 of Philox4x64-10 (Salmon et al., SC 2011): ten rounds of two
-// 64x64 -> 128-bit products with the round constants, the halves mixed with
-// the other counter words and the key, the key bumped by the Weyl constants.
-__device__ inline uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
-                                            uint64_t k0, uint64_t k1) {
-    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
-        c0 = hi1 ^ c1 ^ k0;
-        c1 = lo1;
-        c2 = hi0 ^ c3 ^ k1;
-        c3 = lo0;
-        k0 += 0x9E3779B97F4A7C15ull;
-        k1 += 0xBB67AE8584CAA73Bull;
-    }
-    return c0;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
     __shared__ float sQ[GBM][D + 4];
@@ -152,9 +132,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
                 m[rr] = m_new;
                 float pv = p;   // the weight that multiplies V: after dropout, the sum stays undropped
                 if (a.drop_scale > 0.0f && p > 0.0f) {
-                    const uint64_t w = philox4x64_word0((uint64_t)key, (uint64_t)i, (uint64_t)hq, (uint64_t)b,
-                                                        a.drop_seed, 0);
-                    pv = (uint32_t)(w >> 40) >= a.drop_threshold ? p * a.drop_scale : 0.0f;
+                    pv = dropout_keep(a, b, hq, i, key) ? p * a.drop_scale : 0.0f;
                 }
                 sP[wave][rr][lane] = pv;
 #pragma unroll

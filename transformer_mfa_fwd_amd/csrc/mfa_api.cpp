@@ -124,6 +124,40 @@ void prepare_pool(int dev) {
     });
 }
 
+mfa::FwdArgs make_args(const Call& c) {
+    mfa::FwdArgs a{};
+    a.q = c.q; a.k = c.k; a.v = c.v; a.out = c.out; a.lse = c.lse;
+    a.key_mask = c.key_mask;
+    a.B = c.B; a.Lq = c.Lq; a.Lk = c.Lk; a.Hq = c.Hq; a.Hkv = c.Hkv; a.D = c.D;
+    a.group = c.Hq / c.Hkv;
+    a.causal = c.causal ? 1 : 0;
+    a.window = c.window > 0 ? c.window : 0;
+    a.q_offset = c.q_offset;
+    a.words_per_batch = words_per_batch(c.Lk);
+    a.q_stride = (int64_t)c.Hq * c.D;
+    a.kv_stride = (int64_t)c.Hkv * c.D;
+    a.o_stride = (int64_t)c.Hq * c.D;
+    a.seq_bounds = nullptr;
+    if (c.bias) {
+        a.bias = c.bias;
+        const int64_t n3 = c.bias_dims[3], n2 = c.bias_dims[2] * n3, n1 = c.bias_dims[1] * n2;
+        a.bias_stride[0] = c.bias_dims[0] > 1 ? n1 : 0;
+        a.bias_stride[1] = c.bias_dims[1] > 1 ? n2 : 0;
+        a.bias_stride[2] = c.bias_dims[2] > 1 ? n3 : 0;
+        a.bias_stride[3] = c.bias_dims[3] > 1 ? 1 : 0;
+    }
+    if (c.dropout_p > 0.0f) {
+        a.drop_threshold = (uint32_t)std::llround((double)c.dropout_p * 16777216.0);
+        a.drop_scale = 1.0f / (1.0f - c.dropout_p);
+        a.drop_seed = c.seed;
+    }
+    a.scale = c.scale;
+    a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
+    const float log2e = 1.4426950408889634f;
+    a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * c.scale;
+    return a;
+}
+
 int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, hipStream_t stream) {
     int st = validate(c);
     if (st != MFA_SUCCESS) return st;
@@ -160,36 +194,7 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
             return fail(MFA_ERROR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     }
 
-    mfa::FwdArgs a{};
-    a.q = c.q; a.k = c.k; a.v = c.v; a.out = c.out; a.lse = c.lse;
-    a.key_mask = c.key_mask;
-    a.B = c.B; a.Lq = c.Lq; a.Lk = c.Lk; a.Hq = c.Hq; a.Hkv = c.Hkv; a.D = c.D;
-    a.group = group;
-    a.causal = c.causal ? 1 : 0;
-    a.window = c.window > 0 ? c.window : 0;
-    a.q_offset = c.q_offset;
-    a.words_per_batch = words_per_batch(c.Lk);
-    a.q_stride = (int64_t)c.Hq * c.D;
-    a.kv_stride = (int64_t)c.Hkv * c.D;
-    a.o_stride = (int64_t)c.Hq * c.D;
-    a.seq_bounds = nullptr;
-    if (c.bias) {
-        a.bias = c.bias;
-        const int64_t n3 = c.bias_dims[3], n2 = c.bias_dims[2] * n3, n1 = c.bias_dims[1] * n2;
-        a.bias_stride[0] = c.bias_dims[0] > 1 ? n1 : 0;
-        a.bias_stride[1] = c.bias_dims[1] > 1 ? n2 : 0;
-        a.bias_stride[2] = c.bias_dims[2] > 1 ? n3 : 0;
-        a.bias_stride[3] = c.bias_dims[3] > 1 ? 1 : 0;
-    }
-    if (c.dropout_p > 0.0f) {
-        a.drop_threshold = (uint32_t)std::llround((double)c.dropout_p * 16777216.0);
-        a.drop_scale = 1.0f / (1.0f - c.dropout_p);
-        a.drop_seed = c.seed;
-    }
-    a.scale = c.scale;
-    a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
-    const float log2e = 1.4426950408889634f;
-    a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * c.scale;
+    mfa::FwdArgs a = make_args(c);
 
     const bool needs_ws = c.key_mask != nullptr || path == MFA_PATH_SPLIT_DECODE;
     void* ws = workspace;
@@ -516,6 +521,64 @@ int mfa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* out,
     c.dropout_p = dropout_p;
     c.seed = seed;
     return run(c, MFA_PATH_AUTO, 0, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+size_t mfa_bwd_workspace_size(int B, int Lq, int Hq) {
+    if (B <= 0 || Lq <= 0 || Hq <= 0) return 0;
+    return align256((size_t)B * Hq * Lq * sizeof(float));
+}
+
+int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+            void* dq, void* dk, void* dv, int B, int Lq, int Lk, int Hq, int Hkv, int D,
+            float scale, int causal, int window, int q_offset, float softcap,
+            const float* key_mask, const float* bias, int bias_B, int bias_H, int bias_Lq, int bias_Lk,
+            float dropout_p, unsigned long long seed, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    Call c{q, k, v, const_cast<void*>(out), const_cast<float*>(lse), B, Lq, Lk, Hq, Hkv, D, scale, causal, window,
+           q_offset, softcap, key_mask, dtype};
+    c.bias = bias;
+    c.bias_dims[0] = bias_B; c.bias_dims[1] = bias_H; c.bias_dims[2] = bias_Lq; c.bias_dims[3] = bias_Lk;
+    c.dropout_p = dropout_p;
+    c.seed = seed;
+    int st = validate(c);
+    if (st != MFA_SUCCESS) return st;
+    if (!dout || !lse || !dq || !dk || !dv)
+        return fail(MFA_ERROR_INVALID_VALUE, "dout, lse, dq, dk and dv must be non-null");
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return fail(MFA_ERROR_INVALID_VALUE, "dout, dq, dk and dv must be 16-byte aligned");
+    if (B == 0) return MFA_SUCCESS;   // (Lq = 0 still writes the zero dK and dV)
+    const size_t need = mfa_bwd_workspace_size(B, Lq, Hq);
+    const bool use_pool = workspace == nullptr && ws_bytes == 0;
+    if (!use_pool) {
+        if (!workspace) return fail(MFA_ERROR_INVALID_VALUE, "workspace is null but ws_bytes > 0");
+        if (!aligned(workspace, 256)) return fail(MFA_ERROR_INVALID_VALUE, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(MFA_ERROR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    }
+    const mfa::FwdArgs a = make_args(c);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    if (use_pool && need > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
+        prepare_pool(dev);
+        hipError_t e = hipMallocAsync(&ws, need, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
+                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
+        }
+    }
+    hipError_t e = mfa::launch_backward(a, dout, static_cast<float*>(ws), dq, dk, dv, dtype, s);
+    if (use_pool && need > 0) {
+        hipError_t e2 = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return MFA_SUCCESS;
 }
 
 size_t mfa_fwd_workspace_size(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype) {

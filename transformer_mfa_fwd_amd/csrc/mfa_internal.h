@@ -82,6 +82,34 @@ __device__ inline void row_key_range(const FwdArgs& a, int i, int& lo, int& hi) 
     }
 }
 
+// Word 0 of Philox4x64-10 (Salmon et al., SC 2011): ten rounds of two
+// 64x64 -> 128-bit products with the round constants, the halves mixed with
+// the other counter words and the key, the key bumped by the Weyl constants.
+__device__ inline uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                            uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += 0x9E3779B97F4A7C15ull;
+        k1 += 0xBB67AE8584CAA73Bull;
+    }
+    return c0;
+}
+
+// Dropout decision of weight (b, hq, i, j): the top 24 bits of word 0 of
+// Philox4x64-10 with counter (j, i, hq, b) and key (seed, 0) against the
+// threshold round(p * 2^24).
+__device__ inline bool dropout_keep(const FwdArgs& a, int b, int hq, int i, int j) {
+    const uint64_t w = philox4x64_word0((uint64_t)j, (uint64_t)i, (uint64_t)hq, (uint64_t)b, a.drop_seed, 0);
+    return (uint32_t)(w >> 40) >= a.drop_threshold;
+}
+
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s);
 // Per-row position and key bounds of a varlen packing: row i of sequence b
@@ -91,6 +119,11 @@ hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s);
 hipError_t launch_varlen_rows(const int* cu_q, const int* cu_k, int batch, int Tq, int Tk, int* row_pos,
                               int* seq_bounds, hipStream_t s);
 hipError_t launch_generic(const FwdArgs& a, int dtype, hipStream_t s);
+// Backward on the generic path: a.out is the forward output O, a.lse its LSE;
+// dout [B, Lq, Hq, D] the upstream gradient; delta [B, Hq, Lq] fp32 scratch.
+// dq, dk, dv are written in the input dtype (every element overwritten).
+hipError_t launch_backward(const FwdArgs& a, const void* dout, float* delta, void* dq, void* dk, void* dv,
+                           int dtype, hipStream_t s);
 hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s);
 bool mfma_prefill_supported(int dtype, int D);
 // Split decode: a.Lq query rows per batch (1 unless d_len is given).  With
