@@ -43,6 +43,9 @@ for dtype in ("f16", "bf16"):
                                      D, True))
 SMALL.append(wl.Workload("declen_softcap_bf16_D128_R4", "bf16", 8, 4, 400, 8, 2, 128, True, softcap=5.0,
                          std=2.0))
+# all 16 MFMA columns in use: R * Hq/Hkv = 16
+SMALL.append(wl.Workload("declen_R2_g8_bf16_D128", "bf16", 6, 2, 300, 16, 2, 128, True))
+SMALL.append(wl.Workload("declen_R16_g1_f16_D64", "f16", 6, 16, 300, 4, 4, 64, True))
 
 
 @pytest.mark.parametrize("splits", [0, 1, 7])

@@ -186,3 +186,14 @@ def test_packed_encoder_exact_counts():
     want = np.minimum(sbc[:, 1] - 1, r + half) - np.maximum(sbc[:, 0], r - half) + 1
     got = torch.exp(lse.double()).round().to(torch.int64).cpu().numpy()
     assert np.array_equal(got, np.broadcast_to(want, got.shape))
+
+
+def test_packed_single_row_sequences():
+    """Every sequence one row long: each row attends only to itself (O = V)."""
+    H, D, L = 2, 128, 300
+    qkv, sb = wl.make_packed_qkv([1] * L, H, D, "bf16", DEV, seed=12)
+    out, lse = mfa.packed_qkv_fwd(qkv, sb, H)
+    torch.cuda.synchronize()
+    x = qkv.view(L, 3, H * D)
+    assert torch.equal(out, x[:, 2])
+    check(qkv, sb, H, out, lse, "bf16", scale=1.0 / np.sqrt(D), window=0, softcap=0.0, what="single rows")

@@ -110,6 +110,10 @@ EDGE = [
     wl.Workload("big_bidir_window_bf16", "bf16", 1, 96, 96, 1, 1, 128, False, window=1000),
     wl.Workload("mqa_g16_f16", "f16", 1, 80, 80, 16, 1, 64, True),
     wl.Workload("mqa_g32_decode_bf16", "bf16", 2, 1, 300, 32, 1, 128, True),
+    wl.Workload("gqa16_ragged_f16_D64", "f16", 3, 333, 333, 16, 1, 64, True, window=100),
+    wl.Workload("lq_1_of_many_keys_bidir_bf16", "bf16", 2, 1, 1000, 4, 4, 128, False, window=300),
+    wl.Workload("long_window_cap_mask_bf16", "bf16", 1, 700, 900, 4, 2, 128, True, window=513, softcap=10.0,
+                mask="random_frac", mask_frac=0.4, std=2.0),
 ]
 
 

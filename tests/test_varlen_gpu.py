@@ -168,3 +168,18 @@ def test_varlen_no_out_of_bounds_writes_and_deterministic():
         assert torch.all(lbuf[:guard] == 7.0) and torch.all(lbuf[-guard:] == 7.0)
         res.append((out.clone(), lse.clone()))
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_varlen_many_tiny_sequences():
+    """Hundreds of 0-5 row sequences: every 128-row block straddles dozens of
+    them, and some have queries but no keys or keys but no queries."""
+    rng = np.random.default_rng(31)
+    lq = rng.integers(0, 6, 300).tolist()
+    lk = rng.integers(0, 6, 300).tolist()
+    for causal, window in ((True, 0), (False, 3)):
+        q, k, v = make(lq, lk, 4, 2, 64, "bf16", seed=32)
+        cq, ck = cu(lq), cu(lk)
+        out, lse = mfa.varlen_fwd(q, k, v, cq.to(DEV), ck.to(DEV), causal=causal, window=window)
+        torch.cuda.synchronize()
+        check(q, k, v, cq, ck, out, lse, "bf16", causal=causal, window=window, softcap=0.0,
+              what=f"tiny sequences causal={causal}")
