@@ -17,9 +17,9 @@ HBM GB/s of compulsory traffic, and so is the decode over a device-held length
 under "decode_len".  "packed_encoder" times the bidirectional encoder workload
 (B=8, L=8192, H=12, D=64, fp16, window 128, tail padding) twice: padded with a
 key mask through mfa_fwd, and packed without its padding through
-mfa_packed_qkv_fwd.  "bias_dropout" times the causal GQA prefill with a
-[1, 1, L, L] float32 additive mask and dropout 0.1 (mfa_fwd_bias_dropout, on
-the fp32-arithmetic generic kernel).  "backward" times mfa_bwd (dQ, dK, dV) on
+mfa_packed_qkv_fwd.  "bias_mfma" times the causal GQA prefill with a
+[1, 1, L, L] float32 additive mask (the MFMA kernel), "bias_dropout" the same
+with dropout 0.1 (the fp32-arithmetic generic kernel).  "backward" times mfa_bwd (dQ, dK, dV) on
 the causal GQA prefill shape.
 
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
@@ -258,6 +258,31 @@ def packed_encoder(steps: int, warmup: int, warmup_ms: float):
     return res
 
 
+def bias_mfma(steps: int, warmup: int, warmup_ms: float):
+    """The prefill shape with a [1, 1, L, L] additive mask and no dropout: the
+    MFMA kernel's BIAS instantiation."""
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    w = wl.GQA_CAUSAL_PREFILL_BF16
+    q, k, v, _ = wl.make_inputs(w, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    bias = torch.randn((1, 1, w.Lq, w.Lk), generator=g, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
+    wall, kern = time_calls(lambda: mfa.fwd(q, k, v, causal=True, bias=bias, out=out, lse=lse), steps, warmup,
+                            warmup_ms)
+    pairs = visible_pairs(w, None)
+    res = {"workload": w.name, "api": "mfa_fwd_bias_dropout", "bias_shape": [1, 1, w.Lq, w.Lk], "dropout_p": 0.0,
+           "path": "mfma", "unit": "TFLOP/s", "ms_per_step": round(wall, 5), "kernel_ms_avg": round(kern, 5),
+           "value": round(4.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
+    del q, k, v, bias, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def bias_dropout(steps: int, warmup: int, warmup_ms: float):
     import torch
     import transformer_mfa_fwd_amd as mfa
@@ -461,6 +486,7 @@ def main():
     if not args.no_bias_dropout:
         tensors = None
         torch.cuda.empty_cache()
+        line["bias_mfma"] = bias_mfma(max(10, args.steps // 2), max(3, args.warmup // 2), args.warmup_ms)
         line["bias_dropout"] = bias_dropout(5, 2, args.warmup_ms)
 
     if not args.no_backward:

@@ -87,3 +87,36 @@ def test_all_neg_inf_row_is_empty_and_seeds_differ():
     o3, _ = mfa.fwd(q, k, v, dropout_p=0.5, seed=2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and not torch.equal(o1, o3)
+
+
+# Additive masks the MFMA prefill kernel reads itself (no dropout, fp16/bf16,
+# key dimension full, Lk a multiple of four): several tiles, ragged tails.
+MFMA_BIAS = []
+for dtype in ("f16", "bf16"):
+    for D in (64, 128):
+        MFMA_BIAS.append(wl.Workload(f"bm_causal_gqa_{dtype}_D{D}", dtype, 2, 150, 196, 4, 2, D, True, window=90,
+                                     mask="random_frac", mask_frac=0.2))
+        # unit-variance inputs: with |V| up to ~8 (std 2) the 16-bit rounding of the
+        # weights that multiply V alone approaches the 1e-2 bound
+        MFMA_BIAS.append(wl.Workload(f"bm_bidir_cap_{dtype}_D{D}", dtype, 2, 130, 132, 2, 2, D, False, softcap=8.0))
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 0, 0, 1), (0, 1, 1, 1), (0, 0, 1, 1)],
+                         ids=lambda s: "".join(map(str, s)))
+@pytest.mark.parametrize("w", MFMA_BIAS, ids=lambda w: w.name)
+def test_bias_on_mfma_kernel_all_rows(w, shape):
+    run_and_check(w, shape, 0.0, 0)
+    if shape == (1, 1, 1, 1):
+        run_and_check(w, shape, 0.0, 0, neg_inf_frac=0.3)
+
+
+def test_bias_mfma_matches_generic_rounding_free_case():
+    """An all-zero mask on the MFMA kernel gives mfa_fwd's bits without a mask
+    (same kernel arithmetic on the scores, bias added as +0)."""
+    w = wl.Workload("bm_zero", "bf16", 2, 256, 256, 4, 2, 128, True)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    o1, l1 = mfa.fwd(q, k, v, causal=True)
+    o2, l2 = mfa.fwd(q, k, v, causal=True, bias=torch.zeros((1, 1, 256, 256), device=DEV))
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-4

@@ -122,8 +122,11 @@ __device__ inline uint64_t range_bits64(int lo, int hi) {
     return (~0ull << lo) & (~0ull >> (63 - hi));
 }
 
-template <typename T, int D, bool CAP, bool MASK, bool SEQ>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a, int nqt) {
+// BIAS adds an additive score mask read from global memory into registers one
+// tile ahead (32 more VGPRs: one workgroup per CU at D = 128, two at D = 64).
+template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS>
+__global__ __launch_bounds__(256, BIAS ? (D == 64 ? 2 : 1) : (D == 64 ? 3 : 2))
+void prefill_kernel(FwdArgs a, int nqt) {
     typedef PfLds<D> L;
     constexpr int CPR = L::CPR;
     constexpr int NKS = D / 16;             // k-steps of Q.K^T
@@ -131,7 +134,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
     constexpr int NDB = D / 32;             // 32-wide d blocks of O
     constexpr int RPI = 64 / CPR;           // tile rows per DMA instruction
     constexpr int IPW = BN / RPI / 4;       // DMA instructions per wave per tile
-    constexpr int NSA = CAP ? 13 : 9;       // softmax steps run beside Q.K^T
+    constexpr bool LOGIT = CAP || BIAS;     // scores turned into base-2 logits before the max
+    constexpr int NSA = LOGIT ? 13 : 9;     // softmax steps run beside Q.K^T
     constexpr int TRS = NQK - QK_LA;        // slot issuing the first V reads
     static_assert(TRS > 0 && TRS + QK_LA == NQK, "V reads follow the last K read");
     typedef typename Mfma<T>::v8 v8;
@@ -250,6 +254,29 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
     int kt_lo = 0, kt_hi = -1;
     if (lo_blk <= hi_blk) { kt_lo = lo_blk / BN; kt_hi = hi_blk / BN; }
 
+    // additive mask of this lane's row (rows past the end read the last row);
+    // bnx[g] holds the bias of scores 4 g .. 4 g + 3 of the next tile to finish
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    f32x4v bnx[8];
+    const float* brow = nullptr;
+    if constexpr (BIAS)
+        brow = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] +
+               (int64_t)(qrow <= i_last ? qrow : i_last) * a.bias_stride[2];
+    (void)bnx; (void)brow;
+// bias of tile TT: group g covers keys TT*BN + 32 (g/4) + 8 (g%4) + 4 h2 .. +3;
+// groups at or past key Lk (which the mask clears) read nothing
+#define MFA_BIAS_LOAD(TT)                                                                    \
+    do {                                                                                     \
+        if constexpr (BIAS) {                                                                \
+            const int _kb0 = (TT) * BN + 4 * h2;                                             \
+            _Pragma("unroll") for (int _g = 0; _g < 8; ++_g) {                               \
+                const int _key = _kb0 + 32 * (_g >> 2) + 8 * (_g & 3);                       \
+                bnx[_g] = _key < a.Lk ? *reinterpret_cast<const f32x4v*>(brow + _key)         \
+                                      : f32x4v{0.0f, 0.0f, 0.0f, 0.0f};                      \
+            }                                                                                \
+        }                                                                                    \
+    } while (0)
+
 // next tile at or after x that has a visible key
 #define MFA_NEXT_TILE(x) ({ int _t = (x); if (MASK) while (_t <= kt_hi && words[_t] == 0ull) ++_t; _t; })
 
@@ -302,11 +329,16 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
 // 24 exponentials run beside the P.V MFMAs, which leave the VALU idle.
 #define MFA_SA(U, SC)                                                                        \
     do {                                                                                     \
-        constexpr int _u = (U) - (CAP ? 4 : 0);                                              \
-        if constexpr (CAP && (U) < 4) {                                                      \
+        constexpr int _u = (U) - (LOGIT ? 4 : 0);                                            \
+        if constexpr (LOGIT && (U) < 4) {                                                    \
             _Pragma("unroll") for (int _e = 0; _e < 8; ++_e) {                               \
                 const float _s = MFA_X(SC, 8 * (U) + _e);                                    \
-                MFA_X(SC, 8 * (U) + _e) = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(_s * cap_arg) + 1.0f); \
+                float _x;                                                                    \
+                if constexpr (CAP) _x = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(_s * cap_arg) + 1.0f); \
+                else _x = _s * c_log2;                                                       \
+                /* score i = 8 U + e has its bias in group i / 4, component i % 4 */        \
+                if constexpr (BIAS) _x = fmaf(bnx[(8 * (U) + _e) >> 2][(8 * (U) + _e) & 3], LOG2E, _x); \
+                MFA_X(SC, 8 * (U) + _e) = _x;                                                \
             }                                                                                \
         } else if constexpr (_u == 0) {                                                      \
             if (!interior) {                                                                 \
@@ -335,7 +367,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
             _t = fmax_fast(_t, fmax_fast(fmax_fast(pm[6], pm[7]), pm[8]));                   \
             _t = fmax_fast(fmax_fast(_t, pm[9]), pm[10]);                                    \
             _t = xor32_max(_t);                                                              \
-            const float _tl2 = CAP ? _t : _t * c_log2;   /* base-2 logit units */           \
+            const float _tl2 = LOGIT ? _t : _t * c_log2;   /* base-2 logit units */         \
             /* Lazy rescale: the running max only moves when a tile's max     */            \
             /* exceeds it by more than 8 (base 2), so every weight 2^(x - m)  */            \
             /* stays <= 256 and the accumulator is rescaled rarely.  Exact    */            \
@@ -352,7 +384,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
         } else {                                                                             \
             _Pragma("unroll") for (int _d = 0; _d < 2; ++_d) {                               \
                 const int _e = 2 * (_u - 5) + _d;                                            \
-                MFA_X(SC, _e) = CAP ? fast_exp2(MFA_X(SC, _e) + neg_m)                       \
+                MFA_X(SC, _e) = LOGIT ? fast_exp2(MFA_X(SC, _e) + neg_m)                     \
                                     : fast_exp2(fmaf(MFA_X(SC, _e), c_log2, neg_m));         \
             }                                                                                \
             psum0 += MFA_X(SC, 2 * (_u - 5));                                                \
@@ -369,7 +401,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
         if constexpr ((S4) < 3) {                                                            \
             _Pragma("unroll") for (int _d = 0; _d < 2; ++_d) {                               \
                 const int _e = 8 + 8 * (S4) + 2 * (U) + _d;                                  \
-                MFA_X(SC, _e) = CAP ? fast_exp2(MFA_X(SC, _e) + neg_m)                       \
+                MFA_X(SC, _e) = LOGIT ? fast_exp2(MFA_X(SC, _e) + neg_m)                     \
                                     : fast_exp2(fmaf(MFA_X(SC, _e), c_log2, neg_m));         \
             }                                                                                \
             psum0 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U));                                      \
@@ -474,6 +506,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
         v8 pop[4];                                                                           \
         /* stage ST ^ 1 holds K(tnxt); on the last tile its scores are discarded */         \
         MFA_PART1(SC, SN, (ST) ^ 1, true);                                                   \
+        if (has_nxt) MFA_BIAS_LOAD(tnxt);   /* this tile's bias is consumed: fetch the next */ \
         MFA_PV_STEP(0, SC) MFA_PV_STEP(1, SC) MFA_PV_STEP(2, SC) MFA_PV_STEP(3, SC)          \
         __syncthreads();  /* copies of this iteration landed; stages handed over */         \
     } while (0)
@@ -485,6 +518,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
         // prologue: K,V of the first tile into stage 0, K of the second into stage 1
         MFA_DMA(tcur, 0, true, true);
         if (tnxt <= kt_hi) MFA_DMA(tnxt, 1, true, false);
+        MFA_BIAS_LOAD(tcur);
         __syncthreads();
         f32x16_t sa[2], sb[2];
         {
@@ -513,6 +547,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
         }
     }
 #undef MFA_NEXT_TILE
+#undef MFA_BIAS_LOAD
 #undef MFA_DMA
 #undef MFA_DMA1
 #undef MFA_DMA_IF
@@ -562,11 +597,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_kernel(FwdArgs a
         a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qrow] = l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
 }
 
-template <typename T, int D, bool CAP, bool MASK, bool SEQ>
+template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS = false>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int nqt = (a.Lq + BM - 1) / BM;
     const int64_t blocks = (int64_t)a.B * a.Hq * nqt;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK, SEQ>), dim3((unsigned)blocks), dim3(256), 0, s, a, nqt);
+    hipLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK, SEQ, BIAS>), dim3((unsigned)blocks), dim3(256), 0, s, a,
+                       nqt);
     return hipGetLastError();
 }
 
@@ -575,6 +611,11 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     const bool cap = a.softcap > 0.0f, mask = a.key_mask != nullptr;
+    if (a.bias) {
+        if (a.seq_bounds || a.row_pos || !mfma_bias_supported(a)) return hipErrorInvalidValue;
+        if (cap) return mask ? launch_t<T, D, true, true, false, true>(a, s) : launch_t<T, D, true, false, false, true>(a, s);
+        return mask ? launch_t<T, D, false, true, false, true>(a, s) : launch_t<T, D, false, false, false, true>(a, s);
+    }
     if (a.seq_bounds || a.row_pos) {
         if (mask) return hipErrorInvalidValue;
         return cap ? launch_t<T, D, true, false, true>(a, s) : launch_t<T, D, false, false, true>(a, s);
@@ -584,6 +625,12 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool mfma_bias_supported(const FwdArgs& a) {
+    // 16-byte loads of four keys: keys contiguous, every row start 16-byte aligned
+    return a.bias && a.bias_stride[3] == 1 && a.Lk % 4 == 0 && (reinterpret_cast<uintptr_t>(a.bias) & 15) == 0 &&
+           a.bias_stride[0] % 4 == 0 && a.bias_stride[1] % 4 == 0 && a.bias_stride[2] % 4 == 0;
+}
 
 bool mfma_prefill_supported(int dtype, int D) {
     return (dtype == kBF16 || dtype == kF16) && (D == 64 || D == 128);

@@ -164,11 +164,19 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
     if (c.B == 0 || c.Lq == 0) return MFA_SUCCESS;
 
     const int group = c.Hq / c.Hkv;
-    const bool extras = c.bias != nullptr || c.dropout_p > 0.0f;   // only the generic kernel has them
+    // dropout runs on the generic kernel only; an additive mask also on the
+    // MFMA prefill kernel when its rows can be read four keys at a time
+    bool bias_mfma = false;
+    if (c.bias && c.dropout_p == 0.0f && mfa::mfma_prefill_supported(c.dtype, c.D)) {
+        const mfa::FwdArgs t = make_args(c);
+        bias_mfma = mfa::mfma_bias_supported(t);
+    }
+    const bool extras = c.bias != nullptr || c.dropout_p > 0.0f;
     if (path == MFA_PATH_AUTO)
-        path = extras ? MFA_PATH_GENERIC : auto_path(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D, c.dtype);
-    if (extras && path != MFA_PATH_GENERIC)
-        return fail(MFA_ERROR_NOT_SUPPORTED, "an additive mask or dropout needs the generic path");
+        path = extras ? (bias_mfma ? MFA_PATH_MFMA : MFA_PATH_GENERIC)
+                      : auto_path(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D, c.dtype);
+    if (extras && path != MFA_PATH_GENERIC && !(bias_mfma && path == MFA_PATH_MFMA))
+        return fail(MFA_ERROR_NOT_SUPPORTED, "dropout, or this additive mask, needs the generic path");
     switch (path) {
         case MFA_PATH_GENERIC: break;
         case MFA_PATH_MFMA:

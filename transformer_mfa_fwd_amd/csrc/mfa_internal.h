@@ -126,6 +126,9 @@ hipError_t launch_backward(const FwdArgs& a, const void* dout, float* delta, voi
                            int dtype, hipStream_t s);
 hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s);
 bool mfma_prefill_supported(int dtype, int D);
+// Whether the MFMA prefill kernel can read a's additive mask (keys contiguous,
+// Lk and every row start a multiple of four floats).
+bool mfma_bias_supported(const FwdArgs& a);
 // Split decode: a.Lq query rows per batch (1 unless d_len is given).  With
 // d_len (device [B]) the key range of batch b is its first d_len[b] keys.
 hipError_t launch_split_decode(const FwdArgs& a, const int* d_len, int dtype, int splits,
