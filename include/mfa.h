@@ -112,8 +112,9 @@ int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *               reproducible from the seed alone.
  *
  * A row whose every visible key has a bias of -inf gets O = 0, LSE = -inf.
- * These features run on the fp32-arithmetic kernel (MFA_PATH_GENERIC) for
- * every dtype.  Other arguments, errors and streams as for mfa_fwd; a bias
+ * Without dropout, an fp16/bf16 call whose bias has bias_Lk = Lk, with Lk a
+ * multiple of 4 and bias 16-byte aligned, runs on the MFMA prefill kernel;
+ * every other call runs on the fp32-arithmetic kernel (MFA_PATH_GENERIC).  Other arguments, errors and streams as for mfa_fwd; a bias
  * dimension other than 1 or full size, or p outside [0, 1), is
  * MFA_ERROR_INVALID_VALUE.
  */
