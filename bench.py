@@ -319,7 +319,7 @@ def backward(steps: int, warmup: int, warmup_ms: float):
     wall, kern = time_calls(lambda: mfa.bwd(q, k, v, out, dout, lse, causal=True, dq=dq, dk=dk, dv=dv),
                             steps, warmup, warmup_ms)
     pairs = visible_pairs(w, None)
-    res = {"workload": w.name, "api": "mfa_bwd", "path": "generic", "unit": "TFLOP/s",
+    res = {"workload": w.name, "api": "mfa_bwd", "path": "mfma", "unit": "TFLOP/s",
            "flops_per_pair": 10 * w.D, "ms_per_step": round(wall, 5), "kernel_ms_avg": round(kern, 5),
            "value": round(10.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
     del q, k, v, out, lse, dout, dq, dk, dv

@@ -99,3 +99,21 @@ def test_backward_deterministic_and_zero_for_unseen_keys():
         assert torch.equal(a, b)
     # rows sit at keys 136..199 and each sees 16 keys: keys < 121 are unseen
     assert torch.all(r1[1][:, :121] == 0) and torch.all(r1[2][:, :121] == 0)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+def test_matrix_core_backward_agrees_with_fp32_kernels(dtype, D):
+    """fp16/bf16 without a mask or dropout take the matrix-core backward; an
+    all-zero additive mask sends the same call to the fp32 kernels."""
+    w = wl.Workload(f"bwd_paths_{dtype}", dtype, 2, 300, 300, 8, 2, D, True, window=200)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    dout = torch.randn_like(q)
+    out, lse = mfa.fwd(q, k, v, causal=True, window=200)
+    a = mfa.bwd(q, k, v, out, dout, lse, causal=True, window=200)
+    zero = torch.zeros((1, 1, 1, w.Lk), device=DEV)
+    g = mfa.bwd(q, k, v, out, dout, lse, causal=True, window=200, bias=zero)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), a, g):
+        scale = max(1.0, float(y.float().abs().max()))
+        err = float((x.float() - y.float()).abs().max())
+        assert err <= 1e-2 * scale, (name, err, scale)

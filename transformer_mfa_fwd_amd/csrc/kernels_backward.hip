@@ -295,6 +295,16 @@ hipError_t launch_bwd_t(const FwdArgs& a, const void* dout, float* delta, void* 
 }
 
 template <typename T>
+hipError_t launch_delta_t(const FwdArgs& a, const void* dout, float* delta, hipStream_t s) {
+    const T* g = static_cast<const T*>(dout);
+    if (a.D == 64)
+        hipLaunchKernelGGL((bwd_delta_kernel<T, 64>), dim3((a.Lq + 3) / 4, a.Hq, a.B), dim3(256), 0, s, a, g, delta);
+    else
+        hipLaunchKernelGGL((bwd_delta_kernel<T, 128>), dim3((a.Lq + 3) / 4, a.Hq, a.B), dim3(256), 0, s, a, g, delta);
+    return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_bwd_d(const FwdArgs& a, const void* dout, float* delta, void* dq, void* dk, void* dv,
                         hipStream_t s) {
     return a.D == 64 ? launch_bwd_t<T, 64>(a, dout, delta, dq, dk, dv, s)
@@ -305,6 +315,14 @@ hipError_t launch_bwd_d(const FwdArgs& a, const void* dout, float* delta, void* 
 
 hipError_t launch_backward(const FwdArgs& a, const void* dout, float* delta, void* dq, void* dk, void* dv,
                            int dtype, hipStream_t s) {
+    if (bwd_mfma_supported(a, dtype)) {   // Delta here, the rest on the matrix cores
+        hipError_t e = hipSuccess;
+        if (a.Lq > 0) {
+            e = dtype == kBF16 ? launch_delta_t<__bf16>(a, dout, delta, s) : launch_delta_t<_Float16>(a, dout, delta, s);
+            if (e != hipSuccess) return e;
+        }
+        return launch_backward_mfma(a, dout, delta, dq, dk, dv, dtype, s);
+    }
     switch (dtype) {
         case kF32: return launch_bwd_d<float>(a, dout, delta, dq, dk, dv, s);
         case kF16: return launch_bwd_d<_Float16>(a, dout, delta, dq, dk, dv, s);

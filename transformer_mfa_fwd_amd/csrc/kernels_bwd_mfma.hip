@@ -1,0 +1,355 @@
+// kernels_bwd_mfma.hip -- the backward on the matrix cores for fp16/bf16
+// inputs (no additive mask, no dropout; those calls take the fp32 kernels).
+//
+// Same formulas as kernels_backward.hip (vision_rs flash_attn2.rs, backward
+// kernels): P = exp(s - LSE) from the saved LSE, Delta = <dO, O>,
+// dS = P (dO V^T - Delta) * d s / d<Q, K>, dQ = dS K, dK = dS^T Q, dV = P^T dO.
+// Every product is a 32x32x16 MFMA with fp32 accumulation; P and dS are
+// rounded to the input type to serve as operands, as the forward rounds P.
+//
+//   bwd_dq_mfma_kernel    one wave per 32 query rows, walking 32-key tiles:
+//       S^T  = K Q^T    (K rows from LDS, Q^T in registers)
+//       dP^T = V dO^T   (V rows from LDS, dO^T in registers)
+//       dQ^T += K^T dS^T (K^T by transposing LDS reads, dS^T straight from the
+//                         accumulator of S^T)
+//   bwd_dkdv_mfma_kernel  one wave per 32 keys, walking the 32-row query tiles
+//                         of every query head of its GQA group:
+//       S  = Q K^T      (Q rows from LDS, K^T in registers)
+//       dP = dO V^T
+//       dV^T += dO^T P,  dK^T += Q^T dS   (transposing LDS reads of dO and Q)
+// An accumulator's 16 elements per lane serve as the B operand of the next
+// product in the order the transposing reads deliver the A operand's rows, so
+// no score crosses lanes.  Each gradient element has one writer (no atomics).
+#include "mfa_device.h"
+#include "mfa_internal.h"
+
+#include <math.h>
+
+namespace mfa {
+namespace {
+
+constexpr float BW_LOG2E = 1.4426950408889634f;
+
+template <int D>
+struct BwLds {
+    static constexpr int RS = D * 2 + 16;    // bytes per 32-element-wide tile row, padded
+    static constexpr int TILE = 32 * RS;     // one 32-row tile
+};
+
+// A operand from a row-major 16-bit LDS tile: lane l takes row l % 32 and the
+// eight elements from column c0 + 8 (l / 32).
+template <typename T, int D>
+__device__ inline typename Mfma<T>::v8 rows_a(const char* tile, int lane, int c0) {
+    const char* p = tile + (lane & 31) * BwLds<D>::RS + (c0 + 8 * (lane >> 5)) * 2;
+    return bitcast<typename Mfma<T>::v8>(*reinterpret_cast<const u32x4_t*>(p));
+}
+
+// A operand = M^T for a row-major 16-bit LDS tile M[k][m]: k-step s (16 of the
+// tile's 32 rows), m-block mb (32 columns).  Lane l takes column 32 mb + l % 32
+// at rows 16 s + 8 (e / 4) + 4 (l / 32) + e % 4, e = 0..7: the rows that
+// accumulator elements 8 s .. 8 s + 7 of lane l hold, so pack8_at(acc, 8 s) is
+// the matching B operand.  Two transposing reads per operand (4 rows each).
+template <typename T, int D>
+__device__ inline typename Mfma<T>::v8 cols_a(const char* tile, int lane, int s, int mb) {
+    const int g = lane >> 4, j = lane & 15;
+    const int row = 16 * s + 4 * (g >> 1) + (j >> 2);
+    const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
+    const char* p = tile + row * BwLds<D>::RS + col * 2;
+    const i16x4_t lo = lds_read_tr16(p);
+    const i16x4_t hi = lds_read_tr16(p + 8 * BwLds<D>::RS);
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return bitcast<typename Mfma<T>::v8>(v);
+}
+
+// 32 rows x D of a [rows, stride] 16-bit tensor into a padded LDS tile by all
+// 256 threads; rows at or past `rows_valid` become zero.
+template <typename T, int D>
+__device__ inline void load_tile(char* tile, const T* src, int64_t stride, int rows_valid, int tid) {
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    for (int c = tid; c < 32 * CPR; c += 256) {
+        const int r = c / CPR, k = c % CPR;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (r < rows_valid) v = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * stride + k * 8);
+        *reinterpret_cast<u32x4_t*>(tile + r * BwLds<D>::RS + k * 16) = v;
+    }
+}
+
+// logit and d logit / d dot of a raw dot product (scale, optional soft-cap),
+// the logit in base-2 units
+template <bool CAP>
+__device__ inline float logit2(const FwdArgs& a, float dot, float& dl) {
+    const float t = dot * a.scale;
+    if constexpr (CAP) {
+        const float th = tanhf(t / a.softcap);
+        dl = a.scale * (1.0f - th * th);
+        return a.softcap * th * BW_LOG2E;
+    } else {
+        dl = a.scale;
+        return t * BW_LOG2E;
+    }
+}
+
+template <typename T, int D, bool CAP>
+__global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+                                                             const float* __restrict__ delta, T* __restrict__ dq) {
+    typedef typename Mfma<T>::v8 v8;
+    constexpr int NKS = D / 16, NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) char sK[BwLds<D>::TILE];
+    __shared__ __attribute__((aligned(16))) char sV[BwLds<D>::TILE];
+    __shared__ float sM[32];   // 1: key kept (in range of the axis and of the key mask)
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int hq = blockIdx.y, b = blockIdx.z, kvh = hq / a.group;
+    const int i0 = blockIdx.x * 128, i_last = min(i0 + 127, a.Lq - 1);
+    const int row = i0 + 32 * wave + (lane & 31);
+    const int rowc = row <= i_last ? row : i_last;
+    const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
+    const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
+    const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+    const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+
+    v8 qop[NKS], gop[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        qop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(qb + (int64_t)rowc * a.q_stride + 16 * ks + 8 * h));
+        gop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(gb + (int64_t)rowc * a.o_stride + 16 * ks + 8 * h));
+    }
+    int rlo = 1, rhi = 0;
+    float lse2 = 0.0f, dlt = 0.0f;
+    if (row <= i_last) {
+        row_key_range<false>(a, row, rlo, rhi);
+        const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + row];
+        if (l == -INFINITY) { rlo = 1; rhi = 0; }   // no weight anywhere in the row
+        lse2 = l * BW_LOG2E;
+        dlt = delta[((int64_t)b * a.Hq + hq) * a.Lq + row];
+    }
+    int lo_blk, t0, t1, hi_blk;
+    row_key_range<false>(a, i0, lo_blk, t0);
+    row_key_range<false>(a, i_last, t1, hi_blk);
+
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
+
+    if (lo_blk <= hi_blk) {
+        for (int t = lo_blk / 32; t <= hi_blk / 32; ++t) {
+            const int k0 = 32 * t;
+            __syncthreads();
+            load_tile<T, D>(sK, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            load_tile<T, D>(sV, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            if (tid < 32) {
+                const int key = k0 + tid;
+                sM[tid] = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
+            }
+            __syncthreads();
+            f32x16_t s = {}, dp = {};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                s = Mfma<T>::mma32(rows_a<T, D>(sK, lane, 16 * ks), qop[ks], s);
+                dp = Mfma<T>::mma32(rows_a<T, D>(sV, lane, 16 * ks), gop[ks], dp);
+            }
+            // element r of lane l: key k0 + 8 (r / 4) + 4 h + r % 4 of this lane's row
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r >> 2) + 4 * h + (r & 3), key = k0 + kk;
+                float ds = 0.0f;
+                if (key >= rlo && key <= rhi && sM[kk] != 0.0f) {
+                    float dl;
+                    const float x = logit2<CAP>(a, s[r], dl);
+                    const float p = fast_exp2(x - lse2);
+                    ds = p * (dp[r] - dlt) * dl;
+                }
+                s[r] = ds;
+            }
+#pragma unroll
+            for (int sx = 0; sx < 2; ++sx) {
+                const v8 bop = pack8_at<T>(s, 8 * sx);
+#pragma unroll
+                for (int mb = 0; mb < NDB; ++mb) acc[mb] = Mfma<T>::mma32(cols_a<T, D>(sK, lane, sx, mb), bop, acc[mb]);
+            }
+        }
+    }
+    // acc[mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's row
+    if (row <= i_last) {
+        T* out = dq + ((int64_t)b * a.Lq + row) * a.q_stride + (int64_t)hq * D;
+#pragma unroll
+        for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                T v4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v4[i] = static_cast<T>(acc[mb][4 * j + i]);
+                *reinterpret_cast<uint2*>(out + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(v4);
+            }
+    }
+}
+
+// 32 gradient accumulator registers per d block (dK and dV) plus K and V in
+// registers: one workgroup per CU at D = 128.
+template <typename T, int D, bool CAP>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+                                                               const float* __restrict__ delta, T* __restrict__ dk,
+                                                               T* __restrict__ dv) {
+    typedef typename Mfma<T>::v8 v8;
+    constexpr int NKS = D / 16, NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) char sQ[BwLds<D>::TILE];
+    __shared__ __attribute__((aligned(16))) char sG[BwLds<D>::TILE];   // dO rows
+    __shared__ __attribute__((aligned(16))) float sL[32];   // LSE (base 2) of the tile's rows
+    __shared__ __attribute__((aligned(16))) float sD[32];   // Delta
+    __shared__ __attribute__((aligned(16))) int sLo[32];    // key range of each row
+    __shared__ __attribute__((aligned(16))) int sHi[32];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int j0 = blockIdx.x * 128, j_last = min(j0 + 127, a.Lk - 1);
+    const int key = j0 + 32 * wave + (lane & 31);
+    const int keyc = key <= j_last ? key : j_last;
+    const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+    const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+
+    v8 kop[NKS], vop[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        kop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(kb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h));
+        vop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(vb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h));
+    }
+    const bool kept = key <= j_last && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f);
+
+    f32x16_t dka[NDB], dva[NDB];
+#pragma unroll
+    for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dka[mb][e] = dva[mb][e] = 0.0f;
+
+    const int nqt = (a.Lq + 31) / 32;
+    for (int hq = kvh * a.group; hq < (kvh + 1) * a.group; ++hq) {
+        const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
+        const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
+        for (int qt = 0; qt < nqt; ++qt) {
+            const int r0 = 32 * qt, r_last = min(r0 + 31, a.Lq - 1);
+            int lo_f, hi_f, lo_l, hi_l;
+            row_key_range<false>(a, r0, lo_f, hi_f);
+            row_key_range<false>(a, r_last, lo_l, hi_l);
+            if (lo_f > j_last || hi_l < j0 || lo_f > hi_l) continue;   // no row of the tile sees these keys
+            __syncthreads();
+            load_tile<T, D>(sQ, qb + (int64_t)r0 * a.q_stride, a.q_stride, a.Lq - r0, tid);
+            load_tile<T, D>(sG, gb + (int64_t)r0 * a.o_stride, a.o_stride, a.Lq - r0, tid);
+            if (tid < 32) {
+                const int r = r0 + tid;
+                int lo = 1, hi = 0;
+                float l2 = 0.0f, dl = 0.0f;
+                if (r < a.Lq) {
+                    row_key_range<false>(a, r, lo, hi);
+                    const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + r];
+                    if (l == -INFINITY) { lo = 1; hi = 0; }
+                    l2 = l * BW_LOG2E;
+                    dl = delta[((int64_t)b * a.Hq + hq) * a.Lq + r];
+                }
+                sLo[tid] = lo; sHi[tid] = hi; sL[tid] = l2; sD[tid] = dl;
+            }
+            __syncthreads();
+            f32x16_t s = {}, dp = {};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                s = Mfma<T>::mma32(rows_a<T, D>(sQ, lane, 16 * ks), kop[ks], s);
+                dp = Mfma<T>::mma32(rows_a<T, D>(sG, lane, 16 * ks), vop[ks], dp);
+            }
+            // element r of lane l: tile row 8 (r / 4) + 4 h + r % 4 for this lane's key
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m0 = 8 * j + 4 * h;
+                const int4 lo4 = *reinterpret_cast<const int4*>(&sLo[m0]);
+                const int4 hi4 = *reinterpret_cast<const int4*>(&sHi[m0]);
+                const float4 l4 = *reinterpret_cast<const float4*>(&sL[m0]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&sD[m0]);
+                const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+                const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * j + i;
+                    float p = 0.0f, dsv = 0.0f;
+                    if (kept && key >= los[i] && key <= his[i]) {
+                        float dl;
+                        const float x = logit2<CAP>(a, s[r], dl);
+                        p = fast_exp2(x - ls[i]);
+                        dsv = p * (dp[r] - ds4[i]) * dl;
+                    }
+                    s[r] = p;
+                    dp[r] = dsv;
+                }
+            }
+#pragma unroll
+            for (int sx = 0; sx < 2; ++sx) {
+                const v8 pop = pack8_at<T>(s, 8 * sx);
+                const v8 dop = pack8_at<T>(dp, 8 * sx);
+#pragma unroll
+                for (int mb = 0; mb < NDB; ++mb) {
+                    dva[mb] = Mfma<T>::mma32(cols_a<T, D>(sG, lane, sx, mb), pop, dva[mb]);
+                    dka[mb] = Mfma<T>::mma32(cols_a<T, D>(sQ, lane, sx, mb), dop, dka[mb]);
+                }
+            }
+        }
+    }
+    // dka / dva [mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's key
+    if (key <= j_last) {
+        T* ko = dk + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
+        T* vo = dv + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
+#pragma unroll
+        for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                T k4[4], v4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    k4[i] = static_cast<T>(dka[mb][4 * j + i]);
+                    v4[i] = static_cast<T>(dva[mb][4 * j + i]);
+                }
+                *reinterpret_cast<uint2*>(ko + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(k4);
+                *reinterpret_cast<uint2*>(vo + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(v4);
+            }
+    }
+}
+
+template <typename T, int D, bool CAP>
+hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
+                             hipStream_t s) {
+    const T* g = static_cast<const T*>(dout);
+    if (a.Lq > 0) {
+        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3((a.Lq + 127) / 128, a.Hq, a.B), dim3(256), 0, s, a,
+                           g, delta, static_cast<T*>(dq));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP>), dim3((a.Lk + 127) / 128, a.Hkv, a.B), dim3(256), 0, s,
+                       a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_mfma_d(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
+                             hipStream_t s) {
+    const bool cap = a.softcap > 0.0f;
+    if (a.D == 64)
+        return cap ? launch_bwd_mfma_t<T, 64, true>(a, dout, delta, dq, dk, dv, s)
+                   : launch_bwd_mfma_t<T, 64, false>(a, dout, delta, dq, dk, dv, s);
+    return cap ? launch_bwd_mfma_t<T, 128, true>(a, dout, delta, dq, dk, dv, s)
+               : launch_bwd_mfma_t<T, 128, false>(a, dout, delta, dq, dk, dv, s);
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(const FwdArgs& a, int dtype) {
+    return (dtype == kBF16 || dtype == kF16) && (a.D == 64 || a.D == 128) && !a.bias && a.drop_scale == 0.0f &&
+           !a.seq_bounds && !a.row_pos;
+}
+
+hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
+                                int dtype, hipStream_t s) {
+    if (dtype == kBF16) return launch_bwd_mfma_d<__bf16>(a, dout, delta, dq, dk, dv, s);
+    if (dtype == kF16) return launch_bwd_mfma_d<_Float16>(a, dout, delta, dq, dk, dv, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mfa
