@@ -61,16 +61,33 @@ __device__ inline typename Mfma<T>::v8 cols_a(const char* tile, int lane, int s,
     return bitcast<typename Mfma<T>::v8>(v);
 }
 
-// 32 rows x D of a [rows, stride] 16-bit tensor into a padded LDS tile by all
-// 256 threads; rows at or past `rows_valid` become zero.
+// A 32-row x D tile of a [rows, stride] 16-bit tensor moves in two halves:
+// fetch_tile reads it into registers (thread tid holds 16-byte chunks tid and
+// tid + 256; rows at or past `rows_valid` are zero) so that the next tile's
+// global reads overlap the current tile's products, and store_tile writes the
+// registers into the padded LDS tile.
+template <int D>
+struct TileRegs {
+    static constexpr int N = 32 * (D / 8) / 256;   // chunks per thread: 1 (D = 64) or 2 (D = 128)
+    u32x4_t v[N];
+};
 template <typename T, int D>
-__device__ inline void load_tile(char* tile, const T* src, int64_t stride, int rows_valid, int tid) {
-    constexpr int CPR = D / 8;   // 16-byte chunks per row
-    for (int c = tid; c < 32 * CPR; c += 256) {
-        const int r = c / CPR, k = c % CPR;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (r < rows_valid) v = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * stride + k * 8);
-        *reinterpret_cast<u32x4_t*>(tile + r * BwLds<D>::RS + k * 16) = v;
+__device__ inline void fetch_tile(TileRegs<D>& t, const T* src, int64_t stride, int rows_valid, int tid) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int n = 0; n < TileRegs<D>::N; ++n) {
+        const int c = tid + 256 * n, r = c / CPR, k = c % CPR;
+        t.v[n] = u32x4_t{0u, 0u, 0u, 0u};
+        if (r < rows_valid) t.v[n] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * stride + k * 8);
+    }
+}
+template <int D>
+__device__ inline void store_tile(char* tile, const TileRegs<D>& t, int tid) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int n = 0; n < TileRegs<D>::N; ++n) {
+        const int c = tid + 256 * n, r = c / CPR, k = c % CPR;
+        *reinterpret_cast<u32x4_t*>(tile + r * BwLds<D>::RS + k * 16) = t.v[n];
     }
 }
 
@@ -99,8 +116,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
     __shared__ float sM[32];   // 1: key kept (in range of the axis and of the key mask)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-    const int hq = blockIdx.y, b = blockIdx.z, kvh = hq / a.group;
-    const int i0 = blockIdx.x * 128, i_last = min(i0 + 127, a.Lq - 1);
+    // grid (Hq, B, query blocks), the latest query block first: under a causal
+    // mask it walks the most key tiles
+    const int hq = blockIdx.x, b = blockIdx.y, kvh = hq / a.group;
+    const int i0 = (gridDim.z - 1 - blockIdx.z) * 128, i_last = min(i0 + 127, a.Lq - 1);
     const int row = i0 + 32 * wave + (lane & 31);
     const int rowc = row <= i_last ? row : i_last;
     const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
@@ -134,16 +153,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
         for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
 
     if (lo_blk <= hi_blk) {
-        for (int t = lo_blk / 32; t <= hi_blk / 32; ++t) {
+        const int t_first = lo_blk / 32, t_end = hi_blk / 32 + 1;
+        TileRegs<D> rk, rv;
+        float rm = 0.0f;
+        // tile t's K, V and key-kept flags into registers
+        auto fetch = [&](int t) {
             const int k0 = 32 * t;
-            __syncthreads();
-            load_tile<T, D>(sK, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
-            load_tile<T, D>(sV, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            fetch_tile<T, D>(rv, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
             if (tid < 32) {
                 const int key = k0 + tid;
-                sM[tid] = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
+                rm = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
             }
+        };
+        fetch(t_first);
+        for (int t = t_first; t < t_end; ++t) {
+            const int k0 = 32 * t;
+            __syncthreads();   // the previous tile is no longer read
+            store_tile<D>(sK, rk, tid);
+            store_tile<D>(sV, rv, tid);
+            if (tid < 32) sM[tid] = rm;
             __syncthreads();
+            if (t + 1 < t_end) fetch(t + 1);   // in flight during this tile's products
             f32x16_t s = {}, dp = {};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -202,8 +233,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
     __shared__ __attribute__((aligned(16))) int sHi[32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-    const int kvh = blockIdx.y, b = blockIdx.z;
-    const int j0 = blockIdx.x * 128, j_last = min(j0 + 127, a.Lk - 1);
+    // grid (Hkv, B, key blocks), the first key block first: under a causal mask
+    // the most query rows see it
+    const int kvh = blockIdx.x, b = blockIdx.y;
+    const int j0 = blockIdx.z * 128, j_last = min(j0 + 127, a.Lk - 1);
     const int key = j0 + 32 * wave + (lane & 31);
     const int keyc = key <= j_last ? key : j_last;
     const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
@@ -223,72 +256,88 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
 #pragma unroll
         for (int e = 0; e < 16; ++e) dka[mb][e] = dva[mb][e] = 0.0f;
 
-    const int nqt = (a.Lq + 31) / 32;
-    for (int hq = kvh * a.group; hq < (kvh + 1) * a.group; ++hq) {
+    // the (query head, 32-row tile) steps of this key block, in order, skipping
+    // tiles none of whose rows sees a key of the block
+    const int nqt = (a.Lq + 31) / 32, nsteps = a.group * nqt;
+    auto sees = [&](int it) {
+        const int r0 = 32 * (it % nqt), r_last = min(r0 + 31, a.Lq - 1);
+        int lo_f, hi_f, lo_l, hi_l;
+        row_key_range<false>(a, r0, lo_f, hi_f);
+        row_key_range<false>(a, r_last, lo_l, hi_l);
+        return !(lo_f > j_last || hi_l < j0 || lo_f > hi_l);
+    };
+    auto next_step = [&](int it) { while (it < nsteps && !sees(it)) ++it; return it; };
+    TileRegs<D> rq, rg;
+    int rlo_ = 1, rhi_ = 0;
+    float rl_ = 0.0f, rd_ = 0.0f;
+    // step it's Q and dO rows, and the LSE, Delta and key range of its rows, into registers
+    auto fetch = [&](int it) {
+        const int hq = kvh * a.group + it / nqt, r0 = 32 * (it % nqt);
         const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
         const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
-        for (int qt = 0; qt < nqt; ++qt) {
-            const int r0 = 32 * qt, r_last = min(r0 + 31, a.Lq - 1);
-            int lo_f, hi_f, lo_l, hi_l;
-            row_key_range<false>(a, r0, lo_f, hi_f);
-            row_key_range<false>(a, r_last, lo_l, hi_l);
-            if (lo_f > j_last || hi_l < j0 || lo_f > hi_l) continue;   // no row of the tile sees these keys
-            __syncthreads();
-            load_tile<T, D>(sQ, qb + (int64_t)r0 * a.q_stride, a.q_stride, a.Lq - r0, tid);
-            load_tile<T, D>(sG, gb + (int64_t)r0 * a.o_stride, a.o_stride, a.Lq - r0, tid);
-            if (tid < 32) {
-                const int r = r0 + tid;
-                int lo = 1, hi = 0;
-                float l2 = 0.0f, dl = 0.0f;
-                if (r < a.Lq) {
-                    row_key_range<false>(a, r, lo, hi);
-                    const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + r];
-                    if (l == -INFINITY) { lo = 1; hi = 0; }
-                    l2 = l * BW_LOG2E;
-                    dl = delta[((int64_t)b * a.Hq + hq) * a.Lq + r];
-                }
-                sLo[tid] = lo; sHi[tid] = hi; sL[tid] = l2; sD[tid] = dl;
+        fetch_tile<T, D>(rq, qb + (int64_t)r0 * a.q_stride, a.q_stride, a.Lq - r0, tid);
+        fetch_tile<T, D>(rg, gb + (int64_t)r0 * a.o_stride, a.o_stride, a.Lq - r0, tid);
+        if (tid < 32) {
+            const int r = r0 + tid;
+            rlo_ = 1; rhi_ = 0; rl_ = 0.0f; rd_ = 0.0f;
+            if (r < a.Lq) {
+                row_key_range<false>(a, r, rlo_, rhi_);
+                const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + r];
+                if (l == -INFINITY) { rlo_ = 1; rhi_ = 0; }
+                rl_ = l * BW_LOG2E;
+                rd_ = delta[((int64_t)b * a.Hq + hq) * a.Lq + r];
             }
-            __syncthreads();
-            f32x16_t s = {}, dp = {};
+        }
+    };
+    int it = next_step(0);
+    if (it < nsteps) fetch(it);
+    while (it < nsteps) {
+        const int nxt = next_step(it + 1);
+        __syncthreads();   // the previous step's tiles are no longer read
+        store_tile<D>(sQ, rq, tid);
+        store_tile<D>(sG, rg, tid);
+        if (tid < 32) { sLo[tid] = rlo_; sHi[tid] = rhi_; sL[tid] = rl_; sD[tid] = rd_; }
+        __syncthreads();
+        if (nxt < nsteps) fetch(nxt);   // in flight during this step's products
+        it = nxt;
+        f32x16_t s = {}, dp = {};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                s = Mfma<T>::mma32(rows_a<T, D>(sQ, lane, 16 * ks), kop[ks], s);
-                dp = Mfma<T>::mma32(rows_a<T, D>(sG, lane, 16 * ks), vop[ks], dp);
-            }
-            // element r of lane l: tile row 8 (r / 4) + 4 h + r % 4 for this lane's key
+        for (int ks = 0; ks < NKS; ++ks) {
+            s = Mfma<T>::mma32(rows_a<T, D>(sQ, lane, 16 * ks), kop[ks], s);
+            dp = Mfma<T>::mma32(rows_a<T, D>(sG, lane, 16 * ks), vop[ks], dp);
+        }
+        // element r of lane l: tile row 8 (r / 4) + 4 h + r % 4 for this lane's key
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int m0 = 8 * j + 4 * h;
-                const int4 lo4 = *reinterpret_cast<const int4*>(&sLo[m0]);
-                const int4 hi4 = *reinterpret_cast<const int4*>(&sHi[m0]);
-                const float4 l4 = *reinterpret_cast<const float4*>(&sL[m0]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&sD[m0]);
-                const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
-                const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds4[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int j = 0; j < 4; ++j) {
+            const int m0 = 8 * j + 4 * h;
+            const int4 lo4 = *reinterpret_cast<const int4*>(&sLo[m0]);
+            const int4 hi4 = *reinterpret_cast<const int4*>(&sHi[m0]);
+            const float4 l4 = *reinterpret_cast<const float4*>(&sL[m0]);
+            const float4 d4 = *reinterpret_cast<const float4*>(&sD[m0]);
+            const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+            const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * j + i;
-                    float p = 0.0f, dsv = 0.0f;
-                    if (kept && key >= los[i] && key <= his[i]) {
-                        float dl;
-                        const float x = logit2<CAP>(a, s[r], dl);
-                        p = fast_exp2(x - ls[i]);
-                        dsv = p * (dp[r] - ds4[i]) * dl;
-                    }
-                    s[r] = p;
-                    dp[r] = dsv;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * j + i;
+                float p = 0.0f, dsv = 0.0f;
+                if (kept && key >= los[i] && key <= his[i]) {
+                    float dl;
+                    const float x = logit2<CAP>(a, s[r], dl);
+                    p = fast_exp2(x - ls[i]);
+                    dsv = p * (dp[r] - ds4[i]) * dl;
                 }
+                s[r] = p;
+                dp[r] = dsv;
             }
+        }
 #pragma unroll
-            for (int sx = 0; sx < 2; ++sx) {
-                const v8 pop = pack8_at<T>(s, 8 * sx);
-                const v8 dop = pack8_at<T>(dp, 8 * sx);
+        for (int sx = 0; sx < 2; ++sx) {
+            const v8 pop = pack8_at<T>(s, 8 * sx);
+            const v8 dop = pack8_at<T>(dp, 8 * sx);
 #pragma unroll
-                for (int mb = 0; mb < NDB; ++mb) {
-                    dva[mb] = Mfma<T>::mma32(cols_a<T, D>(sG, lane, sx, mb), pop, dva[mb]);
-                    dka[mb] = Mfma<T>::mma32(cols_a<T, D>(sQ, lane, sx, mb), dop, dka[mb]);
-                }
+            for (int mb = 0; mb < NDB; ++mb) {
+                dva[mb] = Mfma<T>::mma32(cols_a<T, D>(sG, lane, sx, mb), pop, dva[mb]);
+                dka[mb] = Mfma<T>::mma32(cols_a<T, D>(sQ, lane, sx, mb), dop, dka[mb]);
             }
         }
     }
@@ -317,12 +366,12 @@ hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* de
                              hipStream_t s) {
     const T* g = static_cast<const T*>(dout);
     if (a.Lq > 0) {
-        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3((a.Lq + 127) / 128, a.Hq, a.B), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0, s, a,
                            g, delta, static_cast<T*>(dq));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP>), dim3((a.Lk + 127) / 128, a.Hkv, a.B), dim3(256), 0, s,
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0, s,
                        a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     return hipGetLastError();
 }
@@ -342,7 +391,7 @@ hipError_t launch_bwd_mfma_d(const FwdArgs& a, const void* dout, const float* de
 
 bool bwd_mfma_supported(const FwdArgs& a, int dtype) {
     return (dtype == kBF16 || dtype == kF16) && (a.D == 64 || a.D == 128) && !a.bias && a.drop_scale == 0.0f &&
-           !a.seq_bounds && !a.row_pos;
+           !a.seq_bounds && !a.row_pos && (a.Lq + 127) / 128 <= 65535 && (a.Lk + 127) / 128 <= 65535;   // grid z
 }
 
 hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
