@@ -726,6 +726,12 @@ def _numpy_philox_block(ctr, key):
     return [int(x) for x in bg.random_raw(4)]
 
 
+def _numpy_keep(seed, thr, b, h, i, j):
+    """Dropout decision of weight (b, h, i, j) from NumPy's Philox: block
+    (j // 4, i, h, b) under key (seed, 0), word j % 4, top 24 bits >= thr."""
+    return (_numpy_philox_block([j // 4, i, h, b], [seed, 0])[j % 4] >> 40) >= thr
+
+
 def pin_philox_matches_numpy(orc):
     """The oracle's Philox4x64-10 against NumPy's implementation of it."""
     rng = _rng(23)
@@ -740,7 +746,7 @@ def pin_philox_matches_numpy(orc):
 def dense_bias_dropout(q, k, v, *, scale, causal, window, q_offset, softcap=0.0, key_mask=None,
                        bias=None, dropout_p=0.0, seed=0):
     """Full score matrix, bias broadcast by NumPy, dropout pattern from NumPy's
-    Philox with counter (j, i, hq, b) and key (seed, 0)."""
+    Philox: block (j // 4, i, hq, b) under key (seed, 0), word j % 4."""
     q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
@@ -766,7 +772,7 @@ def dense_bias_dropout(q, k, v, *, scale, causal, window, q_offset, softcap=0.0,
                 keep = np.zeros((Lq, Lk), bool)
                 for i in range(Lq):
                     for j in range(Lk):
-                        keep[i, j] = (_numpy_philox_block([j, i, h, b], [seed, 0])[0] >> 40) >= thr
+                        keep[i, j] = _numpy_keep(seed, thr, b, h, i, j)
                 p = np.where(keep, p / (1.0 - dropout_p), 0.0)
             O[b, :, h, :] = p @ v[b, :, h // g, :]
             L[b, h, :] = lse
@@ -907,7 +913,7 @@ def pin_bwd_matches_torch_autograd(orc):
                 for h_ in range(Hq):
                     for i in range(Lq):
                         for j in range(Lk):
-                            keep = (_numpy_philox_block([j, i, h_, b_], [seed, 0])[0] >> 40) >= thr
+                            keep = _numpy_keep(seed, thr, b_, h_, i, j)
                             Z[b_, h_, i, j] = 1.0 / (1.0 - kw["dropout_p"]) if keep else 0.0
             P = P * torch.tensor(Z)
         O = torch.einsum("bhij,bjhd->bihd", P, vr)

@@ -28,6 +28,7 @@ MUTANTS = {
     15: "additive mask indexed with query and key swapped",
     16: "dropout pattern drawn with query and key swapped",
     17: "backward without the derivative of the scale and soft-cap",
+    18: "dropout reading word 0 of the block for every key",
 }
 
 

@@ -34,10 +34,10 @@ struct FwdArgs {
     // (b, hq, i, j) with bias_stride (0 for a broadcast dimension), or null
     const float* bias;
     int64_t bias_stride[4];
-    // attention dropout: a weight is kept iff the top 24 bits of word 0 of
-    // Philox4x64-10(counter (j, i, hq, b), key (drop_seed, 0)) are at least
-    // drop_threshold, and a kept weight is multiplied by drop_scale (> 0
-    // turns dropout on)
+    // attention dropout: weight (b, hq, i, j) is kept iff the top 24 bits of
+    // word j % 4 of Philox4x64-10(counter (j / 4, i, hq, b), key
+    // (drop_seed, 0)) are at least drop_threshold, and a kept weight is
+    // multiplied by drop_scale (> 0 turns dropout on)
     uint32_t drop_threshold;
     float drop_scale;
     uint64_t drop_seed;
@@ -82,11 +82,12 @@ __device__ inline void row_key_range(const FwdArgs& a, int i, int& lo, int& hi) 
     }
 }
 
-// Word 0 of Philox4x64-10 (Salmon et al., SC 2011): ten rounds of two
-// 64x64 -> 128-bit products with the round constants, the halves mixed with
-// the other counter words and the key, the key bumped by the Weyl constants.
-__device__ inline uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
-                                            uint64_t k0, uint64_t k1) {
+// Philox4x64-10 (Salmon et al., SC 2011): ten rounds of two 64x64 -> 128-bit
+// products with the round constants, the halves mixed with the other counter
+// words and the key, the key bumped by the Weyl constants.  c0..c3 in: the
+// counter; out: the block.
+__device__ inline void philox4x64(uint64_t& c0, uint64_t& c1, uint64_t& c2, uint64_t& c3, uint64_t k0,
+                                  uint64_t k1) {
     const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
@@ -99,15 +100,22 @@ __device__ inline uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, uint64_t c
         k0 += 0x9E3779B97F4A7C15ull;
         k1 += 0xBB67AE8584CAA73Bull;
     }
-    return c0;
 }
 
-// Dropout decision of weight (b, hq, i, j): the top 24 bits of word 0 of
-// Philox4x64-10 with counter (j, i, hq, b) and key (seed, 0) against the
-// threshold round(p * 2^24).
+// Dropout decisions of weights (b, hq, i, 4 jb .. 4 jb + 3): bit e set iff
+// the top 24 bits of word e of Philox4x64-10 with counter (jb, i, hq, b) and
+// key (seed, 0) reach the threshold round(p * 2^24).
+__device__ inline uint32_t dropout_keep4(const FwdArgs& a, int b, int hq, int i, int jb) {
+    uint64_t c0 = (uint64_t)jb, c1 = (uint64_t)i, c2 = (uint64_t)hq, c3 = (uint64_t)b;
+    philox4x64(c0, c1, c2, c3, a.drop_seed, 0);
+    const uint32_t t = a.drop_threshold;
+    return ((uint32_t)(c0 >> 40) >= t ? 1u : 0u) | ((uint32_t)(c1 >> 40) >= t ? 2u : 0u) |
+           ((uint32_t)(c2 >> 40) >= t ? 4u : 0u) | ((uint32_t)(c3 >> 40) >= t ? 8u : 0u);
+}
+
+// Dropout decision of weight (b, hq, i, j).
 __device__ inline bool dropout_keep(const FwdArgs& a, int b, int hq, int i, int j) {
-    const uint64_t w = philox4x64_word0((uint64_t)j, (uint64_t)i, (uint64_t)hq, (uint64_t)b, a.drop_seed, 0);
-    return (uint32_t)(w >> 40) >= a.drop_threshold;
+    return (dropout_keep4(a, b, hq, i, j >> 2) >> (j & 3)) & 1u;
 }
 
 // Launchers (each returns the hipError_t of its launch).
