@@ -19,7 +19,7 @@ under "decode_len".  "packed_encoder" times the bidirectional encoder workload
 key mask through mfa_fwd, and packed without its padding through
 mfa_packed_qkv_fwd.  "bias_mfma" times the causal GQA prefill with a
 [1, 1, L, L] float32 additive mask (the MFMA kernel), "bias_dropout" the same
-with dropout 0.1 (the fp32-arithmetic generic kernel).  "backward" times mfa_bwd (dQ, dK, dV) on
+with dropout 0.1 and "dropout" dropout 0.1 alone (the MFMA kernel as well).  "backward" times mfa_bwd (dQ, dK, dV) on
 the causal GQA prefill shape.
 
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
@@ -283,7 +283,9 @@ def bias_mfma(steps: int, warmup: int, warmup_ms: float):
     return res
 
 
-def bias_dropout(steps: int, warmup: int, warmup_ms: float):
+def bias_dropout(steps: int, warmup: int, warmup_ms: float, with_bias: bool = True):
+    """The prefill shape with dropout 0.1, with or without a [1, 1, L, L]
+    additive mask: the MFMA kernel's DROP instantiations."""
     import torch
     import transformer_mfa_fwd_amd as mfa
     from transformer_mfa_fwd_amd import workloads as wl
@@ -292,14 +294,15 @@ def bias_dropout(steps: int, warmup: int, warmup_ms: float):
     q, k, v, _ = wl.make_inputs(w, "cuda")
     g = torch.Generator(device="cuda")
     g.manual_seed(1)
-    bias = torch.randn((1, 1, w.Lq, w.Lk), generator=g, device="cuda")
+    bias = torch.randn((1, 1, w.Lq, w.Lk), generator=g, device="cuda") if with_bias else None
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda")
     wall, kern = time_calls(lambda: mfa.fwd(q, k, v, causal=True, bias=bias, dropout_p=0.1, seed=5,
                                             out=out, lse=lse), steps, warmup, warmup_ms)
     pairs = visible_pairs(w, None)
-    res = {"workload": w.name, "api": "mfa_fwd_bias_dropout", "bias_shape": [1, 1, w.Lq, w.Lk],
-           "dropout_p": 0.1, "path": "generic", "unit": "TFLOP/s", "ms_per_step": round(wall, 5),
+    res = {"workload": w.name, "api": "mfa_fwd_bias_dropout",
+           "bias_shape": [1, 1, w.Lq, w.Lk] if with_bias else None,
+           "dropout_p": 0.1, "path": "mfma", "unit": "TFLOP/s", "ms_per_step": round(wall, 5),
            "kernel_ms_avg": round(kern, 5), "value": round(4.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
     del q, k, v, bias, out, lse
     torch.cuda.empty_cache()
@@ -487,7 +490,9 @@ def main():
         tensors = None
         torch.cuda.empty_cache()
         line["bias_mfma"] = bias_mfma(max(10, args.steps // 2), max(3, args.warmup // 2), args.warmup_ms)
-        line["bias_dropout"] = bias_dropout(5, 2, args.warmup_ms)
+        line["bias_dropout"] = bias_dropout(max(10, args.steps // 2), max(3, args.warmup // 2), args.warmup_ms)
+        line["dropout"] = bias_dropout(max(10, args.steps // 2), max(3, args.warmup // 2), args.warmup_ms,
+                                       with_bias=False)
 
     if not args.no_backward:
         tensors = None

@@ -107,16 +107,18 @@ int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *   dropout_p   in [0, 1): each normalised weight is dropped with this
  *               probability and a kept one divided by 1 - p; the saved LSE
  *               is the undropped one.  Weight (b, hq, i, j) is kept iff the
- *               top 24 bits of word 0 of Philox4x64-10 (counter (j, i, hq, b),
- *               key (seed, 0)) are at least round(p * 2^24), so a pattern is
- *               reproducible from the seed alone.
+ *               top 24 bits of word j mod 4 of the Philox4x64-10 block with
+ *               counter (floor(j / 4), i, hq, b) and key (seed, 0) are at
+ *               least round(p * 2^24), so a pattern is reproducible from the
+ *               seed alone.
  *
  * A row whose every visible key has a bias of -inf gets O = 0, LSE = -inf.
- * Without dropout, an fp16/bf16 call whose bias has bias_Lk = Lk, with Lk a
- * multiple of 4 and bias 16-byte aligned, runs on the MFMA prefill kernel;
- * every other call runs on the fp32-arithmetic kernel (MFA_PATH_GENERIC).  Other arguments, errors and streams as for mfa_fwd; a bias
- * dimension other than 1 or full size, or p outside [0, 1), is
- * MFA_ERROR_INVALID_VALUE.
+ * An fp16/bf16 call with D 64 or 128 runs on the MFMA prefill kernel unless
+ * it has a bias that kernel cannot read four keys at a time (it needs
+ * bias_Lk = Lk, Lk a multiple of 4 and a 16-byte aligned bias); every other
+ * call runs on the fp32-arithmetic kernel (MFA_PATH_GENERIC).  Other
+ * arguments, errors and streams as for mfa_fwd; a bias dimension other than
+ * 1 or full size, or p outside [0, 1), is MFA_ERROR_INVALID_VALUE.
  */
 int mfa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
                          int B, int Lq, int Lk, int Hq, int Hkv, int D,

@@ -73,17 +73,20 @@ def gather_rows(out: torch.Tensor, lse: torch.Tensor, rows: np.ndarray):
     return o, l
 
 
-def compare(dtype: str, o_gpu, l_gpu, o_ref, l_ref, what: str = ""):
-    """Assert the tolerances; returns (max O error, max LSE error)."""
+def compare(dtype: str, o_gpu, l_gpu, o_ref, l_ref, what: str = "", o_scale: float = 1.0):
+    """Assert the tolerances; returns (max O error, max LSE error).  o_scale
+    multiplies the O tolerance: with dropout p the weights are formed (and
+    rounded) before the factor 1 / (1 - p), so their error grows with it."""
     o_gpu = np.asarray(o_gpu, np.float64)
     o_ref = np.asarray(o_ref, np.float64)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
     err = np.abs(o_gpu - o_ref)
-    excess = err - (TOL_O[dtype] + half_ulp(o_ref, dtype))
+    tol = TOL_O[dtype] * o_scale
+    excess = err - (tol + half_ulp(o_ref, dtype))
     worst = int(np.argmax(excess)) if excess.size else 0
     assert excess.size == 0 or excess.flat[worst] <= 0, (
         f"{what}: |O - O_ref| = {err.flat[worst]:.3e} at flat index {worst} exceeds "
-        f"{TOL_O[dtype]:.0e} + half-ulp (max abs err {err.max():.3e})")
+        f"{tol:.1e} + half-ulp (max abs err {err.max():.3e})")
     lerr = 0.0
     if l_gpu is not None:
         l_gpu = np.asarray(l_gpu, np.float64)

@@ -1,5 +1,5 @@
 """GPU parity of the additive score mask and attention dropout
-(mfa_fwd_bias_dropout, generic kernel) against the fp64 oracle on every row:
+(mfa_fwd_bias_dropout, generic and MFMA kernels) against the fp64 oracle on every row:
 broadcast bias shapes, dropout probabilities and seeds, together with the
 causal/window/key-mask/soft-cap features, every dtype and head size."""
 import sys
@@ -47,7 +47,7 @@ def run_and_check(w, bias_shape, p, seed, neg_inf_frac=0.0):
                                     dropout_p=p, seed=seed, nthreads=pu.ORACLE_THREADS)
     og = out.double().cpu().numpy().transpose(0, 2, 1, 3)
     return pu.compare(w.dtype, og, lse.double().cpu().numpy(), O.transpose(0, 2, 1, 3), L,
-                      f"{w.name} bias={shape} p={p}")
+                      f"{w.name} bias={shape} p={p}", o_scale=1.0 / (1.0 - p))
 
 
 BASE = []
@@ -120,3 +120,29 @@ def test_bias_mfma_matches_generic_rounding_free_case():
     torch.cuda.synchronize()
     assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
     assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+# Dropout on the MFMA prefill kernel, alone and with an additive mask it reads
+# itself: several tiles and ragged tails, every combination of cap and key
+# mask, keep probabilities from high to low.
+@pytest.mark.parametrize("p,seed", [(0.1, 5), (0.5, 2**63 + 9), (0.9, 1)])
+@pytest.mark.parametrize("shape", [None, (1, 1, 1, 1), (0, 1, 1, 1)], ids=lambda s: "nobias" if s is None else "".join(map(str, s)))
+@pytest.mark.parametrize("w", MFMA_BIAS, ids=lambda w: w.name)
+def test_dropout_on_mfma_kernel_all_rows(w, shape, p, seed):
+    run_and_check(w, shape, p, seed)
+
+
+def test_dropout_mfma_keep_rate_and_row_sums():
+    """One head of 1024 rows and keys: V = 1 makes every output element the
+    kept weights' sum times 1 / (1 - p); its mean over rows is near 1 and the
+    LSE is the undropped call's."""
+    w = wl.Workload("bm_rate", "bf16", 1, 1024, 1024, 1, 1, 128, False)
+    q, k, _, _ = wl.make_inputs(w, DEV)
+    v = torch.ones_like(k)
+    o0, l0 = mfa.fwd(q, k, v)
+    o1, l1 = mfa.fwd(q, k, v, dropout_p=0.25, seed=3)
+    torch.cuda.synchronize()
+    assert (l0 - l1).abs().max().item() <= 1e-5
+    assert (o0.float() - 1).abs().max().item() <= 1e-2
+    mean = o1.float()[0, :, 0, 0].mean().item()
+    assert abs(mean - 1.0) < 0.02, mean

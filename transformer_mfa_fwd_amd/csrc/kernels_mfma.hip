@@ -124,8 +124,13 @@ __device__ inline uint64_t range_bits64(int lo, int hi) {
 
 // BIAS adds an additive score mask read from global memory into registers one
 // tile ahead (32 more VGPRs: one workgroup per CU at D = 128, two at D = 64).
-template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS>
-__global__ __launch_bounds__(256, BIAS ? (D == 64 ? 2 : 1) : (D == 64 ? 3 : 2))
+// DROP applies attention dropout: the keep bits of a tile's 32 weights per
+// lane come from eight Philox blocks before its softmax, dropped weights are
+// zeroed after they enter the row sum and before they become the P.V operand,
+// and the 1 / (1 - p) factor is folded into the final normalisation (one
+// workgroup per CU at D = 128, or with BIAS too; two at D = 64).
+template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP>
+__global__ __launch_bounds__(256, (BIAS && DROP) ? 1 : (BIAS || DROP) ? (D == 64 ? 2 : 1) : (D == 64 ? 3 : 2))
 void prefill_kernel(FwdArgs a, int nqt) {
     typedef PfLds<D> L;
     constexpr int CPR = L::CPR;
@@ -321,6 +326,25 @@ void prefill_kernel(FwdArgs a, int nqt) {
 // Score i (0..31) of this lane: key k0 + 32 (i / 16) + 8 ((i % 16) / 4) + 4 h2 + i % 4.
 #define MFA_X(SC, I) SC[(I) >> 4][(I) & 15]
 
+// Keep bits of this lane's 32 weights of the tile at key k0 (bit i: score i).
+// Scores 4 G .. 4 G + 3 are keys 4 jb .. 4 jb + 3 of one Philox block, jb =
+// k0 / 4 + 8 (G / 4) + 2 (G % 4) + h2.
+#define MFA_KEEP(K0)                                                                         \
+    ({                                                                                       \
+        uint32_t _kw = 0u;                                                                   \
+        _Pragma("unroll") for (int _g = 0; _g < 8; ++_g)                                     \
+            _kw |= dropout_keep4(a, b, hq, qrow, ((K0) >> 2) + 8 * (_g >> 2) + 2 * (_g & 3) + h2) << (4 * _g); \
+        _kw;                                                                                 \
+    })
+// zero the dropped weights among scores E0 .. E0 + 7 (after the row sum has them)
+#define MFA_DROP8(SC, E0)                                                                    \
+    do {                                                                                     \
+        if constexpr (DROP) {                                                                \
+            _Pragma("unroll") for (int _e = 0; _e < 8; ++_e)                                 \
+                MFA_X(SC, (E0) + _e) = (keepw >> ((E0) + _e)) & 1u ? MFA_X(SC, (E0) + _e) : 0.0f; \
+        }                                                                                    \
+    } while (0)
+
 // Softmax step U (a constant, 0 .. NSA-1) of the tile whose raw scores are in
 // SC.  With a cap the base-2 logit is
 // cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1); without one it is
@@ -389,7 +413,10 @@ void prefill_kernel(FwdArgs a, int nqt) {
             }                                                                                \
             psum0 += MFA_X(SC, 2 * (_u - 5));                                                \
             psum1 += MFA_X(SC, 2 * (_u - 5) + 1);                                            \
-            if constexpr (_u == 8) pop[0] = pack8_at<T>(SC[0], 0);                           \
+            if constexpr (_u == 8) {                                                         \
+                MFA_DROP8(SC, 0);                                                            \
+                pop[0] = pack8_at<T>(SC[0], 0);                                              \
+            }                                                                                \
         }                                                                                    \
     } while (0)
 
@@ -406,7 +433,10 @@ void prefill_kernel(FwdArgs a, int nqt) {
             }                                                                                \
             psum0 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U));                                      \
             psum1 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U) + 1);                                  \
-            if constexpr ((U) == 3) pop[1 + (S4)] = pack8_at<T>(SC[(1 + (S4)) >> 1], 8 * ((1 + (S4)) & 1)); \
+            if constexpr ((U) == 3) {                                                        \
+                MFA_DROP8(SC, 8 * (1 + (S4)));                                               \
+                pop[1 + (S4)] = pack8_at<T>(SC[(1 + (S4)) >> 1], 8 * ((1 + (S4)) & 1));       \
+            }                                                                                \
             if constexpr ((S4) == 2 && (U) == 3) l += psum0 + psum1;                         \
         }                                                                                    \
     } while (0)
@@ -499,6 +529,9 @@ void prefill_kernel(FwdArgs a, int nqt) {
         const uint64_t word = MASK ? words[tcur] : ~0ull;                                    \
         const bool interior = __builtin_amdgcn_readfirstlane(                                \
             (k0 >= wlo_last && k0 + BN - 1 <= whi_first && (!MASK || word == ~0ull)) ? 1 : 0); \
+        uint32_t keepw = ~0u;                                                                \
+        if constexpr (DROP) keepw = MFA_KEEP(k0);                                            \
+        (void)keepw;                                                                         \
         constexpr int _vb = L::VST + (ST) * L::TILE;                                         \
         i16x4_t vlo[2][NDB], vhi[2][NDB];                                                    \
         float pm[11];                                                                        \
@@ -529,6 +562,8 @@ void prefill_kernel(FwdArgs a, int nqt) {
             const int k0 = 0;
             const uint64_t word = 0;
             const bool interior = true;
+            const uint32_t keepw = ~0u;
+            (void)keepw;
             constexpr int _vb = 0, _dk_dst = 0, _dv_dst = 0;
             const auto _rk = MFA_RSRC(kbase, tcur);
             const auto _rv = _rk;
@@ -554,6 +589,8 @@ void prefill_kernel(FwdArgs a, int nqt) {
 #undef MFA_RSRC
 #undef MFA_TR_ISSUE
 #undef MFA_X
+#undef MFA_KEEP
+#undef MFA_DROP8
 #undef MFA_SA
 #undef MFA_SB
 #undef MFA_SA_IF
@@ -569,7 +606,8 @@ void prefill_kernel(FwdArgs a, int nqt) {
     // after the loop's last barrier) so that each store writes whole rows.
     l = xor32_sum(l);
     {
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        // with dropout every kept weight carries the factor 1 / (1 - p)
+        const float inv = l > 0.0f ? (DROP ? a.drop_scale : 1.0f) / l : 0.0f;
         char* stg = smem + wave * 32 * L::RS;
         char* wrow = stg + lq * L::RS;
 #pragma unroll
@@ -597,13 +635,20 @@ void prefill_kernel(FwdArgs a, int nqt) {
         a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qrow] = l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
 }
 
-template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS = false>
+template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS = false, bool DROP = false>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int nqt = (a.Lq + BM - 1) / BM;
     const int64_t blocks = (int64_t)a.B * a.Hq * nqt;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK, SEQ, BIAS>), dim3((unsigned)blocks), dim3(256), 0, s, a,
-                       nqt);
+    hipLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK, SEQ, BIAS, DROP>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       a, nqt);
     return hipGetLastError();
+}
+
+// the additive-mask and dropout kernels of plain batches
+template <typename T, int D, bool BIAS, bool DROP>
+hipError_t launch_extras(const FwdArgs& a, bool cap, bool mask, hipStream_t s) {
+    if (cap) return mask ? launch_t<T, D, true, true, false, BIAS, DROP>(a, s) : launch_t<T, D, true, false, false, BIAS, DROP>(a, s);
+    return mask ? launch_t<T, D, false, true, false, BIAS, DROP>(a, s) : launch_t<T, D, false, false, false, BIAS, DROP>(a, s);
 }
 
 // Packed inputs (per-row positions or sequence bounds) have their own
@@ -611,10 +656,11 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     const bool cap = a.softcap > 0.0f, mask = a.key_mask != nullptr;
-    if (a.bias) {
-        if (a.seq_bounds || a.row_pos || !mfma_bias_supported(a)) return hipErrorInvalidValue;
-        if (cap) return mask ? launch_t<T, D, true, true, false, true>(a, s) : launch_t<T, D, true, false, false, true>(a, s);
-        return mask ? launch_t<T, D, false, true, false, true>(a, s) : launch_t<T, D, false, false, false, true>(a, s);
+    const bool drop = a.drop_scale > 0.0f;
+    if (a.bias || drop) {
+        if (a.seq_bounds || a.row_pos || (a.bias && !mfma_bias_supported(a))) return hipErrorInvalidValue;
+        if (a.bias) return drop ? launch_extras<T, D, true, true>(a, cap, mask, s) : launch_extras<T, D, true, false>(a, cap, mask, s);
+        return launch_extras<T, D, false, true>(a, cap, mask, s);
     }
     if (a.seq_bounds || a.row_pos) {
         if (mask) return hipErrorInvalidValue;

@@ -164,19 +164,22 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
     if (c.B == 0 || c.Lq == 0) return MFA_SUCCESS;
 
     const int group = c.Hq / c.Hkv;
-    // dropout runs on the generic kernel only; an additive mask also on the
-    // MFMA prefill kernel when its rows can be read four keys at a time
-    bool bias_mfma = false;
-    if (c.bias && c.dropout_p == 0.0f && mfa::mfma_prefill_supported(c.dtype, c.D)) {
-        const mfa::FwdArgs t = make_args(c);
-        bias_mfma = mfa::mfma_bias_supported(t);
-    }
+    // an additive mask and dropout run on the MFMA prefill kernel (fp16/bf16,
+    // D 64 or 128) when the mask's rows can be read four keys at a time, and
+    // on the generic kernel otherwise
     const bool extras = c.bias != nullptr || c.dropout_p > 0.0f;
+    bool extras_mfma = false;
+    if (extras && mfa::mfma_prefill_supported(c.dtype, c.D)) {
+        const mfa::FwdArgs t = make_args(c);
+        extras_mfma = !c.bias || mfa::mfma_bias_supported(t);
+    }
     if (path == MFA_PATH_AUTO)
-        path = extras ? (bias_mfma ? MFA_PATH_MFMA : MFA_PATH_GENERIC)
+        path = extras ? (extras_mfma ? MFA_PATH_MFMA : MFA_PATH_GENERIC)
                       : auto_path(c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D, c.dtype);
-    if (extras && path != MFA_PATH_GENERIC && !(bias_mfma && path == MFA_PATH_MFMA))
-        return fail(MFA_ERROR_NOT_SUPPORTED, "dropout, or this additive mask, needs the generic path");
+    if (extras && path != MFA_PATH_GENERIC && !(extras_mfma && path == MFA_PATH_MFMA))
+        return fail(MFA_ERROR_NOT_SUPPORTED,
+                    "this additive mask or dropout call needs the generic path (MFMA: fp16/bf16, D 64/128, "
+                    "mask rows of Lk %% 4 == 0 floats, 16-byte aligned)");
     switch (path) {
         case MFA_PATH_GENERIC: break;
         case MFA_PATH_MFMA:
