@@ -20,7 +20,8 @@ key mask through mfa_fwd, and packed without its padding through
 mfa_packed_qkv_fwd.  "bias_mfma" times the causal GQA prefill with a
 [1, 1, L, L] float32 additive mask (the MFMA kernel), "bias_dropout" the same
 with dropout 0.1 and "dropout" dropout 0.1 alone (the MFMA kernel as well).  "backward" times mfa_bwd (dQ, dK, dV) on
-the causal GQA prefill shape.
+the causal GQA prefill shape, and "backward_bias_dropout" the same with the mask
+and dropout 0.1.
 
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
 average duration comes from HIP events recorded on the launch stream around
@@ -309,23 +310,32 @@ def bias_dropout(steps: int, warmup: int, warmup_ms: float, with_bias: bool = Tr
     return res
 
 
-def backward(steps: int, warmup: int, warmup_ms: float):
+def backward(steps: int, warmup: int, warmup_ms: float, extras: bool = False):
+    """mfa_bwd on the prefill shape; with ``extras`` the forward and backward
+    carry a [1, 1, L, L] additive mask and dropout 0.1."""
     import torch
     import transformer_mfa_fwd_amd as mfa
     from transformer_mfa_fwd_amd import workloads as wl
 
     w = wl.GQA_CAUSAL_PREFILL_BF16
     q, k, v, _ = wl.make_inputs(w, "cuda")
-    out, lse = mfa.fwd(q, k, v, causal=True)
+    kw = dict(causal=True)
+    if extras:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1)
+        kw.update(bias=torch.randn((1, 1, w.Lq, w.Lk), generator=g, device="cuda"), dropout_p=0.1, seed=5)
+    out, lse = mfa.fwd(q, k, v, **kw)
     dout = torch.randn(q.shape, device="cuda").to(q.dtype)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    wall, kern = time_calls(lambda: mfa.bwd(q, k, v, out, dout, lse, causal=True, dq=dq, dk=dk, dv=dv),
+    wall, kern = time_calls(lambda: mfa.bwd(q, k, v, out, dout, lse, dq=dq, dk=dk, dv=dv, **kw),
                             steps, warmup, warmup_ms)
     pairs = visible_pairs(w, None)
     res = {"workload": w.name, "api": "mfa_bwd", "path": "mfma", "unit": "TFLOP/s",
            "flops_per_pair": 10 * w.D, "ms_per_step": round(wall, 5), "kernel_ms_avg": round(kern, 5),
            "value": round(10.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
-    del q, k, v, out, lse, dout, dq, dk, dv
+    if extras:
+        res.update(bias_shape=[1, 1, w.Lq, w.Lk], dropout_p=0.1)
+    del q, k, v, out, lse, dout, dq, dk, dv, kw
     torch.cuda.empty_cache()
     return res
 
@@ -498,6 +508,7 @@ def main():
         tensors = None
         torch.cuda.empty_cache()
         line["backward"] = backward(5, 2, args.warmup_ms)
+        line["backward_bias_dropout"] = backward(5, 2, args.warmup_ms, extras=True)
 
     if not args.no_cpu_baseline:
         if tensors is None:

@@ -142,9 +142,9 @@ int mfa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* out,
  * recomputed from q, k and lse (P = exp(s - LSE)); with Delta = <dO, O> per
  * row, dS = P (Z <dO, V> - Delta) and the chain rule through the scale and
  * soft-cap.  Each gradient element is written by one workgroup, with no
- * atomics, so a call is deterministic.  fp16/bf16 calls without an additive
- * mask or dropout run on the matrix cores (P and dS rounded to the input type
- * as operands, fp32 accumulation); the others in fp32 arithmetic.  The
+ * atomics, so a call is deterministic.  fp16/bf16 calls with D 64 or 128 run
+ * on the matrix cores (P and dS rounded to the input type as operands, fp32
+ * accumulation); the others in fp32 arithmetic.  The
  * workspace holds Delta: caller-owned (256-byte
  * aligned, at least mfa_bwd_workspace_size bytes) or NULL with ws_bytes = 0
  * for the stream-ordered pool.  B = 0 does nothing; Lq = 0 writes zero dK,

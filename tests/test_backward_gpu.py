@@ -78,12 +78,19 @@ def test_backward_matches_oracle(w):
     run_case(w)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_with_bias_and_dropout(dtype):
-    w = wl.Workload(f"bwd_bias_drop_{dtype}", dtype, 2, 80, 96, 4, 2, 64, True, window=60)
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 64), ("f16", 128), ("bf16", 128)])
+def test_backward_with_bias_and_dropout(dtype, D):
+    """fp32 on the fp32 kernels, fp16/bf16 on the matrix cores' mask-and-dropout
+    instantiations: several 32-row and 32-key tiles, ragged tails, a window."""
+    w = wl.Workload(f"bwd_bias_drop_{dtype}_D{D}", dtype, 2, 80, 96, 4, 2, D, True, window=60)
     run_case(w, bias_shape=(0, 1, 1, 1), p=0.0)
     run_case(w, bias_shape=None, p=0.25, seed=2**35 + 1)
     run_case(w, bias_shape=(1, 0, 1, 0), p=0.5, seed=3)
+    if dtype != "f32":
+        wc = wl.Workload(f"bwd_bias_drop_cap_mask_{dtype}_D{D}", dtype, 2, 100, 130, 4, 1, D, False, window=70,
+                         softcap=6.0, mask="random_frac", mask_frac=0.2)
+        run_case(wc, bias_shape=(1, 1, 1, 1), p=0.1, seed=77)
+        run_case(wc, bias_shape=(1, 0, 0, 1), p=0.9, seed=5)
 
 
 def test_backward_deterministic_and_zero_for_unseen_keys():
@@ -103,17 +110,21 @@ def test_backward_deterministic_and_zero_for_unseen_keys():
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
 def test_matrix_core_backward_agrees_with_fp32_kernels(dtype, D):
-    """fp16/bf16 without a mask or dropout take the matrix-core backward; an
-    all-zero additive mask sends the same call to the fp32 kernels."""
+    """The 16-bit call runs on the matrix cores; the same inputs widened to
+    float32 run on the fp32 kernels.  With an all-zero additive mask the call
+    takes the mask-and-dropout instantiations and must agree as well."""
     w = wl.Workload(f"bwd_paths_{dtype}", dtype, 2, 300, 300, 8, 2, D, True, window=200)
     q, k, v, _ = wl.make_inputs(w, DEV)
     dout = torch.randn_like(q)
     out, lse = mfa.fwd(q, k, v, causal=True, window=200)
     a = mfa.bwd(q, k, v, out, dout, lse, causal=True, window=200)
     zero = torch.zeros((1, 1, 1, w.Lk), device=DEV)
-    g = mfa.bwd(q, k, v, out, dout, lse, causal=True, window=200, bias=zero)
+    z = mfa.bwd(q, k, v, out, dout, lse, causal=True, window=200, bias=zero)
+    f = [x.float() for x in (q, k, v, out, dout)]
+    g = mfa.bwd(*f, lse, causal=True, window=200)
     torch.cuda.synchronize()
-    for name, x, y in zip(("dq", "dk", "dv"), a, g):
-        scale = max(1.0, float(y.float().abs().max()))
-        err = float((x.float() - y.float()).abs().max())
+    for name, x, y, zz in zip(("dq", "dk", "dv"), a, g, z):
+        scale = max(1.0, float(y.abs().max()))
+        err = float((x.float() - y).abs().max())
         assert err <= 1e-2 * scale, (name, err, scale)
+        assert float((zz.float() - x.float()).abs().max()) <= 1e-3 * scale, name

@@ -1,9 +1,11 @@
 // kernels_bwd_mfma.hip -- the backward on the matrix cores for fp16/bf16
-// inputs (no additive mask, no dropout; those calls take the fp32 kernels).
+// inputs, with or without an additive mask and dropout.
 //
 // Same formulas as kernels_backward.hip (vision_rs flash_attn2.rs, backward
 // kernels): P = exp(s - LSE) from the saved LSE, Delta = <dO, O>,
-// dS = P (dO V^T - Delta) * d s / d<Q, K>, dQ = dS K, dK = dS^T Q, dV = P^T dO.
+// dS = P (Z dO V^T - Delta) * d s / d<Q, K>, dQ = dS K, dK = dS^T Q,
+// dV = (P Z)^T dO, with Z the dropout factors (keep / (1 - p), or 1) and the
+// additive mask inside s.
 // Every product is a 32x32x16 MFMA with fp32 accumulation; P and dS are
 // rounded to the input type to serve as operands, as the forward rounds P.
 //
@@ -106,8 +108,16 @@ __device__ inline float logit2(const FwdArgs& a, float dot, float& dl) {
     }
 }
 
-template <typename T, int D, bool CAP>
-__global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+// Dropout decisions of four keys 4 jb .. 4 jb + 3 for one row, bits 0..3 (the
+// forward's rule); all kept when dropout is off.
+__device__ inline uint32_t bwd_keep4(const FwdArgs& a, int b, int hq, int row, int jb) {
+    return a.drop_scale > 0.0f ? dropout_keep4(a, b, hq, row, jb) : 0xfu;
+}
+
+// EXTRA kernels also read the additive mask and apply dropout (each when the
+// call has it).
+template <typename T, int D, bool CAP, bool EXTRA>
+__global__ __launch_bounds__(256, (EXTRA && D == 128) ? 1 : 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                              const float* __restrict__ delta, T* __restrict__ dq) {
     typedef typename Mfma<T>::v8 v8;
     constexpr int NKS = D / 16, NDB = D / 32;
@@ -145,6 +155,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
     int lo_blk, t0, t1, hi_blk;
     row_key_range<false>(a, i0, lo_blk, t0);
     row_key_range<false>(a, i_last, t1, hi_blk);
+    // additive mask of this lane's row (EXTRA with a mask)
+    const float* brow = nullptr;
+    if (EXTRA && a.bias)
+        brow = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] + (int64_t)rowc * a.bias_stride[2];
 
     f32x16_t acc[NDB];
 #pragma unroll
@@ -156,7 +170,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
         const int t_first = lo_blk / 32, t_end = hi_blk / 32 + 1;
         TileRegs<D> rk, rv;
         float rm = 0.0f;
-        // tile t's K, V and key-kept flags into registers
+        float rb[EXTRA ? 16 : 1];   // mask of this lane's 16 scores of the tile
+        // tile t's K, V, key-kept flags (and mask values) into registers
         auto fetch = [&](int t) {
             const int k0 = 32 * t;
             fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
@@ -164,6 +179,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
             if (tid < 32) {
                 const int key = k0 + tid;
                 rm = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
+            }
+            if constexpr (EXTRA) {
+                if (brow) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        rb[r] = key < a.Lk ? brow[(int64_t)key * a.bias_stride[3]] : 0.0f;
+                    }
+                }
             }
         };
         fetch(t_first);
@@ -173,8 +197,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
             store_tile<D>(sK, rk, tid);
             store_tile<D>(sV, rv, tid);
             if (tid < 32) sM[tid] = rm;
+            float bv[EXTRA ? 16 : 1];
+            if constexpr (EXTRA) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bv[r] = brow ? rb[r] : 0.0f;
+            }
+            (void)bv;
             __syncthreads();
             if (t + 1 < t_end) fetch(t + 1);   // in flight during this tile's products
+            // keep bits of this lane's 16 scores: scores 4 G .. 4 G + 3 are keys
+            // 4 jb .. 4 jb + 3, jb = k0 / 4 + 2 G + h
+            uint32_t keepm = 0xffffu;
+            if constexpr (EXTRA) {
+                if (a.drop_scale > 0.0f) {
+                    keepm = 0u;
+#pragma unroll
+                    for (int G = 0; G < 4; ++G) keepm |= bwd_keep4(a, b, hq, row, (k0 >> 2) + 2 * G + h) << (4 * G);
+                }
+            }
             f32x16_t s = {}, dp = {};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -188,9 +228,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
                 float ds = 0.0f;
                 if (key >= rlo && key <= rhi && sM[kk] != 0.0f) {
                     float dl;
-                    const float x = logit2<CAP>(a, s[r], dl);
+                    float x = logit2<CAP>(a, s[r], dl);
+                    float dpz = dp[r];
+                    if constexpr (EXTRA) {
+                        x = fmaf(bv[r], BW_LOG2E, x);
+                        if (a.drop_scale > 0.0f) dpz = (keepm >> r) & 1u ? dpz * a.drop_scale : 0.0f;
+                    }
                     const float p = fast_exp2(x - lse2);
-                    ds = p * (dp[r] - dlt) * dl;
+                    ds = p * (dpz - dlt) * dl;
                 }
                 s[r] = ds;
             }
@@ -219,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(FwdArgs a, const T*
 
 // 32 gradient accumulator registers per d block (dK and dV) plus K and V in
 // registers: one workgroup per CU at D = 128.
-template <typename T, int D, bool CAP>
+template <typename T, int D, bool CAP, bool EXTRA>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                                const float* __restrict__ delta, T* __restrict__ dk,
                                                                T* __restrict__ dv) {
@@ -270,13 +315,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
     TileRegs<D> rq, rg;
     int rlo_ = 1, rhi_ = 0;
     float rl_ = 0.0f, rd_ = 0.0f;
-    // step it's Q and dO rows, and the LSE, Delta and key range of its rows, into registers
+    float rb[EXTRA ? 16 : 1];   // mask of this lane's 16 scores of the step
+    // step it's Q and dO rows, the LSE, Delta and key range of its rows (and
+    // the mask values of this lane's scores) into registers
     auto fetch = [&](int it) {
         const int hq = kvh * a.group + it / nqt, r0 = 32 * (it % nqt);
         const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
         const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
         fetch_tile<T, D>(rq, qb + (int64_t)r0 * a.q_stride, a.q_stride, a.Lq - r0, tid);
         fetch_tile<T, D>(rg, gb + (int64_t)r0 * a.o_stride, a.o_stride, a.Lq - r0, tid);
+        if constexpr (EXTRA) {
+            if (a.bias) {
+                const float* bk = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] + (int64_t)keyc * a.bias_stride[3];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    rb[r] = row < a.Lq ? bk[(int64_t)row * a.bias_stride[2]] : 0.0f;
+                }
+            }
+        }
         if (tid < 32) {
             const int r = r0 + tid;
             rlo_ = 1; rhi_ = 0; rl_ = 0.0f; rd_ = 0.0f;
@@ -297,6 +354,33 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
         store_tile<D>(sQ, rq, tid);
         store_tile<D>(sG, rg, tid);
         if (tid < 32) { sLo[tid] = rlo_; sHi[tid] = rhi_; sL[tid] = rl_; sD[tid] = rd_; }
+        float bv[EXTRA ? 16 : 1];
+        if constexpr (EXTRA) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bv[r] = a.bias ? rb[r] : 0.0f;
+        }
+        (void)bv;
+        // keep bits of this lane's 16 scores (rows 8 (r / 4) + 4 h + r % 4 of the
+        // step, all at this lane's key).  The four lanes of keys 4 jb .. 4 jb + 3
+        // share each row's Philox block: lane e = key % 4 evaluates the blocks of
+        // rows r % 4 = e (bit 4 q + w of m: word w of row 4 q + e), and lane e'
+        // takes word e' of every row from the lane that holds it.
+        uint32_t keepm = 0xffffu;
+        if constexpr (EXTRA) {
+            if (a.drop_scale > 0.0f) {
+                const int hq = kvh * a.group + it / nqt, r0 = 32 * (it % nqt), e = lane & 3;
+                uint32_t m = 0u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) m |= bwd_keep4(a, b, hq, r0 + 8 * q + 4 * h + e, keyc >> 2) << (4 * q);
+                keepm = 0u;
+#pragma unroll
+                for (int src = 0; src < 4; ++src) {
+                    const uint32_t ms = (uint32_t)__shfl((int)m, (lane & ~3) | src);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) keepm |= ((ms >> (4 * q + e)) & 1u) << (4 * q + src);
+                }
+            }
+        }
         __syncthreads();
         if (nxt < nsteps) fetch(nxt);   // in flight during this step's products
         it = nxt;
@@ -319,14 +403,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                float p = 0.0f, dsv = 0.0f;
+                float pz = 0.0f, dsv = 0.0f;
                 if (kept && key >= los[i] && key <= his[i]) {
                     float dl;
-                    const float x = logit2<CAP>(a, s[r], dl);
-                    p = fast_exp2(x - ls[i]);
-                    dsv = p * (dp[r] - ds4[i]) * dl;
+                    float x = logit2<CAP>(a, s[r], dl);
+                    float z = 1.0f;
+                    if constexpr (EXTRA) {
+                        x = fmaf(bv[r], BW_LOG2E, x);
+                        if (a.drop_scale > 0.0f) z = (keepm >> r) & 1u ? a.drop_scale : 0.0f;
+                    }
+                    const float p = fast_exp2(x - ls[i]);
+                    dsv = p * (dp[r] * z - ds4[i]) * dl;
+                    pz = p * z;
                 }
-                s[r] = p;
+                s[r] = pz;
                 dp[r] = dsv;
             }
         }
@@ -361,37 +451,44 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
     }
 }
 
-template <typename T, int D, bool CAP>
+template <typename T, int D, bool CAP, bool EXTRA>
 hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                              hipStream_t s) {
     const T* g = static_cast<const T*>(dout);
     if (a.Lq > 0) {
-        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0, s, a,
-                           g, delta, static_cast<T*>(dq));
+        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0,
+                           s, a, g, delta, static_cast<T*>(dq));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0, s,
-                       a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0,
+                       s, a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_mfma_dd(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
+                              hipStream_t s) {
+    const bool cap = a.softcap > 0.0f, extra = a.bias != nullptr || a.drop_scale > 0.0f;
+    if (extra)
+        return cap ? launch_bwd_mfma_t<T, D, true, true>(a, dout, delta, dq, dk, dv, s)
+                   : launch_bwd_mfma_t<T, D, false, true>(a, dout, delta, dq, dk, dv, s);
+    return cap ? launch_bwd_mfma_t<T, D, true, false>(a, dout, delta, dq, dk, dv, s)
+               : launch_bwd_mfma_t<T, D, false, false>(a, dout, delta, dq, dk, dv, s);
 }
 
 template <typename T>
 hipError_t launch_bwd_mfma_d(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                              hipStream_t s) {
-    const bool cap = a.softcap > 0.0f;
-    if (a.D == 64)
-        return cap ? launch_bwd_mfma_t<T, 64, true>(a, dout, delta, dq, dk, dv, s)
-                   : launch_bwd_mfma_t<T, 64, false>(a, dout, delta, dq, dk, dv, s);
-    return cap ? launch_bwd_mfma_t<T, 128, true>(a, dout, delta, dq, dk, dv, s)
-               : launch_bwd_mfma_t<T, 128, false>(a, dout, delta, dq, dk, dv, s);
+    return a.D == 64 ? launch_bwd_mfma_dd<T, 64>(a, dout, delta, dq, dk, dv, s)
+                     : launch_bwd_mfma_dd<T, 128>(a, dout, delta, dq, dk, dv, s);
 }
 
 }  // namespace
 
 bool bwd_mfma_supported(const FwdArgs& a, int dtype) {
-    return (dtype == kBF16 || dtype == kF16) && (a.D == 64 || a.D == 128) && !a.bias && a.drop_scale == 0.0f &&
-           !a.seq_bounds && !a.row_pos && (a.Lq + 127) / 128 <= 65535 && (a.Lk + 127) / 128 <= 65535;   // grid z
+    return (dtype == kBF16 || dtype == kF16) && (a.D == 64 || a.D == 128) && !a.seq_bounds && !a.row_pos &&
+           (a.Lq + 127) / 128 <= 65535 && (a.Lk + 127) / 128 <= 65535;   // grid z
 }
 
 hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,

@@ -132,8 +132,8 @@ hipError_t launch_generic(const FwdArgs& a, int dtype, hipStream_t s);
 // dq, dk, dv are written in the input dtype (every element overwritten).
 hipError_t launch_backward(const FwdArgs& a, const void* dout, float* delta, void* dq, void* dk, void* dv,
                            int dtype, hipStream_t s);
-// The matrix-core backward (fp16/bf16, D 64/128, no additive mask, no dropout,
-// plain batches); delta must already hold <dO, O> per row.
+// The matrix-core backward (fp16/bf16, D 64/128, plain batches, any additive
+// mask and dropout); delta must already hold <dO, O> per row.
 bool bwd_mfma_supported(const FwdArgs& a, int dtype);
 hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                                 int dtype, hipStream_t s);
