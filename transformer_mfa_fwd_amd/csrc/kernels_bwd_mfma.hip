@@ -32,17 +32,27 @@ namespace {
 
 constexpr float BW_LOG2E = 1.4426950408889634f;
 
+// A 32-row tile of D 16-bit columns, rows unpadded, the 16-byte chunks of row r
+// permuted by XOR with swz(r).  Both read patterns then hit 64 distinct banks
+// per pass: row reads (16 rows at one chunk: swz is a permutation over any 16
+// consecutive rows at D = 128, over the 8 rows of each parity at D = 64) and
+// transposing reads (4 consecutive rows x 4 chunks: the row's low bits move
+// the chunk's high bits, the next two row bits its low bits).
 template <int D>
 struct BwLds {
-    static constexpr int RS = D * 2 + 16;    // bytes per 32-element-wide tile row, padded
+    static constexpr int RS = D * 2;         // bytes per tile row
     static constexpr int TILE = 32 * RS;     // one 32-row tile
+    static __device__ inline int swz(int r) {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
 };
 
 // A operand from a row-major 16-bit LDS tile: lane l takes row l % 32 and the
 // eight elements from column c0 + 8 (l / 32).
 template <typename T, int D>
 __device__ inline typename Mfma<T>::v8 rows_a(const char* tile, int lane, int c0) {
-    const char* p = tile + (lane & 31) * BwLds<D>::RS + (c0 + 8 * (lane >> 5)) * 2;
+    const int r = lane & 31;
+    const char* p = tile + r * BwLds<D>::RS + (((c0 >> 3) + (lane >> 5)) ^ BwLds<D>::swz(r)) * 16;
     return bitcast<typename Mfma<T>::v8>(*reinterpret_cast<const u32x4_t*>(p));
 }
 
@@ -56,9 +66,9 @@ __device__ inline typename Mfma<T>::v8 cols_a(const char* tile, int lane, int s,
     const int g = lane >> 4, j = lane & 15;
     const int row = 16 * s + 4 * (g >> 1) + (j >> 2);
     const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
-    const char* p = tile + row * BwLds<D>::RS + col * 2;
-    const i16x4_t lo = lds_read_tr16(p);
-    const i16x4_t hi = lds_read_tr16(p + 8 * BwLds<D>::RS);
+    const int c = col >> 3, w = (col & 7) * 2;
+    const i16x4_t lo = lds_read_tr16(tile + row * BwLds<D>::RS + ((c ^ BwLds<D>::swz(row)) * 16) + w);
+    const i16x4_t hi = lds_read_tr16(tile + (row + 8) * BwLds<D>::RS + ((c ^ BwLds<D>::swz(row + 8)) * 16) + w);
     const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return bitcast<typename Mfma<T>::v8>(v);
 }
@@ -78,9 +88,13 @@ __device__ inline void fetch_tile(TileRegs<D>& t, const T* src, int64_t stride, 
     constexpr int CPR = D / 8;
 #pragma unroll
     for (int n = 0; n < TileRegs<D>::N; ++n) {
+        // rows past the end read the last valid row (rows_valid >= 1) and are
+        // then zeroed: a select, not a branch
         const int c = tid + 256 * n, r = c / CPR, k = c % CPR;
-        t.v[n] = u32x4_t{0u, 0u, 0u, 0u};
-        if (r < rows_valid) t.v[n] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * stride + k * 8);
+        const int rc = r < rows_valid ? r : rows_valid - 1;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + (int64_t)rc * stride + k * 8);
+        const bool ok = r < rows_valid;
+        t.v[n] = u32x4_t{ok ? v[0] : 0u, ok ? v[1] : 0u, ok ? v[2] : 0u, ok ? v[3] : 0u};
     }
 }
 template <int D>
@@ -89,22 +103,23 @@ __device__ inline void store_tile(char* tile, const TileRegs<D>& t, int tid) {
 #pragma unroll
     for (int n = 0; n < TileRegs<D>::N; ++n) {
         const int c = tid + 256 * n, r = c / CPR, k = c % CPR;
-        *reinterpret_cast<u32x4_t*>(tile + r * BwLds<D>::RS + k * 16) = t.v[n];
+        *reinterpret_cast<u32x4_t*>(tile + r * BwLds<D>::RS + (k ^ BwLds<D>::swz(r)) * 16) = t.v[n];
     }
 }
 
-// logit and d logit / d dot of a raw dot product (scale, optional soft-cap),
-// the logit in base-2 units
+// logit of a raw dot product (scale, optional soft-cap) minus the row's LSE,
+// both in base-2 units, and d logit / d dot.  Without a cap that derivative is
+// the constant scale, which the kernels apply once to dQ and dK at the end
+// (dl = 1 here) and the logit is one fma.
 template <bool CAP>
-__device__ inline float logit2(const FwdArgs& a, float dot, float& dl) {
-    const float t = dot * a.scale;
+__device__ inline float logit2_minus(const FwdArgs& a, float dot, float lse2, float& dl) {
     if constexpr (CAP) {
-        const float th = tanhf(t / a.softcap);
+        const float th = tanhf(dot * a.scale / a.softcap);
         dl = a.scale * (1.0f - th * th);
-        return a.softcap * th * BW_LOG2E;
+        return fmaf(a.softcap * BW_LOG2E, th, -lse2);
     } else {
-        dl = a.scale;
-        return t * BW_LOG2E;
+        dl = 1.0f;
+        return fmaf(dot, a.score_to_log2, -lse2);   // score_to_log2 = scale * log2(e) without a cap
     }
 }
 
@@ -117,7 +132,7 @@ __device__ inline uint32_t bwd_keep4(const FwdArgs& a, int b, int hq, int row, i
 // EXTRA kernels also read the additive mask and apply dropout (each when the
 // call has it).
 template <typename T, int D, bool CAP, bool EXTRA>
-__global__ __launch_bounds__(256, (EXTRA && D == 128) ? 1 : 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+__global__ __launch_bounds__(256, ((EXTRA || CAP) && D == 128) ? 1 : 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                              const float* __restrict__ delta, T* __restrict__ dq) {
     typedef typename Mfma<T>::v8 v8;
     constexpr int NKS = D / 16, NDB = D / 32;
@@ -149,7 +164,7 @@ __global__ __launch_bounds__(256, (EXTRA && D == 128) ? 1 : 2) void bwd_dq_mfma_
         row_key_range<false>(a, row, rlo, rhi);
         const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + row];
         if (l == -INFINITY) { rlo = 1; rhi = 0; }   // no weight anywhere in the row
-        lse2 = l * BW_LOG2E;
+        lse2 = l == -INFINITY ? 0.0f : l * BW_LOG2E;   // finite: hidden logits are -inf
         dlt = delta[((int64_t)b * a.Hq + hq) * a.Lq + row];
     }
     int lo_blk, t0, t1, hi_blk;
@@ -225,19 +240,18 @@ __global__ __launch_bounds__(256, (EXTRA && D == 128) ? 1 : 2) void bwd_dq_mfma_
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int kk = 8 * (r >> 2) + 4 * h + (r & 3), key = k0 + kk;
-                float ds = 0.0f;
-                if (key >= rlo && key <= rhi && sM[kk] != 0.0f) {
-                    float dl;
-                    float x = logit2<CAP>(a, s[r], dl);
-                    float dpz = dp[r];
-                    if constexpr (EXTRA) {
-                        x = fmaf(bv[r], BW_LOG2E, x);
-                        if (a.drop_scale > 0.0f) dpz = (keepm >> r) & 1u ? dpz * a.drop_scale : 0.0f;
-                    }
-                    const float p = fast_exp2(x - lse2);
-                    ds = p * (dpz - dlt) * dl;
+                // a hidden score's logit becomes -inf, so its weight is exactly 0
+                // (a select on the logit, not a branch around the arithmetic)
+                float dl;
+                float x = logit2_minus<CAP>(a, s[r], lse2, dl);
+                float dpz = dp[r];
+                if constexpr (EXTRA) {
+                    x = fmaf(bv[r], BW_LOG2E, x);
+                    if (a.drop_scale > 0.0f) dpz = (keepm >> r) & 1u ? dpz * a.drop_scale : 0.0f;
                 }
-                s[r] = ds;
+                x = ((key >= rlo) & (key <= rhi) & (sM[kk] != 0.0f)) ? x : -INFINITY;   // & : no short circuit
+                const float p = fast_exp2(x);
+                s[r] = CAP ? p * (dpz - dlt) * dl : p * (dpz - dlt);
             }
 #pragma unroll
             for (int sx = 0; sx < 2; ++sx) {
@@ -247,7 +261,9 @@ __global__ __launch_bounds__(256, (EXTRA && D == 128) ? 1 : 2) void bwd_dq_mfma_
             }
         }
     }
-    // acc[mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's row
+    // acc[mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's row;
+    // without a cap the scale (d logit / d dot) is applied here
+    const float oscale = CAP ? 1.0f : a.scale;
     if (row <= i_last) {
         T* out = dq + ((int64_t)b * a.Lq + row) * a.q_stride + (int64_t)hq * D;
 #pragma unroll
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(256, (EXTRA && D == 128) ? 1 : 2) void bwd_dq_mfma_
             for (int j = 0; j < 4; ++j) {
                 T v4[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v4[i] = static_cast<T>(acc[mb][4 * j + i]);
+                for (int i = 0; i < 4; ++i) v4[i] = static_cast<T>(acc[mb][4 * j + i] * oscale);
                 *reinterpret_cast<uint2*>(out + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(v4);
             }
     }
@@ -265,7 +281,7 @@ __global__ __launch_bounds__(256, (EXTRA && D == 128) ? 1 : 2) void bwd_dq_mfma_
 // 32 gradient accumulator registers per d block (dK and dV) plus K and V in
 // registers: one workgroup per CU at D = 128.
 template <typename T, int D, bool CAP, bool EXTRA>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+__global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                                const float* __restrict__ delta, T* __restrict__ dk,
                                                                T* __restrict__ dv) {
     typedef typename Mfma<T>::v8 v8;
@@ -301,25 +317,41 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
 #pragma unroll
         for (int e = 0; e < 16; ++e) dka[mb][e] = dva[mb][e] = 0.0f;
 
-    // the (query head, 32-row tile) steps of this key block, in order, skipping
-    // tiles none of whose rows sees a key of the block
-    const int nqt = (a.Lq + 31) / 32, nsteps = a.group * nqt;
-    auto sees = [&](int it) {
-        const int r0 = 32 * (it % nqt), r_last = min(r0 + 31, a.Lq - 1);
-        int lo_f, hi_f, lo_l, hi_l;
-        row_key_range<false>(a, r0, lo_f, hi_f);
-        row_key_range<false>(a, r_last, lo_l, hi_l);
-        return !(lo_f > j_last || hi_l < j0 || lo_f > hi_l);
-    };
-    auto next_step = [&](int it) { while (it < nsteps && !sees(it)) ++it; return it; };
+    // The 32-row query tiles that can see a key of this block form one run
+    // [qt_lo, qt_hi]: both ends of a row's (clipped) key range are
+    // nondecreasing in the row, so "the tile's last row's range ends at or
+    // after j0" turns true once and "its first row's range starts by j_last"
+    // turns false once.  A tile inside the run whose rows see none of the keys
+    // only costs time (every row still applies its own range).  Steps walk
+    // (query head, tile) over the run for every query head of the group.
+    const int nqt = (a.Lq + 31) / 32;
+    int qt_lo, qt_hi;
+    {
+        int lo = 0, hi = nqt;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            int l0, h0;
+            row_key_range<false>(a, min(32 * mid + 31, a.Lq - 1), l0, h0);
+            if (h0 >= j0) hi = mid; else lo = mid + 1;
+        }
+        qt_lo = lo;
+        hi = nqt;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            int l0, h0;
+            row_key_range<false>(a, 32 * mid, l0, h0);
+            if (l0 > j_last) hi = mid; else lo = mid + 1;
+        }
+        qt_hi = lo - 1;
+    }
+    const int nv = qt_hi >= qt_lo ? qt_hi - qt_lo + 1 : 0, nsteps = a.group * nv;
     TileRegs<D> rq, rg;
     int rlo_ = 1, rhi_ = 0;
     float rl_ = 0.0f, rd_ = 0.0f;
     float rb[EXTRA ? 16 : 1];   // mask of this lane's 16 scores of the step
     // step it's Q and dO rows, the LSE, Delta and key range of its rows (and
     // the mask values of this lane's scores) into registers
-    auto fetch = [&](int it) {
-        const int hq = kvh * a.group + it / nqt, r0 = 32 * (it % nqt);
+    auto fetch = [&](int hq, int r0) {
         const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
         const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
         fetch_tile<T, D>(rq, qb + (int64_t)r0 * a.q_stride, a.q_stride, a.Lq - r0, tid);
@@ -341,15 +373,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
                 row_key_range<false>(a, r, rlo_, rhi_);
                 const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + r];
                 if (l == -INFINITY) { rlo_ = 1; rhi_ = 0; }
-                rl_ = l * BW_LOG2E;
+                rl_ = l == -INFINITY ? 0.0f : l * BW_LOG2E;   // finite: hidden logits are -inf
                 rd_ = delta[((int64_t)b * a.Hq + hq) * a.Lq + r];
             }
         }
     };
-    int it = next_step(0);
-    if (it < nsteps) fetch(it);
-    while (it < nsteps) {
-        const int nxt = next_step(it + 1);
+    // step (head hq, tile rows from r0); the next step's (nhq, nr0)
+    int hq = kvh * a.group, r0 = 32 * qt_lo;
+    if (nsteps > 0) fetch(hq, r0);
+    for (int it = 0; it < nsteps; ++it) {
+        int nhq = hq, nr0 = r0 + 32;
+        if (nr0 > 32 * qt_hi) { nr0 = 32 * qt_lo; ++nhq; }
         __syncthreads();   // the previous step's tiles are no longer read
         store_tile<D>(sQ, rq, tid);
         store_tile<D>(sG, rg, tid);
@@ -368,7 +402,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
         uint32_t keepm = 0xffffu;
         if constexpr (EXTRA) {
             if (a.drop_scale > 0.0f) {
-                const int hq = kvh * a.group + it / nqt, r0 = 32 * (it % nqt), e = lane & 3;
+                const int e = lane & 3;
                 uint32_t m = 0u;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) m |= bwd_keep4(a, b, hq, r0 + 8 * q + 4 * h + e, keyc >> 2) << (4 * q);
@@ -382,8 +416,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
             }
         }
         __syncthreads();
-        if (nxt < nsteps) fetch(nxt);   // in flight during this step's products
-        it = nxt;
+        if (it + 1 < nsteps) fetch(nhq, nr0);   // in flight during this step's products
         f32x16_t s = {}, dp = {};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -403,21 +436,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                float pz = 0.0f, dsv = 0.0f;
-                if (kept && key >= los[i] && key <= his[i]) {
-                    float dl;
-                    float x = logit2<CAP>(a, s[r], dl);
-                    float z = 1.0f;
-                    if constexpr (EXTRA) {
-                        x = fmaf(bv[r], BW_LOG2E, x);
-                        if (a.drop_scale > 0.0f) z = (keepm >> r) & 1u ? a.drop_scale : 0.0f;
-                    }
-                    const float p = fast_exp2(x - ls[i]);
-                    dsv = p * (dp[r] * z - ds4[i]) * dl;
-                    pz = p * z;
+                // a hidden score's logit becomes -inf, so its weight is exactly 0
+                // (a select on the logit, not a branch around the arithmetic)
+                float dl;
+                float x = logit2_minus<CAP>(a, s[r], ls[i], dl);
+                float z = 1.0f;
+                if constexpr (EXTRA) {
+                    x = fmaf(bv[r], BW_LOG2E, x);
+                    if (a.drop_scale > 0.0f) z = (keepm >> r) & 1u ? a.drop_scale : 0.0f;
                 }
-                s[r] = pz;
-                dp[r] = dsv;
+                x = (kept & (key >= los[i]) & (key <= his[i])) ? x : -INFINITY;   // & : no short circuit
+                const float p = fast_exp2(x);
+                if constexpr (EXTRA) dp[r] = CAP ? p * (dp[r] * z - ds4[i]) * dl : p * (dp[r] * z - ds4[i]);
+                else dp[r] = CAP ? p * (dp[r] - ds4[i]) * dl : p * (dp[r] - ds4[i]);
+                s[r] = EXTRA ? p * z : p;
             }
         }
 #pragma unroll
@@ -430,8 +462,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
                 dka[mb] = Mfma<T>::mma32(cols_a<T, D>(sQ, lane, sx, mb), dop, dka[mb]);
             }
         }
+        hq = nhq;
+        r0 = nr0;
     }
-    // dka / dva [mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's key
+    // dka / dva [mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's key;
+    // without a cap the scale (d logit / d dot) is applied to dK here
+    const float oscale = CAP ? 1.0f : a.scale;
     if (key <= j_last) {
         T* ko = dk + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
         T* vo = dv + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
@@ -442,7 +478,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_mfma_kernel(Fwd
                 T k4[4], v4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    k4[i] = static_cast<T>(dka[mb][4 * j + i]);
+                    k4[i] = static_cast<T>(dka[mb][4 * j + i] * oscale);
                     v4[i] = static_cast<T>(dva[mb][4 * j + i]);
                 }
                 *reinterpret_cast<uint2*>(ko + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(k4);
