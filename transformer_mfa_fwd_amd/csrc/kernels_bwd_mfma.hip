@@ -281,17 +281,22 @@ __global__ __launch_bounds__(256, ((EXTRA || CAP) && D == 128) ? 1 : 2) void bwd
 // 32 gradient accumulator registers per d block (dK and dV) plus K and V in
 // registers: one workgroup per CU at D = 128.
 template <typename T, int D, bool CAP, bool EXTRA>
-__global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                                const float* __restrict__ delta, T* __restrict__ dk,
                                                                T* __restrict__ dv) {
     typedef typename Mfma<T>::v8 v8;
     constexpr int NKS = D / 16, NDB = D / 32;
-    __shared__ __attribute__((aligned(16))) char sQ[BwLds<D>::TILE];
-    __shared__ __attribute__((aligned(16))) char sG[BwLds<D>::TILE];   // dO rows
-    __shared__ __attribute__((aligned(16))) float sL[32];   // LSE (base 2) of the tile's rows
-    __shared__ __attribute__((aligned(16))) float sD[32];   // Delta
-    __shared__ __attribute__((aligned(16))) int sLo[32];    // key range of each row
-    __shared__ __attribute__((aligned(16))) int sHi[32];
+    // Three buffers of the per-step data: the Q and dO tiles, and the LSE (base
+    // 2), Delta and key range of their rows.  Step u lives in buffer u % 3: it
+    // is stored two steps ahead, its S and dP are formed one step ahead, and its
+    // softmax and dV/dK products run in its own step.
+    constexpr int NBUF = 3;
+    __shared__ __attribute__((aligned(16))) char sQ[NBUF][BwLds<D>::TILE];
+    __shared__ __attribute__((aligned(16))) char sG[NBUF][BwLds<D>::TILE];   // dO rows
+    __shared__ __attribute__((aligned(16))) float sL[NBUF][32];
+    __shared__ __attribute__((aligned(16))) float sD[NBUF][32];
+    __shared__ __attribute__((aligned(16))) int sLo[NBUF][32];
+    __shared__ __attribute__((aligned(16))) int sHi[NBUF][32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     // grid (Hkv, B, key blocks), the first key block first: under a causal mask
@@ -345,27 +350,21 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
         qt_hi = lo - 1;
     }
     const int nv = qt_hi >= qt_lo ? qt_hi - qt_lo + 1 : 0, nsteps = a.group * nv;
+
+    // step u -> (query head, first row): heads in order, the run's tiles in order
+    auto step_hq = [&](int u) { return kvh * a.group + u / nv; };
+    auto step_r0 = [&](int u) { return 32 * (qt_lo + u % nv); };
+
     TileRegs<D> rq, rg;
     int rlo_ = 1, rhi_ = 0;
     float rl_ = 0.0f, rd_ = 0.0f;
-    float rb[EXTRA ? 16 : 1];   // mask of this lane's 16 scores of the step
-    // step it's Q and dO rows, the LSE, Delta and key range of its rows (and
-    // the mask values of this lane's scores) into registers
-    auto fetch = [&](int hq, int r0) {
+    // step u's Q and dO rows, and the LSE, Delta and key range of its rows, into registers
+    auto fetch = [&](int u) {
+        const int hq = step_hq(u), r0 = step_r0(u);
         const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
         const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
         fetch_tile<T, D>(rq, qb + (int64_t)r0 * a.q_stride, a.q_stride, a.Lq - r0, tid);
         fetch_tile<T, D>(rg, gb + (int64_t)r0 * a.o_stride, a.o_stride, a.Lq - r0, tid);
-        if constexpr (EXTRA) {
-            if (a.bias) {
-                const float* bk = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] + (int64_t)keyc * a.bias_stride[3];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    rb[r] = row < a.Lq ? bk[(int64_t)row * a.bias_stride[2]] : 0.0f;
-                }
-            }
-        }
         if (tid < 32) {
             const int r = r0 + tid;
             rlo_ = 1; rhi_ = 0; rl_ = 0.0f; rd_ = 0.0f;
@@ -378,92 +377,158 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
             }
         }
     };
-    // step (head hq, tile rows from r0); the next step's (nhq, nr0)
-    int hq = kvh * a.group, r0 = 32 * qt_lo;
-    if (nsteps > 0) fetch(hq, r0);
-    for (int it = 0; it < nsteps; ++it) {
-        int nhq = hq, nr0 = r0 + 32;
-        if (nr0 > 32 * qt_hi) { nr0 = 32 * qt_lo; ++nhq; }
-        __syncthreads();   // the previous step's tiles are no longer read
-        store_tile<D>(sQ, rq, tid);
-        store_tile<D>(sG, rg, tid);
-        if (tid < 32) { sLo[tid] = rlo_; sHi[tid] = rhi_; sL[tid] = rl_; sD[tid] = rd_; }
-        float bv[EXTRA ? 16 : 1];
-        if constexpr (EXTRA) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) bv[r] = a.bias ? rb[r] : 0.0f;
-        }
-        (void)bv;
-        // keep bits of this lane's 16 scores (rows 8 (r / 4) + 4 h + r % 4 of the
-        // step, all at this lane's key).  The four lanes of keys 4 jb .. 4 jb + 3
-        // share each row's Philox block: lane e = key % 4 evaluates the blocks of
-        // rows r % 4 = e (bit 4 q + w of m: word w of row 4 q + e), and lane e'
-        // takes word e' of every row from the lane that holds it.
-        uint32_t keepm = 0xffffu;
-        if constexpr (EXTRA) {
-            if (a.drop_scale > 0.0f) {
-                const int e = lane & 3;
-                uint32_t m = 0u;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) m |= bwd_keep4(a, b, hq, r0 + 8 * q + 4 * h + e, keyc >> 2) << (4 * q);
-                keepm = 0u;
-#pragma unroll
-                for (int src = 0; src < 4; ++src) {
-                    const uint32_t ms = (uint32_t)__shfl((int)m, (lane & ~3) | src);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) keepm |= ((ms >> (4 * q + e)) & 1u) << (4 * q + src);
-                }
-            }
-        }
-        __syncthreads();
-        if (it + 1 < nsteps) fetch(nhq, nr0);   // in flight during this step's products
-        f32x16_t s = {}, dp = {};
+    // the fetched step into buffer BUF
+    auto store = [&](int buf) {
+        store_tile<D>(sQ[buf], rq, tid);
+        store_tile<D>(sG[buf], rg, tid);
+        if (tid < 32) { sLo[buf][tid] = rlo_; sHi[buf][tid] = rhi_; sL[buf][tid] = rl_; sD[buf][tid] = rd_; }
+    };
+
+    // S and dP of the step in buffer BUF: the MFMAs of k-step ks
+    auto sdp_mfma = [&](f32x16_t& sn, f32x16_t& dn, int buf, int ks) {
+        sn = Mfma<T>::mma32(rows_a<T, D>(sQ[buf], lane, 16 * ks), kop[ks], sn);
+        dn = Mfma<T>::mma32(rows_a<T, D>(sG[buf], lane, 16 * ks), vop[ks], dn);
+    };
+    // A operands of S and dP (Q and dO rows) of the step in buffer BUF, read
+    // early so that their LDS latency hides behind the softmax before them
+    v8 qa[NKS], ga[NKS];
+    auto read_sdp = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            s = Mfma<T>::mma32(rows_a<T, D>(sQ, lane, 16 * ks), kop[ks], s);
-            dp = Mfma<T>::mma32(rows_a<T, D>(sG, lane, 16 * ks), vop[ks], dp);
+            qa[ks] = rows_a<T, D>(sQ[buf], lane, 16 * ks);
+            ga[ks] = rows_a<T, D>(sG[buf], lane, 16 * ks);
         }
-        // element r of lane l: tile row 8 (r / 4) + 4 h + r % 4 for this lane's key
+    };
+
+    if (nsteps > 0) {
+        // prologue: steps 0 and 1 stored, step 2 fetched, S and dP of step 0
+        fetch(0);
+        store(0);
+        if (nsteps > 1) { fetch(1); store(1); }
+        if (nsteps > 2) fetch(2);
+        __syncthreads();
+        f32x16_t sc = {}, dc = {};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m0 = 8 * j + 4 * h;
-            const int4 lo4 = *reinterpret_cast<const int4*>(&sLo[m0]);
-            const int4 hi4 = *reinterpret_cast<const int4*>(&sHi[m0]);
-            const float4 l4 = *reinterpret_cast<const float4*>(&sL[m0]);
-            const float4 d4 = *reinterpret_cast<const float4*>(&sD[m0]);
-            const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
-            const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * j + i;
-                // a hidden score's logit becomes -inf, so its weight is exactly 0
-                // (a select on the logit, not a branch around the arithmetic)
-                float dl;
-                float x = logit2_minus<CAP>(a, s[r], ls[i], dl);
-                float z = 1.0f;
-                if constexpr (EXTRA) {
-                    x = fmaf(bv[r], BW_LOG2E, x);
-                    if (a.drop_scale > 0.0f) z = (keepm >> r) & 1u ? a.drop_scale : 0.0f;
-                }
-                x = (kept & (key >= los[i]) & (key <= his[i])) ? x : -INFINITY;   // & : no short circuit
-                const float p = fast_exp2(x);
-                if constexpr (EXTRA) dp[r] = CAP ? p * (dp[r] * z - ds4[i]) * dl : p * (dp[r] * z - ds4[i]);
-                else dp[r] = CAP ? p * (dp[r] - ds4[i]) * dl : p * (dp[r] - ds4[i]);
-                s[r] = EXTRA ? p * z : p;
-            }
-        }
-#pragma unroll
-        for (int sx = 0; sx < 2; ++sx) {
-            const v8 pop = pack8_at<T>(s, 8 * sx);
-            const v8 dop = pack8_at<T>(dp, 8 * sx);
+        for (int ks = 0; ks < NKS; ++ks) sdp_mfma(sc, dc, 0, ks);
+
+        int buf = 0;   // buffer of step it
+        for (int it = 0; it < nsteps; ++it) {
+            const int bn = buf == 2 ? 0 : buf + 1, bn2 = bn == 2 ? 0 : bn + 1;   // steps it + 1, it + 2
+            const int hq = step_hq(it), r0 = step_r0(it);
+            read_sdp(bn);   // step it + 1 (stale after the last step; discarded)
+            // A operands of this step's dV and dK products, k-half 0 now and
+            // k-half 1 halfway through the softmax
+            v8 cg[2][NDB], cq[2][NDB];
 #pragma unroll
             for (int mb = 0; mb < NDB; ++mb) {
-                dva[mb] = Mfma<T>::mma32(cols_a<T, D>(sG, lane, sx, mb), pop, dva[mb]);
-                dka[mb] = Mfma<T>::mma32(cols_a<T, D>(sQ, lane, sx, mb), dop, dka[mb]);
+                cg[0][mb] = cols_a<T, D>(sG[buf], lane, 0, mb);
+                cq[0][mb] = cols_a<T, D>(sQ[buf], lane, 0, mb);
             }
+            if (it + 2 < nsteps) store(bn2);   // its buffer was last read by step it - 1
+            if (it + 3 < nsteps) fetch(it + 3);
+
+            // per-step extras of step it: additive mask values and dropout keep bits
+            float bv[EXTRA ? 16 : 1];
+            uint32_t keepm = 0xffffu;
+            if constexpr (EXTRA) {
+                if (a.bias) {
+                    const float* bk = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] + (int64_t)keyc * a.bias_stride[3];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        bv[r] = row < a.Lq ? bk[(int64_t)row * a.bias_stride[2]] : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) bv[r] = 0.0f;
+                }
+                // keep bits of this lane's 16 scores (rows 8 (r / 4) + 4 h + r % 4
+                // of the step, all at this lane's key).  The four lanes of keys
+                // 4 jb .. 4 jb + 3 share each row's Philox block: lane e = key % 4
+                // evaluates the blocks of rows r % 4 = e (bit 4 q + w of m: word w
+                // of row 4 q + e), and lane e' takes word e' of every row from the
+                // lane that holds it.
+                if (a.drop_scale > 0.0f) {
+                    const int e = lane & 3;
+                    uint32_t m = 0u;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) m |= bwd_keep4(a, b, hq, r0 + 8 * q + 4 * h + e, keyc >> 2) << (4 * q);
+                    keepm = 0u;
+#pragma unroll
+                    for (int src = 0; src < 4; ++src) {
+                        const uint32_t ms = (uint32_t)__shfl((int)m, (lane & ~3) | src);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) keepm |= ((ms >> (4 * q + e)) & 1u) << (4 * q + src);
+                    }
+                }
+            }
+            (void)bv;
+
+            // S and dP of step it + 1 on the matrix cores, and beside them the
+            // softmax of step it: element r of lane l is tile row
+            // 8 (r / 4) + 4 h + r % 4 at this lane's key.  After the last step
+            // the products read a stale buffer and are discarded (no branch, so
+            // that the two interleave).
+            f32x16_t sn = {}, dn = {};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j == 2) {
+#pragma unroll
+                    for (int mb = 0; mb < NDB; ++mb) {
+                        cg[1][mb] = cols_a<T, D>(sG[buf], lane, 1, mb);
+                        cq[1][mb] = cols_a<T, D>(sQ[buf], lane, 1, mb);
+                    }
+                }
+                const int m0 = 8 * j + 4 * h;
+                const int4 lo4 = *reinterpret_cast<const int4*>(&sLo[buf][m0]);
+                const int4 hi4 = *reinterpret_cast<const int4*>(&sHi[buf][m0]);
+                const float4 l4 = *reinterpret_cast<const float4*>(&sL[buf][m0]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&sD[buf][m0]);
+                const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+                const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * j + i;
+                    if ((r & 1) == 0 && NKS == 8) {
+                        sn = Mfma<T>::mma32(qa[r >> 1], kop[r >> 1], sn);
+                        dn = Mfma<T>::mma32(ga[r >> 1], vop[r >> 1], dn);
+                    }
+                    if ((r & 3) == 0 && NKS == 4) {
+                        sn = Mfma<T>::mma32(qa[r >> 2], kop[r >> 2], sn);
+                        dn = Mfma<T>::mma32(ga[r >> 2], vop[r >> 2], dn);
+                    }
+                    // a hidden score's logit becomes -inf, so its weight is exactly 0
+                    // (a select on the logit, not a branch around the arithmetic)
+                    float dl;
+                    float x = logit2_minus<CAP>(a, sc[r], ls[i], dl);
+                    float z = 1.0f;
+                    if constexpr (EXTRA) {
+                        x = fmaf(bv[r], BW_LOG2E, x);
+                        if (a.drop_scale > 0.0f) z = (keepm >> r) & 1u ? a.drop_scale : 0.0f;
+                    }
+                    x = (kept & (key >= los[i]) & (key <= his[i])) ? x : -INFINITY;   // & : no short circuit
+                    const float p = fast_exp2(x);
+                    if constexpr (EXTRA) dc[r] = CAP ? p * (dc[r] * z - ds4[i]) * dl : p * (dc[r] * z - ds4[i]);
+                    else dc[r] = CAP ? p * (dc[r] - ds4[i]) * dl : p * (dc[r] - ds4[i]);
+                    sc[r] = EXTRA ? p * z : p;
+                }
+            }
+            // dV += dO^T P and dK += Q^T dS of step it
+#pragma unroll
+            for (int sx = 0; sx < 2; ++sx) {
+                const v8 pop = pack8_at<T>(sc, 8 * sx);
+                const v8 dop = pack8_at<T>(dc, 8 * sx);
+#pragma unroll
+                for (int mb = 0; mb < NDB; ++mb) {
+                    dva[mb] = Mfma<T>::mma32(cg[sx][mb], pop, dva[mb]);
+                    dka[mb] = Mfma<T>::mma32(cq[sx][mb], dop, dka[mb]);
+                }
+            }
+            __syncthreads();   // step it + 2 stored; step it's buffer free for step it + 3
+            sc = sn;
+            dc = dn;
+            buf = bn;
         }
-        hq = nhq;
-        r0 = nr0;
     }
     // dka / dva [mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's key;
     // without a cap the scale (d logit / d dot) is applied to dK here
