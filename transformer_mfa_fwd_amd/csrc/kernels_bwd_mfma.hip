@@ -22,6 +22,9 @@
 // An accumulator's 16 elements per lane serve as the B operand of the next
 // product in the order the transposing reads deliver the A operand's rows, so
 // no score crosses lanes.  Each gradient element has one writer (no atomics).
+// The dK/dV kernel, and the dQ kernel of calls with a mask or dropout
+// (bwd_dq_pipe_mfma_kernel), run a software pipeline: the next tile's S and dP
+// MFMAs beside the current tile's softmax, over three LDS buffers.
 #include "mfa_device.h"
 #include "mfa_internal.h"
 
@@ -129,16 +132,135 @@ __device__ inline uint32_t bwd_keep4(const FwdArgs& a, int b, int hq, int row, i
     return a.drop_scale > 0.0f ? dropout_keep4(a, b, hq, row, jb) : 0xfu;
 }
 
-// EXTRA kernels also read the additive mask and apply dropout (each when the
-// call has it).
-template <typename T, int D, bool CAP, bool EXTRA>
-__global__ __launch_bounds__(256, ((EXTRA || CAP) && D == 128) ? 1 : 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+// dQ of calls without an additive mask or dropout (two workgroups per CU but
+// with a soft-cap at D = 128).
+template <typename T, int D, bool CAP>
+__global__ __launch_bounds__(256, (CAP && D == 128) ? 1 : 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                              const float* __restrict__ delta, T* __restrict__ dq) {
     typedef typename Mfma<T>::v8 v8;
     constexpr int NKS = D / 16, NDB = D / 32;
     __shared__ __attribute__((aligned(16))) char sK[BwLds<D>::TILE];
     __shared__ __attribute__((aligned(16))) char sV[BwLds<D>::TILE];
     __shared__ float sM[32];   // 1: key kept (in range of the axis and of the key mask)
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    // grid (Hq, B, query blocks), the latest query block first: under a causal
+    // mask it walks the most key tiles
+    const int hq = blockIdx.x, b = blockIdx.y, kvh = hq / a.group;
+    const int i0 = (gridDim.z - 1 - blockIdx.z) * 128, i_last = min(i0 + 127, a.Lq - 1);
+    const int row = i0 + 32 * wave + (lane & 31);
+    const int rowc = row <= i_last ? row : i_last;
+    const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
+    const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
+    const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+    const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+
+    v8 qop[NKS], gop[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        qop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(qb + (int64_t)rowc * a.q_stride + 16 * ks + 8 * h));
+        gop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(gb + (int64_t)rowc * a.o_stride + 16 * ks + 8 * h));
+    }
+    int rlo = 1, rhi = 0;
+    float lse2 = 0.0f, dlt = 0.0f;
+    if (row <= i_last) {
+        row_key_range<false>(a, row, rlo, rhi);
+        const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + row];
+        if (l == -INFINITY) { rlo = 1; rhi = 0; }   // no weight anywhere in the row
+        lse2 = l == -INFINITY ? 0.0f : l * BW_LOG2E;   // finite: hidden logits are -inf
+        dlt = delta[((int64_t)b * a.Hq + hq) * a.Lq + row];
+    }
+    int lo_blk, t0, t1, hi_blk;
+    row_key_range<false>(a, i0, lo_blk, t0);
+    row_key_range<false>(a, i_last, t1, hi_blk);
+
+    f32x16_t acc[NDB];
+#pragma unroll
+    for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
+
+    if (lo_blk <= hi_blk) {
+        const int t_first = lo_blk / 32, t_end = hi_blk / 32 + 1;
+        TileRegs<D> rk, rv;
+        float rm = 0.0f;
+        // tile t's K, V and key-kept flags into registers
+        auto fetch = [&](int t) {
+            const int k0 = 32 * t;
+            fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            fetch_tile<T, D>(rv, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            if (tid < 32) {
+                const int key = k0 + tid;
+                rm = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
+            }
+        };
+        fetch(t_first);
+        for (int t = t_first; t < t_end; ++t) {
+            const int k0 = 32 * t;
+            __syncthreads();   // the previous tile is no longer read
+            store_tile<D>(sK, rk, tid);
+            store_tile<D>(sV, rv, tid);
+            if (tid < 32) sM[tid] = rm;
+            __syncthreads();
+            if (t + 1 < t_end) fetch(t + 1);   // in flight during this tile's products
+            f32x16_t s = {}, dp = {};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                s = Mfma<T>::mma32(rows_a<T, D>(sK, lane, 16 * ks), qop[ks], s);
+                dp = Mfma<T>::mma32(rows_a<T, D>(sV, lane, 16 * ks), gop[ks], dp);
+            }
+            // element r of lane l: key k0 + 8 (r / 4) + 4 h + r % 4 of this lane's row
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r >> 2) + 4 * h + (r & 3), key = k0 + kk;
+                // a hidden score's logit becomes -inf, so its weight is exactly 0
+                // (a select on the logit, not a branch around the arithmetic)
+                float dl;
+                float x = logit2_minus<CAP>(a, s[r], lse2, dl);
+                x = ((key >= rlo) & (key <= rhi) & (sM[kk] != 0.0f)) ? x : -INFINITY;   // & : no short circuit
+                const float p = fast_exp2(x);
+                s[r] = CAP ? p * (dp[r] - dlt) * dl : p * (dp[r] - dlt);
+            }
+#pragma unroll
+            for (int sx = 0; sx < 2; ++sx) {
+                const v8 bop = pack8_at<T>(s, 8 * sx);
+#pragma unroll
+                for (int mb = 0; mb < NDB; ++mb) acc[mb] = Mfma<T>::mma32(cols_a<T, D>(sK, lane, sx, mb), bop, acc[mb]);
+            }
+        }
+    }
+    // acc[mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's row;
+    // without a cap the scale (d logit / d dot) is applied here
+    const float oscale = CAP ? 1.0f : a.scale;
+    if (row <= i_last) {
+        T* out = dq + ((int64_t)b * a.Lq + row) * a.q_stride + (int64_t)hq * D;
+#pragma unroll
+        for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                T v4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v4[i] = static_cast<T>(acc[mb][4 * j + i] * oscale);
+                *reinterpret_cast<uint2*>(out + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(v4);
+            }
+    }
+}
+
+// dQ with the additive mask and dropout: a software pipeline over three LDS
+// buffers, as in the dK/dV kernel (one workgroup per CU at D = 128, where
+// these calls' registers leave one anyway; the plain kernel above keeps two).
+template <typename T, int D, bool CAP, bool EXTRA>
+__global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+                                                             const float* __restrict__ delta, T* __restrict__ dq) {
+    typedef typename Mfma<T>::v8 v8;
+    constexpr int NKS = D / 16, NDB = D / 32;
+    // Three buffers of the per-tile data (K and V tiles, key-kept flags): tile
+    // u lives in buffer u % 3, stored two tiles ahead; its S^T and dP^T are
+    // formed one tile ahead, its softmax and dQ product in its own iteration.
+    constexpr int NBUF = 3;
+    __shared__ __attribute__((aligned(16))) char sK[NBUF][BwLds<D>::TILE];
+    __shared__ __attribute__((aligned(16))) char sV[NBUF][BwLds<D>::TILE];
+    __shared__ float sM[NBUF][32];   // 1: key kept (in range of the axis and of the key mask)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     // grid (Hq, B, query blocks), the latest query block first: under a causal
@@ -182,83 +304,121 @@ __global__ __launch_bounds__(256, ((EXTRA || CAP) && D == 128) ? 1 : 2) void bwd
         for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
 
     if (lo_blk <= hi_blk) {
-        const int t_first = lo_blk / 32, t_end = hi_blk / 32 + 1;
+        const int t_first = lo_blk / 32, n_t = hi_blk / 32 + 1 - t_first;
         TileRegs<D> rk, rv;
         float rm = 0.0f;
-        float rb[EXTRA ? 16 : 1];   // mask of this lane's 16 scores of the tile
-        // tile t's K, V, key-kept flags (and mask values) into registers
-        auto fetch = [&](int t) {
-            const int k0 = 32 * t;
+        // tile t_first + u's K, V and key-kept flags into registers
+        auto fetch = [&](int u) {
+            const int k0 = 32 * (t_first + u);
             fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
             fetch_tile<T, D>(rv, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
             if (tid < 32) {
                 const int key = k0 + tid;
                 rm = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
             }
-            if constexpr (EXTRA) {
-                if (brow) {
+        };
+        auto store = [&](int buf) {
+            store_tile<D>(sK[buf], rk, tid);
+            store_tile<D>(sV[buf], rv, tid);
+            if (tid < 32) sM[buf][tid] = rm;
+        };
+        // A operands of S^T and dP^T (K and V rows) of the tile in buffer BUF
+        v8 ka[NKS], va[NKS];
+        auto read_sdp = [&](int buf) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        rb[r] = key < a.Lk ? brow[(int64_t)key * a.bias_stride[3]] : 0.0f;
-                    }
-                }
+            for (int ks = 0; ks < NKS; ++ks) {
+                ka[ks] = rows_a<T, D>(sK[buf], lane, 16 * ks);
+                va[ks] = rows_a<T, D>(sV[buf], lane, 16 * ks);
             }
         };
-        fetch(t_first);
-        for (int t = t_first; t < t_end; ++t) {
-            const int k0 = 32 * t;
-            __syncthreads();   // the previous tile is no longer read
-            store_tile<D>(sK, rk, tid);
-            store_tile<D>(sV, rv, tid);
-            if (tid < 32) sM[tid] = rm;
-            float bv[EXTRA ? 16 : 1];
-            if constexpr (EXTRA) {
+
+        // prologue: tiles 0 and 1 stored, tile 2 fetched, S^T and dP^T of tile 0
+        fetch(0);
+        store(0);
+        if (n_t > 1) { fetch(1); store(1); }
+        if (n_t > 2) fetch(2);
+        __syncthreads();
+        f32x16_t sc = {}, dc = {};
+        read_sdp(0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) bv[r] = brow ? rb[r] : 0.0f;
-            }
-            (void)bv;
-            __syncthreads();
-            if (t + 1 < t_end) fetch(t + 1);   // in flight during this tile's products
-            // keep bits of this lane's 16 scores: scores 4 G .. 4 G + 3 are keys
-            // 4 jb .. 4 jb + 3, jb = k0 / 4 + 2 G + h
+        for (int ks = 0; ks < NKS; ++ks) {
+            sc = Mfma<T>::mma32(ka[ks], qop[ks], sc);
+            dc = Mfma<T>::mma32(va[ks], gop[ks], dc);
+        }
+
+        int buf = 0;   // buffer of tile u
+        for (int u = 0; u < n_t; ++u) {
+            const int bn = buf == 2 ? 0 : buf + 1, bn2 = bn == 2 ? 0 : bn + 1;
+            const int k0 = 32 * (t_first + u);
+            read_sdp(bn);   // tile u + 1 (stale after the last tile; discarded)
+            // A operands of this tile's dQ product, k-half 0 now, k-half 1
+            // halfway through the softmax
+            v8 ck[2][NDB];
+#pragma unroll
+            for (int mb = 0; mb < NDB; ++mb) ck[0][mb] = cols_a<T, D>(sK[buf], lane, 0, mb);
+            if (u + 2 < n_t) store(bn2);   // its buffer was last read by tile u - 1
+            if (u + 3 < n_t) fetch(u + 3);
+
+            // mask values and dropout keep bits of this lane's 16 scores: scores
+            // 4 G .. 4 G + 3 are keys 4 jb .. 4 jb + 3, jb = k0 / 4 + 2 G + h
+            float bv[EXTRA ? 16 : 1];
             uint32_t keepm = 0xffffu;
             if constexpr (EXTRA) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    bv[r] = (brow && key < a.Lk) ? brow[(int64_t)key * a.bias_stride[3]] : 0.0f;
+                }
                 if (a.drop_scale > 0.0f) {
                     keepm = 0u;
 #pragma unroll
                     for (int G = 0; G < 4; ++G) keepm |= bwd_keep4(a, b, hq, row, (k0 >> 2) + 2 * G + h) << (4 * G);
                 }
             }
-            f32x16_t s = {}, dp = {};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                s = Mfma<T>::mma32(rows_a<T, D>(sK, lane, 16 * ks), qop[ks], s);
-                dp = Mfma<T>::mma32(rows_a<T, D>(sV, lane, 16 * ks), gop[ks], dp);
-            }
-            // element r of lane l: key k0 + 8 (r / 4) + 4 h + r % 4 of this lane's row
+            (void)bv;
+
+            // S^T and dP^T of tile u + 1 beside the softmax of tile u: element r
+            // of lane l is key k0 + 8 (r / 4) + 4 h + r % 4 of this lane's row
+            f32x16_t sn = {}, dn = {};
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                if ((r & 1) == 0 && NKS == 8) {
+                    sn = Mfma<T>::mma32(ka[r >> 1], qop[r >> 1], sn);
+                    dn = Mfma<T>::mma32(va[r >> 1], gop[r >> 1], dn);
+                }
+                if ((r & 3) == 0 && NKS == 4) {
+                    sn = Mfma<T>::mma32(ka[r >> 2], qop[r >> 2], sn);
+                    dn = Mfma<T>::mma32(va[r >> 2], gop[r >> 2], dn);
+                }
+                if (r == 8) {
+#pragma unroll
+                    for (int mb = 0; mb < NDB; ++mb) ck[1][mb] = cols_a<T, D>(sK[buf], lane, 1, mb);
+                }
                 const int kk = 8 * (r >> 2) + 4 * h + (r & 3), key = k0 + kk;
                 // a hidden score's logit becomes -inf, so its weight is exactly 0
                 // (a select on the logit, not a branch around the arithmetic)
                 float dl;
-                float x = logit2_minus<CAP>(a, s[r], lse2, dl);
-                float dpz = dp[r];
+                float x = logit2_minus<CAP>(a, sc[r], lse2, dl);
+                float dpz = dc[r];
                 if constexpr (EXTRA) {
                     x = fmaf(bv[r], BW_LOG2E, x);
                     if (a.drop_scale > 0.0f) dpz = (keepm >> r) & 1u ? dpz * a.drop_scale : 0.0f;
                 }
-                x = ((key >= rlo) & (key <= rhi) & (sM[kk] != 0.0f)) ? x : -INFINITY;   // & : no short circuit
+                x = ((key >= rlo) & (key <= rhi) & (sM[buf][kk] != 0.0f)) ? x : -INFINITY;   // & : no short circuit
                 const float p = fast_exp2(x);
-                s[r] = CAP ? p * (dpz - dlt) * dl : p * (dpz - dlt);
+                sc[r] = CAP ? p * (dpz - dlt) * dl : p * (dpz - dlt);
             }
+            // dQ^T += K^T dS^T of tile u
 #pragma unroll
             for (int sx = 0; sx < 2; ++sx) {
-                const v8 bop = pack8_at<T>(s, 8 * sx);
+                const v8 bop = pack8_at<T>(sc, 8 * sx);
 #pragma unroll
-                for (int mb = 0; mb < NDB; ++mb) acc[mb] = Mfma<T>::mma32(cols_a<T, D>(sK, lane, sx, mb), bop, acc[mb]);
+                for (int mb = 0; mb < NDB; ++mb) acc[mb] = Mfma<T>::mma32(ck[sx][mb], bop, acc[mb]);
             }
+            __syncthreads();   // tile u + 2 stored; tile u's buffer free for tile u + 3
+            sc = sn;
+            dc = dn;
+            buf = bn;
         }
     }
     // acc[mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's row;
@@ -417,12 +577,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const 
             const int hq = step_hq(it), r0 = step_r0(it);
             read_sdp(bn);   // step it + 1 (stale after the last step; discarded)
             // A operands of this step's dV and dK products, k-half 0 now and
-            // k-half 1 halfway through the softmax
+            // k-half 1 halfway through the softmax (at use in the variant with
+            // every option, whose registers would otherwise spill)
+            constexpr bool EARLY = !(EXTRA && CAP && D == 128);
             v8 cg[2][NDB], cq[2][NDB];
+            if constexpr (EARLY) {
 #pragma unroll
-            for (int mb = 0; mb < NDB; ++mb) {
-                cg[0][mb] = cols_a<T, D>(sG[buf], lane, 0, mb);
-                cq[0][mb] = cols_a<T, D>(sQ[buf], lane, 0, mb);
+                for (int mb = 0; mb < NDB; ++mb) {
+                    cg[0][mb] = cols_a<T, D>(sG[buf], lane, 0, mb);
+                    cq[0][mb] = cols_a<T, D>(sQ[buf], lane, 0, mb);
+                }
             }
             if (it + 2 < nsteps) store(bn2);   // its buffer was last read by step it - 1
             if (it + 3 < nsteps) fetch(it + 3);
@@ -472,7 +636,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const 
             f32x16_t sn = {}, dn = {};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (j == 2) {
+                if (EARLY && j == 2) {
 #pragma unroll
                     for (int mb = 0; mb < NDB; ++mb) {
                         cg[1][mb] = cols_a<T, D>(sG[buf], lane, 1, mb);
@@ -520,6 +684,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const 
                 const v8 dop = pack8_at<T>(dc, 8 * sx);
 #pragma unroll
                 for (int mb = 0; mb < NDB; ++mb) {
+                    if constexpr (!EARLY) {
+                        cg[sx][mb] = cols_a<T, D>(sG[buf], lane, sx, mb);
+                        cq[sx][mb] = cols_a<T, D>(sQ[buf], lane, sx, mb);
+                    }
                     dva[mb] = Mfma<T>::mma32(cg[sx][mb], pop, dva[mb]);
                     dka[mb] = Mfma<T>::mma32(cq[sx][mb], dop, dka[mb]);
                 }
@@ -557,8 +725,12 @@ hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* de
                              hipStream_t s) {
     const T* g = static_cast<const T*>(dout);
     if (a.Lq > 0) {
-        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0,
-                           s, a, g, delta, static_cast<T*>(dq));
+        if constexpr (EXTRA)
+            hipLaunchKernelGGL((bwd_dq_pipe_mfma_kernel<T, D, CAP, true>), dim3(a.Hq, a.B, (a.Lq + 127) / 128),
+                               dim3(256), 0, s, a, g, delta, static_cast<T*>(dq));
+        else
+            hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0, s,
+                               a, g, delta, static_cast<T*>(dq));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
