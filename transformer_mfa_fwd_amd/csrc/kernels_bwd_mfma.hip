@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
 // 32 gradient accumulator registers per d block (dK and dV) plus K and V in
 // registers: one workgroup per CU at D = 128.
 template <typename T, int D, bool CAP, bool EXTRA>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
+__global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                                const float* __restrict__ delta, T* __restrict__ dk,
                                                                T* __restrict__ dv) {
     typedef typename Mfma<T>::v8 v8;
@@ -575,11 +575,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const 
         for (int it = 0; it < nsteps; ++it) {
             const int bn = buf == 2 ? 0 : buf + 1, bn2 = bn == 2 ? 0 : bn + 1;   // steps it + 1, it + 2
             const int hq = step_hq(it), r0 = step_r0(it);
-            read_sdp(bn);   // step it + 1 (stale after the last step; discarded)
+            if constexpr (D == 128) read_sdp(bn);   // step it + 1 (stale after the last step; discarded)
             // A operands of this step's dV and dK products, k-half 0 now and
-            // k-half 1 halfway through the softmax (at use in the variant with
-            // every option, whose registers would otherwise spill)
-            constexpr bool EARLY = !(EXTRA && CAP && D == 128);
+            // k-half 1 halfway through the softmax; at use where registers are
+            // short (D = 64 keeps two workgroups per CU without options, and the
+            // D = 128 variant with every option would spill)
+            constexpr bool EARLY = D == 128 && !(EXTRA && CAP);
             v8 cg[2][NDB], cq[2][NDB];
             if constexpr (EARLY) {
 #pragma unroll
@@ -657,10 +658,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const 
                         sn = Mfma<T>::mma32(qa[r >> 1], kop[r >> 1], sn);
                         dn = Mfma<T>::mma32(ga[r >> 1], vop[r >> 1], dn);
                     }
-                    if ((r & 3) == 0 && NKS == 4) {
-                        sn = Mfma<T>::mma32(qa[r >> 2], kop[r >> 2], sn);
-                        dn = Mfma<T>::mma32(ga[r >> 2], vop[r >> 2], dn);
-                    }
+                    if ((r & 3) == 0 && NKS == 4) sdp_mfma(sn, dn, bn, r >> 2);   // D = 64: read at use
                     // a hidden score's logit becomes -inf, so its weight is exactly 0
                     // (a select on the logit, not a branch around the arithmetic)
                     float dl;
