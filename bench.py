@@ -1,8 +1,8 @@
 """Benchmark of the fused attention forward (libmfa) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-decode] [--no-decode-len] [--no-packed]
-                    [--no-bias-dropout] [--no-backward]
+                    [--no-decode] [--no-decode-len] [--no-softcap-window]
+                    [--no-packed] [--no-bias-dropout] [--no-backward]
                     [--no-cpu-baseline]
 
 A step is one mfa_fwd call over one batch of synthetic input already resident
@@ -14,7 +14,10 @@ The long-cache decode (B=64, Lk=32768, Hq=32, Hkv=8, D=128, bf16; split over
 keys plus combine) is timed in the same run and reported under "decode" in
 HBM GB/s of compulsory traffic, and so is the decode over a device-held length
 (mfa_decode_len: 4 draft rows per batch on the same cache, full and half-full)
-under "decode_len".  "packed_encoder" times the bidirectional encoder workload
+under "decode_len".  "softcap_window" times the causal sliding-window prefill
+with soft-cap 50 (B=2, L=16384, Hq=16, Hkv=4, D=128, bf16, window 4096, 5 % of
+keys masked, inputs of standard deviation 2) in visible-pair TFLOP/s.
+"packed_encoder" times the bidirectional encoder workload
 (B=8, L=8192, H=12, D=64, fp16, window 128, tail padding) twice: padded with a
 key mask through mfa_fwd, and packed without its padding through
 mfa_packed_qkv_fwd.  "bias_mfma" times the causal GQA prefill with a
@@ -259,6 +262,27 @@ def packed_encoder(steps: int, warmup: int, warmup_ms: float):
     return res
 
 
+def softcap_window(steps: int, warmup: int, warmup_ms: float):
+    """The causal sliding-window GQA prefill with soft-cap and a sparse key mask
+    (MFMA kernel, soft-capped and masked instantiation)."""
+    import torch
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    w = wl.CAUSAL_WINDOW_SOFTCAP_BF16
+    r, t = time_workload(w, steps, warmup, warmup_ms=warmup_ms)
+    del t
+    torch.cuda.empty_cache()
+    flops = 4.0 * w.D * r["pairs"]
+    kern = r["event_ms_avg"]
+    return {"workload": w.name, "path": r["path"], "unit": "TFLOP/s", "input_std": w.std,
+            "ms_per_step": round(r["wall_ms"], 5), "kernel_ms_avg": round(kern, 5),
+            "visible_pairs": r["pairs"], "value": round(flops / (r["wall_ms"] * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "achieved": round(flops / (kern * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": flops}}
+
+
 def bias_mfma(steps: int, warmup: int, warmup_ms: float):
     """The prefill shape with a [1, 1, L, L] additive mask and no dropout: the
     MFMA kernel's BIAS instantiation."""
@@ -380,6 +404,7 @@ def main():
     ap.add_argument("--workload", default="gqa_causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-len", action="store_true")
+    ap.add_argument("--no-softcap-window", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--no-bias-dropout", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
@@ -489,6 +514,12 @@ def main():
                        "frac": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                        "algorithmic_bytes_per_launch": r["bytes"]}
         line["decode_len"] = dl
+
+    if not args.no_softcap_window and w is not wl.CAUSAL_WINDOW_SOFTCAP_BF16:
+        tensors = None
+        torch.cuda.empty_cache()
+        line["softcap_window"] = softcap_window(max(10, args.steps // 2), max(3, args.warmup // 2),
+                                                args.warmup_ms)
 
     if not args.no_packed:
         tensors = None
