@@ -241,9 +241,13 @@ def packed_encoder(steps: int, warmup: int, warmup_ms: float):
     out = torch.empty_like(q)
     wall, kern = time_calls(lambda: mfa.fwd(q, k, v, causal=False, window=w.window, key_mask=m,
                                             out=out, return_lse=False), steps, warmup, warmup_ms)
+    # compulsory bytes of the call (no LSE is written): Q, K, V, the mask, O
+    pbytes = (2 * w.B * w.Lq * w.Hq * w.D + 2 * w.B * w.Lk * w.Hkv * w.D) * q.element_size() + w.B * w.Lk * 4
     res["padded"] = {"api": "mfa_fwd + key mask", "rows": w.B * w.Lq, "ms_per_step": round(wall, 5),
                      "kernel_ms_avg": round(kern, 5),
-                     "visible_pairs": pairs, "value": round(4.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2)}
+                     "visible_pairs": pairs, "value": round(4.0 * w.D * pairs / (wall * 1e-3) / 1e12, 2),
+                     "algorithmic_bytes": pbytes, "hbm_gbs": round(pbytes / (kern * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(pbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del q, k, v, m, out
     torch.cuda.empty_cache()
     lengths = wl.encoder_packing_lengths(w)
@@ -254,9 +258,13 @@ def packed_encoder(steps: int, warmup: int, warmup_ms: float):
     half = w.window // 2
     # the padded form also counts its padding rows' pairs with valid keys near the boundary
     ppairs = w.Hq * sum(sum(min(n - 1, r + half) - max(0, r - half) + 1 for r in range(n)) for n in lengths)
+    # compulsory bytes: the fused QKV rows, the sequence bounds, O
+    kbytes = (qkv.numel() + out.numel()) * qkv.element_size() + sb.numel() * sb.element_size()
     res["packed"] = {"api": "mfa_packed_qkv_fwd", "rows": int(qkv.shape[0]), "ms_per_step": round(wall, 5),
                      "kernel_ms_avg": round(kern, 5),
-                     "visible_pairs": ppairs, "value": round(4.0 * w.D * ppairs / (wall * 1e-3) / 1e12, 2)}
+                     "visible_pairs": ppairs, "value": round(4.0 * w.D * ppairs / (wall * 1e-3) / 1e12, 2),
+                     "algorithmic_bytes": kbytes, "hbm_gbs": round(kbytes / (kern * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(kbytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del qkv, sb, out
     torch.cuda.empty_cache()
     return res
@@ -443,7 +451,10 @@ def main():
     is_prefill = res["path"] in ("mfma", "generic")
     traffic, tnote = measured_traffic(f"{'prefill' if is_prefill else 'decode'}_{w.name}.counters.json",
                                       PREFILL_SOURCES if is_prefill else DECODE_SOURCES)
-    if is_prefill:
+    # a prefill whose flops per compulsory byte fall below the ridge point
+    # (peak flops / peak bandwidth) is bound by HBM, not by the matrix cores
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if is_prefill and flops / res["bytes"] >= ridge:
         roof = {"bound": "mfma", "achieved": round(flops / (kern_ms * 1e-3) / 1e12, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:
