@@ -87,8 +87,10 @@ typedef enum {
 /*
  * Attention forward.  B = 0 or Lq = 0 is an empty call that succeeds without
  * launching anything.  `scale` is used as given (the conventional value is
- * 1/sqrt(D)).  Any workspace the chosen kernels need comes from the device's
- * stream-ordered memory pool and is released in stream order.
+ * 1/sqrt(D)).  Any workspace the chosen kernels need comes from a
+ * stream-ordered memory pool that the library creates on each device on first
+ * use (it keeps freed memory for later calls and never changes the device's
+ * default pool) and is released in stream order.
  */
 int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
             int B, int Lq, int Lk, int Hq, int Hkv, int D,

@@ -177,6 +177,31 @@ def test_workspace_entry_point_matches_pool_entry_point():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_pool_calls_leave_the_default_pool_alone():
+    """Workspace from the library's own pool: the device's default pool keeps
+    its release threshold, and repeated pool calls give the same result."""
+    import ctypes
+    from transformer_mfa_fwd_amd import _binding
+    hip = _binding.load_library()     # symbols resolve in libmfa's own HIP runtime
+    release_threshold = 0x4   # hipMemPoolAttrReleaseThreshold
+    dev = torch.cuda.current_device()
+
+    def default_threshold():
+        pool, thr = ctypes.c_void_p(), ctypes.c_uint64()
+        assert hip.hipDeviceGetDefaultMemPool(ctypes.byref(pool), dev) == 0
+        assert hip.hipMemPoolGetAttribute(pool, release_threshold, ctypes.byref(thr)) == 0
+        return thr.value
+
+    before = default_threshold()
+    w = wl.Workload("pool", "bf16", 2, 1, 700, 8, 2, 128, True, mask="random_frac", mask_frac=0.1)
+    q, k, v, m = wl.make_inputs(w, DEV)
+    o1, l1 = mfa.fwd(q, k, v, causal=True, key_mask=m)      # key mask words + split decode partials
+    o2, l2 = mfa.fwd(q, k, v, causal=True, key_mask=m)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert default_threshold() == before
+
+
 # --- full-size workloads --------------------------------------------------------
 
 FULL = [wl.SINGLE_HEAD_CAUSAL_FP32, wl.GQA_CAUSAL_PREFILL_BF16, wl.BIDIR_WINDOW_ENCODER_FP16,

@@ -109,19 +109,50 @@ size_t workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype,
     return ws;
 }
 
-std::once_flag g_pool_once[64];
+constexpr int kMaxDevices = 64;
+std::once_flag g_pool_once[kMaxDevices];
+hipMemPool_t g_pool[kMaxDevices] = {};
 
-// Keep freed workspace in the device's default pool instead of returning it
-// to the driver after every call.
-void prepare_pool(int dev) {
-    if (dev < 0 || dev >= 64) return;
+// The library's own stream-ordered pool on device dev, created on first use:
+// freed workspace stays in it instead of going back to the driver after every
+// call.  The device's default pool is left as it is.  Null if it could not be
+// created (then the default pool serves).
+hipMemPool_t library_pool(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
     std::call_once(g_pool_once[dev], [dev]() {
-        hipMemPool_t pool;
-        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-            uint64_t thr = UINT64_MAX;
-            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        hipMemPoolProps props{};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
         }
+        uint64_t thr = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        g_pool[dev] = pool;
     });
+    return g_pool[dev];
+}
+
+// Stream-ordered workspace of n bytes on the current device (released with
+// hipFreeAsync on the same stream); an MFA status.
+int pool_alloc(void** p, size_t n, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "hipGetDevice failed");
+    }
+    hipMemPool_t pool = library_pool(dev);
+    hipError_t e = pool ? hipMallocFromPoolAsync(p, n, pool, stream) : hipMallocAsync(p, n, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
+                    "workspace allocation of %zu bytes failed: %s", n, hipGetErrorString(e));
+    }
+    return MFA_SUCCESS;
 }
 
 mfa::FwdArgs make_args(const Call& c) {
@@ -210,15 +241,8 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
     const bool needs_ws = c.key_mask != nullptr || path == MFA_PATH_SPLIT_DECODE;
     void* ws = workspace;
     if (needs_ws && use_pool) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
-        prepare_pool(dev);
-        hipError_t e = hipMallocAsync(&ws, need, stream);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
-                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
-        }
+        const int pst = pool_alloc(&ws, need, stream);
+        if (pst != MFA_SUCCESS) return pst;
     }
     char* wsb = static_cast<char*>(ws);
     hipError_t e = hipSuccess;
@@ -321,15 +345,8 @@ int run_len(const LenCall& c, int splits, void* workspace, size_t ws_bytes, hipS
 
     void* ws = workspace;
     if (use_pool) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
-        prepare_pool(dev);
-        hipError_t e = hipMallocAsync(&ws, need, stream);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
-                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
-        }
+        const int pst = pool_alloc(&ws, need, stream);
+        if (pst != MFA_SUCCESS) return pst;
     }
     hipError_t e = mfa::launch_split_decode(a, c.d_len, c.dtype, splits, static_cast<float*>(ws), stream);
     if (use_pool) {
@@ -427,15 +444,8 @@ int run_varlen(const void* q, const void* k, const void* v, void* out, float* ls
     }
     void* ws = workspace;
     if (use_pool) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
-        prepare_pool(dev);
-        hipError_t e = hipMallocAsync(&ws, need, stream);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
-                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
-        }
+        const int pst = pool_alloc(&ws, need, stream);
+        if (pst != MFA_SUCCESS) return pst;
     }
     int* row_pos = static_cast<int*>(ws);
     int* bounds = row_pos + Tq;
@@ -570,15 +580,8 @@ int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* ws = workspace;
     if (use_pool && need > 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return fail(MFA_ERROR_HIP, "hipGetDevice failed");
-        prepare_pool(dev);
-        hipError_t e = hipMallocAsync(&ws, need, s);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(e == hipErrorOutOfMemory ? MFA_ERROR_OUT_OF_MEMORY : MFA_ERROR_HIP,
-                        "hipMallocAsync(%zu) failed: %s", need, hipGetErrorString(e));
-        }
+        const int pst = pool_alloc(&ws, need, s);
+        if (pst != MFA_SUCCESS) return pst;
     }
     hipError_t e = mfa::launch_backward(a, dout, static_cast<float*>(ws), dq, dk, dv, dtype, s);
     if (use_pool && need > 0) {
