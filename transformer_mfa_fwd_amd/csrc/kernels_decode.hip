@@ -313,12 +313,15 @@ bool decode_len_supported(int dtype, int D, int R, int group) {
            R * group <= 16;
 }
 
-// Enough (split, kv head, batch) waves to fill the chip several times over,
-// but at least 8 tiles (256 keys) per split.
+// About three (split, kv head, batch) waves per CU of the 256-CU part, but at
+// least 8 tiles (256 keys) per split.  Each wave keeps enough loads in flight
+// to stream on its own: swept over batch 4 .. 64 of the long cache, the rate
+// peaks at 512 - 768 waves and falls by 5 - 30 % at the 4096 - 16384 waves of
+// more, shorter splits.
 int split_decode_default_splits(int B, int Hkv, int Lk, int group) {
     (void)group;
     const int64_t streams = (int64_t)B * Hkv;
-    const int64_t target_waves = 8192;
+    const int64_t target_waves = 768;
     int64_t s = (target_waves + streams - 1) / streams;
     const int64_t tiles = (Lk + DT - 1) / DT;
     const int64_t max_s = tiles / 8 > 0 ? tiles / 8 : 1;
