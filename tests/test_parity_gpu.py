@@ -242,6 +242,21 @@ def test_full_workload_sampled_rows(w):
     pu.compare(w.dtype, og, lg, O, L, w.name)
 
 
+@pytest.mark.parametrize("B,splits", [(1, 96), (4, 24)])
+def test_long_cache_decode_small_batch_many_splits(B, splits):
+    """The default split rule gives small batches of a long cache many splits:
+    every head of every batch against the oracle."""
+    w = wl.LONG_CACHE_DECODE_BF16.replace(name=f"long_cache_decode_B{B}", B=B)
+    assert mfa.plan(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, w.torch_dtype) == ("split_decode", splits)
+    q, k, v, m, out, lse = run_case(w)
+    rows = np.array([(b, h, 0) for b in range(B) for h in range(w.Hq)], np.int64)
+    O, L, _ = default_oracle().rows(q, k, v, rows, scale=w.scale, causal=True, window=0,
+                                    q_offset=w.q_offset, softcap=0.0, key_mask=None,
+                                    nthreads=pu.ORACLE_THREADS)
+    og, lg = pu.gather_rows(out, lse, rows)
+    pu.compare(w.dtype, og, lg, O, L, w.name)
+
+
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_full_workload_exact_visible_counts(w):
     """Q = 0: every visible score is 0, so exp(LSE) is the visible-key count."""
