@@ -39,7 +39,10 @@
  *
  * Ownership: every pointer is caller-owned device memory.  The library keeps
  * no reference after a call returns and writes only out, lse and (for the
- * _ws / _ex forms) the workspace.
+ * _ws / _ex forms) the workspace.  In every entry point, a pointer to a tensor
+ * that holds no element (for instance q and out when B = 0 or Lq = 0, k and v
+ * when B = 0, or the key packing of mfa_varlen_fwd when total_k = 0) may be
+ * NULL: nothing is read from or written to it.
  *
  * Streams: every call is asynchronous on `stream` (a hipStream_t; NULL is the
  * null stream) and never synchronises the device.  A fault in a kernel shows

@@ -277,3 +277,19 @@ def test_bwd_unsupported_empty_and_workspace():
     assert call_bwd(B=0) == 0
     assert mfa.bwd_workspace_size(2, 16, 4) >= 2 * 16 * 4 * 4
     assert mfa.bwd_workspace_size(0, 16, 4) == 0
+
+
+def test_empty_calls_accept_null_pointers():
+    """A tensor that holds no element may come as a null pointer (torch's empty
+    tensors do); a tensor that holds elements may not."""
+    assert call(B=0, q=None, k=None, v=None, out=None, lse=None) == 0
+    assert call(Lq=0, q=None, out=None, lse=None) == 0
+    assert call(Lq=0, q=None, out=None, k=None) == 1          # k and v still hold B * Lk rows
+    assert call_len(B=0, q=None, k=None, v=None, out=None, lse=None, d_len=None) == 0
+    assert call_packed(L=0, qkv=None, sb=None, out=None, lse=None) == 0
+    assert call_varlen(Tq=0, q=None, out=None, lse=None) == 0
+    assert call_varlen(Tq=0, Tk=0, q=None, out=None, k=None, v=None) == 0
+    assert call_varlen(Tq=0, cq=None) == 1                     # the prefix sums always hold an entry
+    assert call_bwd(B=0, q=None, k=None, v=None, out=None, dout=None, lse=None, dq=None, dk=None,
+                    dv=None) == 0
+    assert call_bwd(Lq=0, q_offset=0, q=None, out=None, dout=None, lse=None, dq=None, dk=None) == 1

@@ -75,3 +75,155 @@ def test_random_options_every_row(i):
         torch.cuda.synchronize()
         og = out.double().cpu().numpy().transpose(0, 2, 1, 3)
         pu.compare(w.dtype, og, lse.double().cpu().numpy(), O, L, f"fuzz {i} {name}")
+
+
+# --- the other entry points ---------------------------------------------------
+
+def _dtype_D_std(rng):
+    dtype = str(rng.choice(["bf16", "f16", "f32"], p=[0.45, 0.4, 0.15]))
+    D = int(rng.choice([64, 128]))
+    std = float(rng.choice([1.0, 1.5])) if dtype != "bf16" else 1.0
+    return dtype, D, std
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_decode_len_every_row(i):
+    """mfa_decode_len: draft rows, GQA, capacity, per-batch lengths (0, below
+    R, full and random), soft-cap and split count drawn at random."""
+    rng = np.random.default_rng(2000 + i)
+    dtype = str(rng.choice(["bf16", "f16"]))
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.integers(1, 4))
+    g = int(rng.choice([1, 2, 4, 8]))
+    R = int(rng.integers(1, 16 // g + 1))
+    B = int(rng.integers(1, 5))
+    Lmax = int(rng.integers(1, 601))
+    lens = [int(rng.choice([0, max(0, R - 1), Lmax, int(rng.integers(0, Lmax + 1))])) for _ in range(B)]
+    softcap = 0.0 if rng.random() < 0.6 else float(rng.uniform(2.0, 40.0))
+    splits = int(rng.choice([0, 1, 3, 7]))
+    print(f"\n[fuzz] decode_len {i}: {dtype} D={D} B={B} R={R} Hq={Hkv * g} Hkv={Hkv} Lmax={Lmax} "
+          f"lens={lens} softcap={softcap:.2f} splits={splits}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(i)
+    dt = wl.DTYPES[dtype]
+    q = torch.randn((B, R, Hkv * g, D), generator=gen).to(dt)
+    k = torch.randn((B, Lmax, Hkv, D), generator=gen).to(dt)
+    v = torch.randn((B, Lmax, Hkv, D), generator=gen).to(dt)
+    scale = 1.0 / np.sqrt(D)
+    O, L, _ = default_oracle().decode_len(q, k, v, np.array(lens), scale=scale, softcap=softcap,
+                                          nthreads=pu.ORACLE_THREADS)
+    out, lse = mfa.decode_len(q.to(DEV), k.to(DEV), v.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                              softcap=softcap, scale=scale, splits=splits)
+    torch.cuda.synchronize()
+    og = out.double().cpu().numpy().transpose(0, 2, 1, 3)
+    pu.compare(dtype, og, lse.double().cpu().numpy(), O.transpose(0, 2, 1, 3), L, f"decode_len {i}")
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_varlen_every_row(i):
+    """mfa_varlen_fwd: 1-5 sequences with query and key lengths drawn from
+    0..150 (empty sequences included), GQA, causal or not, window, soft-cap."""
+    rng = np.random.default_rng(3000 + i)
+    dtype, D, std = _dtype_D_std(rng)
+    nb = int(rng.integers(1, 6))
+    lq = [int(rng.choice([0, 1, int(rng.integers(0, 151))])) for _ in range(nb)]
+    lk = [int(rng.choice([0, 1, int(rng.integers(0, 151))])) for _ in range(nb)]
+    if sum(lq) == 0:
+        lq[0] = 1
+    Hkv = int(rng.integers(1, 4))
+    Hq = Hkv * int(rng.integers(1, 5))
+    causal = bool(rng.random() < 0.6)
+    window = 0 if rng.random() < 0.5 else int(rng.integers(1, 200))
+    softcap = 0.0 if rng.random() < 0.6 else float(rng.uniform(2.0, 40.0))
+    print(f"\n[fuzz] varlen {i}: {dtype} D={D} lq={lq} lk={lk} Hq={Hq} Hkv={Hkv} causal={causal} "
+          f"window={window} softcap={softcap:.2f}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(i)
+    dt = wl.DTYPES[dtype]
+    Tq, Tk = sum(lq), sum(lk)
+    q = (torch.randn((Tq, Hq, D), generator=gen) * std).to(dt)
+    k = (torch.randn((Tk, Hkv, D), generator=gen) * std).to(dt)
+    v = torch.randn((Tk, Hkv, D), generator=gen).to(dt)
+    cq = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32)
+    ck = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32)
+    O, L, _ = default_oracle().varlen(q, k, v, cq, ck, scale=1.0 / np.sqrt(D), causal=causal, window=window,
+                                      softcap=softcap, nthreads=pu.ORACLE_THREADS)
+    # an empty key packing still passes valid (non-null) device pointers
+    kd = torch.zeros((max(Tk, 1), Hkv, D), dtype=dt, device=DEV)[:Tk]
+    vd = torch.zeros((max(Tk, 1), Hkv, D), dtype=dt, device=DEV)[:Tk]
+    kd.copy_(k.to(DEV))
+    vd.copy_(v.to(DEV))
+    out, lse = mfa.varlen_fwd(q.to(DEV), kd, vd, cq.to(DEV), ck.to(DEV), causal=causal, window=window,
+                              softcap=softcap)
+    torch.cuda.synchronize()
+    pu.compare(dtype, out.double().cpu().numpy().transpose(1, 0, 2), lse.double().cpu().numpy(),
+               O.transpose(1, 0, 2), L, f"varlen {i}")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_packed_qkv_every_row(i):
+    """mfa_packed_qkv_fwd: 1-6 sequences of 1..200 rows in one fused QKV
+    tensor, bidirectional window or none, soft-cap."""
+    rng = np.random.default_rng(4000 + i)
+    dtype, D, std = _dtype_D_std(rng)
+    lengths = [int(rng.integers(1, 201)) for _ in range(int(rng.integers(1, 7)))]
+    H = int(rng.integers(1, 5))
+    window = 0 if rng.random() < 0.4 else int(rng.integers(1, 300))
+    softcap = 0.0 if rng.random() < 0.6 else float(rng.uniform(2.0, 40.0))
+    print(f"\n[fuzz] packed {i}: {dtype} D={D} H={H} lengths={lengths} window={window} "
+          f"softcap={softcap:.2f}", flush=True)
+    qkv, sb = wl.make_packed_qkv(lengths, H, D, dtype, "cpu", seed=i, std=std)
+    O, L, _ = default_oracle().packed_qkv(qkv, sb, H, scale=1.0 / np.sqrt(D), window=window, softcap=softcap,
+                                          nthreads=pu.ORACLE_THREADS)
+    out, lse = mfa.packed_qkv_fwd(qkv.to(DEV), sb.to(DEV), H, window=window, softcap=softcap)
+    torch.cuda.synchronize()
+    og = out.double().cpu().numpy().reshape(O.shape)
+    pu.compare(dtype, og.transpose(1, 0, 2), lse.double().cpu().numpy(), O.transpose(1, 0, 2), L, f"packed {i}")
+
+
+def _check_grad(name, got, ref, dtype, what):
+    rel = {"f32": 1e-4, "f16": 1e-2, "bf16": 1e-2}[dtype]
+    got = got.double().cpu().numpy()
+    bound = rel * max(1.0, float(np.abs(ref).max())) + pu.half_ulp(ref, dtype)
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), f"{what} {name}: non-finite gradient"
+    worst = int(np.argmax(err - bound))
+    assert err.flat[worst] <= bound.flat[worst], (
+        f"{what} {name}: |g - g_ref| = {err.flat[worst]:.3e} > {bound.flat[worst]:.3e}")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_backward_every_element(i):
+    """mfa_bwd after libmfa's own forward: every forward option drawn at
+    random, plus an additive mask of a random broadcast shape and dropout."""
+    rng = np.random.default_rng(5000 + i)
+    dtype, D, std = _dtype_D_std(rng)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.integers(1, 4))
+    Lk = int(rng.integers(1, 161))
+    Lq = 1 if rng.random() < 0.2 else int(rng.integers(1, Lk + 1))
+    q_offset = int(rng.integers(0, Lk - Lq + 1))
+    causal = bool(rng.random() < 0.6)
+    window = 0 if rng.random() < 0.5 else int(rng.integers(1, 2 * Lk + 1))
+    softcap = 0.0 if rng.random() < 0.7 else float(rng.uniform(2.0, 30.0))
+    mask = dict(mask=None) if rng.random() < 0.6 else dict(mask="random_frac", mask_frac=0.25)
+    bias_dims = None if rng.random() < 0.6 else [bool(rng.random() < 0.5) for _ in range(4)]
+    p = 0.0 if rng.random() < 0.6 else float(rng.choice([0.1, 0.5]))
+    w = wl.Workload(f"bwdfuzz{i}", dtype, B, Lq, Lk, Hq, Hkv, D, causal, window=window, softcap=softcap,
+                    std=std, **mask)
+    print(f"\n[fuzz] backward {i}: {w} q_offset={q_offset} bias={bias_dims} p={p}", flush=True)
+    q, k, v, m = wl.make_inputs(w, DEV, seed=i)
+    gen = torch.Generator(device="cpu").manual_seed(100 + i)
+    dout = torch.randn(q.shape, generator=gen).to(q.dtype).to(DEV)
+    bias = None
+    if bias_dims is not None:
+        full = (B, Hq, Lq, Lk)
+        bias = (torch.randn(tuple(full[e] if bias_dims[e] else 1 for e in range(4)), generator=gen) * 1.5)
+    kw = dict(causal=causal, window=window, q_offset=q_offset, softcap=softcap, key_mask=m, scale=w.scale,
+              dropout_p=p, seed=7 + i)
+    bd = None if bias is None else bias.contiguous().to(DEV)
+    out, lse = mfa.fwd(q, k, v, bias=bd, **kw)
+    dq, dk, dv = mfa.bwd(q, k, v, out, dout, lse, bias=bd, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = default_oracle().bwd(q, k, v, dout, bias=bias, nthreads=pu.ORACLE_THREADS, **kw)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check_grad(name, got, ref, dtype, w.name)

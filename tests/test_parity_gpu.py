@@ -202,6 +202,35 @@ def test_pool_calls_leave_the_default_pool_alone():
     assert default_threshold() == before
 
 
+def test_empty_torch_tensors():
+    """Calls whose tensors hold no element, made with torch's empty tensors
+    (null data pointers): they succeed, and the backward with no query rows
+    still writes zero key gradients; varlen sequences without any key give
+    O = 0 and LSE = -inf."""
+    bf = torch.bfloat16
+    z = lambda *s, dt=bf: torch.zeros(s, dtype=dt, device=DEV)
+    out, lse = mfa.fwd(z(0, 16, 4, 64), z(0, 16, 2, 64), z(0, 16, 2, 64), causal=True)
+    assert out.shape == (0, 16, 4, 64) and lse.shape == (0, 4, 16)
+    out, lse = mfa.fwd(z(2, 0, 4, 64), z(2, 16, 2, 64), z(2, 16, 2, 64), causal=True)
+    assert out.shape == (2, 0, 4, 64) and lse.shape == (2, 4, 0)
+    q = torch.randn((5, 4, 64), device=DEV).to(bf)
+    cq = torch.tensor([0, 2, 5], dtype=torch.int32, device=DEV)
+    ck = torch.tensor([0, 0, 0], dtype=torch.int32, device=DEV)
+    out, lse = mfa.varlen_fwd(q, z(0, 2, 64), z(0, 2, 64), cq, ck, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    out, lse = mfa.packed_qkv_fwd(z(0, 3 * 2 * 64), torch.zeros((0, 2), dtype=torch.int32, device=DEV), 2)
+    assert out.numel() == 0
+    out, lse = mfa.decode_len(z(0, 1, 8, 128), z(0, 64, 2, 128), z(0, 64, 2, 128),
+                              torch.zeros((0,), dtype=torch.int32, device=DEV))
+    assert out.numel() == 0
+    k = torch.randn((1, 20, 2, 64), device=DEV).to(bf)
+    dq, dk, dv = mfa.bwd(z(1, 0, 4, 64), k, k, z(1, 0, 4, 64), z(1, 0, 4, 64),
+                         torch.zeros((1, 4, 0), device=DEV), causal=True)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+
+
 # --- full-size workloads --------------------------------------------------------
 
 FULL = [wl.SINGLE_HEAD_CAUSAL_FP32, wl.GQA_CAUSAL_PREFILL_BF16, wl.BIDIR_WINDOW_ENCODER_FP16,

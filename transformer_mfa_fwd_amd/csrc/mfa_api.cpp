@@ -47,13 +47,16 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Host-side checks; no HIP call happens here.
+// A pointer to a tensor that holds no element may be null: nothing is read
+// from or written to it (torch hands out null for empty tensors).
 int validate(const Call& c) {
-    if (!c.q || !c.k || !c.v || !c.out)
-        return fail(MFA_ERROR_INVALID_VALUE, "q, k, v and out must be non-null");
     if (c.B < 0 || c.Lq < 0 || c.Lk <= 0 || c.Hq <= 0 || c.Hkv <= 0 || c.D <= 0)
         return fail(MFA_ERROR_INVALID_VALUE,
                     "bad dimensions B=%d Lq=%d Lk=%d Hq=%d Hkv=%d D=%d (B, Lq >= 0; others > 0)",
                     c.B, c.Lq, c.Lk, c.Hq, c.Hkv, c.D);
+    const bool q_empty = c.B == 0 || c.Lq == 0, kv_empty = c.B == 0;
+    if ((!q_empty && (!c.q || !c.out)) || (!kv_empty && (!c.k || !c.v)))
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k, v and out must be non-null");
     if (c.Hq % c.Hkv != 0)
         return fail(MFA_ERROR_INVALID_VALUE, "Hkv=%d does not divide Hq=%d", c.Hkv, c.Hq);
     if (c.q_offset < 0 || (int64_t)c.q_offset + c.Lq > c.Lk)
@@ -283,7 +286,7 @@ struct LenCall {
 };
 
 int validate_len(const LenCall& c) {
-    if (!c.q || !c.k || !c.v || !c.out || !c.d_len)
+    if (c.B != 0 && (!c.q || !c.k || !c.v || !c.out || !c.d_len))
         return fail(MFA_ERROR_INVALID_VALUE, "q, k_cache, v_cache, out and d_len must be non-null");
     if (c.B < 0 || c.R <= 0 || c.Lmax <= 0 || c.Hq <= 0 || c.Hkv <= 0 || c.D <= 0)
         return fail(MFA_ERROR_INVALID_VALUE,
@@ -362,7 +365,7 @@ int run_len(const LenCall& c, int splits, void* workspace, size_t ws_bytes, hipS
 
 int run_packed(const void* qkv, const int* seq_bounds, void* out, float* lse, int L, int H, int D,
                float scale, int window, float softcap, int dtype, hipStream_t stream) {
-    if (!qkv || !seq_bounds || !out)
+    if (L != 0 && (!qkv || !seq_bounds || !out))
         return fail(MFA_ERROR_INVALID_VALUE, "qkv, seq_bounds and out must be non-null");
     if (L < 0 || H <= 0 || D <= 0)
         return fail(MFA_ERROR_INVALID_VALUE, "bad dimensions L=%d H=%d D=%d (L >= 0; others > 0)", L, H, D);
@@ -414,7 +417,7 @@ size_t varlen_ws_bytes(int Tq) { return align256((size_t)Tq * 3 * sizeof(int)); 
 int run_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int* cu_q,
                const int* cu_k, int batch, int Tq, int Tk, int Hq, int Hkv, int D, float scale, int causal,
                int window, float softcap, int dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
-    if (!q || !k || !v || !out || !cu_q || !cu_k)
+    if ((Tq != 0 && (!q || !out)) || (Tk != 0 && (!k || !v)) || !cu_q || !cu_k)
         return fail(MFA_ERROR_INVALID_VALUE, "q, k, v, out, cu_seqlens_q and cu_seqlens_k must be non-null");
     if (batch < 0 || Tq < 0 || Tk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (batch == 0 && Tq > 0))
         return fail(MFA_ERROR_INVALID_VALUE,
@@ -563,7 +566,8 @@ int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const 
     c.seed = seed;
     int st = validate(c);
     if (st != MFA_SUCCESS) return st;
-    if (!dout || !lse || !dq || !dk || !dv)
+    const bool q_empty = B == 0 || Lq == 0;
+    if ((!q_empty && (!dout || !lse || !dq)) || (B != 0 && (!dk || !dv)))
         return fail(MFA_ERROR_INVALID_VALUE, "dout, lse, dq, dk and dv must be non-null");
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
         return fail(MFA_ERROR_INVALID_VALUE, "dout, dq, dk and dv must be 16-byte aligned");
