@@ -227,3 +227,71 @@ def test_random_backward_every_element(i):
     rq, rk, rv = default_oracle().bwd(q, k, v, dout, bias=bias, nthreads=pu.ORACLE_THREADS, **kw)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check_grad(name, got, ref, dtype, w.name)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_medium_shapes_sampled_rows(i):
+    """Longer axes (keys up to 6000, many query tiles), every forward option
+    drawn as above; sampled rows at tile and window edges plus random rows."""
+    rng = np.random.default_rng(6000 + i)
+    dtype = str(rng.choice(["bf16", "f16"]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    Lk = int(rng.integers(1000, 6001))
+    Lq = 1 if rng.random() < 0.2 else int(rng.integers(1, Lk + 1))
+    q_offset = Lk - Lq if rng.random() < 0.5 else int(rng.integers(0, Lk - Lq + 1))
+    causal = bool(rng.random() < 0.6)
+    window = 0 if rng.random() < 0.4 else int(rng.integers(1, Lk))
+    softcap = 0.0 if rng.random() < 0.6 else float(rng.uniform(5.0, 50.0))
+    r = rng.random()
+    mask = dict(mask=None) if r < 0.5 else (dict(mask="pad_tail", pad_max=Lk // 3) if r < 0.75 else
+                                            dict(mask="random_frac", mask_frac=0.1))
+    w = wl.Workload(f"medium{i}", dtype, B, Lq, Lk, Hq, Hkv, D, causal, window=window, softcap=softcap, **mask)
+    print(f"\n[fuzz] medium {i}: {w} q_offset={q_offset}", flush=True)
+    q, k, v, m = wl.make_inputs(w, DEV, seed=i)
+    kw = dict(causal=causal, window=window, q_offset=q_offset, softcap=softcap, scale=w.scale)
+    out, lse = mfa.fwd(q, k, v, key_mask=m, **kw)
+    torch.cuda.synchronize()
+    rows = pu.sample_rows(w, n_random=8, seed=i)
+    O, L, _ = default_oracle().rows(q, k, v, rows, key_mask=m, nthreads=pu.ORACLE_THREADS, **kw)
+    og, lg = pu.gather_rows(out, lse, rows)
+    pu.compare(dtype, og, lg, O, L, f"medium {i}")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_bias_dropout_forward_every_row(i):
+    """mfa_fwd_bias_dropout: an additive mask of a random broadcast shape
+    and/or dropout, with the other forward options drawn at random."""
+    rng = np.random.default_rng(7000 + i)
+    dtype, D, std = _dtype_D_std(rng)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.integers(1, 4))
+    Lk = int(rng.integers(1, 301))
+    Lq = 1 if rng.random() < 0.2 else int(rng.integers(1, Lk + 1))
+    q_offset = int(rng.integers(0, Lk - Lq + 1))
+    causal = bool(rng.random() < 0.6)
+    window = 0 if rng.random() < 0.5 else int(rng.integers(1, 2 * Lk + 1))
+    softcap = 0.0 if rng.random() < 0.7 else float(rng.uniform(2.0, 30.0))
+    mask = dict(mask=None) if rng.random() < 0.6 else dict(mask="random_frac", mask_frac=0.25)
+    bias_dims = None if rng.random() < 0.3 else [bool(rng.random() < 0.5) for _ in range(4)]
+    p = float(rng.choice([0.0, 0.1, 0.5])) if bias_dims is not None else float(rng.choice([0.1, 0.5]))
+    w = wl.Workload(f"biasfuzz{i}", dtype, B, Lq, Lk, Hq, Hkv, D, causal, window=window, softcap=softcap,
+                    std=std, **mask)
+    print(f"\n[fuzz] bias/dropout {i}: {w} q_offset={q_offset} bias={bias_dims} p={p}", flush=True)
+    q, k, v, m = wl.make_inputs(w, DEV, seed=i)
+    gen = torch.Generator(device="cpu").manual_seed(200 + i)
+    bias = None
+    if bias_dims is not None:
+        full = (B, Hq, Lq, Lk)
+        bias = torch.randn(tuple(full[e] if bias_dims[e] else 1 for e in range(4)), generator=gen) * 1.5
+    kw = dict(causal=causal, window=window, q_offset=q_offset, softcap=softcap, key_mask=m, scale=w.scale,
+              dropout_p=p, seed=11 + i)
+    out, lse = mfa.fwd(q, k, v, bias=None if bias is None else bias.contiguous().to(DEV), **kw)
+    torch.cuda.synchronize()
+    O, L, _ = default_oracle().full(q, k, v, bias=bias, nthreads=pu.ORACLE_THREADS, **kw)
+    og = out.double().cpu().numpy().transpose(0, 2, 1, 3)
+    pu.compare(dtype, og, lse.double().cpu().numpy(), O.transpose(0, 2, 1, 3), L, f"bias/dropout {i}",
+               o_scale=1.0 / (1.0 - p))
