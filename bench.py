@@ -422,7 +422,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: libmfa has no multi-GPU path "
               "(every call runs on one device); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -87,7 +87,7 @@ void mfa_oracle_philox4x64(const uint64_t ctr_in[4], const uint64_t key_in[2], u
 
 /*
  * Dropout decision of score (b, hq, i, j).  The pages fix only that a seed
- * drives the pattern (ferrotensor attention.rs, AttentionOptions); this build
+ * drives the pattern (ferrotensor attention.rs, AttentionOptions); the oracle
  * reads it as: one Philox4x64-10 block per four consecutive keys, counter
  * (floor(j / 4), i, hq, b) and key (seed, 0), its four output words serving
  * keys 4 floor(j / 4) .. +3 in order; the top 24 bits r of word j mod 4 keep
@@ -559,5 +559,5 @@ int mfa_oracle_bwd(const float* q, const float* k, const float* v, const float* 
     return failed ? -1 : 0;
 }
 
-/* Which mistake (0 = none) this build carries; the mutation test reads it. */
+/* Which mistake (0 = none) this compiled oracle carries; the mutation test reads it. */
 int mfa_oracle_mutant(void) { return ORACLE_MUTANT; }
