@@ -1,7 +1,7 @@
 """Benchmark of the fused attention forward (libmfa) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-decode] [--no-decode-len] [--no-softcap-window]
+                    [--no-decode] [--no-decode-len] [--no-softcap-window] [--no-single-head]
                     [--no-packed] [--no-bias-dropout] [--no-backward]
                     [--no-cpu-baseline]
 
@@ -17,6 +17,8 @@ HBM GB/s of compulsory traffic, and so is the decode over a device-held length
 under "decode_len".  "softcap_window" times the causal sliding-window prefill
 with soft-cap 50 (B=2, L=16384, Hq=16, Hkv=4, D=128, bf16, window 4096, 5 % of
 keys masked, inputs of standard deviation 2) in visible-pair TFLOP/s.
+"single_head_fp32" times the single-head causal fp32 workload (B=1, L=128,
+D=64) in microseconds per call.
 "packed_encoder" times the bidirectional encoder workload
 (B=8, L=8192, H=12, D=64, fp16, window 128, tail padding) twice: padded with a
 key mask through mfa_fwd, and packed without its padding through
@@ -270,6 +272,21 @@ def packed_encoder(steps: int, warmup: int, warmup_ms: float):
     return res
 
 
+def single_head_fp32(steps: int, warmup: int, warmup_ms: float):
+    """The single-head causal fp32 workload (B=1, L=128, D=64): bound by launch
+    latency, so it is reported in microseconds per call."""
+    import torch
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    w = wl.SINGLE_HEAD_CAUSAL_FP32
+    r, t = time_workload(w, steps, warmup, warmup_ms=warmup_ms)
+    del t
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "path": r["path"], "unit": "us per call",
+            "us_per_call_wall": round(r["wall_ms"] * 1e3, 2), "us_per_call_kernel": round(r["event_ms_avg"] * 1e3, 2),
+            "visible_pairs": r["pairs"]}
+
+
 def softcap_window(steps: int, warmup: int, warmup_ms: float):
     """The causal sliding-window GQA prefill with soft-cap and a sparse key mask
     (MFMA kernel, soft-capped and masked instantiation)."""
@@ -413,6 +430,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-len", action="store_true")
     ap.add_argument("--no-softcap-window", action="store_true")
+    ap.add_argument("--no-single-head", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--no-bias-dropout", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
@@ -525,6 +543,9 @@ def main():
                        "frac": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                        "algorithmic_bytes_per_launch": r["bytes"]}
         line["decode_len"] = dl
+
+    if not args.no_single_head and w is not wl.SINGLE_HEAD_CAUSAL_FP32:
+        line["single_head_fp32"] = single_head_fp32(max(20, args.steps), max(5, args.warmup), 50.0)
 
     if not args.no_softcap_window and w is not wl.CAUSAL_WINDOW_SOFTCAP_BF16:
         tensors = None

@@ -202,6 +202,24 @@ def test_pool_calls_leave_the_default_pool_alone():
     assert default_threshold() == before
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,L,Hq,Hkv,wg64", [(2, 512, 8, 2, 128), (2, 1024, 16, 4, 512)],
+                         ids=["4_rows_per_wave", "16_rows_per_wave"])
+def test_fp32_kernel_grid_forms_sampled_rows(D, B, L, Hq, Hkv, wg64):
+    """fp32 inputs take the generic kernel, whose rows per wave follow the
+    number of 64-row workgroups (below 64: 1, below 512: 4, else 16; the small
+    shapes elsewhere take 1): the 4- and 16-row forms on sampled rows."""
+    w = wl.Workload(f"fp32_B{B}_L{L}_H{Hq}_D{D}", "f32", B, L, L, Hq, Hkv, D, True, window=700,
+                    mask="random_frac", mask_frac=0.2)
+    assert (w.Lq + 63) // 64 * w.Hq * w.B == wg64
+    q, k, v, m, out, lse = run_case(w)
+    rows = pu.sample_rows(w, n_random=8)
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, q_offset=w.q_offset, softcap=w.softcap)
+    O, L_, _ = default_oracle().rows(q, k, v, rows, key_mask=m, nthreads=pu.ORACLE_THREADS, **kw)
+    og, lg = pu.gather_rows(out, lse, rows)
+    pu.compare(w.dtype, og, lg, O, L_, w.name)
+
+
 def test_empty_torch_tensors():
     """Calls whose tensors hold no element, made with torch's empty tensors
     (null data pointers): they succeed, and the backward with no query rows

@@ -18,15 +18,17 @@
 namespace mfa {
 namespace {
 
-constexpr int GBM = 64;  // query rows per workgroup
 constexpr int GBN = 64;  // keys per tile
-constexpr int ROWS_PER_WAVE = 16;
 
 template <typename T>
 __device__ inline float to_f32(T x) { return static_cast<float>(x); }
 
-template <typename T, int D>
+// RPW query rows per wave, 4 RPW per workgroup: 16 where the grid is large,
+// 4 or 1 for small problems, which then spread over more workgroups.
+template <typename T, int D, int RPW>
 __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
+    constexpr int ROWS_PER_WAVE = RPW;
+    constexpr int GBM = 4 * RPW;   // query rows per workgroup
     __shared__ float sQ[GBM][D + 4];
     __shared__ float sK[GBN][D + 4];
     __shared__ float sV[GBN][D];
@@ -204,14 +206,23 @@ __global__ __launch_bounds__(256) void varlen_rows_kernel(const int* __restrict_
     seq_bounds[2 * i + 1] = k1;
 }
 
+template <typename T, int RPW>
+hipError_t launch_generic_r(const FwdArgs& a, hipStream_t s) {
+    dim3 grid((a.Lq + 4 * RPW - 1) / (4 * RPW), a.Hq, a.B);
+    if (a.D == 64)
+        hipLaunchKernelGGL((generic_fwd_kernel<T, 64, RPW>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((generic_fwd_kernel<T, 128, RPW>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_generic_t(const FwdArgs& a, hipStream_t s) {
-    dim3 grid((a.Lq + GBM - 1) / GBM, a.Hq, a.B);
-    if (a.D == 64)
-        hipLaunchKernelGGL((generic_fwd_kernel<T, 64>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((generic_fwd_kernel<T, 128>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    // fewer 64-row workgroups than two per CU: 16-row workgroups instead, and
+    // 4-row ones below a quarter of the CUs
+    const int64_t wg64 = (int64_t)((a.Lq + 63) / 64) * a.Hq * a.B;
+    if (wg64 < 64) return launch_generic_r<T, 1>(a, s);
+    return wg64 < 512 ? launch_generic_r<T, 4>(a, s) : launch_generic_r<T, 16>(a, s);
 }
 
 }  // namespace
