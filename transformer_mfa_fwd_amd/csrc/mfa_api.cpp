@@ -116,10 +116,11 @@ constexpr int kMaxDevices = 64;
 std::once_flag g_pool_once[kMaxDevices];
 hipMemPool_t g_pool[kMaxDevices] = {};
 
-// The library's own stream-ordered pool on device dev, created on first use:
-// freed workspace stays in it instead of going back to the driver after every
-// call.  The device's default pool is left as it is.  Null if it could not be
-// created (then the default pool serves).
+// The library's own stream-ordered pool on device dev, created on first use
+// and kept until the process ends: freed workspace stays in it instead of
+// going back to the driver after every call.  The device's default pool is
+// left as it is.  Null if it could not be created (then the default pool
+// serves).
 hipMemPool_t library_pool(int dev) {
     if (dev < 0 || dev >= kMaxDevices) return nullptr;
     std::call_once(g_pool_once[dev], [dev]() {
