@@ -413,8 +413,10 @@ def cpu_baseline(w, tensors, target_s: float = 12.0, seed: int = 0):
     _, _, nv = orc.rows(qc, kc, vc, sample, **kw)
     dt = time.perf_counter() - t0
     pairs = int(nv.sum())
+    total_pairs = visible_pairs(w, mc)
     return {"value": 4.0 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "pairs_per_s": round(pairs / dt),
+            "full_workload_s_extrapolated": round(total_pairs / (pairs / dt), 2),
             "sample": f"{n} of {len(rows)} query rows (seeded shuffle), {pairs} visible pairs, "
                       f"{dt:.1f} s, fp64 C oracle with {cores} threads"}
 
