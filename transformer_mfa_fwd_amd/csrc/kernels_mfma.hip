@@ -572,6 +572,9 @@ void prefill_kernel(FwdArgs a, int nqt) {
             (void)_rk; (void)_rv;
             MFA_PART1(sa, sa, 0, false);
         }
+        // The first iteration copies K of the tile after next into stage 0,
+        // which the scores above just read: every wave must be past them.
+        __syncthreads();
         while (true) {
             MFA_ITER(sa, sb, 0);
             if (!has_nxt) break;
