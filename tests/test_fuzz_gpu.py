@@ -295,3 +295,35 @@ def test_random_bias_dropout_forward_every_row(i):
     og = out.double().cpu().numpy().transpose(0, 2, 1, 3)
     pu.compare(dtype, og, lse.double().cpu().numpy(), O.transpose(0, 2, 1, 3), L, f"bias/dropout {i}",
                o_scale=1.0 / (1.0 - p))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_backward_longer_axes(i):
+    """mfa_bwd on 200-1500 query and 300-1500 key rows (many pipeline steps
+    per key block), options drawn as above, every gradient element."""
+    rng = np.random.default_rng(9000 + i)
+    dtype = str(rng.choice(["bf16", "f16"]))
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    Lk = int(rng.integers(300, 1501))
+    Lq = int(rng.integers(200, Lk + 1))
+    q_offset = int(rng.integers(0, Lk - Lq + 1))
+    causal = bool(rng.random() < 0.7)
+    window = 0 if rng.random() < 0.5 else int(rng.integers(1, Lk))
+    softcap = 0.0 if rng.random() < 0.7 else float(rng.uniform(5.0, 40.0))
+    mask = dict(mask=None) if rng.random() < 0.7 else dict(mask="random_frac", mask_frac=0.2)
+    p = float(rng.choice([0.1, 0.3])) if rng.random() < 0.3 else 0.0
+    w = wl.Workload(f"bwdlong{i}", dtype, 1, Lq, Lk, Hq, Hkv, D, causal, window=window, softcap=softcap, **mask)
+    print(f"\n[fuzz] backward longer {i}: {w} q_offset={q_offset} p={p}", flush=True)
+    q, k, v, m = wl.make_inputs(w, DEV, seed=i)
+    gen = torch.Generator(device="cpu").manual_seed(300 + i)
+    dout = torch.randn(q.shape, generator=gen).to(q.dtype).to(DEV)
+    kw = dict(causal=causal, window=window, q_offset=q_offset, softcap=softcap, key_mask=m, scale=w.scale,
+              dropout_p=p, seed=5 + i)
+    out, lse = mfa.fwd(q, k, v, **kw)
+    dq, dk, dv = mfa.bwd(q, k, v, out, dout, lse, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = default_oracle().bwd(q, k, v, dout, nthreads=pu.ORACLE_THREADS, **kw)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check_grad(name, got, ref, dtype, w.name)
