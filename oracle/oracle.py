@@ -219,6 +219,38 @@ class Oracle:
             O[b], L[b], N[b] = Ob[0], Lb[0], Nb[0]
         return O, L, N
 
+    def decode_masked(self, q, k, v, mask, *, scale, window=0, softcap=0.0, nthreads=1):
+        """Single-query decode over a fixed-capacity cache whose valid keys are
+        marked by a key mask (brotensor flash_attention.h,
+        flash_attention_decode_masked).  Batch b's query sits at position p,
+        the last key whose mask value is above 0.5; key j is kept when its
+        mask value is above 0.5 and, with window > 0, j > p - window (keys
+        [max(0, p - window + 1), p]); window <= 0 keeps every valid key.  A
+        batch without a valid key gets O = 0 and LSE = -inf.  That is the
+        plain causal forward at one query row with q_offset = p, the window
+        and the mask, which is how it is evaluated here.
+        q [B, 1, Hq, D]; k, v [B, Lmax, Hkv, D]; mask [B, Lmax].  Returns
+        O [B, 1, Hq, D], LSE [B, Hq, 1] and the visible counts [B, Hq, 1].
+        """
+        q, k, v, m = _f32(q), _f32(k), _f32(v), _f32(mask)
+        B, R, Hq, D = q.shape
+        assert R == 1, "one query row per batch"
+        Lmax = k.shape[1]
+        assert m.shape == (B, Lmax)
+        O = np.zeros((B, 1, Hq, D), np.float64)
+        L = np.full((B, Hq, 1), -np.inf, np.float64)
+        N = np.zeros((B, Hq, 1), np.int64)
+        for b in range(B):
+            valid = np.nonzero(m[b] > 0.5)[0]
+            if valid.size == 0:
+                continue
+            p = int(valid[-1])
+            Ob, Lb, Nb = self.full(q[b:b + 1], k[b:b + 1], v[b:b + 1], scale=scale, causal=True,
+                                   window=window, q_offset=p, softcap=softcap, key_mask=m[b:b + 1],
+                                   nthreads=nthreads)
+            O[b], L[b], N[b] = Ob[0], Lb[0], Nb[0]
+        return O, L, N
+
     def packed_qkv(self, qkv, seq_bounds, num_heads, *, scale, window=0, softcap=0.0, nthreads=1):
         """Bidirectional attention over sequences packed back to back in one
         fused QKV tensor (brotensor flash_attention.h,

@@ -515,6 +515,121 @@ def pin_decode_len_ignores_rows_past_length(orc):
 
 
 # ---------------------------------------------------------------------------
+# single-query decode over a fixed-capacity cache with a key mask
+# ---------------------------------------------------------------------------
+
+def decode_masked_visibility(mask_b, window):
+    """[Lmax] kept keys as brotensor flash_attention.h states them for
+    flash_attention_decode_masked: the query's position p is the last valid
+    key (mask value > 0.5); a key is kept when it is valid and, with
+    window > 0, lies after p - window."""
+    valid = np.asarray(mask_b, np.float64) > 0.5
+    if not valid.any():
+        return valid
+    p = int(np.max(np.nonzero(valid)[0]))
+    j = np.arange(valid.size)
+    return valid & ((j > p - window) if window > 0 else True)
+
+
+def dense_decode_masked(q, k, v, mask, *, scale, window, softcap=0.0):
+    """Full score row over the whole capacity with the literal kept set."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    B, _, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    O = np.zeros((B, 1, Hq, D))
+    L = np.full((B, Hq, 1), -np.inf)
+    for b in range(B):
+        vis = decode_masked_visibility(mask[b], window)
+        if not vis.any():
+            continue
+        for h in range(Hq):
+            s = scale * (k[b, :, h // g, :] @ q[b, 0, h, :])
+            if softcap > 0:
+                s = softcap * np.tanh(s / softcap)
+            s = np.where(vis, s, -np.inf)
+            lse = logsumexp(s)
+            O[b, 0, h, :] = np.exp(s - lse) @ v[b, :, h // g, :]
+            L[b, h, 0] = lse
+    return O, L
+
+
+def _decode_masks(rng, B, Lmax):
+    """Prefix masks, masks with holes, single valid keys at either end, and a
+    batch with no valid key."""
+    m = np.zeros((B, Lmax), np.float32)
+    m[0, :Lmax // 2] = 1.0                                # prefix
+    m[1] = (rng.random(Lmax) < 0.6).astype(np.float32)    # holes
+    m[2, 0] = 1.0                                         # only key 0
+    m[3, Lmax - 1] = 1.0                                  # only the last key
+    m[4] = 1.0                                            # full capacity
+    m[5, 3:Lmax - 4] = (rng.random(Lmax - 7) < 0.3)       # holes, last valid key inside
+    m[5, Lmax - 5] = 0.9                                  # above 0.5: valid
+    m[5, Lmax - 4:] = 0.5                                 # not above 0.5: invalid
+    # m[6] stays all zero: no valid key
+    return m
+
+
+def pin_decode_masked_matches_dense(orc):
+    """Against the dense formulation with the literal kept set: windows off,
+    negative, 1, short and longer than the valid span; GQA; soft-cap."""
+    rng = _rng(31)
+    B, Lmax, D = 7, 23, 8
+    for Hq, Hkv, window, softcap in [(4, 2, 0, 0.0), (4, 1, -3, 0.0), (2, 2, 1, 0.0), (4, 2, 3, 2.0),
+                                     (6, 3, 7, 0.0), (2, 1, 100, 5.0)]:
+        q = _rand(rng, (B, 1, Hq, D), 2.0)
+        k, v = _rand(rng, (B, Lmax, Hkv, D), 2.0), _rand(rng, (B, Lmax, Hkv, D))
+        m = _decode_masks(rng, B, Lmax)
+        O, L, n = orc.decode_masked(q, k, v, m, scale=0.4, window=window, softcap=softcap)
+        Od, Ld = dense_decode_masked(q, k, v, m, scale=0.4, window=window, softcap=softcap)
+        _close(O, Od, TIGHT, f"decode_masked O w={window}")
+        _close(L, Ld, TIGHT, f"decode_masked LSE w={window}")
+        for b in range(B):
+            cnt = int(decode_masked_visibility(m[b], window).sum())
+            assert np.all(n[b] == cnt), (b, n[b], cnt)
+
+
+def pin_decode_masked_prefix_equals_decode_at_valid_length(orc):
+    """mask = [1] * n + [0] * (Lmax - n) gives exactly (bit for bit) the
+    plain single-query decode over the first n keys, with or without a
+    window, as the page states for this function."""
+    rng = _rng(32)
+    Lmax, Hq, Hkv, D = 40, 4, 2, 8
+    for n in (1, 2, 17, 39, 40):
+        for window, softcap in ((0, 0.0), (5, 0.0), (12, 3.0)):
+            q = _rand(rng, (1, 1, Hq, D), 2.0)
+            k, v = _rand(rng, (1, Lmax, Hkv, D)), _rand(rng, (1, Lmax, Hkv, D))
+            m = np.zeros((1, Lmax), np.float32)
+            m[0, :n] = 1.0
+            O, L, _ = orc.decode_masked(q, k, v, m, scale=0.3, window=window, softcap=softcap)
+            Od, Ld, _ = orc.full(q, k[:, :n], v[:, :n], scale=0.3, causal=True, window=window, q_offset=n - 1,
+                                 softcap=softcap)
+            assert np.array_equal(O, Od) and np.array_equal(L, Ld), (n, window)
+
+
+def pin_decode_masked_zero_query_closed_form(orc):
+    """Q = 0: the output is the mean of the kept V rows and LSE = ln(count),
+    with the kept set from the literal rule; no valid key: O = 0,
+    LSE = -inf."""
+    rng = _rng(33)
+    B, Lmax, Hq, Hkv, D = 7, 19, 4, 2, 8
+    q = np.zeros((B, 1, Hq, D), np.float32)
+    k, v = _rand(rng, (B, Lmax, Hkv, D)), _rand(rng, (B, Lmax, Hkv, D))
+    m = _decode_masks(rng, B, Lmax)
+    for window in (0, 1, 4):
+        O, L, _ = orc.decode_masked(q, k, v, m, scale=0.9, window=window, softcap=1.5)
+        for b in range(B):
+            vis = decode_masked_visibility(m[b], window)
+            for h in range(Hq):
+                if not vis.any():
+                    assert np.all(O[b, 0, h] == 0) and L[b, h, 0] == -np.inf
+                    continue
+                mean = v[b, vis, h // (Hq // Hkv), :].astype(np.float64).mean(0)
+                assert np.max(np.abs(O[b, 0, h] - mean)) <= TIGHT, (b, h, window)
+                assert abs(L[b, h, 0] - math.log(int(vis.sum()))) <= TIGHT
+
+
+# ---------------------------------------------------------------------------
 # sequences packed back to back in one fused QKV tensor
 # ---------------------------------------------------------------------------
 
@@ -944,6 +1059,9 @@ ALL_PINS = [
     pin_decode_len_matches_dense,
     pin_decode_len_zero_query_closed_form,
     pin_decode_len_ignores_rows_past_length,
+    pin_decode_masked_matches_dense,
+    pin_decode_masked_prefix_equals_decode_at_valid_length,
+    pin_decode_masked_zero_query_closed_form,
     pin_packed_matches_dense,
     pin_packed_zero_query_closed_form,
     pin_packed_sequences_are_independent,
