@@ -1,7 +1,8 @@
 """Benchmark of the fused attention forward (libmfa) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-decode] [--no-decode-len] [--no-softcap-window] [--no-single-head]
+                    [--no-decode] [--no-decode-len] [--no-decode-masked] [--no-softcap-window]
+                    [--no-single-head]
                     [--no-packed] [--no-bias-dropout] [--no-backward]
                     [--no-cpu-baseline]
 
@@ -14,7 +15,9 @@ The long-cache decode (B=64, Lk=32768, Hq=32, Hkv=8, D=128, bf16; split over
 keys plus combine) is timed in the same run and reported under "decode" in
 HBM GB/s of compulsory traffic, and so is the decode over a device-held length
 (mfa_decode_len: 4 draft rows per batch on the same cache, full and half-full)
-under "decode_len".  "softcap_window" times the causal sliding-window prefill
+under "decode_len", and the decode over a cache whose valid keys a device mask
+marks (mfa_decode_masked: all valid, valid keys with holes, and all valid with
+a 4096-key window) under "decode_masked".  "softcap_window" times the causal sliding-window prefill
 with soft-cap 50 (B=2, L=16384, Hq=16, Hkv=4, D=128, bf16, window 4096, 5 % of
 keys masked, inputs of standard deviation 2) in visible-pair TFLOP/s.
 "single_head_fp32" times the single-head causal fp32 workload (B=1, L=128,
@@ -28,10 +31,15 @@ with dropout 0.1 and "dropout" dropout 0.1 alone (the MFMA kernel as well).  "ba
 the causal GQA prefill shape, and "backward_bias_dropout" the same with the mask
 and dropout 0.1.
 
+Calls take a caller-owned workspace (the allocation-free forms); the headline
+is also timed through mfa_fwd's stream-ordered pool ("ms_per_step_pool").
 Rank 0 prints one JSON line.  "roofline" describes the dominant kernel: its
-average duration comes from HIP events recorded on the launch stream around
-every timed call, and "traffic" is read from the committed rocprofv3 counter
-summary in profiles/ (null when the kernel sources changed since).
+average duration comes from HIP events that libmfa records on the launch
+stream immediately around that kernel in every timed call
+(mfa_set_kernel_events), and "traffic" is read from the committed rocprofv3
+counter summary in profiles/ (null when the kernel sources changed since).
+"warmup" is the requested count; "warmup_steps_run" the calls actually run
+before timing, which continue until --warmup-ms has passed.
 "cpu_baseline" times the fp64 CPU oracle on a bounded row sample of the same
 workload on this host's cores.
 """
@@ -126,7 +134,63 @@ def measured_traffic(name: str, sources) -> tuple:
 # timing
 # ---------------------------------------------------------------------------
 
-def time_workload(w, steps: int, warmup: int, seed: int = 0, warmup_ms: float = 0.0):
+def timed(fn, steps: int, warmup: int, warmup_ms: float = 0.0) -> dict:
+    """Run fn() W times untimed (continued until warmup_ms has passed too: the
+    GPU clocks take a few hundred milliseconds of load to settle), then K
+    timed times back to back with nothing between the calls (wall clock, and
+    HIP events around the whole loop), then K more with HIP events on the
+    launch stream around each call and, attached by libmfa to its main
+    kernel's dispatch (mfa_set_kernel_events), around that kernel.  Returns
+    wall ms per call, GPU ms per call of the plain loop, the per-call
+    events' averages and the number of warm-up calls run."""
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+
+    n_warm = 0
+    t_w = time.perf_counter()
+    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
+        fn()
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # plain loop: the throughput a caller sees
+    s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s0.record(stream)
+    for _ in range(steps):
+        fn()
+    e0.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    gpu_ms = s0.elapsed_time(e0) / steps
+
+    # instrumented loop: each call and its main kernel
+    def events():
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:         # created on first record
+            a.record(stream)
+            b.record(stream)
+        return ev
+    call_ev, kern_ev = events(), events()
+    torch.cuda.synchronize()
+    for (cs, ce), (ks, ke) in zip(call_ev, kern_ev):
+        mfa.set_kernel_events(ks, ke)
+        cs.record(stream)
+        fn()
+        ce.record(stream)
+    torch.cuda.synchronize()
+    mfa.set_kernel_events(None, None)
+    kern = [a.elapsed_time(b) for a, b in kern_ev]
+    return dict(wall_ms=wall_ms, gpu_ms=gpu_ms, call_ms=float(np.mean([a.elapsed_time(b) for a, b in call_ev])),
+                kernel_ms=float(np.mean(kern)), kernel_ms_min=float(np.min(kern)), warmup_run=n_warm)
+
+
+def time_workload(w, steps: int, warmup: int, seed: int = 0, warmup_ms: float = 0.0, pool: bool = False):
+    """mfa_fwd on workload w with a caller-owned workspace (mfa_fwd_ws, the
+    allocation-free form) or, with ``pool``, from the library's pool."""
     import torch
     import transformer_mfa_fwd_amd as mfa
     from transformer_mfa_fwd_amd import workloads as wl
@@ -134,35 +198,15 @@ def time_workload(w, steps: int, warmup: int, seed: int = 0, warmup_ms: float = 
     q, k, v, m = wl.make_inputs(w, "cuda", seed)
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=q.device)
+    nbytes = mfa.workspace_size(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)
+    ws = None if pool or nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     kw = dict(causal=w.causal, window=w.window, q_offset=w.q_offset, softcap=w.softcap,
-              key_mask=m, scale=w.scale, out=out, lse=lse)
-    # W untimed steps, continued until warmup_ms has passed as well: the GPU
-    # clocks take a few hundred milliseconds of load to settle
-    n_warm = 0
-    t_w = time.perf_counter()
-    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
-        mfa.fwd(q, k, v, **kw)
-        n_warm += 1
-        if n_warm % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
-        mfa.fwd(q, k, v, **kw)
-        e.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    per_call = [s.elapsed_time(e) for s, e in ev]
-    res = dict(wall_ms=wall_ms, event_ms_avg=float(np.mean(per_call)),
-               event_ms_min=float(np.min(per_call)), event_ms_median=float(np.median(per_call)),
-               path=mfa.plan(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)[0],
-               pairs=visible_pairs(w, None if m is None else m.cpu()),
-               bytes=algorithmic_bytes(w, q), warmup_steps=n_warm)
-    return res, (q, k, v, m)
+              key_mask=m, scale=w.scale, out=out, lse=lse, workspace=ws)
+    r = timed(lambda: mfa.fwd(q, k, v, **kw), steps, warmup, warmup_ms)
+    r.update(path=mfa.plan(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)[0],
+             pairs=visible_pairs(w, None if m is None else m.cpu()), bytes=algorithmic_bytes(w, q))
+    del ws, out, lse
+    return r, (q, k, v, m)
 
 
 def time_decode_len(w, lens_cpu, steps: int, warmup: int, warmup_ms: float = 0.0, seed: int = 0):
@@ -179,54 +223,51 @@ def time_decode_len(w, lens_cpu, steps: int, warmup: int, warmup_ms: float = 0.0
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=q.device)
     nbytes = mfa.decode_len_workspace_size(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    n_warm = 0
-    t_w = time.perf_counter()
-    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
-        mfa.decode_len(q, k, v, d_len, out=out, lse=lse, workspace=ws)
-        n_warm += 1
-        if n_warm % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t0 = time.perf_counter()
-    for s_, e_ in ev:
-        s_.record(stream)
-        mfa.decode_len(q, k, v, d_len, out=out, lse=lse, workspace=ws)
-        e_.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    r = timed(lambda: mfa.decode_len(q, k, v, d_len, out=out, lse=lse, workspace=ws), steps, warmup, warmup_ms)
     el = q.element_size()
     valid = int(lens_cpu.clamp(0, w.Lk).sum())
-    nbytes_alg = (2 * q.numel() * el + lse.numel() * 4 + w.B * 4 + 2 * valid * w.Hkv * w.D * el)
+    r["bytes"] = (2 * q.numel() * el + lse.numel() * 4 + w.B * 4 + 2 * valid * w.Hkv * w.D * el)
+    r["valid_keys"] = valid
     del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
-    return dict(wall_ms=wall_ms, kernel_ms=kern_ms, bytes=nbytes_alg, valid_keys=valid)
+    return r
+
+
+def time_decode_masked(w, mask_cpu, window: int, steps: int, warmup: int, warmup_ms: float = 0.0, seed: int = 0):
+    """mfa_decode_masked on workload w (one query row per batch, Lk = capacity)
+    with the given [B, Lk] validity mask.  Algorithmic bytes: Q, O, the LSE,
+    the mask and the K and V rows of the 32-key tiles that hold a used key
+    (the tiles the kernel must read)."""
+    import torch
+    import transformer_mfa_fwd_amd as mfa
+    from transformer_mfa_fwd_amd import workloads as wl
+
+    q, k, v, _ = wl.make_inputs(w, "cuda", seed)
+    d_mask = mask_cpu.to("cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, 1), dtype=torch.float32, device=q.device)
+    nbytes = mfa.decode_masked_workspace_size(w.B, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    r = timed(lambda: mfa.decode_masked(q, k, v, d_mask, window=window, out=out, lse=lse, workspace=ws),
+              steps, warmup, warmup_ms)
+    el = q.element_size()
+    tiles = 0
+    for b in range(w.B):
+        valid = np.nonzero(mask_cpu[b].numpy() > 0.5)[0]
+        if valid.size == 0:
+            continue
+        used = valid[valid > valid[-1] - window] if window > 0 else valid
+        tiles += np.unique(used // 32).size
+    r["bytes"] = 2 * q.numel() * el + lse.numel() * 4 + mask_cpu.numel() * 4 + 2 * tiles * 32 * w.Hkv * w.D * el
+    del q, k, v, out, lse, ws, d_mask
+    torch.cuda.empty_cache()
+    return r
 
 
 def time_calls(fn, steps: int, warmup: int, warmup_ms: float = 0.0):
-    """Average wall ms per call and average HIP-event ms per call of fn()."""
-    import torch
-    n_warm = 0
-    t_w = time.perf_counter()
-    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < warmup_ms:
-        fn()
-        n_warm += 1
-        if n_warm % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t0 = time.perf_counter()
-    for s_, e_ in ev:
-        s_.record(stream)
-        fn()
-        e_.record(stream)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    """(wall ms per call, main-kernel ms per call) of fn()."""
+    r = timed(fn, steps, warmup, warmup_ms)
+    return r["wall_ms"], r["kernel_ms"]
 
 
 def packed_encoder(steps: int, warmup: int, warmup_ms: float):
@@ -283,7 +324,7 @@ def single_head_fp32(steps: int, warmup: int, warmup_ms: float):
     del t
     torch.cuda.empty_cache()
     return {"workload": w.name, "path": r["path"], "unit": "us per call",
-            "us_per_call_wall": round(r["wall_ms"] * 1e3, 2), "us_per_call_kernel": round(r["event_ms_avg"] * 1e3, 2),
+            "us_per_call_wall": round(r["wall_ms"] * 1e3, 2), "us_per_call_kernel": round(r["kernel_ms"] * 1e3, 2),
             "visible_pairs": r["pairs"]}
 
 
@@ -298,7 +339,7 @@ def softcap_window(steps: int, warmup: int, warmup_ms: float):
     del t
     torch.cuda.empty_cache()
     flops = 4.0 * w.D * r["pairs"]
-    kern = r["event_ms_avg"]
+    kern = r["kernel_ms"]
     return {"workload": w.name, "path": r["path"], "unit": "TFLOP/s", "input_std": w.std,
             "ms_per_step": round(r["wall_ms"], 5), "kernel_ms_avg": round(kern, 5),
             "visible_pairs": r["pairs"], "value": round(flops / (r["wall_ms"] * 1e-3) / 1e12, 2),
@@ -376,8 +417,8 @@ def backward(steps: int, warmup: int, warmup_ms: float, extras: bool = False):
     out, lse = mfa.fwd(q, k, v, **kw)
     dout = torch.randn(q.shape, device="cuda").to(q.dtype)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    wall, kern = time_calls(lambda: mfa.bwd(q, k, v, out, dout, lse, dq=dq, dk=dk, dv=dv, **kw),
-                            steps, warmup, warmup_ms)
+    r = timed(lambda: mfa.bwd(q, k, v, out, dout, lse, dq=dq, dk=dk, dv=dv, **kw), steps, warmup, warmup_ms)
+    wall, kern = r["wall_ms"], r["call_ms"]     # the backward's three kernels
     pairs = visible_pairs(w, None)
     res = {"workload": w.name, "api": "mfa_bwd", "path": "mfma", "unit": "TFLOP/s",
            "flops_per_pair": 10 * w.D, "ms_per_step": round(wall, 5), "kernel_ms_avg": round(kern, 5),
@@ -431,6 +472,7 @@ def main():
     ap.add_argument("--workload", default="gqa_causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-len", action="store_true")
+    ap.add_argument("--no-decode-masked", action="store_true")
     ap.add_argument("--no-softcap-window", action="store_true")
     ap.add_argument("--no-single-head", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
@@ -467,7 +509,7 @@ def main():
     res, tensors = time_workload(w, args.steps, args.warmup, warmup_ms=args.warmup_ms)
     flops = 4.0 * w.D * res["pairs"]
     tflops_wall = flops / (res["wall_ms"] * 1e-3) / 1e12
-    kern_ms = res["event_ms_avg"]
+    kern_ms = res["kernel_ms"]
     is_prefill = res["path"] in ("mfma", "generic")
     traffic, tnote = measured_traffic(f"{'prefill' if is_prefill else 'decode'}_{w.name}.counters.json",
                                       PREFILL_SOURCES if is_prefill else DECODE_SOURCES)
@@ -482,7 +524,8 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = traffic
-    roof["kernel"] = {"mfma": "prefill_kernel", "generic": "generic_fwd_kernel",
+    roof["kernel"] = {"mfma": "v16_prepass_kernel + prefill_kernel" if w.dtype == "bf16" else "prefill_kernel",
+                      "generic": "generic_fwd_kernel",
                       "split_decode": "decode_split_kernel + decode_combine_kernel"}[res["path"]]
     roof["kernel_ms_avg"] = round(kern_ms, 5)
     roof["algorithmic_flops_per_launch"] = flops
@@ -494,15 +537,29 @@ def main():
         "metric": METRIC,
         "value": round(tflops_wall if is_prefill else res["bytes"] / (res["wall_ms"] * 1e-3) / 1e9, 2),
         "unit": "TFLOP/s" if is_prefill else "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": res["warmup_steps"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_steps_run": res["warmup_run"], "warmup_ms": args.warmup_ms,
         "ms_per_step": round(res["wall_ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Lq": w.Lq, "Lk": w.Lk, "Hq": w.Hq, "Hkv": w.Hkv,
                    "D": w.D, "causal": w.causal, "window": w.window, "softcap": w.softcap,
-                   "key_mask": w.mask, "path": res["path"], "visible_pairs": res["pairs"]},
+                   "key_mask": w.mask, "path": res["path"], "visible_pairs": res["pairs"],
+                   "api": "mfa_fwd_ws (caller-owned workspace)"},
         "roofline": roof,
+        # GPU time per call of the plain loop; and, from the instrumented
+        # loop, the whole call (events around it) less the main kernel (for
+        # bf16 the V conversion plus the prefill): key-mask packing, launch
+        # gaps and the event markers themselves
+        "gpu_ms_per_step": round(res["gpu_ms"], 5),
+        "call_ms_avg": round(res["call_ms"], 5),
+        "outside_main_kernel_ms": round(res["call_ms"] - kern_ms, 5),
     }
+    # the same calls with the workspace from the library's stream-ordered pool (mfa_fwd)
+    del tensors
+    torch.cuda.empty_cache()
+    rp, tensors = time_workload(w, args.steps, args.warmup, warmup_ms=50.0, pool=True)
+    line["ms_per_step_pool"] = round(rp["wall_ms"], 5)
 
     if not args.no_decode and w is not wl.LONG_CACHE_DECODE_BF16:
         del tensors
@@ -511,7 +568,7 @@ def main():
         rd, td = time_workload(wd, max(10, args.steps // 2), max(3, args.warmup // 2),
                                warmup_ms=args.warmup_ms)
         dtraffic, dnote = measured_traffic(f"decode_{wd.name}.counters.json", DECODE_SOURCES)
-        dk = rd["event_ms_avg"]
+        dk = rd["kernel_ms"]
         line["decode"] = {
             "workload": wd.name, "path": rd["path"], "unit": "GB/s",
             "value": round(rd["bytes"] / (rd["wall_ms"] * 1e-3) / 1e9, 1),
@@ -545,6 +602,26 @@ def main():
                        "frac": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                        "algorithmic_bytes_per_launch": r["bytes"]}
         line["decode_len"] = dl
+
+    if not args.no_decode_masked:
+        tensors = None
+        torch.cuda.empty_cache()
+        wm = wl.LONG_CACHE_DECODE_BF16
+        dm = {"workload": wm.name, "api": "mfa_decode_masked", "unit": "GB/s", "capacity": wm.Lk,
+              "peak": PEAK_HBM_GBS,
+              "bytes_note": "Q, O, LSE, the mask and the K/V rows of every 32-key tile holding a used key"}
+        full = torch.ones((wm.B, wm.Lk))
+        holes = wl.make_cache_masks(wm.B, wm.Lk, seed=3, edges=False)
+        for tag, mask, window in (("full", full, 0), ("holes", holes, 0), ("window4096", full, 4096)):
+            r = time_decode_masked(wm, mask, window, max(10, args.steps // 2), max(3, args.warmup // 2),
+                                   warmup_ms=args.warmup_ms)
+            dm[tag] = {"window": window, "valid_keys": int((mask > 0.5).sum()),
+                       "value": round(r["bytes"] / (r["wall_ms"] * 1e-3) / 1e9, 1),
+                       "ms_per_step": round(r["wall_ms"], 5), "kernel_ms_avg": round(r["kernel_ms"], 5),
+                       "achieved": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                       "frac": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes_per_launch": r["bytes"]}
+        line["decode_masked"] = dm
 
     if not args.no_single_head and w is not wl.SINGLE_HEAD_CAUSAL_FP32:
         line["single_head_fp32"] = single_head_fp32(max(20, args.steps), max(5, args.warmup), 50.0)

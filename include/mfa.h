@@ -94,6 +94,13 @@ typedef enum {
  * stream-ordered memory pool that the library creates on each device on first
  * use (it keeps freed memory for later calls and never changes the device's
  * default pool) and is released in stream order.
+ *
+ * Precision: fp16/bf16 inputs multiply in their own type with fp32
+ * accumulation; the softmax weights enter P.V as fp16 (11 significant bits)
+ * for both, so a bf16 call on the MFMA prefill first converts V to an fp16
+ * copy in the workspace (B * Lk * Hkv * D * 2 bytes, plus a flag byte per
+ * 64 keys).  A (batch, kv head) whose V holds a magnitude of 65504 or more
+ * runs on bf16 operands (8-bit weights) instead.
  */
 int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
             int B, int Lq, int Lk, int Hq, int Hkv, int D,
@@ -230,6 +237,49 @@ size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, in
                                      int splits);
 
 /*
+ * Single-query decode over a fixed-capacity KV cache whose valid rows are
+ * marked by a key mask in device memory (brotensor flash_attention.h,
+ * flash_attention_decode_masked: the graph-capturable twin of the plain
+ * decode, validity kept in the mask, fully masked key tiles skipped without
+ * touching K/V).  For batch b, key j is valid when d_mask[b*Lmax + j] > 0.5.
+ * The query's position p_b is the highest valid key index; key j is used
+ * when it is valid and, with window > 0, also j > p_b - window, i.e. j in
+ * [max(0, p_b - window + 1), p_b]; window <= 0 uses every valid key.  GQA,
+ * scale and soft-cap as in mfa_fwd.
+ *
+ *   q, out             [B, 1, Hq, D]     element type `dtype` (fp16 or bf16)
+ *   k_cache, v_cache   [B, Lmax, Hkv, D] element type `dtype`
+ *   lse                [B, Hq, 1]        float32, may be NULL
+ *   d_mask             [B, Lmax]         float32 in device memory, read by the
+ *                                        kernels when they run
+ *
+ * p_b is found on the device, so the launch shape depends only on B, Lmax,
+ * Hq, Hkv and D: the call can be captured once in a HIP graph and replayed
+ * while the caller rewrites d_mask between replays.  The key splits divide
+ * the tiles of [max(0, p_b - window + 1), p_b] (or [0, p_b]); tiles holding
+ * no valid key are skipped before any K/V read.  With the prefix mask of n
+ * valid keys the result is bit-identical to mfa_decode_len with R = 1,
+ * d_len[b] = n and the same split count (the same tiles and arithmetic).  A
+ * batch with no valid key gets O = 0 and LSE = -inf.  Requires D in
+ * {64, 128} and Hq/Hkv <= 16 (otherwise MFA_ERROR_NOT_SUPPORTED).  `splits`
+ * <= 0 chooses the split count from B, Hkv and Lmax.  The workspace holds the
+ * packed mask bits and the split partials: caller-owned (256-byte aligned, at
+ * least mfa_decode_masked_workspace_size bytes, not used by other work until
+ * this call's kernels finish), or NULL with ws_bytes = 0 for the
+ * stream-ordered pool (not for graph capture).  q, k_cache, v_cache and out
+ * 16-byte aligned, lse and d_mask 4-byte aligned.  Errors, ownership and
+ * streams as for mfa_fwd.
+ */
+int mfa_decode_masked(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                      const float* d_mask, int B, int Lmax, int Hq, int Hkv, int D,
+                      float scale, int window, float softcap, int dtype, int splits,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes mfa_decode_masked needs for these sizes and split count
+ * (`splits` <= 0: the count it would choose); 0 for unsupported arguments. */
+size_t mfa_decode_masked_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, int dtype, int splits);
+
+/*
  * Bidirectional self-attention over many independent sequences packed back to
  * back in one fused QKV tensor, with no padding (brotensor flash_attention.h,
  * flash_attention_packed_qkv_forward: the encoder-batching entry point).
@@ -252,7 +302,10 @@ size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, in
  * sequences containing their rows give unspecified results, but every access
  * stays inside the L rows.  D in {64, 128}; qkv and out 16-byte aligned, lse
  * and seq_bounds 4-byte aligned.  L = 0 succeeds without work.  Errors,
- * ownership and streams as for mfa_fwd; no workspace is needed.
+ * ownership and streams as for mfa_fwd.  fp16 and fp32 calls need no
+ * workspace; a bf16 call takes the fp16 copy of V that its P.V operands
+ * need (see mfa_fwd) from the stream-ordered pool, so capture bf16 calls in
+ * a graph only where stream-ordered allocation may be captured.
  */
 int mfa_packed_qkv_fwd(const void* qkv, const int* seq_bounds, void* out, float* lse,
                        int L, int H, int D, float scale, int window, float softcap, int dtype,
@@ -282,7 +335,8 @@ int mfa_packed_qkv_fwd(const void* qkv, const int* seq_bounds, void* out, float*
  * results, but every access stays inside the given tensors.  A first kernel
  * turns the prefix sums into per-row positions and key bounds in the
  * workspace: caller-owned (256-byte aligned, at least
- * mfa_varlen_workspace_size(total_q) bytes), or NULL with ws_bytes = 0 for the
+ * mfa_varlen_workspace_size(total_q, total_k, Hkv, D, dtype) bytes), or NULL
+ * with ws_bytes = 0 for the
  * stream-ordered pool.  batch >= 1 unless total_q = 0 (then nothing is done).
  * D in {64, 128}; alignment, errors, ownership and streams as for mfa_fwd.
  */
@@ -291,8 +345,9 @@ int mfa_varlen_fwd(const void* q, const void* k, const void* v, void* out, float
                    int Hq, int Hkv, int D, float scale, int causal, int window, float softcap, int dtype,
                    void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes mfa_varlen_fwd needs (0 when total_q <= 0). */
-size_t mfa_varlen_workspace_size(int total_q);
+/* Workspace bytes mfa_varlen_fwd needs (0 when total_q <= 0): the per-row
+ * positions and bounds, plus for bf16 the fp16 copy of V (see mfa_fwd). */
+size_t mfa_varlen_workspace_size(int total_q, int total_k, int Hkv, int D, int dtype);
 
 /* The path mfa_fwd would take for these arguments (an mfa_path value), and
  * the split count it would use (through *splits, may be NULL). */
@@ -303,6 +358,19 @@ const char* mfa_status_string(int status);
 
 /* Detail of the last failed call on this host thread ("" if none). */
 const char* mfa_last_error(void);
+
+/*
+ * Instrumentation.  begin and end are hipEvent_t handles (or NULL, the
+ * default, for none; created by the caller before use) that every later
+ * forward or decode call made on this host thread attaches to the launch of
+ * its main kernel as start and stop events (hipExtLaunchKernel), so that
+ * hipEventElapsedTime between them gives that dispatch's own duration: the
+ * prefill kernel (MFMA or fp32), for bf16 the conversion of V through the
+ * prefill kernel, or the split decode kernel through its combine kernel; not
+ * the key-mask packing or the varlen row prepass.  The caller keeps the
+ * events alive while they are set.  The backward uses neither.
+ */
+void mfa_set_kernel_events(void* begin, void* end);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int mfa_version(void);

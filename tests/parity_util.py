@@ -99,3 +99,35 @@ def compare(dtype: str, o_gpu, l_gpu, o_ref, l_ref, what: str = "", o_scale: flo
             assert lerr <= TOL_LSE, f"{what}: LSE error {lerr:.3e} > {TOL_LSE}"
         assert np.all(o_gpu[inf_ref] == 0.0), f"{what}: empty rows must be exactly 0"
     return float(err.max()) if err.size else 0.0, lerr
+
+
+# Gradient tolerance: fp32 arithmetic throughout (1e-4); 16-bit inputs also
+# round P and dS to the operand type and feed the backward libmfa's own
+# rounded O (1e-2).
+TOL_G = {"f32": 1e-4, "f16": 1e-2, "bf16": 1e-2}
+
+
+def compare_grad(name: str, got, ref, dtype: str, what: str = "", dropout_p: float = 0.0):
+    """Each gradient row (the D values of one query, key or value vector)
+    within TOL_G * max(1, max |g_ref| over that row) / (1 - dropout_p) + half
+    an ulp of the stored element.
+
+    The bound is per row rather than per element: an element is a sum over
+    many rows or keys whose terms can be much larger than their sum, and the
+    operand rounding errs relative to the terms, not to the sum (a measured
+    bf16 dV element of -0.057 built from terms near 1 is off by 0.014).  A
+    whole wrong row or key block still fails.  Kept weights carry the factor
+    1 / (1 - p) before they are rounded, so every term's rounding error grows
+    with it, as for the forward's O under dropout.  Returns the max abs
+    error."""
+    got = got.double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what} {name}: non-finite gradient"
+    err = np.abs(got - ref)
+    row_scale = np.maximum(1.0, np.abs(ref).max(axis=-1, keepdims=True)) if ref.size else ref
+    bound = TOL_G[dtype] * row_scale / (1.0 - dropout_p) + half_ulp(ref, dtype)
+    worst = int(np.argmax(err - bound)) if err.size else 0
+    assert err.size == 0 or err.flat[worst] <= bound.flat[worst], (
+        f"{what} {name}: |g - g_ref| = {err.flat[worst]:.3e} > {bound.flat[worst]:.3e} at flat index "
+        f"{worst} (g_ref {ref.flat[worst]:.3e}; max abs err {err.max():.3e})")
+    return float(err.max()) if err.size else 0.0

@@ -103,11 +103,25 @@ def test_forced_path_rejection():
 
 def test_workspace_size_and_plan():
     import torch
-    assert mfa.workspace_size(4, 2048, 2048, 32, 8, 128, torch.bfloat16) >= 4 * 32 * 8
+    # a bf16 prefill holds the fp16 copy of V
+    bf = mfa.workspace_size(4, 2048, 2048, 32, 8, 128, torch.bfloat16)
+    f16 = mfa.workspace_size(4, 2048, 2048, 32, 8, 128, torch.float16)   # key-mask words only
+    assert f16 >= 4 * 32 * 8 and bf - f16 >= 4 * 2048 * 8 * 128 * 2
     path, splits = mfa.plan(64, 1, 32768, 32, 8, 128, torch.bfloat16)
     assert path in ("split_decode", "generic", "mfma")
     p32, _ = mfa.plan(1, 128, 128, 1, 1, 64, torch.float32)
     assert p32 == "generic"
+
+
+def test_bf16_prefill_without_workspace_rejected_by_ws_form():
+    lib = mfa.load_library()
+    st = lib.mfa_fwd_ws(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], 2, 16, 16, 4, 2, 64, 0.125, 1, 0, 0, 0.0,
+                        None, 2, None, 0, None)
+    assert st == 1 and "workspace" in lib.mfa_last_error().decode()
+    # fp16 needs none
+    st = lib.mfa_fwd_ws(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], 0, 16, 16, 4, 2, 64, 0.125, 1, 0, 0, 0.0,
+                        None, 1, None, 0, None)
+    assert st == 0
 
 
 def call_len(**over):
@@ -155,6 +169,51 @@ def test_decode_len_empty_batch_and_workspace_size():
     assert mfa.decode_len_workspace_size(64, 5, 32768, 32, 8, 128, torch.bfloat16) == 0
     assert mfa.decode_len_workspace_size(2, 1, 64, 8, 2, 128, torch.bfloat16, splits=3) >= \
         2 * 8 * 3 * (128 + 2) * 4
+
+
+def call_masked(**over):
+    lib = mfa.load_library()
+    a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], lse=FAKE[4], d_mask=FAKE[5], B=2, Lmax=64,
+             Hq=8, Hkv=2, D=128, scale=0.1, window=0, softcap=0.0, dtype=2, splits=0, ws=None, ws_bytes=0)
+    a.update(over)
+    return lib.mfa_decode_masked(a["q"], a["k"], a["v"], a["out"], a["lse"], a["d_mask"], a["B"],
+                                 a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["window"],
+                                 a["softcap"], a["dtype"], a["splits"], a["ws"], a["ws_bytes"], None)
+
+
+MASKED_INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(out=None), dict(d_mask=None),
+    dict(B=-1), dict(Lmax=0), dict(Hq=0), dict(Hkv=0), dict(D=0), dict(Hq=6, Hkv=4),
+    dict(scale=float("nan")), dict(softcap=float("inf")),
+    dict(q=ctypes.c_void_p(0x10008)), dict(lse=ctypes.c_void_p(0x10002)),
+    dict(d_mask=ctypes.c_void_p(0x10001)),
+    dict(ws=None, ws_bytes=1024), dict(ws=ctypes.c_void_p(0x10010), ws_bytes=1 << 30),
+    dict(ws=ctypes.c_void_p(0x10000), ws_bytes=256),
+]
+
+
+@pytest.mark.parametrize("over", MASKED_INVALID, ids=lambda d: ",".join(f"{k}" for k in d))
+def test_decode_masked_invalid_arguments_rejected(over):
+    assert call_masked(**over) == 1, over
+    assert mfa.load_library().mfa_last_error().decode()
+
+
+@pytest.mark.parametrize("over", [dict(D=96), dict(dtype=0), dict(dtype=5), dict(Hq=32, Hkv=1)])
+def test_decode_masked_unsupported_rejected(over):
+    assert call_masked(**over) == 2, over
+
+
+def test_decode_masked_empty_batch_and_workspace_size():
+    import torch
+    assert call_masked(B=0) == 0
+    n = mfa.decode_masked_workspace_size(64, 32768, 32, 8, 128, torch.bfloat16)
+    s = ctypes.c_int(0)
+    mfa.load_library().mfa_fwd_plan(64, 1, 32768, 32, 8, 128, 2, ctypes.byref(s))
+    # packed mask bits, then (m, l) and D partial sums for every (batch, head, split)
+    assert n >= 64 * (32768 // 64) * 8 + 64 * 32 * s.value * (128 + 2) * 4
+    assert mfa.decode_masked_workspace_size(64, 32768, 32, 1, 128, torch.bfloat16) == 0
+    assert mfa.decode_masked_workspace_size(2, 100, 8, 2, 64, torch.float16, splits=3) >= \
+        2 * 2 * 8 + 2 * 8 * 3 * (64 + 2) * 4
 
 
 def call_packed(**over):
@@ -217,8 +276,11 @@ def test_varlen_unsupported_rejected(over):
 def test_varlen_empty_and_workspace_size():
     assert call_varlen(Tq=0) == 0
     assert call_varlen(Tq=0, batch=0) == 0
-    assert mfa.varlen_workspace_size(0) == 0
-    assert mfa.varlen_workspace_size(1000) >= 1000 * 3 * 4
+    import torch
+    assert mfa.varlen_workspace_size(0, 100, 2, 64, torch.bfloat16) == 0
+    assert mfa.varlen_workspace_size(1000, 100, 2, 64, torch.float16) >= 1000 * 3 * 4
+    # bf16 adds the fp16 copy of V: total_k * Hkv * D * 2 bytes
+    assert mfa.varlen_workspace_size(1000, 900, 2, 64, torch.bfloat16) >= 1000 * 3 * 4 + 900 * 2 * 64 * 2
 
 
 def call_bd(**over):

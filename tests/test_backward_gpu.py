@@ -17,26 +17,9 @@ from transformer_mfa_fwd_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-# max |g - g_ref| <= REL * max |g_ref| (+ half an ulp of the stored gradient):
-# fp32 arithmetic throughout; 16-bit inputs also feed the backward a rounded O.
-REL = {"f32": 1e-4, "f16": 1e-2, "bf16": 1e-2}
-
-
 def say(msg):
     print(f"\n[backward] {msg}", flush=True)
     sys.stdout.flush()
-
-
-def check_grad(name, got, ref, dtype, what):
-    got = got.double().cpu().numpy()
-    scale = max(1.0, float(np.abs(ref).max()))
-    err = np.abs(got - ref)
-    bound = REL[dtype] * scale + pu.half_ulp(ref, dtype)
-    worst = int(np.argmax(err - bound))
-    assert np.all(np.isfinite(got)), f"{what} {name}: non-finite gradient"
-    assert err.flat[worst] <= bound.flat[worst], (
-        f"{what} {name}: |g - g_ref| = {err.flat[worst]:.3e} > {bound.flat[worst]:.3e} "
-        f"(max abs err {err.max():.3e}, scale {scale:.3e})")
 
 
 def run_case(w, bias_shape=None, p=0.0, seed=0):
@@ -58,7 +41,7 @@ def run_case(w, bias_shape=None, p=0.0, seed=0):
     rq, rk, rv = default_oracle().bwd(q, k, v, dout, bias=bias, dropout_p=p, seed=seed,
                                       nthreads=pu.ORACLE_THREADS, **kw)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        check_grad(name, got, ref, w.dtype, w.name)
+        pu.compare_grad(name, got, ref, w.dtype, f"{w.name} bias={bias_shape} p={p}", dropout_p=p)
 
 
 CASES = []

@@ -4,7 +4,8 @@ Each case draws its shape and flags from one seeded generator: dtype, head
 size, batch, kv heads and group size, query and key lengths (decode rows
 included), an arbitrary q_offset in [0, Lk - Lq], causal or bidirectional,
 no window / a negative window / a window from 1 to 2 Lk, a soft-cap, no mask /
-a padding mask / a random key mask, and the input scale (1 or 2; 1 for bf16).
+a padding mask / a random key mask, and the input scale (standard deviation 1
+or 2).
 Every row of every case is compared with the fp64 oracle, through the automatic
 path and through each forced kernel path that serves the call (the split
 decode with a drawn split count).
@@ -46,11 +47,9 @@ def draw_case(i: int):
         mask = dict(mask="pad_tail", pad_max=max(1, Lk // 2))
     else:
         mask = dict(mask="random_frac", mask_frac=float(rng.uniform(0.05, 0.6)))
-    # bf16 rounds the softmax weights to 8 significant bits before P.V, which
-    # alone costs up to ~0.015 on short, peaked rows of std-2 data (computed
-    # with the weights rounded in fp64): beyond the 1e-2 bound, so std 2 is
-    # drawn for fp16 and fp32 only
-    std = float(rng.choice([1.0, 2.0])) if dtype != "bf16" else 1.0
+    # std 2 with bf16 is the class of inputs that needs the fp16 P.V operands
+    # (8-bit bf16 weights alone err by up to ~0.03 on short, peaked rows)
+    std = float(rng.choice([1.0, 2.0]))
     w = wl.Workload(f"fuzz{i}", dtype, B, Lq, Lk, Hq, Hkv, D, causal, window=window, softcap=softcap,
                     std=std, **mask)
     splits = int(rng.choice([0, 1, 3, 7]))
@@ -79,10 +78,15 @@ def test_random_options_every_row(i):
 
 # --- the other entry points ---------------------------------------------------
 
-def _dtype_D_std(rng):
+def _dtype_D_std(rng, backward=False):
     dtype = str(rng.choice(["bf16", "f16", "f32"], p=[0.45, 0.4, 0.15]))
     D = int(rng.choice([64, 128]))
-    std = float(rng.choice([1.0, 1.5])) if dtype != "bf16" else 1.0
+    # The backward's products take bf16 operands (P, dS: 8 significant bits),
+    # whose rounding on wider data exceeds the per-row 1e-2 gradient bound
+    # (std 1.5 with dropout 0.5 measured 0.023 against 0.022): its bf16 draws
+    # keep std 1.  The forward keeps its weights in fp16 and draws std 2 too.
+    stds = [1.0] if backward and dtype == "bf16" else [1.0, 1.5, 2.0]
+    std = float(rng.choice(stds))
     return dtype, D, std
 
 
@@ -101,13 +105,14 @@ def test_random_decode_len_every_row(i):
     lens = [int(rng.choice([0, max(0, R - 1), Lmax, int(rng.integers(0, Lmax + 1))])) for _ in range(B)]
     softcap = 0.0 if rng.random() < 0.6 else float(rng.uniform(2.0, 40.0))
     splits = int(rng.choice([0, 1, 3, 7]))
+    std = float(rng.choice([1.0, 2.0]))
     print(f"\n[fuzz] decode_len {i}: {dtype} D={D} B={B} R={R} Hq={Hkv * g} Hkv={Hkv} Lmax={Lmax} "
-          f"lens={lens} softcap={softcap:.2f} splits={splits}", flush=True)
+          f"lens={lens} softcap={softcap:.2f} splits={splits} std={std}", flush=True)
     gen = torch.Generator(device="cpu").manual_seed(i)
     dt = wl.DTYPES[dtype]
-    q = torch.randn((B, R, Hkv * g, D), generator=gen).to(dt)
-    k = torch.randn((B, Lmax, Hkv, D), generator=gen).to(dt)
-    v = torch.randn((B, Lmax, Hkv, D), generator=gen).to(dt)
+    q = (torch.randn((B, R, Hkv * g, D), generator=gen) * std).to(dt)
+    k = (torch.randn((B, Lmax, Hkv, D), generator=gen) * std).to(dt)
+    v = (torch.randn((B, Lmax, Hkv, D), generator=gen) * std).to(dt)
     scale = 1.0 / np.sqrt(D)
     O, L, _ = default_oracle().decode_len(q, k, v, np.array(lens), scale=scale, softcap=softcap,
                                           nthreads=pu.ORACLE_THREADS)
@@ -135,13 +140,13 @@ def test_random_varlen_every_row(i):
     window = 0 if rng.random() < 0.5 else int(rng.integers(1, 200))
     softcap = 0.0 if rng.random() < 0.6 else float(rng.uniform(2.0, 40.0))
     print(f"\n[fuzz] varlen {i}: {dtype} D={D} lq={lq} lk={lk} Hq={Hq} Hkv={Hkv} causal={causal} "
-          f"window={window} softcap={softcap:.2f}", flush=True)
+          f"window={window} softcap={softcap:.2f} std={std}", flush=True)
     gen = torch.Generator(device="cpu").manual_seed(i)
     dt = wl.DTYPES[dtype]
     Tq, Tk = sum(lq), sum(lk)
     q = (torch.randn((Tq, Hq, D), generator=gen) * std).to(dt)
     k = (torch.randn((Tk, Hkv, D), generator=gen) * std).to(dt)
-    v = torch.randn((Tk, Hkv, D), generator=gen).to(dt)
+    v = (torch.randn((Tk, Hkv, D), generator=gen) * std).to(dt)
     cq = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32)
     ck = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32)
     O, L, _ = default_oracle().varlen(q, k, v, cq, ck, scale=1.0 / np.sqrt(D), causal=causal, window=window,
@@ -179,23 +184,12 @@ def test_random_packed_qkv_every_row(i):
     pu.compare(dtype, og.transpose(1, 0, 2), lse.double().cpu().numpy(), O.transpose(1, 0, 2), L, f"packed {i}")
 
 
-def _check_grad(name, got, ref, dtype, what):
-    rel = {"f32": 1e-4, "f16": 1e-2, "bf16": 1e-2}[dtype]
-    got = got.double().cpu().numpy()
-    bound = rel * max(1.0, float(np.abs(ref).max())) + pu.half_ulp(ref, dtype)
-    err = np.abs(got - ref)
-    assert np.all(np.isfinite(got)), f"{what} {name}: non-finite gradient"
-    worst = int(np.argmax(err - bound))
-    assert err.flat[worst] <= bound.flat[worst], (
-        f"{what} {name}: |g - g_ref| = {err.flat[worst]:.3e} > {bound.flat[worst]:.3e}")
-
-
 @pytest.mark.parametrize("i", range(16))
 def test_random_backward_every_element(i):
     """mfa_bwd after libmfa's own forward: every forward option drawn at
     random, plus an additive mask of a random broadcast shape and dropout."""
     rng = np.random.default_rng(5000 + i)
-    dtype, D, std = _dtype_D_std(rng)
+    dtype, D, std = _dtype_D_std(rng, backward=True)
     B = int(rng.integers(1, 3))
     Hkv = int(rng.integers(1, 3))
     Hq = Hkv * int(rng.integers(1, 4))
@@ -226,7 +220,7 @@ def test_random_backward_every_element(i):
     torch.cuda.synchronize()
     rq, rk, rv = default_oracle().bwd(q, k, v, dout, bias=bias, nthreads=pu.ORACLE_THREADS, **kw)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        _check_grad(name, got, ref, dtype, w.name)
+        pu.compare_grad(name, got, ref, dtype, w.name, dropout_p=p)
 
 
 @pytest.mark.parametrize("i", range(12))
@@ -248,7 +242,9 @@ def test_random_medium_shapes_sampled_rows(i):
     r = rng.random()
     mask = dict(mask=None) if r < 0.5 else (dict(mask="pad_tail", pad_max=Lk // 3) if r < 0.75 else
                                             dict(mask="random_frac", mask_frac=0.1))
-    w = wl.Workload(f"medium{i}", dtype, B, Lq, Lk, Hq, Hkv, D, causal, window=window, softcap=softcap, **mask)
+    std = float(rng.choice([1.0, 2.0]))
+    w = wl.Workload(f"medium{i}", dtype, B, Lq, Lk, Hq, Hkv, D, causal, window=window, softcap=softcap,
+                    std=std, **mask)
     print(f"\n[fuzz] medium {i}: {w} q_offset={q_offset}", flush=True)
     q, k, v, m = wl.make_inputs(w, DEV, seed=i)
     kw = dict(causal=causal, window=window, q_offset=q_offset, softcap=softcap, scale=w.scale)
@@ -326,4 +322,4 @@ def test_random_backward_longer_axes(i):
     torch.cuda.synchronize()
     rq, rk, rv = default_oracle().bwd(q, k, v, dout, nthreads=pu.ORACLE_THREADS, **kw)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        _check_grad(name, got, ref, dtype, w.name)
+        pu.compare_grad(name, got, ref, dtype, w.name, dropout_p=p)

@@ -197,3 +197,34 @@ def test_packed_single_row_sequences():
     x = qkv.view(L, 3, H * D)
     assert torch.equal(out, x[:, 2])
     check(qkv, sb, H, out, lse, "bf16", scale=1.0 / np.sqrt(D), window=0, softcap=0.0, what="single rows")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("f32", 64)])
+def test_packed_hostile_bounds_stay_in_bounds(dtype, D):
+    """Bounds that break the rules (negative, past L, reversed, INT_MIN/MAX)
+    give unspecified values but every access stays inside the tensors: the
+    sequence ends are clamped to [0, L] before any key range is formed.
+    Guard bands around the outputs stay untouched; the outputs are finite."""
+    H = 2
+    lengths = ragged_lengths(4, 300)
+    qkv, sb = wl.make_packed_qkv(lengths, H, D, dtype, DEV, seed=4)
+    L = qkv.shape[0]
+    rng = np.random.default_rng(21)
+    hostile = np.array([-2**31, -2**31 + 1, -100000, -65, -1, 0, 1, 63, 64, 65, L - 1, L, L + 1, L + 64,
+                        2**31 - 2, 2**31 - 1], dtype=np.int64)
+    b = sb.cpu().numpy().astype(np.int64)
+    pick = rng.random(b.shape) < 0.5
+    b[pick] = rng.choice(hostile, size=int(pick.sum()))
+    bounds = torch.from_numpy(b.astype(np.int32)).to(DEV)
+    n, nl, guard = L * H * D, H * L, 4096
+    obuf = torch.full((n + 2 * guard,), 7.0, dtype=qkv.dtype, device=DEV)
+    lbuf = torch.full((nl + 2 * guard,), 7.0, dtype=torch.float32, device=DEV)
+    out = obuf[guard:guard + n].view(L, H * D)
+    lse = lbuf[guard:guard + nl].view(H, L)
+    print(f"\n[packed] hostile bounds {dtype} D{D} L={L}", flush=True)
+    for window in (0, 64):
+        mfa.packed_qkv_fwd(qkv, bounds, H, window=window, out=out, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.all(obuf[:guard] == 7.0) and torch.all(obuf[-guard:] == 7.0)
+        assert torch.all(lbuf[:guard] == 7.0) and torch.all(lbuf[-guard:] == 7.0)
+        assert torch.all(torch.isfinite(out.float()))

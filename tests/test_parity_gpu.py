@@ -335,3 +335,99 @@ def test_full_workload_exact_visible_counts(w):
     empty = want == 0
     assert np.array_equal(got[~empty], want[~empty])
     assert torch.all(torch.isneginf(lse.cpu()[torch.from_numpy(np.ascontiguousarray(empty))]))
+
+
+# --- scale <= 0 ----------------------------------------------------------------
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, -0.7])
+@pytest.mark.parametrize("path", ["generic", "mfma", "split_decode"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nonpositive_scale_every_path(scale, path, dtype):
+    """A zero or negative scale is used as given: with a causal window and a
+    key mask (boundary tiles, masked keys) every path matches the oracle.
+    Zero gives uniform weights over the visible keys."""
+    if path == "split_decode":
+        w = wl.Workload(f"scale{scale}_dec_{dtype}", dtype, 2, 1, 700, 8, 2, 128, True, window=300,
+                        mask="random_frac", mask_frac=0.3)
+    else:
+        w = wl.Workload(f"scale{scale}_{path}_{dtype}", dtype, 2, 150, 200, 4, 2, 64, True, window=70,
+                        mask="random_frac", mask_frac=0.3)
+    q, k, v, m = wl.make_inputs(w, DEV)
+    say(f"{w.name} path={path} scale={scale}")
+    out, lse = mfa.fwd(q, k, v, causal=True, window=w.window, key_mask=m, scale=scale, path=PATHS[path])
+    torch.cuda.synchronize()
+    O, L, _ = default_oracle().full(q, k, v, scale=scale, causal=True, window=w.window, q_offset=w.q_offset,
+                                    key_mask=m, nthreads=pu.ORACLE_THREADS)
+    pu.compare(w.dtype, out.double().cpu().numpy().transpose(0, 2, 1, 3), lse.double().cpu().numpy(),
+               O.transpose(0, 2, 1, 3), L, f"{w.name}/{path}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+def test_nonpositive_scale_with_cap_and_bias(scale):
+    """The soft-capped and additive-mask MFMA kernels turn scores into logits
+    before masking; a zero or negative scale goes through them as given."""
+    w = wl.Workload("scale_cap_bias", "bf16", 1, 128, 128, 2, 1, 128, True, window=50, softcap=4.0)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    out, lse = mfa.fwd(q, k, v, causal=True, window=50, softcap=4.0, scale=scale)
+    torch.cuda.synchronize()
+    O, L, _ = default_oracle().full(q, k, v, scale=scale, causal=True, window=50, q_offset=0, softcap=4.0)
+    pu.compare("bf16", out.double().cpu().numpy().transpose(0, 2, 1, 3), lse.double().cpu().numpy(),
+               O.transpose(0, 2, 1, 3), L, "cap")
+    bias = torch.randn((1, 1, 128, 132), generator=torch.Generator().manual_seed(3))[..., :128].contiguous()
+    out, lse = mfa.fwd(q, k, v, causal=True, window=50, scale=scale, bias=bias.to(DEV))
+    torch.cuda.synchronize()
+    O, L, _ = default_oracle().full(q, k, v, scale=scale, causal=True, window=50, q_offset=0, bias=bias)
+    pu.compare("bf16", out.double().cpu().numpy().transpose(0, 2, 1, 3), lse.double().cpu().numpy(),
+               O.transpose(0, 2, 1, 3), L, "bias")
+
+
+# --- bf16 V beyond the fp16 range ------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("where", ["first_tile", "middle_tile", "last_tile", "two_tiles"])
+def test_bf16_large_v_runs_on_bf16_operands(D, where):
+    """bf16 P.V runs on fp16 operands, which cannot hold |v| >= 65504: the
+    tile holding such values is noticed when its V rows are converted and the
+    row block is computed again on bf16 operands.  Rows that see them are
+    checked relative to the largest |V| they see (bf16 weights err by up to
+    2^-8 of it), the others against the usual bound."""
+    w = wl.Workload(f"bigv_{where}_D{D}", "bf16", 2, 300, 300, 4, 2, D, True)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    spans = {"first_tile": [(2, 5)], "middle_tile": [(130, 133)], "last_tile": [(290, 300)],
+             "two_tiles": [(70, 72), (200, 201)]}[where]
+    v = v.clone()
+    for s0, s1 in spans:
+        v[:, s0:s1, 0, :] = (v[:, s0:s1, 0, :].float() * 1e6).to(v.dtype)
+        v[:, s0, 1, 3] = 1e30
+    say(f"{w.name}")
+    out, lse = mfa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    O, L, _ = default_oracle().full(q, k, v, scale=w.scale, causal=True, q_offset=0, nthreads=pu.ORACLE_THREADS)
+    og = out.double().cpu().numpy()                               # [B, Lq, Hq, D]
+    assert np.all(np.isfinite(og))
+    vmax = v.double().abs().amax(dim=3).cpu().numpy()             # [B, Lk, Hkv]
+    seen = np.maximum.accumulate(vmax, axis=1)                    # causal: row i sees keys 0..i
+    g = w.Hq // w.Hkv
+    scale = np.maximum(1.0, seen[:, :, np.arange(w.Hq) // g])     # [B, Lq, Hq]
+    bound = pu.TOL_O["bf16"] * scale[..., None] + pu.half_ulp(O, "bf16")
+    err = np.abs(og - O)
+    worst = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+    assert np.all(err <= bound), (worst, err[worst], bound[worst])
+    assert np.max(np.abs(lse.double().cpu().numpy() - L)) <= pu.TOL_LSE
+
+
+def test_bf16_prefill_caller_workspace_matches_pool():
+    """A bf16 prefill converts V to fp16 in its workspace: the caller-owned
+    form (mfa_fwd_ws, sized by mfa_fwd_workspace_size) gives the pool form's
+    bits, with and without a key mask."""
+    w = wl.Workload("ws_bf16_prefill", "bf16", 2, 300, 333, 8, 2, 128, True, window=200, std=2.0,
+                    mask="random_frac", mask_frac=0.2)
+    q, k, v, m = wl.make_inputs(w, DEV)
+    nbytes = mfa.workspace_size(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.D, q.dtype)
+    assert nbytes >= w.B * w.Lk * w.Hkv * w.D * 2
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    for mask in (None, m):
+        o1, l1 = mfa.fwd(q, k, v, causal=True, window=200, key_mask=mask)
+        o2, l2 = mfa.fwd(q, k, v, causal=True, window=200, key_mask=mask, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -124,7 +124,7 @@ def test_varlen_graph_replay_with_new_lengths():
     lq_b, lk_b = split(Tq, 6), split(Tk, 6)
     q, k, v = make(lq_a, lk_a, Hq, Hkv, D, "bf16", seed=13)
     cq, ck = cu(lq_a).to(DEV), cu(lk_a).to(DEV)
-    ws = torch.empty(mfa.varlen_workspace_size(Tq), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(mfa.varlen_workspace_size(Tq, Tk, Hkv, D, q.dtype), dtype=torch.uint8, device=DEV)
     out = torch.empty_like(q)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=DEV)
     side = torch.cuda.Stream()

@@ -24,10 +24,11 @@ PATH_NAMES = {PATH_AUTO: "auto", PATH_GENERIC: "generic", PATH_MFMA: "mfma",
 _DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: MFA_BF16}
 
 EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
-            "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_packed_qkv_fwd",
+            "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_decode_masked",
+            "mfa_decode_masked_workspace_size", "mfa_packed_qkv_fwd",
             "mfa_varlen_fwd", "mfa_varlen_workspace_size", "mfa_fwd_bias_dropout",
             "mfa_bwd", "mfa_bwd_workspace_size",
-            "mfa_status_string", "mfa_last_error", "mfa_version")
+            "mfa_status_string", "mfa_last_error", "mfa_version", "mfa_set_kernel_events")
 
 
 class MFAError(RuntimeError):
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_fwd_plan.argtypes = [_I] * 7 + [ctypes.POINTER(_I)]
     lib.mfa_decode_len.restype = _I
     lib.mfa_decode_len.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_decode_masked.restype = _I
+    lib.mfa_decode_masked.argtypes = [_P] * 6 + [_I] * 5 + [_F, _I, _F, _I, _I, _P, ctypes.c_size_t, _P]
+    lib.mfa_decode_masked_workspace_size.restype = ctypes.c_size_t
+    lib.mfa_decode_masked_workspace_size.argtypes = [_I] * 7
     lib.mfa_fwd_bias_dropout.restype = _I
     lib.mfa_fwd_bias_dropout.argtypes = _FWD_ARGS[:-1] + [_P, _I, _I, _I, _I, _F, ctypes.c_ulonglong, _I, _P]
     lib.mfa_bwd.restype = _I
@@ -75,7 +80,7 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_varlen_fwd.restype = _I
     lib.mfa_varlen_fwd.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _I, _F, _I, _P, ctypes.c_size_t, _P]
     lib.mfa_varlen_workspace_size.restype = ctypes.c_size_t
-    lib.mfa_varlen_workspace_size.argtypes = [_I]
+    lib.mfa_varlen_workspace_size.argtypes = [_I] * 5
     lib.mfa_packed_qkv_fwd.restype = _I
     lib.mfa_packed_qkv_fwd.argtypes = [_P] * 4 + [_I] * 3 + [_F, _I, _F, _I, _P]
     lib.mfa_decode_len_workspace_size.restype = ctypes.c_size_t
@@ -86,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_last_error.argtypes = []
     lib.mfa_version.restype = _I
     lib.mfa_version.argtypes = []
+    lib.mfa_set_kernel_events.restype = None
+    lib.mfa_set_kernel_events.argtypes = [_P, _P]
     _lib = lib
     return lib
 
@@ -236,6 +243,57 @@ def decode_len(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, lse
 
 
+def decode_masked(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  d_mask: torch.Tensor, *, window: int = 0, softcap: float = 0.0,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, return_lse: bool = True, splits: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Single-query decode over a fixed-capacity cache whose valid keys are
+    marked by a device key mask (mfa_decode_masked).
+
+    q [B, 1, Hq, D]; k_cache, v_cache [B, Lmax, Hkv, D] (fp16 or bf16, one
+    dtype, contiguous, on one GPU); d_mask float32 [B, Lmax] on the same GPU,
+    read by the kernels when they run.  The query sits at each batch's last
+    valid key; ``window`` > 0 keeps only the valid keys after that position
+    minus the window.  Returns (out [B, 1, Hq, D], lse [B, Hq, 1] float32 or
+    None).  ``workspace`` (a uint8 device tensor of at least
+    decode_masked_workspace_size bytes) makes the call allocation-free, as
+    graph capture needs.
+    """
+    lib = load_library()
+    B, R, Lmax, Hq, Hkv, D = _dims(q, k_cache, v_cache)
+    if R != 1:
+        raise ValueError("q must hold one query row per batch: [B, 1, Hq, D]")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or \
+            v_cache.dtype != q.dtype:
+        raise TypeError(f"dtypes must match and be float16 or bfloat16 "
+                        f"(got {q.dtype}, {k_cache.dtype}, {v_cache.dtype})")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if d_mask.dtype != torch.float32 or tuple(d_mask.shape) != (B, Lmax) or not d_mask.is_cuda or \
+            not d_mask.is_contiguous():
+        raise ValueError("d_mask must be a contiguous float32 GPU tensor of shape [B, Lmax]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous and match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, Hq, 1) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, Hq, 1]")
+    with torch.cuda.device(q.device):
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib.mfa_decode_masked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                     _ptr(d_mask), B, Lmax, Hq, Hkv, D, float(scale), int(window),
+                                     float(softcap), _DTYPE_CODES[q.dtype], int(splits), _ptr(workspace),
+                                     ws_bytes, _stream(stream)))
+    return out, lse
+
+
 def packed_qkv_fwd(qkv: torch.Tensor, seq_bounds: torch.Tensor, num_heads: int, *,
                    window: int = 0, softcap: float = 0.0, scale: Optional[float] = None,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -378,13 +436,19 @@ def bwd_workspace_size(B: int, Lq: int, Hq: int) -> int:
     return int(load_library().mfa_bwd_workspace_size(B, Lq, Hq))
 
 
-def varlen_workspace_size(total_q: int) -> int:
-    return int(load_library().mfa_varlen_workspace_size(int(total_q)))
+def varlen_workspace_size(total_q: int, total_k: int, Hkv: int, D: int, dtype: torch.dtype) -> int:
+    return int(load_library().mfa_varlen_workspace_size(int(total_q), int(total_k), int(Hkv), int(D),
+                                                        _DTYPE_CODES[dtype]))
 
 
 def decode_len_workspace_size(B, R, Lmax, Hq, Hkv, D, dtype: torch.dtype, splits: int = 0) -> int:
     return int(load_library().mfa_decode_len_workspace_size(B, R, Lmax, Hq, Hkv, D,
                                                             _DTYPE_CODES[dtype], int(splits)))
+
+
+def decode_masked_workspace_size(B, Lmax, Hq, Hkv, D, dtype: torch.dtype, splits: int = 0) -> int:
+    return int(load_library().mfa_decode_masked_workspace_size(B, Lmax, Hq, Hkv, D, _DTYPE_CODES[dtype],
+                                                               int(splits)))
 
 
 def workspace_size(B, Lq, Lk, Hq, Hkv, D, dtype: torch.dtype) -> int:
@@ -400,3 +464,12 @@ def plan(B, Lq, Lk, Hq, Hkv, D, dtype: torch.dtype):
 
 def version() -> int:
     return int(load_library().mfa_version())
+
+
+def set_kernel_events(begin=None, end=None):
+    """Events (torch.cuda.Event, already recorded once so that they exist, or
+    None) that later calls on this thread record around their main kernel
+    (mfa_set_kernel_events)."""
+    def handle(e):
+        return None if e is None else ctypes.c_void_p(e.cuda_event)
+    load_library().mfa_set_kernel_events(handle(begin), handle(end))

@@ -14,7 +14,11 @@
 //   online softmax per query column (running max m, rescaled sum l), base 2
 //   O^T[16 d x 16 q] += V^T . P^T          MFMA 16x16x32; P^T is the score
 //                                          accumulator itself, V^T comes from
-//                                          transposing LDS reads
+//                                          transposing LDS reads; for bf16 the
+//                                          weights go in as two operands, the
+//                                          rounded weight and its rounded
+//                                          residue (the loop is bound by HBM,
+//                                          so the second product is free)
 // Query heads beyond Hq/Hkv (columns g..15) compute on zeros and are dropped.
 //
 // With a device-held length (same header, flash_attention_decode_len) the
@@ -23,6 +27,13 @@
 // of the cache.  The length is read on the device and the splits divide its
 // tiles, so the launch shape depends on the cache capacity only and rows past
 // the length cost nothing.
+//
+// With a key mask over a fixed-capacity cache (same header,
+// flash_attention_decode_masked) the single query sits at the batch's last
+// valid key, found on the device from the packed mask words, and a window
+// counts back from it; the splits divide the tiles of that range and tiles
+// without a valid key are skipped before any K/V read, so the launch shape
+// depends on the capacity only.
 //
 // Each split writes (m, l, O_unnormalised[D]) in base-2 units; the combine
 // kernel merges them: M = max m_s, w_s = 2^(m_s - M), O = sum w_s O_s / sum
@@ -33,6 +44,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace mfa {
 namespace {
 
@@ -41,6 +54,7 @@ constexpr int DT = 32;  // keys per tile
 struct DecodeArgs {
     FwdArgs f;                // Lq = R query rows per batch; Lk = cache rows
     const int* d_len;         // [B] valid lengths on the device, or null (Lq = 1, key_range)
+    int pos_from_mask;        // Lq = 1: the query sits at the batch's last valid key (needs the mask)
     int splits;
     float* part_ml;   // [B, R, Hq, S, 2]: m (base 2), l
     float* part_o;    // [B, R, Hq, S, D]
@@ -59,6 +73,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
     constexpr int NLD = DT / RPL;       // loads per tensor per tile
     constexpr int NDB = D / 16;         // 16-wide d blocks
     constexpr int NKS = D / 32;         // 32-wide k steps of Q.K
+    constexpr bool SPLIT_P = std::is_same<T, __bf16>::value;   // weights as bf16 hi + lo
     typedef typename Mfma<T>::v8 v8;
 
     __shared__ u32x4_t sK[DT * CPR];
@@ -79,8 +94,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
 
     // Keys [lo, hi] of all columns, this column's last key hi_col and the last
     // key every column sees (hi_min), then this split's share of the tiles.
+    const uint64_t* words = MASK ? a.mask_words + (int64_t)b * a.words_per_batch : nullptr;
     int lo, hi, hi_col, hi_min;
-    if (da.d_len) {
+    if (MASK && da.pos_from_mask) {
+        // the last valid key (highest set bit of the batch's mask words) is
+        // the query's position; keys after position - window, up to it
+        int p = -1;
+        for (int w = lane; w < a.words_per_batch; w += 64) {
+            const uint64_t x = words[w];
+            if (x) p = w * 64 + 63 - __clzll((long long)x);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) p = max(p, __shfl_xor(p, off));
+        lo = (p >= 0 && a.window > 0 && p - a.window + 1 > 0) ? p - a.window + 1 : 0;
+        hi = p;
+        hi_col = hi_min = hi;
+    } else if (da.d_len) {
         int n = da.d_len[b];
         n = n < 0 ? 0 : (n > a.Lk ? a.Lk : n);
         lo = 0;
@@ -97,7 +126,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
         t_begin = t_lo + (int)((int64_t)n_t * split / da.splits);
         t_end = t_lo + (int)((int64_t)n_t * (split + 1) / da.splits);
     }
-    const uint64_t* words = MASK ? a.mask_words + (int64_t)b * a.words_per_batch : nullptr;
 
     // Q^T operand: lane (col, grp) holds Q[row crow][head kvh*g + chead][32 ks + 8 grp .. +7]
     const T* __restrict__ qp = static_cast<const T*>(a.q);
@@ -213,6 +241,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
         }
         l = l * alpha + psum;
         const v8 pop = pack8<T>(x);
+        // bf16 keeps 8 significant bits of a weight; the rounding residue
+        // x - bf16(x), itself rounded, is a second operand whose products
+        // restore about 16 bits (fp16 weights already keep 11)
+        v8 pop_lo;
+        if constexpr (SPLIT_P) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pop_lo[e] = static_cast<T>(x[e] - static_cast<float>(pop[e]));
+        }
+        (void)pop_lo;
 
         // O^T += V^T P^T over the 32 keys of the tile
 #pragma unroll
@@ -230,6 +267,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
             const i16x4_t hi4 = lds_read_tr16(p1);
             const i16x8_t vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
             oacc[db] = Mfma<T>::mma16(bitcast<v8>(vv), pop, oacc[db]);
+            if constexpr (SPLIT_P) oacc[db] = Mfma<T>::mma16(bitcast<v8>(vv), pop_lo, oacc[db]);
         }
         t = tn;
     }
@@ -287,10 +325,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs da) {
 template <typename T, int D, bool CAP, bool MASK>
 hipError_t launch_t(const DecodeArgs& da, hipStream_t s) {
     const FwdArgs& a = da.f;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, CAP, MASK>), dim3(da.splits, a.Hkv, a.B), dim3(64), 0, s, da);
+    // instrumentation events: start of the split kernel, end of the combine
+    hipExtLaunchKernelGGL((decode_split_kernel<T, D, CAP, MASK>), dim3(da.splits, a.Hkv, a.B), dim3(64), 0, s,
+                          instr_event_begin(), nullptr, 0, da);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Lq * a.Hq), dim3(64), 0, s, da);
+    hipExtLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.Lq * a.Hq), dim3(64), 0, s, nullptr,
+                          instr_event_end(), 0, da);
     return hipGetLastError();
 }
 
@@ -337,10 +378,12 @@ size_t split_decode_workspace_bytes(int B, int R, int Hq, int D, int splits) {
 }
 
 hipError_t launch_split_decode(const FwdArgs& a, const int* d_len, int dtype, int splits, float* partials,
-                               hipStream_t s) {
+                               hipStream_t s, bool pos_from_mask) {
+    if (pos_from_mask && (!a.key_mask || !a.mask_words || a.Lq != 1 || d_len)) return hipErrorInvalidValue;
     DecodeArgs da;
     da.f = a;
     da.d_len = d_len;
+    da.pos_from_mask = pos_from_mask ? 1 : 0;
     da.splits = splits;
     const size_t slots = (size_t)a.B * a.Lq * a.Hq * splits;
     da.part_ml = partials;

@@ -210,9 +210,11 @@ template <typename T, int RPW>
 hipError_t launch_generic_r(const FwdArgs& a, hipStream_t s) {
     dim3 grid((a.Lq + 4 * RPW - 1) / (4 * RPW), a.Hq, a.B);
     if (a.D == 64)
-        hipLaunchKernelGGL((generic_fwd_kernel<T, 64, RPW>), grid, dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL((generic_fwd_kernel<T, 64, RPW>), grid, dim3(256), 0, s, instr_event_begin(),
+                              instr_event_end(), 0, a);
     else
-        hipLaunchKernelGGL((generic_fwd_kernel<T, 128, RPW>), grid, dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL((generic_fwd_kernel<T, 128, RPW>), grid, dim3(256), 0, s, instr_event_begin(),
+                              instr_event_end(), 0, a);
     return hipGetLastError();
 }
 

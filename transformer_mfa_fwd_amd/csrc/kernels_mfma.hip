@@ -43,6 +43,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace mfa {
 namespace {
 
@@ -122,16 +124,35 @@ __device__ inline uint64_t range_bits64(int lo, int hi) {
     return (~0ull << lo) & (~0ull >> (63 - hi));
 }
 
-// BIAS adds an additive score mask read from global memory into registers one
-// tile ahead (32 more VGPRs: one workgroup per CU at D = 128, two at D = 64).
-// DROP applies attention dropout: the keep bits of a tile's 32 weights per
-// lane come from eight Philox blocks before its softmax, dropped weights are
-// zeroed after they enter the row sum and before they become the P.V operand,
-// and the 1 / (1 - p) factor is folded into the final normalisation (one
-// workgroup per CU at D = 128, or with BIAS too; two at D = 64).
-template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP>
-__global__ __launch_bounds__(256, (BIAS && DROP) ? 1 : (BIAS || DROP) ? (D == 64 ? 2 : 1) : (D == 64 ? 3 : 2))
-void prefill_kernel(FwdArgs a, int nqt) {
+// ---- bf16 inputs: fp16 operands for P.V.  Rounding a weight to bf16 keeps 8
+// significant bits, which on std-2 data costs up to about 0.03 in O (V up to
+// ~9, two comparable weights); fp16 keeps 11.  The MFMA needs both operands
+// in one type, so V is converted to fp16 once per call by v16_prepass_kernel
+// (exact below 65504 in magnitude: bf16 has fewer significant bits), and the
+// prefill reads that copy.  A (batch, kv head) whose V holds a magnitude of
+// 65504 or more (or an infinity) is flagged and its blocks run on bf16
+// operands from the original V.  Converting in the prefill instead, once per
+// workgroup and tile, measured 14 % slower on the causal GQA prefill: every V
+// tile is read by ~32 workgroups there.
+
+// One dword of two bf16 values as two fp16 values (round to nearest even,
+// exact below 65504 in magnitude); their magnitudes are folded into mx.
+__device__ inline uint32_t cvt_bf16x2_f16x2(uint32_t x, float& mx) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
+    mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+    const h2 r = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// The work of one workgroup: its 128 query rows of one query head, from
+// the first copies to the stores.  With CV (bf16 inputs, a.v16 holding V
+// converted to fp16) P.V runs on fp16 operands; it returns false at once,
+// having done nothing, when the block's (batch, kv head) is flagged, and the
+// caller then runs it with CV off.  smem: the kernel's LDS (L::BYTES bytes,
+// 1024-byte aligned).
+template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP, bool CV>
+__device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArgs& a, int nqt, char* smem) {
     typedef PfLds<D> L;
     constexpr int CPR = L::CPR;
     constexpr int NKS = D / 16;             // k-steps of Q.K^T
@@ -145,8 +166,9 @@ void prefill_kernel(FwdArgs a, int nqt) {
     static_assert(TRS > 0 && TRS + QK_LA == NQK, "V reads follow the last K read");
     typedef typename Mfma<T>::v8 v8;
     constexpr float LOG2E = 1.4426950408889634f;
-
-    __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+    // CV: P.V on fp16 operands (see cvt_bf16x2_f16x2)
+    typedef typename std::conditional<CV, _Float16, T>::type PT;   // P.V operand type
+    typedef typename Mfma<PT>::v8 pv8;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -198,7 +220,18 @@ void prefill_kernel(FwdArgs a, int nqt) {
     const int64_t kv_stride = a.kv_stride;
     const T* __restrict__ qbase = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * q_stride + (int64_t)hq * D;
     const T* __restrict__ kbase = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * kv_stride + (int64_t)kvh * D;
-    const T* __restrict__ vbase = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * kv_stride + (int64_t)kvh * D;
+    // CV: V from the fp16 copy (same element offsets as V)
+    const PT* __restrict__ vbase = static_cast<const PT*>(CV ? a.v16 : a.v) + (int64_t)b * a.Lk * kv_stride +
+                                   (int64_t)kvh * D;
+    if constexpr (CV) {
+        // a (batch, kv head) whose V could not all be converted runs on bf16
+        // operands, and so does a call without the copy
+        if (!a.v16) return false;
+        const uint32_t* fl = reinterpret_cast<const uint32_t*>(a.v16_flags + (int64_t)bk * a.v16_fwords * 4);
+        uint32_t any = 0u;
+        for (int w = lane; w < a.v16_fwords; w += 64) any |= fl[w];
+        if (__any(any != 0u)) return false;
+    }
     const uint64_t* words = MASK ? a.mask_words + (int64_t)b * a.words_per_batch : nullptr;
 
     // ---- Q^T operand: lane holds Q[qrow][16 ks + 8 h2 .. +7]
@@ -207,7 +240,11 @@ void prefill_kernel(FwdArgs a, int nqt) {
         const int r = qrow <= i_last ? qrow : i_last;
         const T* qp = qbase + (int64_t)r * q_stride + h2 * 8;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(qp + ks * 16));
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qp + ks * 16);
+            if constexpr (!LOGIT) raw = (raw ^ a.q_xor) & ~a.q_clear;   // scale <= 0: see the launcher
+            qop[ks] = bitcast<v8>(raw);
+        }
     }
 
     // ---- DMA: instruction i of this wave fills tile rows R..R+RPI-1,
@@ -415,7 +452,7 @@ void prefill_kernel(FwdArgs a, int nqt) {
             psum1 += MFA_X(SC, 2 * (_u - 5) + 1);                                            \
             if constexpr (_u == 8) {                                                         \
                 MFA_DROP8(SC, 0);                                                            \
-                pop[0] = pack8_at<T>(SC[0], 0);                                              \
+                pop[0] = pack8_at<PT>(SC[0], 0);                                             \
             }                                                                                \
         }                                                                                    \
     } while (0)
@@ -435,7 +472,7 @@ void prefill_kernel(FwdArgs a, int nqt) {
             psum1 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U) + 1);                                  \
             if constexpr ((U) == 3) {                                                        \
                 MFA_DROP8(SC, 8 * (1 + (S4)));                                               \
-                pop[1 + (S4)] = pack8_at<T>(SC[(1 + (S4)) >> 1], 8 * ((1 + (S4)) & 1));       \
+                pop[1 + (S4)] = pack8_at<PT>(SC[(1 + (S4)) >> 1], 8 * ((1 + (S4)) & 1));      \
             }                                                                                \
             if constexpr ((S4) == 2 && (U) == 3) l += psum0 + psum1;                         \
         }                                                                                    \
@@ -446,11 +483,11 @@ void prefill_kernel(FwdArgs a, int nqt) {
 // slot (SM).  Slot TRS, the first after the last K read is issued, also issues
 // the transposing V reads of the first P.V step (SM).
 #define MFA_SA_IF(U, F, SC) if constexpr ((U) < ((F) + 1) * NSA / NQK) MFA_SA(U, SC);
-// copy J of the iteration (K copies, then V copies) goes in slot J * NQK / (2 IPW)
+// copy J of the iteration (V copies, then K copies) goes in slot J * NQK / (2 IPW)
 #define MFA_DMA_IF(F, J)                                                                     \
     if constexpr ((J) < 2 * IPW && (F) == (J) * NQK / (2 * IPW)) {                           \
-        if constexpr ((J) < IPW) MFA_DMA1(_rk, dma_koff, (J), _dk_dst);                      \
-        else MFA_DMA1(_rv, dma_voff, (J) - IPW, _dv_dst);                                    \
+        if constexpr ((J) < IPW) MFA_DMA1(_rv, dma_voff, (J), _dv_dst);                      \
+        else MFA_DMA1(_rk, dma_koff, (J) - IPW, _dk_dst);                                    \
     }
 #define MFA_QK_SLOT(F, SC, SN, SM)                                                           \
     if constexpr ((F) < NQK) {                                                               \
@@ -490,19 +527,19 @@ void prefill_kernel(FwdArgs a, int nqt) {
     } while (0)
 
 // Slot (S4, DB) of the P.V pass (constants): at DB = 0 wait for the V
-// fragments of step S4 and issue those of S4 + 1; then the MFMA and the
-// softmax work assigned to the slot.
+// fragments of step S4 (step 0's wait comes before the pass) and issue those
+// of S4 + 1; then the MFMA and the softmax work assigned to the slot.
 #define MFA_SB_IF(S4, U, DB, SC) if constexpr ((U) < ((DB) + 1) * 4 / NDB) MFA_SB(S4, U, SC);
-#define MFA_PV_SLOT(S4, DB, SC)                                                              \
+#define MFA_PV_SLOT(S4, DB, SC)                                                          \
     if constexpr ((DB) < NDB) {                                                              \
         if constexpr ((DB) == 0) {                                                           \
-            lds_wait<NDB>(vlo[(S4) & 1], vhi[(S4) & 1]);                                     \
+            if constexpr ((S4) > 0) lds_wait<NDB>(vlo[(S4) & 1], vhi[(S4) & 1]);             \
             if constexpr ((S4) < 3) MFA_TR_ISSUE((S4) + 1, vlo[((S4) + 1) & 1], vhi[((S4) + 1) & 1]); \
         }                                                                                    \
         {                                                                                    \
             const i16x4_t _lo4 = vlo[(S4) & 1][DB], _hi4 = vhi[(S4) & 1][DB];                \
             const i16x8_t _vv = {_lo4[0], _lo4[1], _lo4[2], _lo4[3], _hi4[0], _hi4[1], _hi4[2], _hi4[3]}; \
-            oacc[DB] = Mfma<T>::mma32(bitcast<v8>(_vv), pop[S4], oacc[DB]);                 \
+            oacc[DB] = Mfma<PT>::mma32(bitcast<pv8>(_vv), pop[S4], oacc[DB]);                \
         }                                                                                    \
         MFA_SB_IF(S4, (DB) * 4 / NDB + 0, DB, SC)                                            \
         MFA_SB_IF(S4, (DB) * 4 / NDB + 1, DB, SC)                                            \
@@ -536,14 +573,16 @@ void prefill_kernel(FwdArgs a, int nqt) {
         i16x4_t vlo[2][NDB], vhi[2][NDB];                                                    \
         float pm[11];                                                                        \
         float neg_m = 0.0f, psum0 = 0.0f, psum1 = 0.0f;                                      \
-        v8 pop[4];                                                                           \
+        pv8 pop[4];                                                                          \
         /* stage ST ^ 1 holds K(tnxt); on the last tile its scores are discarded */         \
         MFA_PART1(SC, SN, (ST) ^ 1, true);                                                   \
         if (has_nxt) MFA_BIAS_LOAD(tnxt);   /* this tile's bias is consumed: fetch the next */ \
+        lds_wait<NDB>(vlo[0], vhi[0]);      /* V fragments of P.V step 0 */                  \
         MFA_PV_STEP(0, SC) MFA_PV_STEP(1, SC) MFA_PV_STEP(2, SC) MFA_PV_STEP(3, SC)          \
         __syncthreads();  /* copies of this iteration landed; stages handed over */         \
     } while (0)
 
+    // ---- the prologue and the pipelined loop over the block's key tiles
     int tcur = MFA_NEXT_TILE(kt_lo);
     if (tcur <= kt_hi) {
         int tnxt = MFA_NEXT_TILE(tcur + 1), tnx2;
@@ -558,7 +597,7 @@ void prefill_kernel(FwdArgs a, int nqt) {
             // scores of the first tile; no softmax and no V reads (names unused)
             i16x4_t vlo[2][NDB], vhi[2][NDB];
             float pm[11], neg_m, psum0, psum1;
-            v8 pop[4];
+            pv8 pop[4];
             const int k0 = 0;
             const uint64_t word = 0;
             const bool interior = true;
@@ -636,13 +675,83 @@ void prefill_kernel(FwdArgs a, int nqt) {
     }
     if (a.lse && h2 == 0 && qrow <= i_last)
         a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qrow] = l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
+    return true;
 }
+
+// The block on bf16 operands, out of line so that its registers and code
+// stay apart from the kernel's hot loop (it runs only for a (batch, kv head)
+// whose V holds a magnitude that fp16 cannot carry).
+// It reads the kernel's arguments straight from the kernel-argument segment
+// (kargs: the kernel's first argument), so the kernel keeps no copy of them.
+template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP>
+__device__ __attribute__((noinline)) void prefill_block_bf16_operands(const void* kargs, int nqt, char* smem) {
+    const FwdArgs& a = *static_cast<const FwdArgs*>(kargs);
+    prefill_block<T, D, CAP, MASK, SEQ, BIAS, DROP, false>(a, nqt, smem);
+}
+
+// BIAS adds an additive score mask read from global memory into registers one
+// tile ahead (32 more VGPRs: one workgroup per CU at D = 128, two at D = 64).
+// DROP applies attention dropout: the keep bits of a tile's 32 weights per
+// lane come from eight Philox blocks before its softmax, dropped weights are
+// zeroed after they enter the row sum and before they become the P.V operand,
+// and the 1 / (1 - p) factor is folded into the final normalisation (one
+// workgroup per CU at D = 128, or with BIAS too; two at D = 64).  bf16
+// inputs run P.V on fp16 operands.
+template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP>
+__global__ __launch_bounds__(256, (BIAS && DROP) ? 1 : (BIAS || DROP) ? (D == 64 ? 2 : 1) : (D == 64 ? 3 : 2))
+void prefill_kernel(FwdArgs a, int nqt) {
+    constexpr bool CVT = std::is_same<T, __bf16>::value;
+    __shared__ __attribute__((aligned(1024))) char smem[PfLds<D>::BYTES];
+    if constexpr (CVT) {
+        // every wave sees the same flags and leaves before any copy
+        if (!prefill_block<T, D, CAP, MASK, SEQ, BIAS, DROP, true>(a, nqt, smem))
+            prefill_block_bf16_operands<T, D, CAP, MASK, SEQ, BIAS, DROP>(
+                (const void*)__builtin_amdgcn_kernarg_segment_ptr(), nqt, smem);
+    } else {
+        prefill_block<T, D, CAP, MASK, SEQ, BIAS, DROP, false>(a, nqt, smem);
+    }
+}
+
+// V of a bf16 call to fp16, one 64-row tile of one (batch, kv head) per
+// workgroup, with the same element offsets as V (so also for the packed QKV
+// layout); flag byte (b, kv head, tile) = 1 when a magnitude reached 65504
+// (or is infinite).  Rows past Lk are not touched.
+template <int D>
+__global__ __launch_bounds__(256) void v16_prepass_kernel(const __bf16* __restrict__ v, _Float16* __restrict__ v16,
+                                                         uint8_t* __restrict__ flags, int Lk, int Hkv,
+                                                         int64_t kv_stride, int ntiles, int fwords) {
+    constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    constexpr int NCH = 64 * CPR / 256;            // chunks per thread
+    const int t = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int64_t base = ((int64_t)b * Lk) * kv_stride + (int64_t)kvh * D;
+    float mx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int chunk = threadIdx.x + 256 * c;
+        const int row = t * 64 + chunk / CPR;
+        if (row < Lk) {
+            const int64_t off = base + (int64_t)row * kv_stride + (chunk % CPR) * 8;
+            u32x4_t x = *reinterpret_cast<const u32x4_t*>(v + off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = cvt_bf16x2_f16x2(x[e], mx);
+            *reinterpret_cast<u32x4_t*>(v16 + off) = x;
+        }
+    }
+    const int over = __syncthreads_or(!(mx < 65504.0f) && mx == mx);   // NaN is no reason
+    if (threadIdx.x == 0) flags[((int64_t)b * Hkv + kvh) * fwords * 4 + t] = over ? 1 : 0;
+    // the padding bytes of the last word are cleared by its own tiles' threads
+    if (t == ntiles - 1 && threadIdx.x > 0 && threadIdx.x < fwords * 4 - t)
+        flags[((int64_t)b * Hkv + kvh) * fwords * 4 + t + threadIdx.x] = 0;
+}
+
 
 template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS = false, bool DROP = false>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int nqt = (a.Lq + BM - 1) / BM;
     const int64_t blocks = (int64_t)a.B * a.Hq * nqt;
-    hipLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK, SEQ, BIAS, DROP>), dim3((unsigned)blocks), dim3(256), 0, s,
+    // instrumentation: a bf16 call's start event went on its V conversion
+    hipExtLaunchKernelGGL((prefill_kernel<T, D, CAP, MASK, SEQ, BIAS, DROP>), dim3((unsigned)blocks), dim3(256), 0, s,
+                          a.v16 ? nullptr : instr_event_begin(), instr_event_end(), 0,
                        a, nqt);
     return hipGetLastError();
 }
@@ -675,6 +784,33 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+size_t v16_workspace_bytes(const FwdArgs& a) {
+    const int ntiles = (a.Lk + 63) / 64, fwords = (ntiles + 3) / 4;
+    const size_t v16 = ((size_t)a.B * a.Lk * a.kv_stride * 2 + 255) & ~size_t(255);
+    return v16 + (((size_t)a.B * a.Hkv * fwords * 4 + 255) & ~size_t(255));
+}
+
+hipError_t launch_v16_prepass(FwdArgs& a, void* ws, hipStream_t s) {
+    const int ntiles = (a.Lk + 63) / 64, fwords = (ntiles + 3) / 4;
+    const size_t v16 = ((size_t)a.B * a.Lk * a.kv_stride * 2 + 255) & ~size_t(255);
+    a.v16 = ws;
+    a.v16_flags = static_cast<const uint8_t*>(ws) + v16;
+    a.v16_fwords = fwords;
+    uint8_t* flags = static_cast<uint8_t*>(ws) + v16;
+    const dim3 grid(ntiles, a.Hkv, a.B);
+    // instrumentation: the conversion belongs to the bf16 prefill it feeds,
+    // so the start event goes here and the stop event on the prefill kernel
+    if (a.D == 64)
+        hipExtLaunchKernelGGL(v16_prepass_kernel<64>, grid, dim3(256), 0, s, instr_event_begin(), nullptr, 0,
+                              static_cast<const __bf16*>(a.v), static_cast<_Float16*>(ws), flags, a.Lk, a.Hkv,
+                              a.kv_stride, ntiles, fwords);
+    else
+        hipExtLaunchKernelGGL(v16_prepass_kernel<128>, grid, dim3(256), 0, s, instr_event_begin(), nullptr, 0,
+                              static_cast<const __bf16*>(a.v), static_cast<_Float16*>(ws), flags, a.Lk, a.Hkv,
+                              a.kv_stride, ntiles, fwords);
+    return hipGetLastError();
+}
+
 bool mfma_bias_supported(const FwdArgs& a) {
     // 16-byte loads of four keys: keys contiguous, every row start 16-byte aligned
     return a.bias && a.bias_stride[3] == 1 && a.Lk % 4 == 0 && (reinterpret_cast<uintptr_t>(a.bias) & 15) == 0 &&
@@ -685,8 +821,26 @@ bool mfma_prefill_supported(int dtype, int D) {
     return (dtype == kBF16 || dtype == kF16) && (D == 64 || D == 128);
 }
 
-hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s) {
-    if ((int64_t)a.B * a.Hq * ((a.Lq + BM - 1) / BM) > 0x7fffffff) return hipErrorInvalidValue;
+hipError_t launch_mfma_prefill(const FwdArgs& a0, int dtype, hipStream_t s) {
+    if ((int64_t)a0.B * a0.Hq * ((a0.Lq + BM - 1) / BM) > 0x7fffffff) return hipErrorInvalidValue;
+    FwdArgs a = a0;
+    a.q_xor = 0u;
+    a.q_clear = 0u;
+    // Without a soft-cap or an additive mask the kernel masks raw scores and
+    // takes their max before applying scale * log2(e), which needs a positive
+    // factor.  A negative scale moves onto Q instead (its elements change
+    // sign, the factor becomes |scale| log2(e)); a zero scale zeroes Q, so
+    // every score is 0 whatever factor is used.
+    if (!(a.softcap > 0.0f) && !a.bias && !(a.scale > 0.0f)) {
+        const float log2e = 1.4426950408889634f;
+        if (a.scale < 0.0f) {
+            a.q_xor = 0x80008000u;
+            a.score_to_log2 = -a.scale * log2e;
+        } else {
+            a.q_clear = 0xffffffffu;
+            a.score_to_log2 = log2e;
+        }
+    }
     if (dtype == kBF16) return a.D == 64 ? launch_d<__bf16, 64>(a, s) : launch_d<__bf16, 128>(a, s);
     if (dtype == kF16) return a.D == 64 ? launch_d<_Float16, 64>(a, s) : launch_d<_Float16, 128>(a, s);
     return hipErrorInvalidValue;

@@ -16,6 +16,9 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Instrumentation events (mfa_set_kernel_events), per host thread.
+thread_local hipEvent_t g_ev_begin = nullptr, g_ev_end = nullptr;
+
 int fail(int status, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -102,13 +105,21 @@ int words_per_batch(int Lk) { return (Lk + 63) / 64; }
 
 size_t mask_words_bytes(int B, int Lk) { return align256((size_t)B * words_per_batch(Lk) * 8); }
 
+// Bytes of the fp16 copy of V (and its flags) that a bf16 call on the MFMA
+// prefill kernel needs; kv_stride elements from one key row to the next.
+size_t v16_bytes(int B, int Lk, int Hkv, int D, int64_t kv_stride) {
+    mfa::FwdArgs t{};
+    t.B = B; t.Lk = Lk; t.Hkv = Hkv; t.D = D; t.kv_stride = kv_stride;
+    return align256(mfa::v16_workspace_bytes(t));
+}
+
 size_t workspace_bytes(int B, int Lq, int Lk, int Hq, int Hkv, int D, int dtype, int path, int splits) {
     size_t ws = mask_words_bytes(B, Lk);
     if (path == MFA_PATH_SPLIT_DECODE) {
-        (void)Lq; (void)dtype;
+        (void)Lq;
         ws += align256(mfa::split_decode_workspace_bytes(B, 1, Hq, D, splits));
     }
-    (void)Hkv;
+    if (path == MFA_PATH_MFMA && dtype == MFA_BF16) ws += v16_bytes(B, Lk, Hkv, D, (int64_t)Hkv * D);
     return ws;
 }
 
@@ -242,7 +253,8 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
 
     mfa::FwdArgs a = make_args(c);
 
-    const bool needs_ws = c.key_mask != nullptr || path == MFA_PATH_SPLIT_DECODE;
+    const bool v16 = path == MFA_PATH_MFMA && c.dtype == MFA_BF16;
+    const bool needs_ws = c.key_mask != nullptr || path == MFA_PATH_SPLIT_DECODE || v16;
     void* ws = workspace;
     if (needs_ws && use_pool) {
         const int pst = pool_alloc(&ws, need, stream);
@@ -254,6 +266,7 @@ int run(const Call& c, int path, int splits, void* workspace, size_t ws_bytes, h
         a.mask_words = reinterpret_cast<const uint64_t*>(wsb);
         e = mfa::launch_mask_words(a, reinterpret_cast<uint64_t*>(wsb), stream);
     }
+    if (e == hipSuccess && v16) e = mfa::launch_v16_prepass(a, wsb + mask_words_bytes(c.B, c.Lk), stream);
     if (e == hipSuccess) {
         switch (path) {
             case MFA_PATH_GENERIC: e = mfa::launch_generic(a, c.dtype, stream); break;
@@ -364,6 +377,104 @@ int run_len(const LenCall& c, int splits, void* workspace, size_t ws_bytes, hipS
     return MFA_SUCCESS;
 }
 
+struct MaskedCall {
+    const void *q, *k, *v;
+    void* out;
+    float* lse;
+    const float* d_mask;
+    int B, Lmax, Hq, Hkv, D;
+    float scale;
+    int window;
+    float softcap;
+    int dtype;
+};
+
+int validate_masked(const MaskedCall& c) {
+    if (c.B != 0 && (!c.q || !c.k || !c.v || !c.out || !c.d_mask))
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k_cache, v_cache, out and d_mask must be non-null");
+    if (c.B < 0 || c.Lmax <= 0 || c.Hq <= 0 || c.Hkv <= 0 || c.D <= 0)
+        return fail(MFA_ERROR_INVALID_VALUE,
+                    "bad dimensions B=%d Lmax=%d Hq=%d Hkv=%d D=%d (B >= 0; others > 0)",
+                    c.B, c.Lmax, c.Hq, c.Hkv, c.D);
+    if (c.Hq % c.Hkv != 0)
+        return fail(MFA_ERROR_INVALID_VALUE, "Hkv=%d does not divide Hq=%d", c.Hkv, c.Hq);
+    if (!std::isfinite(c.scale) || !std::isfinite(c.softcap))
+        return fail(MFA_ERROR_INVALID_VALUE, "scale and softcap must be finite");
+    if (c.dtype != MFA_F32 && c.dtype != MFA_F16 && c.dtype != MFA_BF16)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "unknown dtype %d", c.dtype);
+    if (!mfa::split_decode_supported(c.dtype, c.D, 1, c.Hq / c.Hkv))
+        return fail(MFA_ERROR_NOT_SUPPORTED,
+                    "masked decode needs fp16/bf16, D in {64,128} and Hq/Hkv <= 16 (dtype=%d D=%d Hq/Hkv=%d)",
+                    c.dtype, c.D, c.Hq / c.Hkv);
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.out, 16))
+        return fail(MFA_ERROR_INVALID_VALUE, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (!aligned(c.lse, 4) || !aligned(c.d_mask, 4))
+        return fail(MFA_ERROR_INVALID_VALUE, "lse and d_mask must be 4-byte aligned");
+    const int64_t q_elems = (int64_t)c.B * c.Hq * c.D;
+    const int64_t kv_elems = (int64_t)c.B * c.Lmax * c.Hkv * c.D;
+    if (q_elems < 0 || kv_elems < 0 || (int64_t)c.B * c.Hq > (int64_t)1 << 30)
+        return fail(MFA_ERROR_INVALID_VALUE, "problem too large");
+    return MFA_SUCCESS;
+}
+
+size_t masked_ws_bytes(int B, int Lmax, int Hq, int D, int splits) {
+    return mask_words_bytes(B, Lmax) + align256(mfa::split_decode_workspace_bytes(B, 1, Hq, D, splits));
+}
+
+int run_masked(const MaskedCall& c, int splits, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    int st = validate_masked(c);
+    if (st != MFA_SUCCESS) return st;
+    if (c.B == 0) return MFA_SUCCESS;
+    const int group = c.Hq / c.Hkv;
+    splits = len_splits(c.B, c.Hkv, c.Lmax, group, splits);
+    const size_t need = masked_ws_bytes(c.B, c.Lmax, c.Hq, c.D, splits);
+    const bool use_pool = workspace == nullptr && ws_bytes == 0;
+    if (!use_pool) {
+        if (!workspace) return fail(MFA_ERROR_INVALID_VALUE, "workspace is null but ws_bytes > 0");
+        if (!aligned(workspace, 256)) return fail(MFA_ERROR_INVALID_VALUE, "workspace must be 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(MFA_ERROR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+    }
+
+    mfa::FwdArgs a{};
+    a.q = c.q; a.k = c.k; a.v = c.v; a.out = c.out; a.lse = c.lse;
+    a.key_mask = c.d_mask;
+    a.B = c.B; a.Lq = 1; a.Lk = c.Lmax; a.Hq = c.Hq; a.Hkv = c.Hkv; a.D = c.D;
+    a.group = group;
+    a.causal = 1;
+    a.window = c.window > 0 ? c.window : 0;
+    a.words_per_batch = words_per_batch(c.Lmax);
+    a.q_stride = (int64_t)c.Hq * c.D;
+    a.kv_stride = (int64_t)c.Hkv * c.D;
+    a.o_stride = (int64_t)c.Hq * c.D;
+    a.scale = c.scale;
+    a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;
+    const float log2e = 1.4426950408889634f;
+    a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * c.scale;
+
+    void* ws = workspace;
+    if (use_pool) {
+        const int pst = pool_alloc(&ws, need, stream);
+        if (pst != MFA_SUCCESS) return pst;
+    }
+    char* wsb = static_cast<char*>(ws);
+    a.mask_words = reinterpret_cast<const uint64_t*>(wsb);
+    hipError_t e = mfa::launch_mask_words(a, reinterpret_cast<uint64_t*>(wsb), stream);
+    if (e == hipSuccess)
+        e = mfa::launch_split_decode(a, nullptr, c.dtype, splits,
+                                     reinterpret_cast<float*>(wsb + mask_words_bytes(c.B, c.Lmax)), stream,
+                                     /*pos_from_mask=*/true);
+    if (use_pool) {
+        hipError_t e2 = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return MFA_SUCCESS;
+}
+
 int run_packed(const void* qkv, const int* seq_bounds, void* out, float* lse, int L, int H, int D,
                float scale, int window, float softcap, int dtype, hipStream_t stream) {
     if (L != 0 && (!qkv || !seq_bounds || !out))
@@ -404,8 +515,20 @@ int run_packed(const void* qkv, const int* seq_bounds, void* out, float* lse, in
     a.softcap = softcap > 0.0f ? softcap : 0.0f;
     const float log2e = 1.4426950408889634f;
     a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * scale;
-    const hipError_t e = mfa::mfma_prefill_supported(dtype, D) ? mfa::launch_mfma_prefill(a, dtype, stream)
-                                                                : mfa::launch_generic(a, dtype, stream);
+    const bool mfma = mfa::mfma_prefill_supported(dtype, D);
+    // bf16 on the MFMA kernel: the fp16 copy of V comes from the pool
+    const bool v16 = mfma && dtype == MFA_BF16;
+    void* ws = nullptr;
+    if (v16) {
+        const int pst = pool_alloc(&ws, v16_bytes(1, L, H, D, a.kv_stride), stream);
+        if (pst != MFA_SUCCESS) return pst;
+    }
+    hipError_t e = v16 ? mfa::launch_v16_prepass(a, ws, stream) : hipSuccess;
+    if (e == hipSuccess) e = mfma ? mfa::launch_mfma_prefill(a, dtype, stream) : mfa::launch_generic(a, dtype, stream);
+    if (v16) {
+        hipError_t e2 = hipFreeAsync(ws, stream);
+        if (e == hipSuccess) e = e2;
+    }
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(MFA_ERROR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -413,7 +536,14 @@ int run_packed(const void* qkv, const int* seq_bounds, void* out, float* lse, in
     return MFA_SUCCESS;
 }
 
-size_t varlen_ws_bytes(int Tq) { return align256((size_t)Tq * 3 * sizeof(int)); }
+// Per-row positions and bounds, then (bf16 on the MFMA kernel) the fp16 copy
+// of V.
+size_t varlen_ws_bytes(int Tq, int Tk, int Hkv, int D, int dtype) {
+    size_t ws = align256((size_t)Tq * 3 * sizeof(int));
+    if (dtype == MFA_BF16 && mfa::mfma_prefill_supported(dtype, D) && Tk > 0)
+        ws += v16_bytes(1, Tk, Hkv, D, (int64_t)Hkv * D);
+    return ws;
+}
 
 int run_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int* cu_q,
                const int* cu_k, int batch, int Tq, int Tk, int Hq, int Hkv, int D, float scale, int causal,
@@ -438,7 +568,7 @@ int run_varlen(const void* q, const void* k, const void* v, void* out, float* ls
     if ((int64_t)Tq * Hq * D < 0 || (int64_t)Tk * Hkv * D < 0 || Hq > (1 << 20))
         return fail(MFA_ERROR_INVALID_VALUE, "problem too large");
     if (Tq == 0) return MFA_SUCCESS;
-    const size_t need = varlen_ws_bytes(Tq);
+    const size_t need = varlen_ws_bytes(Tq, Tk, Hkv, D, dtype);
     const bool use_pool = workspace == nullptr && ws_bytes == 0;
     if (!use_pool) {
         if (!workspace) return fail(MFA_ERROR_INVALID_VALUE, "workspace is null but ws_bytes > 0");
@@ -471,9 +601,10 @@ int run_varlen(const void* q, const void* k, const void* v, void* out, float* ls
     const float log2e = 1.4426950408889634f;
     a.score_to_log2 = a.softcap > 0.0f ? log2e : log2e * scale;
     hipError_t e = mfa::launch_varlen_rows(cu_q, cu_k, batch, Tq, Tk, row_pos, bounds, stream);
-    if (e == hipSuccess)
-        e = mfa::mfma_prefill_supported(dtype, D) ? mfa::launch_mfma_prefill(a, dtype, stream)
-                                                   : mfa::launch_generic(a, dtype, stream);
+    const bool mfma = mfa::mfma_prefill_supported(dtype, D);
+    if (e == hipSuccess && mfma && dtype == MFA_BF16 && Tk > 0)
+        e = mfa::launch_v16_prepass(a, static_cast<char*>(ws) + align256((size_t)Tq * 3 * sizeof(int)), stream);
+    if (e == hipSuccess) e = mfma ? mfa::launch_mfma_prefill(a, dtype, stream) : mfa::launch_generic(a, dtype, stream);
     if (use_pool) {
         hipError_t e2 = hipFreeAsync(ws, stream);
         if (e == hipSuccess) e = e2;
@@ -487,6 +618,11 @@ int run_varlen(const void* q, const void* k, const void* v, void* out, float* ls
 
 }  // namespace
 
+namespace mfa {
+hipEvent_t instr_event_begin() { return g_ev_begin; }
+hipEvent_t instr_event_end() { return g_ev_end; }
+}  // namespace mfa
+
 extern "C" {
 
 int mfa_varlen_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -499,7 +635,10 @@ int mfa_varlen_fwd(const void* q, const void* k, const void* v, void* out, float
                       static_cast<hipStream_t>(stream));
 }
 
-size_t mfa_varlen_workspace_size(int total_q) { return total_q > 0 ? varlen_ws_bytes(total_q) : 0; }
+size_t mfa_varlen_workspace_size(int total_q, int total_k, int Hkv, int D, int dtype) {
+    if (total_q <= 0 || total_k < 0 || Hkv <= 0 || D <= 0) return 0;
+    return varlen_ws_bytes(total_q, total_k, Hkv, D, dtype);
+}
 
 int mfa_packed_qkv_fwd(const void* qkv, const int* seq_bounds, void* out, float* lse,
                        int L, int H, int D, float scale, int window, float softcap, int dtype,
@@ -523,6 +662,22 @@ size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, in
     if (!mfa::decode_len_supported(dtype, D, R, Hq / Hkv)) return 0;
     splits = len_splits(B, Hkv, Lmax, Hq / Hkv, splits);
     return align256(mfa::split_decode_workspace_bytes(B, R, Hq, D, splits));
+}
+
+int mfa_decode_masked(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                      const float* d_mask, int B, int Lmax, int Hq, int Hkv, int D,
+                      float scale, int window, float softcap, int dtype, int splits,
+                      void* workspace, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    MaskedCall c{q, k_cache, v_cache, out, lse, d_mask, B, Lmax, Hq, Hkv, D, scale, window, softcap, dtype};
+    return run_masked(c, splits, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t mfa_decode_masked_workspace_size(int B, int Lmax, int Hq, int Hkv, int D, int dtype, int splits) {
+    if (B <= 0 || Lmax <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return 0;
+    if (!mfa::split_decode_supported(dtype, D, 1, Hq / Hkv)) return 0;
+    splits = len_splits(B, Hkv, Lmax, Hq / Hkv, splits);
+    return masked_ws_bytes(B, Lmax, Hq, D, splits);
 }
 
 int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -616,8 +771,9 @@ int mfa_fwd_ws(const void* q, const void* k, const void* v, void* out, float* ls
     Call c{q, k, v, out, lse, B, Lq, Lk, Hq, Hkv, D, scale, causal, window, q_offset, softcap, key_mask, dtype};
     if (!workspace && ws_bytes == 0) {
         // nothing given: valid only when the plan needs no workspace
+        const int p = auto_path(B, Lq, Lk, Hq, Hkv, D, dtype);
         if (mfa_fwd_workspace_size(B, Lq, Lk, Hq, Hkv, D, dtype) > 0 &&
-            (key_mask || auto_path(B, Lq, Lk, Hq, Hkv, D, dtype) == MFA_PATH_SPLIT_DECODE))
+            (key_mask || p == MFA_PATH_SPLIT_DECODE || (p == MFA_PATH_MFMA && dtype == MFA_BF16)))
             return fail(MFA_ERROR_INVALID_VALUE, "this call needs a workspace");
     }
     return run(c, MFA_PATH_AUTO, 0, workspace, ws_bytes, static_cast<hipStream_t>(stream));
@@ -660,6 +816,11 @@ const char* mfa_status_string(int status) {
 
 const char* mfa_last_error(void) { return g_last_error.c_str(); }
 
-int mfa_version(void) { return 200; }
+void mfa_set_kernel_events(void* begin, void* end) {
+    g_ev_begin = static_cast<hipEvent_t>(begin);
+    g_ev_end = static_cast<hipEvent_t>(end);
+}
+
+int mfa_version(void) { return 300; }
 
 }  // extern "C"

@@ -2,6 +2,7 @@
 // shared by the libmfa host code and its HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,6 +42,16 @@ struct FwdArgs {
     uint32_t drop_threshold;
     float drop_scale;
     uint64_t drop_seed;
+    // MFMA prefill only: each 32-bit word of the Q operand is replaced by
+    // (word ^ q_xor) & ~q_clear when it is loaded (sign flip or zeroing of
+    // the 16-bit elements), set by its launcher for a scale <= 0
+    uint32_t q_xor, q_clear;
+    // MFMA prefill of bf16 inputs: V converted to fp16 (same element offsets
+    // as v) and one flag byte per (batch, kv head, 64-key tile), v16_fwords
+    // 32-bit words per (batch, kv head); set by launch_v16_prepass
+    const void* v16;
+    const uint8_t* v16_flags;
+    int v16_fwords;
 };
 
 // Keys [lo, hi] (inclusive) in range for a query at absolute position aq,
@@ -71,11 +82,16 @@ __host__ __device__ inline void key_range(int aq, int Lk, int causal, int window
 // (rows past a window's reach lie at the end of their sequence).
 // SEQ = false ignores row_pos and seq_bounds (kernels instantiated for
 // plain batches); SEQ = true reads whichever of them is given.
+// Whatever the bounds hold, the sequence ends are first clamped to [0, Lk],
+// so a nonempty range always lies inside [0, Lk - 1] and an empty one is
+// [s1, s1 - 1] with s1 in [0, Lk].
 template <bool SEQ = true>
-__device__ inline void row_key_range(const FwdArgs& a, int i, int& lo, int& hi) {
+__host__ __device__ inline void row_key_range(const FwdArgs& a, int i, int& lo, int& hi) {
     key_range(SEQ && a.row_pos ? a.row_pos[i] : i + a.q_offset, a.Lk, a.causal, a.window, lo, hi);
     if (SEQ && a.seq_bounds) {
-        const int s0 = a.seq_bounds[2 * i], s1 = a.seq_bounds[2 * i + 1];
+        int s0 = a.seq_bounds[2 * i], s1 = a.seq_bounds[2 * i + 1];
+        s0 = s0 < 0 ? 0 : (s0 > a.Lk ? a.Lk : s0);
+        s1 = s1 < 0 ? 0 : (s1 > a.Lk ? a.Lk : s1);
         lo = lo > s0 ? lo : s0;
         hi = hi < s1 - 1 ? hi : s1 - 1;
         if (lo > hi) { lo = s1; hi = s1 - 1; }
@@ -118,6 +134,14 @@ __device__ inline bool dropout_keep(const FwdArgs& a, int b, int hq, int i, int 
     return (dropout_keep4(a, b, hq, i, j >> 2) >> (j & 3)) & 1u;
 }
 
+// Instrumentation events of the calling host thread (mfa_set_kernel_events,
+// null when unset): the main kernel launch of a call takes them as the start
+// and stop events of hipExtLaunchKernelGGL, whose timestamps come from the
+// dispatch itself (a separate event record would add a marker packet and a
+// gap of its own between kernels).
+hipEvent_t instr_event_begin();
+hipEvent_t instr_event_end();
+
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_mask_words(const FwdArgs& a, uint64_t* words, hipStream_t s);
 // Per-row position and key bounds of a varlen packing: row i of sequence b
@@ -138,14 +162,23 @@ bool bwd_mfma_supported(const FwdArgs& a, int dtype);
 hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                                 int dtype, hipStream_t s);
 hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s);
+// bf16 MFMA prefill: bytes of the fp16 copy of V and its flags, and the
+// launch that fills them from a.v into ws (256-byte aligned) and points
+// a.v16 / a.v16_flags / a.v16_fwords there.  Must precede launch_mfma_prefill
+// on the same stream.
+size_t v16_workspace_bytes(const FwdArgs& a);
+hipError_t launch_v16_prepass(FwdArgs& a, void* ws, hipStream_t s);
 bool mfma_prefill_supported(int dtype, int D);
 // Whether the MFMA prefill kernel can read a's additive mask (keys contiguous,
 // Lk and every row start a multiple of four floats).
 bool mfma_bias_supported(const FwdArgs& a);
 // Split decode: a.Lq query rows per batch (1 unless d_len is given).  With
 // d_len (device [B]) the key range of batch b is its first d_len[b] keys.
+// With pos_from_mask (one query row, a key mask and its packed words in
+// a.mask_words) the query sits at the batch's last valid key and a window
+// counts back from there.
 hipError_t launch_split_decode(const FwdArgs& a, const int* d_len, int dtype, int splits,
-                               float* partials, hipStream_t s);
+                               float* partials, hipStream_t s, bool pos_from_mask = false);
 bool split_decode_supported(int dtype, int D, int Lq, int group);
 bool decode_len_supported(int dtype, int D, int R, int group);
 int split_decode_default_splits(int B, int Hkv, int Lk, int group);

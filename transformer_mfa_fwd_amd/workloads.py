@@ -122,6 +122,36 @@ def make_cache_lengths(B: int, Lmax: int, R: int, seed: int = 0, edges: bool = T
     return n.to(torch.int32)
 
 
+def make_cache_masks(B: int, Lmax: int, seed: int = 0, edges: bool = True) -> torch.Tensor:
+    """[B, Lmax] float32 validity masks of a fixed-capacity cache on the CPU
+    (1 valid, 0 not): per batch a valid prefix of length uniform in [1, Lmax]
+    in which each key is then dropped with a probability uniform in [0, 0.5),
+    from a CPU generator seeded with ``seed``.  With ``edges`` the first
+    batches get, as many as fit: no valid key, only key 0, only the last key,
+    a full cache, a plain prefix of half the capacity, and valid keys spread
+    over the whole capacity with the last one valid."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    m = torch.zeros((B, Lmax), dtype=torch.float32)
+    n = torch.randint(1, Lmax + 1, (B,), generator=g)
+    drop = torch.rand((B,), generator=g) * 0.5
+    u = torch.rand((B, Lmax), generator=g)
+    for b in range(B):
+        m[b, :int(n[b])] = (u[b, :int(n[b])] >= drop[b]).float()
+    if edges:
+        fixed = []
+        z = torch.zeros(Lmax)
+        fixed.append(z.clone())                            # no valid key
+        t = z.clone(); t[0] = 1.0; fixed.append(t)         # only key 0
+        t = z.clone(); t[-1] = 1.0; fixed.append(t)        # only the last key
+        fixed.append(torch.ones(Lmax))                     # full
+        t = z.clone(); t[:max(1, Lmax // 2)] = 1.0; fixed.append(t)   # half prefix
+        t = (u[0] < 0.3).float(); t[-1] = 1.0; fixed.append(t)        # spread, last valid
+        for i, x in enumerate(fixed[:B]):
+            m[i] = x
+    return m
+
+
 def seq_bounds_from_lengths(lengths) -> torch.Tensor:
     """[L, 2] int32 on the CPU for sequences of the given lengths packed back to
     back: row r of a sequence spanning rows [s, e) holds (s, e)."""
