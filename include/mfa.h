@@ -236,6 +236,28 @@ int mfa_decode_len(const void* q, const void* k_cache, const void* v_cache, void
 size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, int D, int dtype,
                                      int splits);
 
+/* Bytes of device scratch that mfa_decode_len_noalloc holds on each device. */
+#define MFA_NOALLOC_SCRATCH_BYTES ((size_t)16 * 1024 * 1024)
+
+/*
+ * mfa_decode_len for callers that cannot allocate device memory or hand in a
+ * workspace: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  Same arguments (minus the workspace), checks,
+ * kernels and results as mfa_decode_len with the same split count; the split
+ * partials go to a static device array of MFA_NOALLOC_SCRATCH_BYTES that each
+ * device holds from its first such call until the process ends.  The call
+ * itself allocates nothing: its first call on a device only looks up that
+ * array's address there.  Sizes whose workspace
+ * (mfa_decode_len_workspace_size) exceeds MFA_NOALLOC_SCRATCH_BYTES are
+ * rejected with MFA_ERROR_INVALID_VALUE before any device work (a smaller
+ * `splits` shrinks it).  Every call on one device shares its array, so calls
+ * whose kernels overlap on one device (other streams, or other host threads)
+ * race and give undefined results; calls in order on one stream are safe.
+ */
+int mfa_decode_len_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                           const int* d_len, int B, int R, int Lmax, int Hq, int Hkv, int D,
+                           float scale, float softcap, int dtype, int splits, void* stream);
+
 /*
  * Single-query decode over a fixed-capacity KV cache whose valid rows are
  * marked by a key mask in device memory (brotensor flash_attention.h,

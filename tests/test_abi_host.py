@@ -171,6 +171,48 @@ def test_decode_len_empty_batch_and_workspace_size():
         2 * 8 * 3 * (128 + 2) * 4
 
 
+def call_len_noalloc(**over):
+    lib = mfa.load_library()
+    a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], lse=FAKE[4], d_len=FAKE[5], B=2, R=2,
+             Lmax=64, Hq=8, Hkv=2, D=128, scale=0.1, softcap=0.0, dtype=2, splits=0)
+    a.update(over)
+    return lib.mfa_decode_len_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["d_len"], a["B"],
+                                      a["R"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                      a["softcap"], a["dtype"], a["splits"], None)
+
+
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
+
+
+@pytest.mark.parametrize("over", [o for o in LEN_INVALID if "ws" not in o],
+                         ids=lambda d: ",".join(f"{k}" for k in d))
+def test_decode_len_noalloc_invalid_arguments_rejected(over):
+    assert call_len_noalloc(**over) == 1, over
+    assert mfa.load_library().mfa_last_error().decode()
+
+
+@pytest.mark.parametrize("over", [dict(D=96), dict(dtype=0), dict(R=5, Hq=8, Hkv=2)])
+def test_decode_len_noalloc_unsupported_rejected(over):
+    assert call_len_noalloc(**over) == 2, over
+
+
+def test_decode_len_noalloc_scratch_limit():
+    """Sizes whose partials exceed the static scratch are rejected before any
+    device work; the header states the same limit."""
+    import torch
+    assert call_len_noalloc(B=0) == 0
+    assert re.search(r"#define\s+MFA_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)16 \* 1024 \* 1024\)",
+                     open(HEADER).read())
+    big = dict(B=64, R=4, Lmax=4096, Hq=32, Hkv=8, D=128, splits=8)
+    need = mfa.decode_len_workspace_size(64, 4, 4096, 32, 8, 128, torch.bfloat16, splits=8)
+    assert need > NOALLOC_SCRATCH_BYTES
+    assert call_len_noalloc(**big) == 1
+    msg = mfa.load_library().mfa_last_error().decode()
+    assert str(need) in msg and str(NOALLOC_SCRATCH_BYTES) in msg, msg
+    # the full device-length decode fits at its chosen split count
+    assert mfa.decode_len_workspace_size(64, 4, 32768, 32, 8, 128, torch.bfloat16) <= NOALLOC_SCRATCH_BYTES
+
+
 def call_masked(**over):
     lib = mfa.load_library()
     a = dict(q=FAKE[0], k=FAKE[1], v=FAKE[2], out=FAKE[3], lse=FAKE[4], d_mask=FAKE[5], B=2, Lmax=64,

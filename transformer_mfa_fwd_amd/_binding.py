@@ -24,7 +24,7 @@ PATH_NAMES = {PATH_AUTO: "auto", PATH_GENERIC: "generic", PATH_MFMA: "mfma",
 _DTYPE_CODES = {torch.float32: MFA_F32, torch.float16: MFA_F16, torch.bfloat16: MFA_BF16}
 
 EXPORTED = ("mfa_fwd", "mfa_fwd_workspace_size", "mfa_fwd_ws", "mfa_fwd_ex", "mfa_fwd_plan",
-            "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_decode_masked",
+            "mfa_decode_len", "mfa_decode_len_workspace_size", "mfa_decode_len_noalloc", "mfa_decode_masked",
             "mfa_decode_masked_workspace_size", "mfa_packed_qkv_fwd",
             "mfa_varlen_fwd", "mfa_varlen_workspace_size", "mfa_fwd_bias_dropout",
             "mfa_bwd", "mfa_bwd_workspace_size",
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.mfa_decode_len.restype = _I
     lib.mfa_decode_len.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P, ctypes.c_size_t, _P]
     lib.mfa_decode_masked.restype = _I
+    lib.mfa_decode_len_noalloc.restype = _I
+    lib.mfa_decode_len_noalloc.argtypes = [_P] * 6 + [_I] * 6 + [_F, _F, _I, _I, _P]
     lib.mfa_decode_masked.argtypes = [_P] * 6 + [_I] * 5 + [_F, _I, _F, _I, _I, _P, ctypes.c_size_t, _P]
     lib.mfa_decode_masked_workspace_size.restype = ctypes.c_size_t
     lib.mfa_decode_masked_workspace_size.argtypes = [_I] * 7
@@ -195,6 +197,21 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     return out, lse
 
 
+def _decode_len_dims(q, k_cache, v_cache, d_len):
+    B, R, Lmax, Hq, Hkv, D = _dims(q, k_cache, v_cache)
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or \
+            v_cache.dtype != q.dtype:
+        raise TypeError(f"dtypes must match and be float16 or bfloat16 "
+                        f"(got {q.dtype}, {k_cache.dtype}, {v_cache.dtype})")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if d_len.dtype != torch.int32 or tuple(d_len.shape) != (B,) or not d_len.is_cuda or \
+            not d_len.is_contiguous():
+        raise ValueError("d_len must be a contiguous int32 GPU tensor of shape [B]")
+    return B, R, Lmax, Hq, Hkv, D
+
+
 def decode_len(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                d_len: torch.Tensor, *, softcap: float = 0.0, scale: Optional[float] = None,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -213,17 +230,7 @@ def decode_len(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     capture needs.
     """
     lib = load_library()
-    B, R, Lmax, Hq, Hkv, D = _dims(q, k_cache, v_cache)
-    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or \
-            v_cache.dtype != q.dtype:
-        raise TypeError(f"dtypes must match and be float16 or bfloat16 "
-                        f"(got {q.dtype}, {k_cache.dtype}, {v_cache.dtype})")
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if d_len.dtype != torch.int32 or tuple(d_len.shape) != (B,) or not d_len.is_cuda or \
-            not d_len.is_contiguous():
-        raise ValueError("d_len must be a contiguous int32 GPU tensor of shape [B]")
+    B, R, Lmax, Hq, Hkv, D = _decode_len_dims(q, k_cache, v_cache, d_len)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -241,6 +248,30 @@ def decode_len(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                   _DTYPE_CODES[q.dtype], int(splits), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
     return out, lse
+
+
+def decode_len_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       d_len: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor] = None, *,
+                       softcap: float = 0.0, scale: Optional[float] = None, splits: int = 0,
+                       stream=None) -> None:
+    """decode_len into caller-given out [B, R, Hq, D] (and lse [B, Hq, R]
+    float32, or None) with the split partials in the library's static device
+    scratch (mfa_decode_len_noalloc): neither this function nor the library
+    allocates device memory.  Calls whose kernels overlap on one device share
+    that scratch and race."""
+    lib = load_library()
+    B, R, Lmax, Hq, Hkv, D = _decode_len_dims(q, k_cache, v_cache, d_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be contiguous and match q")
+    if lse is not None and (lse.shape != (B, Hq, R) or lse.dtype != torch.float32 or
+                            not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be contiguous float32 [B, Hq, R] on q's device")
+    with torch.cuda.device(q.device):
+        _check(lib.mfa_decode_len_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                          _ptr(d_len), B, R, Lmax, Hq, Hkv, D, float(scale), float(softcap),
+                                          _DTYPE_CODES[q.dtype], int(splits), _stream(stream)))
 
 
 def decode_masked(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

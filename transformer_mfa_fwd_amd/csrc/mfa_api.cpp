@@ -377,6 +377,14 @@ int run_len(const LenCall& c, int splits, void* workspace, size_t ws_bytes, hipS
     return MFA_SUCCESS;
 }
 
+// Per-device addresses of the static scratch of mfa_decode_len_noalloc
+// (defined after this namespace), looked up once per device.
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+
+int noalloc_scratch(void** p);
+
 struct MaskedCall {
     const void *q, *k, *v;
     void* out;
@@ -618,6 +626,42 @@ int run_varlen(const void* q, const void* k, const void* v, void* out, float* ls
 
 }  // namespace
 
+// Scratch of mfa_decode_len_noalloc: the split partials of that call live
+// here rather than in caller or pool memory.  Every device that runs the call
+// holds its own copy of the array until the process ends.  On the host the
+// name only stands in for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, never the name itself.
+static __device__ __align__(256) unsigned char scratch[MFA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// This device's address of `scratch`, found with hipGetSymbolAddress on the
+// first call made with the device current and kept for later calls (a failed
+// lookup is kept too and reported by every later call on that device).
+int noalloc_scratch(void** p) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MFA_ERROR_HIP, "hipGetDevice failed");
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MFA_ERROR_NOT_SUPPORTED, "device %d is beyond the %d the library serves", dev, kMaxDevices);
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) (void)hipGetLastError();
+        g_scratch_err[dev] = e != hipSuccess ? e : (ptr ? hipSuccess : hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return fail(MFA_ERROR_HIP, "no address for the static scratch on device %d: %s", dev,
+                    hipGetErrorString(g_scratch_err[dev]));
+    *p = g_scratch_ptr[dev];
+    return MFA_SUCCESS;
+}
+
+}  // namespace
+
 namespace mfa {
 hipEvent_t instr_event_begin() { return g_ev_begin; }
 hipEvent_t instr_event_end() { return g_ev_end; }
@@ -655,6 +699,28 @@ int mfa_decode_len(const void* q, const void* k_cache, const void* v_cache, void
     g_last_error.clear();
     LenCall c{q, k_cache, v_cache, out, lse, d_len, B, R, Lmax, Hq, Hkv, D, scale, softcap, dtype};
     return run_len(c, splits, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int mfa_decode_len_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                           const int* d_len, int B, int R, int Lmax, int Hq, int Hkv, int D,
+                           float scale, float softcap, int dtype, int splits, void* stream) {
+    g_last_error.clear();
+    LenCall c{q, k_cache, v_cache, out, lse, d_len, B, R, Lmax, Hq, Hkv, D, scale, softcap, dtype};
+    int st = validate_len(c);
+    if (st != MFA_SUCCESS || B == 0) return st;
+    splits = len_splits(B, Hkv, Lmax, Hq / Hkv, splits);
+    const size_t need = align256(mfa::split_decode_workspace_bytes(B, R, Hq, D, splits));
+    if (need > MFA_NOALLOC_SCRATCH_BYTES)
+        return fail(MFA_ERROR_INVALID_VALUE,
+                    "these sizes need %zu bytes of scratch (B=%d R=%d Hq=%d D=%d, %d splits) but the static "
+                    "scratch holds %zu: pass fewer splits, or call mfa_decode_len with a workspace",
+                    need, B, R, Hq, D, splits, (size_t)MFA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != MFA_SUCCESS) return st;
+    // every partial slot the combine reads is written by the split kernel of
+    // the same call first, so nothing in the scratch needs clearing
+    return run_len(c, splits, ws, MFA_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
 }
 
 size_t mfa_decode_len_workspace_size(int B, int R, int Lmax, int Hq, int Hkv, int D, int dtype, int splits) {
