@@ -60,12 +60,6 @@ struct DecodeArgs {
     float* part_o;    // [B, R, Hq, S, D]
 };
 
-// Visible-key bits of tile t (keys 32t .. 32t+31) from the packed mask.
-__device__ inline uint32_t tile_mask_bits(const uint64_t* words, int t) {
-    const uint64_t w = words[t >> 1];
-    return (uint32_t)(w >> ((t & 1) * 32));
-}
-
 template <typename T, int D, bool CAP, bool MASK>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
     constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -141,6 +135,25 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
         }
     }
 
+    // Mask bits of tile t.  Lane l holds word wbase + l of the batch (a window
+    // of 64 words, 128 tiles), reloaded when the tiles move past it, so the
+    // choice of the next tile costs a cross-lane read instead of a memory
+    // round trip before that tile's loads can issue.  Tiles only move forward.
+    int wbase = -64;
+    uint32_t wlo = 0u, whi = 0u;
+    auto bits_of = [&](int t) -> uint32_t {
+        const int w = t >> 1;
+        if (w >= wbase + 64) {
+            wbase = w & ~63;
+            const int ww = wbase + lane;
+            const uint64_t x = ww < a.words_per_batch ? words[ww] : 0ull;
+            wlo = (uint32_t)x;
+            whi = (uint32_t)(x >> 32);
+        }
+        return (uint32_t)__builtin_amdgcn_readlane((int)((t & 1) ? whi : wlo), w - wbase);
+    };
+    (void)bits_of;
+
     const T* __restrict__ kp = static_cast<const T*>(a.k);
     const T* __restrict__ vp = static_cast<const T*>(a.v);
     const int64_t row_stride = (int64_t)a.Hkv * D;
@@ -157,8 +170,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
 
     const float two_log2e_over_cap = CAP ? 2.0f * 1.4426950408889634f / a.softcap : 0.0f;
 
+    // bits_t: mask bits of tile t, read when t was chosen (the window may
+    // have moved on to the next tile's words since)
     int t = t_begin;
-    if (MASK) while (t < t_end && tile_mask_bits(words, t) == 0u) ++t;
+    uint32_t bits_t = 0xffffffffu;
+    if (MASK) while (t < t_end && (bits_t = bits_of(t)) == 0u) ++t;
     if (t < t_end) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
@@ -172,7 +188,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
     while (t < t_end) {
         // next tile with a visible key
         int tn = t + 1;
-        if (MASK) while (tn < t_end && tile_mask_bits(words, tn) == 0u) ++tn;
+        uint32_t bits_n = 0xffffffffu;
+        if (MASK) while (tn < t_end && (bits_n = bits_of(tn)) == 0u) ++tn;
         __syncthreads();  // LDS no longer read by the previous tile
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
@@ -206,7 +223,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
         }
 
         // transform, mask, running max
-        const uint32_t bits = MASK ? tile_mask_bits(words, t) : 0xffffffffu;
+        const uint32_t bits = bits_t;
         const bool interior = t * DT >= lo && t * DT + DT - 1 <= hi_min && (!MASK || bits == 0xffffffffu);
         float x[8];
         float tmax = -INFINITY;
@@ -270,6 +287,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
             if constexpr (SPLIT_P) oacc[db] = Mfma<T>::mma16(bitcast<v8>(vv), pop_lo, oacc[db]);
         }
         t = tn;
+        bits_t = bits_n;
     }
 
     // lane groups hold disjoint keys of the same query column: total the sum
