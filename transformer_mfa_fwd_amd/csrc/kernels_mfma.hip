@@ -232,7 +232,12 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
         for (int w = lane; w < a.v16_fwords; w += 64) any |= fl[w];
         if (__any(any != 0u)) return false;
     }
-    const uint64_t* words = MASK ? a.mask_words + (int64_t)b * a.words_per_batch : nullptr;
+    // The mask words are read-only while the kernel runs (written by the
+    // launch before it): reading them through the constant address space
+    // lets the compiler use scalar loads, which the scalar cache serves,
+    // instead of vector loads whose latency the next copy would wait on.
+    typedef const __attribute__((address_space(4))) uint64_t cword_t;
+    cword_t* words = MASK ? (cword_t*)(a.mask_words + (int64_t)b * a.words_per_batch) : nullptr;
 
     // ---- Q^T operand: lane holds Q[qrow][16 ks + 8 h2 .. +7]
     v8 qop[NKS];
