@@ -48,21 +48,48 @@ __device__ inline bool key_kept(const FwdArgs& a, int b, int j) {
     return j < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + j] > 0.5f);
 }
 
+// Delta of every query row: the rows of [B, Lq, Hq, D] are taken in memory
+// order, D/E lanes per row read 16 bytes (E elements) each of O and dO, and
+// the row's lanes add their partial sums.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(FwdArgs a, const T* __restrict__ dout,
                                                         float* __restrict__ delta) {
-    const int lane = threadIdx.x & 63;
-    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int hq = blockIdx.y, b = blockIdx.z;
-    if (i >= a.Lq) return;
-    const int64_t off = ((int64_t)b * a.Lq + i) * a.o_stride + (int64_t)hq * D;
-    const T* o = static_cast<const T*>(a.out) + off;
+    constexpr int E = 16 / (int)sizeof(T);    // elements per 16-byte chunk
+    constexpr int LPR = D / E;                // lanes per row
+    constexpr int RPB = 256 / LPR;            // rows per block
+    static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0, "a row's lanes lie in one wave");
+    const int64_t nrows = (int64_t)a.B * a.Lq * a.Hq;
+    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // (b * Lq + i) * Hq + hq
+    const int c = threadIdx.x % LPR;
     float s = 0.0f;
+    int64_t bi = 0;
+    int hq = 0;
+    if (r < nrows) {
+        bi = r / a.Hq;
+        hq = (int)(r - bi * a.Hq);
+        const int64_t off = bi * a.o_stride + (int64_t)hq * D + c * E;
+        const T* o = static_cast<const T*>(a.out) + off;
+        const T* g = dout + off;
+        T ov[E], gv[E];
+        *reinterpret_cast<uint4*>(ov) = *reinterpret_cast<const uint4*>(o);
+        *reinterpret_cast<uint4*>(gv) = *reinterpret_cast<const uint4*>(g);
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) s = fmaf(f32(o[lane + 64 * c]), f32(dout[off + lane + 64 * c]), s);
+        for (int e = 0; e < E; ++e) s = fmaf(f32(ov[e]), f32(gv[e]), s);
+    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-    if (lane == 0) delta[((int64_t)b * a.Hq + hq) * a.Lq + i] = s;
+    for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (r < nrows && c == 0) {
+        const int64_t b = bi / a.Lq, i = bi - b * a.Lq;
+        delta[(b * a.Hq + hq) * a.Lq + i] = s;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_delta(const FwdArgs& a, const T* dout, float* delta, hipStream_t s) {
+    constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
+    const int64_t blocks = ((int64_t)a.B * a.Lq * a.Hq + RPB - 1) / RPB;
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a, dout, delta);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -281,8 +308,7 @@ hipError_t launch_bwd_t(const FwdArgs& a, const void* dout, float* delta, void* 
     const T* g = static_cast<const T*>(dout);
     hipError_t e;
     if (a.Lq > 0) {   // with no query rows only the (zero) key gradients remain
-        hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((a.Lq + 3) / 4, a.Hq, a.B), dim3(256), 0, s, a, g, delta);
-        e = hipGetLastError();
+        e = launch_delta<T, D>(a, g, delta, s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3((a.Lq + QT - 1) / QT, a.Hq, a.B), dim3(256), 0, s, a, g,
                            delta, static_cast<T*>(dq));
@@ -297,11 +323,7 @@ hipError_t launch_bwd_t(const FwdArgs& a, const void* dout, float* delta, void* 
 template <typename T>
 hipError_t launch_delta_t(const FwdArgs& a, const void* dout, float* delta, hipStream_t s) {
     const T* g = static_cast<const T*>(dout);
-    if (a.D == 64)
-        hipLaunchKernelGGL((bwd_delta_kernel<T, 64>), dim3((a.Lq + 3) / 4, a.Hq, a.B), dim3(256), 0, s, a, g, delta);
-    else
-        hipLaunchKernelGGL((bwd_delta_kernel<T, 128>), dim3((a.Lq + 3) / 4, a.Hq, a.B), dim3(256), 0, s, a, g, delta);
-    return hipGetLastError();
+    return a.D == 64 ? launch_delta<T, 64>(a, g, delta, s) : launch_delta<T, 128>(a, g, delta, s);
 }
 
 template <typename T>
