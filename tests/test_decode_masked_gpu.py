@@ -186,3 +186,25 @@ def test_decode_masked_long_cache_exact_counts(window):
     assert np.array_equal(got[~empty], np.broadcast_to(want[~empty, None], got[~empty].shape))
     assert torch.all(torch.isneginf(lse[torch.from_numpy(empty)].cpu()))
     assert torch.all(out[torch.from_numpy(empty)].cpu() == 0)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_masked_sparse_keys_far_apart(splits):
+    """Valid keys thousands of positions apart (runs of empty tiles longer
+    than the kernel keeps mask words of at a time), a lone key in a window's
+    last tile, and valid keys only past the first 4096: every batch against
+    the oracle, with and without a window."""
+    w = wl.Workload("decmask_sparse_bf16_D128_cap20000", "bf16", 6, 1, 20000, 8, 2, 128, True)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    mask = torch.zeros((w.B, w.Lk), dtype=torch.float32)
+    mask[0, [0, 4100, 12345, 19999]] = 1.0
+    mask[1, [8191, 8192]] = 1.0
+    mask[2, 4096:4160] = 1.0
+    mask[3, [5, 17000]] = 1.0
+    mask[4, ::4097] = 1.0
+    mask[5, 19000:] = 1.0
+    for window in (0, 3000):
+        say(f"{w.name} splits={splits} window={window}")
+        out, lse = mfa.decode_masked(q, k, v, mask.to(DEV), window=window, splits=splits)
+        torch.cuda.synchronize()
+        check(w, mask, out, lse, q, k, v, window, what=f"{w.name}/s{splits}/w{window}")
