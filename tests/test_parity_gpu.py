@@ -441,6 +441,37 @@ def test_bf16_large_v_runs_on_bf16_operands(D, where):
     assert np.max(np.abs(lse.double().cpu().numpy() - L)) <= pu.TOL_LSE
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("spans", [[(16200, 16203)], [(16500, 16504)], [(40, 41), (16900, 16901)]],
+                         ids=["in_first_16k", "past_16k", "both"])
+def test_bf16_large_v_long_cache(D, spans):
+    """The same with more than 16384 keys per (batch, kv head), where the
+    conversion flags of the keys past the first 16384 are looked at only
+    after the loop: a block seeing such a tile is computed again on bf16
+    operands wherever the tile lies.  Only kv head 0 holds the large values;
+    the other head is checked against the usual bound."""
+    w = wl.Workload(f"bigv_long_D{D}", "bf16", 1, 100, 17000, 4, 2, D, False)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    v = v.clone()
+    for s0, s1 in spans:
+        v[:, s0:s1, 0, :] = (v[:, s0:s1, 0, :].float() * 1e6).to(v.dtype)
+    say(f"{w.name} {spans}")
+    out, lse = mfa.fwd(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    O, L, _ = default_oracle().full(q, k, v, scale=w.scale, causal=False, q_offset=w.q_offset,
+                                    nthreads=pu.ORACLE_THREADS)
+    og = out.double().cpu().numpy()                               # [B, Lq, Hq, D]
+    assert np.all(np.isfinite(og))
+    vmax = v.double().abs().amax(dim=(1, 3)).cpu().numpy()        # [B, Hkv]: every row sees every key
+    g = w.Hq // w.Hkv
+    scale = np.maximum(1.0, vmax[:, np.arange(w.Hq) // g])[:, None, :]   # [B, 1, Hq]
+    bound = pu.TOL_O["bf16"] * scale[..., None] + pu.half_ulp(O, "bf16")
+    err = np.abs(og - O)
+    worst = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+    assert np.all(err <= bound), (worst, err[worst], bound[worst])
+    assert np.max(np.abs(lse.double().cpu().numpy() - L)) <= pu.TOL_LSE
+
+
 def test_bf16_prefill_caller_workspace_matches_pool():
     """A bf16 prefill converts V to fp16 in its workspace: the caller-owned
     form (mfa_fwd_ws, sized by mfa_fwd_workspace_size) gives the pool form's

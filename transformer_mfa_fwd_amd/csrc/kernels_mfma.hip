@@ -223,15 +223,24 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
     // CV: V from the fp16 copy (same element offsets as V)
     const PT* __restrict__ vbase = static_cast<const PT*>(CV ? a.v16 : a.v) + (int64_t)b * a.Lk * kv_stride +
                                    (int64_t)kvh * D;
+    // CV: a (batch, kv head) whose V could not all be converted runs on bf16
+    // operands, and so does a call without the copy.  The first 64 flag
+    // words (16384 keys) are loaded here and arrive under the prologue's
+    // first barrier; any further ones are read after the loop, where all are
+    // tested: a flagged block drops what it computed and is redone (rare: a
+    // magnitude of 65504 or more in V).  No loop or branch on the flags comes
+    // before the first copies, so their latency overlaps the copies'.
+    const uint32_t* v16_fl = nullptr;
+    uint32_t v16_any = 0u;
+    bool v16_flagged = false;
     if constexpr (CV) {
-        // a (batch, kv head) whose V could not all be converted runs on bf16
-        // operands, and so does a call without the copy
         if (!a.v16) return false;
-        const uint32_t* fl = reinterpret_cast<const uint32_t*>(a.v16_flags + (int64_t)bk * a.v16_fwords * 4);
-        uint32_t any = 0u;
-        for (int w = lane; w < a.v16_fwords; w += 64) any |= fl[w];
-        if (__any(any != 0u)) return false;
+        v16_fl = reinterpret_cast<const uint32_t*>(a.v16_flags + (int64_t)bk * a.v16_fwords * 4);
+        // unconditional (index clamped, value masked): a branch here would
+        // pull the test, and its wait, ahead of the copies
+        v16_any = v16_fl[lane < a.v16_fwords ? lane : a.v16_fwords - 1] & (lane < a.v16_fwords ? ~0u : 0u);
     }
+    (void)v16_fl; (void)v16_any; (void)v16_flagged;
     // The mask words are read-only while the kernel runs (written by the
     // launch before it): reading them through the constant address space
     // lets the compiler use scalar loads, which the scalar cache serves,
@@ -597,6 +606,10 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
         if (tnxt <= kt_hi) MFA_DMA(tnxt, 1, true, false);
         MFA_BIAS_LOAD(tcur);
         __syncthreads();
+        if constexpr (CV) {
+            asm volatile("" : "+v"(v16_any));   // first use here, past the barrier
+            v16_flagged = __any(v16_any != 0u);
+        }
         f32x16_t sa[2], sb[2];
         {
             // scores of the first tile; no softmax and no V reads (names unused)
@@ -647,6 +660,12 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
 #undef MFA_PV_STEP
 #undef MFA_PART1
 #undef MFA_ITER
+
+    if constexpr (CV) {
+        uint32_t more = 0u;
+        for (int w = lane + 64; w < a.v16_fwords; w += 64) more |= v16_fl[w];
+        if (v16_flagged || __any(more != 0u)) return false;
+    }
 
     // ---- epilogue: normalise, round, store; LSE in natural log.  O is staged
     // through LDS (this wave's 32 rows, chunk-swizzled; every stage is free
@@ -709,7 +728,8 @@ void prefill_kernel(FwdArgs a, int nqt) {
     constexpr bool CVT = std::is_same<T, __bf16>::value;
     __shared__ __attribute__((aligned(1024))) char smem[PfLds<D>::BYTES];
     if constexpr (CVT) {
-        // every wave sees the same flags and leaves before any copy
+        // every wave sees the same flags, so a flagged block leaves with all
+        // its waves past the loop's last barrier (no copy or LDS read left)
         if (!prefill_block<T, D, CAP, MASK, SEQ, BIAS, DROP, true>(a, nqt, smem))
             prefill_block_bf16_operands<T, D, CAP, MASK, SEQ, BIAS, DROP>(
                 (const void*)__builtin_amdgcn_kernarg_segment_ptr(), nqt, smem);
