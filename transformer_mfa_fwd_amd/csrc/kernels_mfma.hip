@@ -147,10 +147,10 @@ __device__ inline uint32_t cvt_bf16x2_f16x2(uint32_t x, float& mx) {
 
 // The work of one workgroup: its 128 query rows of one query head, from
 // the first copies to the stores.  With CV (bf16 inputs, a.v16 holding V
-// converted to fp16) P.V runs on fp16 operands; it returns false at once,
-// having done nothing, when the block's (batch, kv head) is flagged, and the
-// caller then runs it with CV off.  smem: the kernel's LDS (L::BYTES bytes,
-// 1024-byte aligned).
+// converted to fp16) P.V runs on fp16 operands; it returns false, having
+// written nothing to global memory, when the block's (batch, kv head) is
+// flagged, and the caller then runs it with CV off.  smem: the kernel's LDS
+// (L::BYTES bytes, 1024-byte aligned).
 template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP, bool CV>
 __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArgs& a, int nqt, char* smem) {
     typedef PfLds<D> L;
@@ -601,11 +601,16 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
     if (tcur <= kt_hi) {
         int tnxt = MFA_NEXT_TILE(tcur + 1), tnx2;
         bool has_nxt;
-        // prologue: K,V of the first tile into stage 0, K of the second into stage 1
+        // prologue: K,V of the first tile into stage 0, K of the second into
+        // stage 1 (K of the first again when there is no second: never read).
+        // The same copies in every case, so that the first scores wait only
+        // for K of the first tile (copies complete in order; the additive
+        // mask's loads come later still, and with them this waits for more);
+        // the other two land while the scores run.
         MFA_DMA(tcur, 0, true, true);
-        if (tnxt <= kt_hi) MFA_DMA(tnxt, 1, true, false);
+        MFA_DMA(tnxt <= kt_hi ? tnxt : tcur, 1, true, false);
         MFA_BIAS_LOAD(tcur);
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(2 * IPW));
         if constexpr (CV) {
             asm volatile("" : "+v"(v16_any));   // first use here, past the barrier
             v16_flagged = __any(v16_any != 0u);
@@ -630,7 +635,8 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
             MFA_PART1(sa, sa, 0, false);
         }
         // The first iteration copies K of the tile after next into stage 0,
-        // which the scores above just read: every wave must be past them.
+        // which the scores above just read: every wave must be past them; it
+        // also reads V(tcur) and K(tnxt), which must have landed.
         __syncthreads();
         while (true) {
             MFA_ITER(sa, sb, 0);
