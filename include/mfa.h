@@ -37,6 +37,14 @@
  *
  * A row with no visible key gets O = 0 and LSE = -inf.
  *
+ * Unused K/V rows (masked keys, keys outside every query's window, cache rows
+ * past a decode length): the split decode kernels (mfa_fwd at Lq = 1 on that
+ * path, mfa_decode_len, mfa_decode_masked) never read them, so they may hold
+ * anything (NaN in unwritten cache slots, say).  The other forward kernels
+ * read every row of each 64-key tile they visit and give the unused ones zero
+ * weight, so there those rows must hold finite values; rows at or past Lk
+ * are never read.
+ *
  * Ownership: every pointer is caller-owned device memory.  The library keeps
  * no reference after a call returns and writes only out, lse and (for the
  * _ws / _ex forms) the workspace.  In every entry point, a pointer to a tensor

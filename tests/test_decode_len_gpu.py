@@ -59,6 +59,28 @@ def test_decode_len_small_all_rows(w, splits):
     check(w, lens, out, lse, q, k, v, what=f"{w.name}/s{splits}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_len_never_reads_past_the_length(dtype, D):
+    """Cache rows at and past each batch's length hold NaN (an unwritten
+    cache, say): they are never read, so the results are finite and match the
+    oracle on the valid prefix, also where the length ends inside a key tile
+    and with several splits."""
+    w = wl.Workload(f"declen_nan_tail_{dtype}_D{D}", dtype, 6, 4, 300, 8, 2, D, True)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    lens = torch.tensor([0, 3, 33, 64, 161, 300], dtype=torch.int32)
+    k, v = k.clone(), v.clone()
+    for b in range(w.B):
+        k[b, int(lens[b]):] = float("nan")
+        v[b, int(lens[b]):] = float("nan")
+    for splits in (1, 3):
+        say(f"{w.name} splits={splits} lens={lens.tolist()}")
+        out, lse = mfa.decode_len(q, k, v, lens.to(DEV), splits=splits)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        check(w, lens, out, lse, q, k, v, what=f"{w.name}/s{splits}")
+
+
 def test_decode_len_matches_forward_on_valid_prefix():
     """Where every row sees a key, decode_len equals mfa_fwd over the first
     len keys with the rows at positions len - R .. len - 1 (other kernels,

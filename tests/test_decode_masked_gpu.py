@@ -59,6 +59,30 @@ def test_decode_masked_small_every_batch(w, window, splits):
     check(w, mask, out, lse, q, k, v, window, what=f"{w.name}/w{window}/s{splits}")
 
 
+@pytest.mark.parametrize("window", [0, 37])
+@pytest.mark.parametrize("w", SMALL[:4], ids=lambda w: w.name)
+def test_decode_masked_never_reads_unused_rows(w, window):
+    """Masked cache rows, and with a window the valid rows before it, hold
+    NaN: they are never read, so the results are finite and match the
+    oracle (which never touches them), with one and several splits."""
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    mask = wl.make_cache_masks(w.B, w.Lk, seed=11 + window)
+    k, v = k.clone(), v.clone()
+    for b in range(w.B):
+        valid = torch.nonzero(mask[b] > 0.5).flatten()
+        unused = mask[b] <= 0.5
+        if window > 0 and valid.numel() > 0:
+            unused[:max(0, int(valid[-1]) - window + 1)] = True
+        k[b, unused.to(DEV)] = float("nan")
+        v[b, unused.to(DEV)] = float("nan")
+    for splits in (1, 4):
+        say(f"{w.name} window={window} splits={splits} (NaN in unused rows)")
+        out, lse = mfa.decode_masked(q, k, v, mask.to(DEV), window=window, softcap=w.softcap, splits=splits)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        check(w, mask, out, lse, q, k, v, window, what=f"{w.name}/w{window}/s{splits}/nan")
+
+
 @pytest.mark.parametrize("splits", [0, 5])
 def test_decode_masked_prefix_bit_identical_to_decode_len(splits):
     """mask = [1] * n + [0] * (Lmax - n) runs the same tiles and arithmetic as

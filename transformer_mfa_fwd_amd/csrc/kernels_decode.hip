@@ -175,16 +175,30 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
     int t = t_begin;
     uint32_t bits_t = 0xffffffffu;
     if (MASK) while (t < t_end && (bits_t = bits_of(t)) == 0u) ++t;
-    if (t < t_end) {
+    // Rows of tile tt into registers.  A row no query row can use (outside
+    // [lo, hi], or masked) is not read: it becomes zeros, so whatever the
+    // cache holds there (unwritten slots past the length, say) never meets a
+    // zero weight in the products, and the skipped rows cost no bandwidth.
+    auto load_tile = [&](int tt, uint32_t tbits) {
+        // bit r: row r of the tile is used (wave-uniform, built on the scalar unit)
+        const int l0 = lo - tt * DT, h0 = hi - tt * DT;
+        uint32_t use = MASK ? tbits : 0xffffffffu;
+        if (h0 < DT - 1) use &= h0 < 0 ? 0u : (0xffffffffu >> (DT - 1 - h0));
+        if (l0 > 0) use &= l0 >= DT ? 0u : (0xffffffffu << l0);
+        const uint32_t mine = use >> ld_row;   // bit i * RPL: this lane's row of load i
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            int key = t * DT + i * RPL + ld_row;
-            key = key < a.Lk ? key : a.Lk - 1;  // rows past the end are masked below
-            const int64_t off = (int64_t)key * row_stride + ld_chunk * 8;
-            kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-            vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+            u32x4_t kx = u32x4_t{0u, 0u, 0u, 0u}, vx = u32x4_t{0u, 0u, 0u, 0u};
+            if ((mine >> (i * RPL)) & 1u) {
+                const int64_t off = (int64_t)(tt * DT + i * RPL + ld_row) * row_stride + ld_chunk * 8;
+                kx = *reinterpret_cast<const u32x4_t*>(kbase + off);
+                vx = *reinterpret_cast<const u32x4_t*>(vbase + off);
+            }
+            kreg[i] = kx;
+            vreg[i] = vx;
         }
-    }
+    };
+    if (t < t_end) load_tile(t, bits_t);
     while (t < t_end) {
         // next tile with a visible key
         int tn = t + 1;
@@ -197,16 +211,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs da) {
             sK[r * CPR + swz_k<D>(r, ld_chunk)] = kreg[i];
             sV[r * CPR + swz_v<D>(r, ld_chunk)] = vreg[i];
         }
-        if (tn < t_end) {
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                int key = tn * DT + i * RPL + ld_row;
-                key = key < a.Lk ? key : a.Lk - 1;
-                const int64_t off = (int64_t)key * row_stride + ld_chunk * 8;
-                kreg[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-                vreg[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
-            }
-        }
+        if (tn < t_end) load_tile(tn, bits_n);
         __syncthreads();
 
         // scores: two 16-key blocks
