@@ -236,8 +236,9 @@ def time_decode_len(w, lens_cpu, steps: int, warmup: int, warmup_ms: float = 0.0
 def time_decode_masked(w, mask_cpu, window: int, steps: int, warmup: int, warmup_ms: float = 0.0, seed: int = 0):
     """mfa_decode_masked on workload w (one query row per batch, Lk = capacity)
     with the given [B, Lk] validity mask.  Algorithmic bytes: Q, O, the LSE,
-    the mask and the K and V rows of the 32-key tiles that hold a used key
-    (the tiles the kernel must read)."""
+    the mask and the K and V rows of the used keys (valid, and inside the
+    window when there is one): the rows the kernel must read, and the only
+    ones it reads."""
     import torch
     import transformer_mfa_fwd_amd as mfa
     from transformer_mfa_fwd_amd import workloads as wl
@@ -251,14 +252,14 @@ def time_decode_masked(w, mask_cpu, window: int, steps: int, warmup: int, warmup
     r = timed(lambda: mfa.decode_masked(q, k, v, d_mask, window=window, out=out, lse=lse, workspace=ws),
               steps, warmup, warmup_ms)
     el = q.element_size()
-    tiles = 0
+    used_keys = 0
     for b in range(w.B):
         valid = np.nonzero(mask_cpu[b].numpy() > 0.5)[0]
         if valid.size == 0:
             continue
         used = valid[valid > valid[-1] - window] if window > 0 else valid
-        tiles += np.unique(used // 32).size
-    r["bytes"] = 2 * q.numel() * el + lse.numel() * 4 + mask_cpu.numel() * 4 + 2 * tiles * 32 * w.Hkv * w.D * el
+        used_keys += used.size
+    r["bytes"] = 2 * q.numel() * el + lse.numel() * 4 + mask_cpu.numel() * 4 + 2 * used_keys * w.Hkv * w.D * el
     del q, k, v, out, lse, ws, d_mask
     torch.cuda.empty_cache()
     return r
@@ -609,7 +610,7 @@ def main():
         wm = wl.LONG_CACHE_DECODE_BF16
         dm = {"workload": wm.name, "api": "mfa_decode_masked", "unit": "GB/s", "capacity": wm.Lk,
               "peak": PEAK_HBM_GBS,
-              "bytes_note": "Q, O, LSE, the mask and the K/V rows of every 32-key tile holding a used key"}
+              "bytes_note": "Q, O, LSE, the mask and the K/V rows of the used keys"}
         full = torch.ones((wm.B, wm.Lk))
         holes = wl.make_cache_masks(wm.B, wm.Lk, seed=3, edges=False)
         for tag, mask, window in (("full", full, 0), ("holes", holes, 0), ("window4096", full, 4096)):
