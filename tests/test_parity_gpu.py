@@ -99,6 +99,55 @@ def test_small_all_rows(w, path):
     check_all_rows(w, path)
 
 
+MASKED = [w for w in SMALL if w.mask is not None]
+
+
+@pytest.mark.parametrize("path", ["generic", "mfma", "split_decode", "auto"])
+@pytest.mark.parametrize("w", MASKED, ids=lambda w: w.name)
+def test_masked_rows_may_hold_nan(w, path):
+    """K and V rows of masked keys hold NaN (never-written memory, say): every
+    path keeps them out of the products, so the output is finite and matches
+    the oracle, which never touches them."""
+    if path != "auto" and not path_available(path, w):
+        pytest.skip(f"path {path} does not serve {w.name}")
+    if path == "mfma" and w.dtype == "f32":
+        pytest.skip("MFMA path is fp16/bf16 only")
+    q, k, v, m = wl.make_inputs(w, DEV, 0)
+    k, v = k.clone(), v.clone()
+    dropped = m <= 0.5
+    k[dropped] = float("nan")
+    v[dropped] = float("nan")
+    say(f"{w.name} path={path} (NaN in {int(dropped.sum())} masked rows)")
+    out, lse = mfa.fwd(q, k, v, causal=w.causal, window=w.window, q_offset=w.q_offset, softcap=w.softcap,
+                       key_mask=m, scale=w.scale, path=PATHS.get(path, mfa.PATH_AUTO))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    O, L, _ = default_oracle().full(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
+                                    q_offset=w.q_offset, softcap=w.softcap, key_mask=m,
+                                    nthreads=pu.ORACLE_THREADS)
+    pu.compare(w.dtype, out.double().cpu().numpy().transpose(0, 2, 1, 3), lse.double().cpu().numpy(),
+               O.transpose(0, 2, 1, 3), L, f"{w.name}/{path}/nan")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_masked_rows_may_hold_nan_with_additive_mask(dtype):
+    """The same through the additive-mask kernels."""
+    w = wl.Workload(f"nan_rows_bias_{dtype}", dtype, 2, 190, 190, 4, 2, 128, True, window=37,
+                    mask="random_frac", mask_frac=0.3)
+    q, k, v, m = wl.make_inputs(w, DEV, 1)
+    k, v = k.clone(), v.clone()
+    k[m <= 0.5] = float("nan")
+    v[m <= 0.5] = float("nan")
+    bias = torch.randn((1, 1, w.Lq, w.Lk), generator=torch.Generator().manual_seed(5))
+    out, lse = mfa.fwd(q, k, v, causal=True, window=w.window, key_mask=m, scale=w.scale, bias=bias.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    O, L, _ = default_oracle().full(q, k, v, scale=w.scale, causal=True, window=w.window, q_offset=0,
+                                    key_mask=m, bias=bias, nthreads=pu.ORACLE_THREADS)
+    pu.compare(dtype, out.double().cpu().numpy().transpose(0, 2, 1, 3), lse.double().cpu().numpy(),
+               O.transpose(0, 2, 1, 3), L, f"{w.name}/nan")
+
+
 # --- edge cases ---------------------------------------------------------------
 
 EDGE = [

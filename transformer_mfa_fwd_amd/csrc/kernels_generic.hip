@@ -82,8 +82,10 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
             for (int x = tid; x < GBN * D; x += 256) {
                 const int j = x / D, d = x % D;
                 const int key = kt * GBN + j;
+                // a masked key's row stays zero: whatever it holds (NaN in
+                // never-written memory) cannot reach O through its zero weight
                 float kv = 0.0f, vv = 0.0f;
-                if (key < a.Lk) {
+                if (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) {
                     const int64_t off = ((int64_t)b * a.Lk + key) * kv_row_stride + (int64_t)kvh * D + d;
                     kv = to_f32(k[off]);
                     vv = to_f32(v[off]);

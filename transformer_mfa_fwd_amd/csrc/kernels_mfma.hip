@@ -349,6 +349,16 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
 // LDS tile at byte offset DST
 #define MFA_DMA1(RS, OFF, I, DST)                                                            \
     buffer_copy16_to_lds((RS).p, (RS).n, smem + (wave * IPW + (I)) * 1024 + (DST), OFF[I])
+// copy I of a V tile; M = MFA_VMASKED(key-mask word of the tile).  With a key
+// mask the row of a masked key is read out of range (bit 31 set in its
+// offset), so the copy writes zeros there and fetches nothing: its weight is
+// zero, and whatever the row holds (never-written memory, NaN) cannot reach O
+// through a product with it.  Bit RPI * I of M: this lane's row of copy I is
+// masked.  (CV: the fp16 copy of V already holds zeros in those rows.)
+#define MFA_VMASKED(W) ((MASK && !CV) ? ~(uint32_t)((W) >> dma_r0) : 0u)
+#define MFA_DMAV(RS, I, DST, M)                                                              \
+    buffer_copy16_to_lds((RS).p, (RS).n, smem + (wave * IPW + (I)) * 1024 + (DST),           \
+                         dma_voff[I] | (((M) >> (RPI * (I))) << 31))
 // copy K (and/or V) of tile TT into stage STG
 #define MFA_DMA(TT, STG, DO_K, DO_V)                                                         \
     do {                                                                                     \
@@ -359,8 +369,9 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
         }                                                                                    \
         if (DO_V) {                                                                          \
             const auto _r = MFA_RSRC(vbase, TT);                                             \
+            const uint32_t _m = MFA_VMASKED(MASK ? words[TT] : ~0ull);                       \
             _Pragma("unroll") for (int i = 0; i < IPW; ++i)                                  \
-                MFA_DMA1(_r, dma_voff, i, L::VST + (STG) * L::TILE);                         \
+                MFA_DMAV(_r, i, L::VST + (STG) * L::TILE, _m);                               \
         }                                                                                    \
     } while (0)
 
@@ -500,7 +511,7 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
 // copy J of the iteration (V copies, then K copies) goes in slot J * NQK / (2 IPW)
 #define MFA_DMA_IF(F, J)                                                                     \
     if constexpr ((J) < 2 * IPW && (F) == (J) * NQK / (2 * IPW)) {                           \
-        if constexpr ((J) < IPW) MFA_DMA1(_rv, dma_voff, (J), _dv_dst);                      \
+        if constexpr ((J) < IPW) MFA_DMAV(_rv, (J), _dv_dst, _wv);                           \
         else MFA_DMA1(_rk, dma_koff, (J) - IPW, _dk_dst);                                    \
     }
 #define MFA_QK_SLOT(F, SC, SN, SM)                                                           \
@@ -574,6 +585,7 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
         /* instead (harmless: those stages are not read again)                        */    \
         const auto _rk = MFA_RSRC(kbase, tnx2 <= kt_hi ? tnx2 : tcur);                       \
         const auto _rv = MFA_RSRC(vbase, has_nxt ? tnxt : tcur);                             \
+        const uint32_t _wv = MFA_VMASKED(MASK ? words[has_nxt ? tnxt : tcur] : ~0ull);       \
         constexpr int _dk_dst = L::KST + (ST) * L::TILE;                                     \
         constexpr int _dv_dst = L::VST + ((ST) ^ 1) * L::TILE;                               \
         const int k0 = tcur * BN;                                                            \
@@ -629,6 +641,8 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
             constexpr int _vb = 0, _dk_dst = 0, _dv_dst = 0;
             const auto _rk = MFA_RSRC(kbase, tcur);
             const auto _rv = _rk;
+            const uint32_t _wv = 0u;
+            (void)_wv;
             (void)vlo; (void)vhi; (void)pm; (void)neg_m; (void)psum0; (void)psum1; (void)pop;
             (void)k0; (void)word; (void)interior; (void)_vb; (void)_dk_dst; (void)_dv_dst;
             (void)_rk; (void)_rv;
@@ -651,6 +665,8 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
 #undef MFA_BIAS_LOAD
 #undef MFA_DMA
 #undef MFA_DMA1
+#undef MFA_DMAV
+#undef MFA_VMASKED
 #undef MFA_DMA_IF
 #undef MFA_RSRC
 #undef MFA_TR_ISSUE
@@ -750,12 +766,16 @@ void prefill_kernel(FwdArgs a, int nqt) {
 // (or is infinite).  Rows past Lk are not touched.
 template <int D>
 __global__ __launch_bounds__(256) void v16_prepass_kernel(const __bf16* __restrict__ v, _Float16* __restrict__ v16,
-                                                         uint8_t* __restrict__ flags, int Lk, int Hkv,
-                                                         int64_t kv_stride, int ntiles, int fwords) {
+                                                         uint8_t* __restrict__ flags,
+                                                         const uint64_t* __restrict__ words, int words_per_batch,
+                                                         int Lk, int Hkv, int64_t kv_stride, int ntiles, int fwords) {
     constexpr int CPR = D / 8;                     // 16-byte chunks per row
     constexpr int NCH = 64 * CPR / 256;            // chunks per thread
     const int t = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int64_t base = ((int64_t)b * Lk) * kv_stride + (int64_t)kvh * D;
+    // key-mask bits of the tile's 64 keys: a masked key's row is not read
+    // and its copy holds zeros (so never-written memory cannot reach O)
+    const uint64_t keep = words ? words[(int64_t)b * words_per_batch + t] : ~0ull;
     float mx = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -763,9 +783,12 @@ __global__ __launch_bounds__(256) void v16_prepass_kernel(const __bf16* __restri
         const int row = t * 64 + chunk / CPR;
         if (row < Lk) {
             const int64_t off = base + (int64_t)row * kv_stride + (chunk % CPR) * 8;
-            u32x4_t x = *reinterpret_cast<const u32x4_t*>(v + off);
+            u32x4_t x = u32x4_t{0u, 0u, 0u, 0u};
+            if ((keep >> (chunk / CPR)) & 1ull) {
+                x = *reinterpret_cast<const u32x4_t*>(v + off);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = cvt_bf16x2_f16x2(x[e], mx);
+                for (int e = 0; e < 4; ++e) x[e] = cvt_bf16x2_f16x2(x[e], mx);
+            }
             *reinterpret_cast<u32x4_t*>(v16 + off) = x;
         }
     }
@@ -834,11 +857,13 @@ hipError_t launch_v16_prepass(FwdArgs& a, void* ws, hipStream_t s) {
     // so the start event goes here and the stop event on the prefill kernel
     if (a.D == 64)
         hipExtLaunchKernelGGL(v16_prepass_kernel<64>, grid, dim3(256), 0, s, instr_event_begin(), nullptr, 0,
-                              static_cast<const __bf16*>(a.v), static_cast<_Float16*>(ws), flags, a.Lk, a.Hkv,
+                              static_cast<const __bf16*>(a.v), static_cast<_Float16*>(ws), flags,
+                              a.key_mask ? a.mask_words : nullptr, a.words_per_batch, a.Lk, a.Hkv,
                               a.kv_stride, ntiles, fwords);
     else
         hipExtLaunchKernelGGL(v16_prepass_kernel<128>, grid, dim3(256), 0, s, instr_event_begin(), nullptr, 0,
-                              static_cast<const __bf16*>(a.v), static_cast<_Float16*>(ws), flags, a.Lk, a.Hkv,
+                              static_cast<const __bf16*>(a.v), static_cast<_Float16*>(ws), flags,
+                              a.key_mask ? a.mask_words : nullptr, a.words_per_batch, a.Lk, a.Hkv,
                               a.kv_stride, ntiles, fwords);
     return hipGetLastError();
 }
