@@ -37,16 +37,17 @@
  *
  * A row with no visible key gets O = 0 and LSE = -inf.
  *
- * Rows nobody uses, in the forward entry points: the K and V rows of masked
- * keys may hold anything (NaN in unwritten cache slots, say).  They never
- * reach O: their V rows are not fetched, and a score from their K rows is
- * replaced, never used in arithmetic.  The split decode kernels (mfa_fwd at
- * Lq = 1 on that path, mfa_decode_len, mfa_decode_masked) also never fetch
- * rows outside every query's window or past the length.  The prefill
- * kernels read every unmasked row of each key tile they visit, including
- * rows that the causal or window bounds hide from some queries, so unmasked
- * rows must hold finite values.  Rows at or past Lk are never read.  (The
- * backward, mfa_bwd, reads every row of the tiles it visits.)
+ * Rows nobody uses: the K and V rows of masked keys may hold anything (NaN
+ * in unwritten cache slots, say).  They never reach O: their V rows are not
+ * fetched, and a score from their K rows is replaced, never used in
+ * arithmetic.  The split decode kernels (mfa_fwd at Lq = 1 on that path,
+ * mfa_decode_len, mfa_decode_masked) also never fetch rows outside every
+ * query's window or past the length.  The prefill kernels read every
+ * unmasked row of each key tile they visit, including rows that the causal
+ * or window bounds hide from some queries, so unmasked rows must hold finite
+ * values.  Rows at or past Lk are never read.  The backward (mfa_bwd) treats
+ * masked rows the same way: they never reach a gradient, and the gradients
+ * of masked keys are zero.
  *
  * Ownership: every pointer is caller-owned device memory.  The library keeps
  * no reference after a call returns and writes only out, lse and (for the

@@ -22,8 +22,13 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_case(w, bias_shape=None, p=0.0, seed=0):
+def run_case(w, bias_shape=None, p=0.0, seed=0, nan_masked=False):
     q, k, v, m = wl.make_inputs(w, DEV)
+    if nan_masked:
+        # masked keys' rows hold NaN: no kernel may let them reach a gradient
+        k, v = k.clone(), v.clone()
+        k[m <= 0.5] = float("nan")
+        v[m <= 0.5] = float("nan")
     g = torch.Generator(device="cpu")
     g.manual_seed(5)
     dout = (torch.randn(q.shape, generator=g)).to(q.dtype).to(DEV)
@@ -40,6 +45,8 @@ def run_case(w, bias_shape=None, p=0.0, seed=0):
     torch.cuda.synchronize()
     rq, rk, rv = default_oracle().bwd(q, k, v, dout, bias=bias, dropout_p=p, seed=seed,
                                       nthreads=pu.ORACLE_THREADS, **kw)
+    if nan_masked:
+        assert torch.isfinite(out).all() and all(torch.isfinite(t).all() for t in (dq, dk, dv))
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         pu.compare_grad(name, got, ref, w.dtype, f"{w.name} bias={bias_shape} p={p}", dropout_p=p)
 
@@ -74,6 +81,23 @@ def test_backward_with_bias_and_dropout(dtype, D):
                          softcap=6.0, mask="random_frac", mask_frac=0.2)
         run_case(wc, bias_shape=(1, 1, 1, 1), p=0.1, seed=77)
         run_case(wc, bias_shape=(1, 0, 0, 1), p=0.9, seed=5)
+
+
+MASKED = [w for w in CASES if w.mask is not None]
+
+
+@pytest.mark.parametrize("w", MASKED, ids=lambda w: w.name)
+def test_backward_masked_rows_may_hold_nan(w):
+    """NaN in the K and V rows of masked keys: finite gradients equal to the
+    oracle's (which never reads those rows), on every path."""
+    run_case(w, nan_masked=True)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_masked_rows_may_hold_nan_with_bias_and_dropout(dtype):
+    wc = wl.Workload(f"bwd_nan_rows_extra_{dtype}", dtype, 2, 100, 130, 4, 1, 128, False, window=70,
+                     softcap=6.0, mask="random_frac", mask_frac=0.2)
+    run_case(wc, bias_shape=(1, 1, 1, 1), p=0.1, seed=77, nan_masked=True)
 
 
 def test_backward_deterministic_and_zero_for_unseen_keys():

@@ -137,8 +137,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(FwdArgs a, const T* __restr
             for (int x = tid; x < KT * D; x += 256) {
                 const int j = x / D, d = x % D, key = kt * KT + j;
                 const int64_t off = ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D + d;
-                sK[j][d] = key < a.Lk ? f32(k[off]) : 0.0f;
-                sV[j][d] = key < a.Lk ? f32(v[off]) : 0.0f;
+                // a masked key's rows stay zero (whatever they hold cannot reach a gradient)
+                const bool use = key_kept(a, b, key);
+                sK[j][d] = use ? f32(k[off]) : 0.0f;
+                sV[j][d] = use ? f32(v[off]) : 0.0f;
             }
             __syncthreads();
             const int key = kt * KT + lane;
@@ -211,8 +213,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(FwdArgs a, const T* __res
     for (int x = tid; x < DK_KEYS * D; x += 256) {
         const int j = x / D, d = x % D, key = j0 + j;
         const int64_t off = ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D + d;
-        sK[j][d] = key < a.Lk ? f32(k[off]) : 0.0f;
-        sV[j][d] = key < a.Lk ? f32(v[off]) : 0.0f;
+        const bool use = key_kept(a, b, key);   // a masked key's rows stay zero
+        sK[j][d] = use ? f32(k[off]) : 0.0f;
+        sV[j][d] = use ? f32(v[off]) : 0.0f;
     }
     float dka[8][D / 64], dva[8][D / 64];
 #pragma unroll

@@ -87,16 +87,18 @@ struct TileRegs {
     u32x4_t v[N];
 };
 template <typename T, int D>
-__device__ inline void fetch_tile(TileRegs<D>& t, const T* src, int64_t stride, int rows_valid, int tid) {
+__device__ inline void fetch_tile(TileRegs<D>& t, const T* src, int64_t stride, int rows_valid, int tid,
+                                  const float* keep = nullptr) {
     constexpr int CPR = D / 8;
 #pragma unroll
     for (int n = 0; n < TileRegs<D>::N; ++n) {
         // rows past the end read the last valid row (rows_valid >= 1) and are
-        // then zeroed: a select, not a branch
+        // then zeroed: a select, not a branch; so are the rows of keys whose
+        // mask value (keep[r], when given) drops them
         const int c = tid + 256 * n, r = c / CPR, k = c % CPR;
         const int rc = r < rows_valid ? r : rows_valid - 1;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + (int64_t)rc * stride + k * 8);
-        const bool ok = r < rows_valid;
+        const bool ok = r < rows_valid && (!keep || keep[rc] > 0.5f);
         t.v[n] = u32x4_t{ok ? v[0] : 0u, ok ? v[1] : 0u, ok ? v[2] : 0u, ok ? v[3] : 0u};
     }
 }
@@ -187,8 +189,10 @@ __global__ __launch_bounds__(256, (CAP && D == 128) ? 1 : 2) void bwd_dq_mfma_ke
         // tile t's K, V and key-kept flags into registers
         auto fetch = [&](int t) {
             const int k0 = 32 * t;
-            fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
-            fetch_tile<T, D>(rv, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            // a masked key's K and V rows stay zero (whatever they hold cannot reach dQ)
+            const float* keep = a.key_mask ? a.key_mask + (int64_t)b * a.Lk + k0 : nullptr;
+            fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid, keep);
+            fetch_tile<T, D>(rv, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid, keep);
             if (tid < 32) {
                 const int key = k0 + tid;
                 rm = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
@@ -310,8 +314,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
         // tile t_first + u's K, V and key-kept flags into registers
         auto fetch = [&](int u) {
             const int k0 = 32 * (t_first + u);
-            fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
-            fetch_tile<T, D>(rv, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid);
+            // a masked key's K and V rows stay zero (whatever they hold cannot reach dQ)
+            const float* keep = a.key_mask ? a.key_mask + (int64_t)b * a.Lk + k0 : nullptr;
+            fetch_tile<T, D>(rk, kb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid, keep);
+            fetch_tile<T, D>(rv, vb + (int64_t)k0 * a.kv_stride, a.kv_stride, a.Lk - k0, tid, keep);
             if (tid < 32) {
                 const int key = k0 + tid;
                 rm = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
@@ -468,13 +474,18 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
     const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
     const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
 
+    // a masked key's K and V rows stay zero (whatever they hold cannot reach a gradient)
+    const bool mask_ok = !a.key_mask || a.key_mask[(int64_t)b * a.Lk + keyc] > 0.5f;
+    const bool kept = key <= j_last && mask_ok;
     v8 kop[NKS], vop[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-        kop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(kb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h));
-        vop[ks] = bitcast<v8>(*reinterpret_cast<const u32x4_t*>(vb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h));
+        u32x4_t kx = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h);
+        u32x4_t vx = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h);
+        if (!mask_ok) kx = vx = u32x4_t{0u, 0u, 0u, 0u};
+        kop[ks] = bitcast<v8>(kx);
+        vop[ks] = bitcast<v8>(vx);
     }
-    const bool kept = key <= j_last && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f);
 
     f32x16_t dka[NDB], dva[NDB];
 #pragma unroll
