@@ -87,23 +87,27 @@ void mfa_oracle_philox4x64(const uint64_t ctr_in[4], const uint64_t key_in[2], u
 
 /*
  * Dropout decision of score (b, hq, i, j).  The pages fix only that a seed
- * drives the pattern (ferrotensor attention.rs, AttentionOptions); the oracle
- * reads it as: one Philox4x64-10 block per four consecutive keys, counter
- * (floor(j / 4), i, hq, b) and key (seed, 0), its four output words serving
- * keys 4 floor(j / 4) .. +3 in order; the top 24 bits r of word j mod 4 keep
- * the weight iff r >= round(p * 2^24).
+ * drives the pattern, of which only the low 32 bits are used (ferrotensor
+ * attention.rs, AttentionOptions, `seed`); the oracle reads the rest as: one
+ * Philox4x64-10 block per sixteen consecutive keys, counter
+ * (floor(j / 16), i, hq, b) and key (seed mod 2^32, 0); its four 64-bit
+ * output words hold sixteen 16-bit fields, field f being bits 16 (f mod 4) ..
+ * 16 (f mod 4) + 15 of word floor(f / 4), and key j reads field j mod 16; the
+ * weight is kept iff that field is >= round(p * 2^16).
  */
 int mfa_oracle_dropout_keep(uint64_t seed, double p, int64_t b, int64_t hq, int64_t i, int64_t j)
 {
-    const uint64_t ctr[4] = {(uint64_t)(j / 4), (uint64_t)i, (uint64_t)hq, (uint64_t)b};
-    const uint64_t key[2] = {seed, 0};
+    const uint64_t ctr[4] = {(uint64_t)(j / 16), (uint64_t)i, (uint64_t)hq, (uint64_t)b};
+    const uint64_t key[2] = {seed & 0xffffffffull, 0};
     uint64_t out[4];
     mfa_oracle_philox4x64(ctr, key, out);
-    const uint64_t threshold = (uint64_t)llround(p * 16777216.0);
+    const uint64_t threshold = (uint64_t)llround(p * 65536.0);
+    const int64_t f = j % 16;
 #if ORACLE_MUTANT == 18
-    return (out[0] >> 40) >= threshold;      /* every key of the block reads word 0 */
+    (void)f;
+    return (out[0] & 0xffffu) >= threshold;  /* every key of the block reads field 0 */
 #else
-    return (out[j % 4] >> 40) >= threshold;
+    return ((out[f / 4] >> (16 * (f % 4))) & 0xffffu) >= threshold;
 #endif
 }
 

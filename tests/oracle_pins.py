@@ -843,8 +843,11 @@ def _numpy_philox_block(ctr, key):
 
 def _numpy_keep(seed, thr, b, h, i, j):
     """Dropout decision of weight (b, h, i, j) from NumPy's Philox: block
-    (j // 4, i, h, b) under key (seed, 0), word j % 4, top 24 bits >= thr."""
-    return (_numpy_philox_block([j // 4, i, h, b], [seed, 0])[j % 4] >> 40) >= thr
+    (j // 16, i, h, b) under key (seed mod 2^32, 0); 16-bit field j % 16 (bits
+    16 (f % 4) .. +15 of word f // 4) >= thr."""
+    f = j % 16
+    word = _numpy_philox_block([j // 16, i, h, b], [seed % 2 ** 32, 0])[f // 4]
+    return ((word >> (16 * (f % 4))) & 0xFFFF) >= thr
 
 
 def pin_philox_matches_numpy(orc):
@@ -861,13 +864,14 @@ def pin_philox_matches_numpy(orc):
 def dense_bias_dropout(q, k, v, *, scale, causal, window, q_offset, softcap=0.0, key_mask=None,
                        bias=None, dropout_p=0.0, seed=0):
     """Full score matrix, bias broadcast by NumPy, dropout pattern from NumPy's
-    Philox: block (j // 4, i, hq, b) under key (seed, 0), word j % 4."""
+    Philox: block (j // 16, i, hq, b) under key (seed mod 2^32, 0), 16-bit
+    field j % 16."""
     q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     g = Hq // Hkv
     bb = None if bias is None else np.broadcast_to(np.asarray(bias, np.float64), (B, Hq, Lq, Lk))
-    thr = int(round(dropout_p * 2 ** 24))
+    thr = int(round(dropout_p * 2 ** 16))
     O = np.zeros((B, Lq, Hq, D))
     L = np.zeros((B, Hq, Lq))
     for b in range(B):
@@ -931,11 +935,41 @@ def pin_bias_row_shift_and_neg_inf(orc):
     _close(L2, L3, 1e-12, "-inf bias vs key mask LSE")
 
 
+def pin_dropout_keep_matches_numpy(orc):
+    """Every dropout decision of a grid spanning several 16-key blocks, rows,
+    heads and batches against NumPy's Philox with the field layout written
+    out; the seed's bits above the low 32 change nothing (the pages: only the
+    low 32 bits of the seed are used), its low bits do; the kept fraction is
+    1 - p within five standard deviations."""
+    for seed, p in [(0, 0.5), (2**32 + 11, 0.1), (2**63 + 5, 0.9)]:
+        thr = int(round(p * 2 ** 16))
+        for b in range(2):
+            for h in (0, 3):
+                for i in (0, 1, 17):
+                    for j in range(0, 70, 3):
+                        assert orc.dropout_keep(seed, p, b, h, i, j) == _numpy_keep(seed, thr, b, h, i, j), \
+                            (seed, p, b, h, i, j)
+    pairs = [(b, h, i, j) for b in range(2) for h in range(2) for i in range(3) for j in range(64)]
+    for seed in (7, 2**40 + 7):
+        a = [orc.dropout_keep(seed, 0.5, *x) for x in pairs]
+        assert a == [orc.dropout_keep(seed + 2**32, 0.5, *x) for x in pairs]
+        assert a != [orc.dropout_keep(seed + 1, 0.5, *x) for x in pairs]
+    n = 0
+    kept = 0
+    for i in range(40):
+        for j in range(256):
+            kept += orc.dropout_keep(99, 0.3, 1, 2, i, j)
+            n += 1
+    sd = (0.3 * 0.7 / n) ** 0.5
+    assert abs(kept / n - 0.7) < 5 * sd, kept / n
+
+
 def pin_dropout_matches_dense(orc):
-    """Dropout against the dense form with NumPy's Philox drawing the pattern;
-    the LSE ignores dropout and p = 0 is no dropout."""
+    """Dropout against the dense form with NumPy's Philox drawing the pattern
+    over three 16-key blocks; the LSE ignores dropout and p = 0 is no
+    dropout."""
     rng = _rng(26)
-    B, Lq, Lk, Hq, Hkv, D = 2, 6, 8, 2, 1, 8
+    B, Lq, Lk, Hq, Hkv, D = 2, 6, 40, 2, 1, 8
     q, k, v = _rand(rng, (B, Lq, Hq, D), 2.0), _rand(rng, (B, Lk, Hkv, D), 2.0), _rand(rng, (B, Lk, Hkv, D))
     for p, seed, causal in [(0.1, 1234, True), (0.5, 2**40 + 7, False), (0.9, 3, True)]:
         kw = dict(scale=0.5, causal=causal, window=0, q_offset=Lk - Lq, dropout_p=p, seed=seed)
@@ -1022,7 +1056,7 @@ def pin_bwd_matches_torch_autograd(orc):
         S = S.masked_fill(~torch.tensor(vis)[:, None], -float("inf"))
         P = torch.softmax(S, dim=-1)
         if kw["dropout_p"] > 0:
-            thr = int(round(kw["dropout_p"] * 2 ** 24))
+            thr = int(round(kw["dropout_p"] * 2 ** 16))
             Z = np.zeros((B, Hq, Lq, Lk))
             for b_ in range(B):
                 for h_ in range(Hq):
@@ -1071,6 +1105,7 @@ ALL_PINS = [
     pin_philox_matches_numpy,
     pin_bias_matches_dense,
     pin_bias_row_shift_and_neg_inf,
+    pin_dropout_keep_matches_numpy,
     pin_dropout_matches_dense,
     pin_bwd_matches_finite_differences,
     pin_bwd_matches_torch_autograd,
