@@ -128,11 +128,6 @@ __device__ inline float logit2_minus(const FwdArgs& a, float dot, float lse2, fl
     }
 }
 
-// Dropout decisions of four keys 4 jb .. 4 jb + 3 for one row, bits 0..3 (the
-// forward's rule); all kept when dropout is off.
-__device__ inline uint32_t bwd_keep4(const FwdArgs& a, int b, int hq, int row, int jb) {
-    return a.drop_scale > 0.0f ? dropout_keep4(a, b, hq, row, jb) : 0xfu;
-}
 
 // dQ of calls without an additive mask or dropout (two workgroups per CU but
 // with a soft-cap at D = 128).
@@ -365,8 +360,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
             if (u + 2 < n_t) store(bn2);   // its buffer was last read by tile u - 1
             if (u + 3 < n_t) fetch(u + 3);
 
-            // mask values and dropout keep bits of this lane's 16 scores: scores
-            // 4 G .. 4 G + 3 are keys 4 jb .. 4 jb + 3, jb = k0 / 4 + 2 G + h
+            // mask values and dropout keep bits of this lane's 16 scores: score
+            // 4 G + e is key k0 + 8 G + 4 h + e
             float bv[EXTRA ? 16 : 1];
             uint32_t keepm = 0xffffu;
             if constexpr (EXTRA) {
@@ -376,9 +371,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
                     bv[r] = (brow && key < a.Lk) ? brow[(int64_t)key * a.bias_stride[3]] : 0.0f;
                 }
                 if (a.drop_scale > 0.0f) {
-                    keepm = 0u;
-#pragma unroll
-                    for (int G = 0; G < 4; ++G) keepm |= bwd_keep4(a, b, hq, row, (k0 >> 2) + 2 * G + h) << (4 * G);
+                    // the tile's 32 keys are two 16-key Philox blocks of this
+                    // row, which lanes l and l ^ 32 share: each evaluates one
+                    const uint32_t own = dropout_keep16(a, b, hq, row, (k0 >> 4) + h);
+                    const uint32_t oth = (uint32_t)__shfl_xor((int)own, 32);
+                    const uint32_t m32 = h ? (oth | (own << 16)) : (own | (oth << 16));   // keys 0 .. 31
+                    keepm = pack_even_nibbles(m32 >> (4 * h));
                 }
             }
             (void)bv;
@@ -619,22 +617,21 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
                     for (int r = 0; r < 16; ++r) bv[r] = 0.0f;
                 }
                 // keep bits of this lane's 16 scores (rows 8 (r / 4) + 4 h + r % 4
-                // of the step, all at this lane's key).  The four lanes of keys
-                // 4 jb .. 4 jb + 3 share each row's Philox block: lane e = key % 4
-                // evaluates the blocks of rows r % 4 = e (bit 4 q + w of m: word w
-                // of row 4 q + e), and lane e' takes word e' of every row from the
-                // lane that holds it.
+                // of the step, all at this lane's key).  The step's 32 rows and
+                // the wave's 32 keys make 64 16-key Philox blocks (row, key
+                // half): lane L evaluates the block of row L % 32 and key half
+                // L / 32, and each lane takes its bit of each of its rows' blocks
+                // from the lane that holds it.
                 if (a.drop_scale > 0.0f) {
-                    const int e = lane & 3;
-                    uint32_t m = 0u;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) m |= bwd_keep4(a, b, hq, r0 + 8 * q + 4 * h + e, keyc >> 2) << (4 * q);
+                    const int kb0 = (j0 + 32 * wave) >> 4;   // first key block of the wave
+                    const uint32_t m = dropout_keep16(a, b, hq, r0 + (lane & 31), kb0 + (lane >> 5));
+                    const int src_half = ((lane & 31) >> 4) * 32, bit = lane & 15;
                     keepm = 0u;
 #pragma unroll
-                    for (int src = 0; src < 4; ++src) {
-                        const uint32_t ms = (uint32_t)__shfl((int)m, (lane & ~3) | src);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) keepm |= ((ms >> (4 * q + e)) & 1u) << (4 * q + src);
+                    for (int r = 0; r < 16; ++r) {
+                        const int rho = 8 * (r >> 2) + 4 * h + (r & 3);
+                        const uint32_t ms = (uint32_t)__shfl((int)m, rho + src_half);
+                        keepm |= ((ms >> bit) & 1u) << r;
                     }
                 }
             }

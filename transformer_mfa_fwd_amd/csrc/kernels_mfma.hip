@@ -388,15 +388,19 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
 // Score i (0..31) of this lane: key k0 + 32 (i / 16) + 8 ((i % 16) / 4) + 4 h2 + i % 4.
 #define MFA_X(SC, I) SC[(I) >> 4][(I) & 15]
 
-// Keep bits of this lane's 32 weights of the tile at key k0 (bit i: score i).
-// Scores 4 G .. 4 G + 3 are keys 4 jb .. 4 jb + 3 of one Philox block, jb =
-// k0 / 4 + 8 (G / 4) + 2 (G % 4) + h2.
+// Keep bits of this lane's 32 weights of the tile at key K0 (bit i: score i,
+// key K0 + 32 (i / 16) + 8 ((i % 16) / 4) + 4 h2 + i % 4).  The tile's 64 keys
+// are four 16-key Philox blocks of this lane's row, which lanes l and l ^ 32
+// share: each evaluates two (blocks h2 and h2 + 2) and they swap them.
 #define MFA_KEEP(K0)                                                                         \
     ({                                                                                       \
-        uint32_t _kw = 0u;                                                                   \
-        _Pragma("unroll") for (int _g = 0; _g < 8; ++_g)                                     \
-            _kw |= dropout_keep4(a, b, hq, qrow, ((K0) >> 2) + 8 * (_g >> 2) + 2 * (_g & 3) + h2) << (4 * _g); \
-        _kw;                                                                                 \
+        const uint32_t _own = dropout_keep16(a, b, hq, qrow, ((K0) >> 4) + h2) |             \
+                              (dropout_keep16(a, b, hq, qrow, ((K0) >> 4) + 2 + h2) << 16);   \
+        const uint32_t _oth = (uint32_t)__shfl_xor((int)_own, 32);                           \
+        const uint32_t _b02 = h2 ? _oth : _own, _b13 = h2 ? _own : _oth;                     \
+        const uint32_t _lo = (_b02 & 0xffffu) | (_b13 << 16);          /* keys 0 .. 31 */    \
+        const uint32_t _hi = (_b02 >> 16) | (_b13 & 0xffff0000u);      /* keys 32 .. 63 */   \
+        pack_even_nibbles(_lo >> (4 * h2)) | (pack_even_nibbles(_hi >> (4 * h2)) << 16);     \
     })
 // zero the dropped weights among scores E0 .. E0 + 7 (after the row sum has them)
 #define MFA_DROP8(SC, E0)                                                                    \

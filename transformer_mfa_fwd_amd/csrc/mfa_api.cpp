@@ -193,9 +193,9 @@ mfa::FwdArgs make_args(const Call& c) {
         a.bias_stride[3] = c.bias_dims[3] > 1 ? 1 : 0;
     }
     if (c.dropout_p > 0.0f) {
-        a.drop_threshold = (uint32_t)std::llround((double)c.dropout_p * 16777216.0);
+        a.drop_threshold = (uint32_t)std::llround((double)c.dropout_p * 65536.0);
         a.drop_scale = 1.0f / (1.0f - c.dropout_p);
-        a.drop_seed = c.seed;
+        a.drop_seed = c.seed & 0xffffffffull;   // only the seed's low 32 bits drive the pattern
     }
     a.scale = c.scale;
     a.softcap = c.softcap > 0.0f ? c.softcap : 0.0f;

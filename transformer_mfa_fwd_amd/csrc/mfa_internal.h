@@ -35,10 +35,12 @@ struct FwdArgs {
     // (b, hq, i, j) with bias_stride (0 for a broadcast dimension), or null
     const float* bias;
     int64_t bias_stride[4];
-    // attention dropout: weight (b, hq, i, j) is kept iff the top 24 bits of
-    // word j % 4 of Philox4x64-10(counter (j / 4, i, hq, b), key
-    // (drop_seed, 0)) are at least drop_threshold, and a kept weight is
-    // multiplied by drop_scale (> 0 turns dropout on)
+    // attention dropout: weight (b, hq, i, j) is kept iff 16-bit field
+    // f = j % 16 (bits 16 (f % 4) .. +15 of word f / 4) of
+    // Philox4x64-10(counter (j / 16, i, hq, b), key (drop_seed, 0)) is at
+    // least drop_threshold (round(p * 2^16)); drop_seed holds the low 32 bits
+    // of the caller's seed; a kept weight is multiplied by drop_scale (> 0
+    // turns dropout on)
     uint32_t drop_threshold;
     float drop_scale;
     uint64_t drop_seed;
@@ -118,20 +120,33 @@ __device__ inline void philox4x64(uint64_t& c0, uint64_t& c1, uint64_t& c2, uint
     }
 }
 
-// Dropout decisions of weights (b, hq, i, 4 jb .. 4 jb + 3): bit e set iff
-// the top 24 bits of word e of Philox4x64-10 with counter (jb, i, hq, b) and
-// key (seed, 0) reach the threshold round(p * 2^24).
-__device__ inline uint32_t dropout_keep4(const FwdArgs& a, int b, int hq, int i, int jb) {
+// Dropout decisions of weights (b, hq, i, 16 jb .. 16 jb + 15): bit f set
+// iff 16-bit field f (bits 16 (f % 4) .. +15 of word f / 4) of
+// Philox4x64-10 with counter (jb, i, hq, b) and key (drop_seed, 0) reaches
+// the threshold round(p * 2^16).
+__device__ inline uint32_t dropout_keep16(const FwdArgs& a, int b, int hq, int i, int jb) {
     uint64_t c0 = (uint64_t)jb, c1 = (uint64_t)i, c2 = (uint64_t)hq, c3 = (uint64_t)b;
     philox4x64(c0, c1, c2, c3, a.drop_seed, 0);
     const uint32_t t = a.drop_threshold;
-    return ((uint32_t)(c0 >> 40) >= t ? 1u : 0u) | ((uint32_t)(c1 >> 40) >= t ? 2u : 0u) |
-           ((uint32_t)(c2 >> 40) >= t ? 4u : 0u) | ((uint32_t)(c3 >> 40) >= t ? 8u : 0u);
+    const uint32_t w[8] = {(uint32_t)c0, (uint32_t)(c0 >> 32), (uint32_t)c1, (uint32_t)(c1 >> 32),
+                           (uint32_t)c2, (uint32_t)(c2 >> 32), (uint32_t)c3, (uint32_t)(c3 >> 32)};
+    uint32_t m = 0u;
+#pragma unroll
+    for (int f = 0; f < 16; ++f) m |= ((((w[f >> 1] >> (16 * (f & 1))) & 0xffffu) >= t) ? 1u : 0u) << f;
+    return m;
 }
 
 // Dropout decision of weight (b, hq, i, j).
 __device__ inline bool dropout_keep(const FwdArgs& a, int b, int hq, int i, int j) {
-    return (dropout_keep4(a, b, hq, i, j >> 2) >> (j & 3)) & 1u;
+    return (dropout_keep16(a, b, hq, i, j >> 4) >> (j & 15)) & 1u;
+}
+
+// The nibbles at bits 0, 8, 16 and 24 of x (every other nibble) packed into
+// bits 0 .. 15.
+__device__ inline uint32_t pack_even_nibbles(uint32_t x) {
+    x &= 0x0f0f0f0fu;
+    x = (x | (x >> 4)) & 0x00ff00ffu;
+    return (x | (x >> 8)) & 0x0000ffffu;
 }
 
 // Instrumentation events of the calling host thread (mfa_set_kernel_events,
