@@ -130,11 +130,13 @@ int mfa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *               key masks; may be NULL; finite values or -inf
  *   dropout_p   in [0, 1): each normalised weight is dropped with this
  *               probability and a kept one divided by 1 - p; the saved LSE
- *               is the undropped one.  Weight (b, hq, i, j) is kept iff the
- *               top 24 bits of word j mod 4 of the Philox4x64-10 block with
- *               counter (floor(j / 4), i, hq, b) and key (seed, 0) are at
- *               least round(p * 2^24), so a pattern is reproducible from the
- *               seed alone.
+ *               is the undropped one.  Weight (b, hq, i, j) is kept iff
+ *               16-bit field f = j mod 16 (bits 16 (f mod 4) .. +15 of word
+ *               floor(f / 4)) of the Philox4x64-10 block with counter
+ *               (floor(j / 16), i, hq, b) and key (seed mod 2^32, 0) is at
+ *               least round(p * 2^16), so a pattern is reproducible from the
+ *               seed alone; only the seed's low 32 bits count
+ *               (ferrotensor attention.rs, AttentionOptions).
  *
  * A row whose every visible key has a bias of -inf gets O = 0, LSE = -inf.
  * An fp16/bf16 call with D 64 or 128 runs on the MFMA prefill kernel unless

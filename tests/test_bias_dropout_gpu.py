@@ -89,6 +89,23 @@ def test_all_neg_inf_row_is_empty_and_seeds_differ():
     assert torch.equal(o1, o2) and not torch.equal(o1, o3)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_dropout_seed_uses_its_low_32_bits(dtype):
+    """Only the seed's low 32 bits drive the pattern (the pages' rule for the
+    seed): seeds that differ above them give the same bits, on the MFMA and
+    the fp32 kernels and in the backward."""
+    w = wl.Workload(f"bd_seed32_{dtype}", dtype, 1, 70, 90, 2, 1, 64, True)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    outs = [mfa.fwd(q, k, v, causal=True, dropout_p=0.3, seed=s)[0] for s in (5, 5 + 2**32, 5 + 2**63, 6)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]) and not torch.equal(outs[0], outs[3])
+    g = torch.randn(q.shape, generator=torch.Generator().manual_seed(2)).to(q.dtype).to(DEV)
+    out, lse = mfa.fwd(q, k, v, causal=True, dropout_p=0.3, seed=5)
+    grads = [mfa.bwd(q, k, v, out, g, lse, causal=True, dropout_p=0.3, seed=s) for s in (5, 5 + 2**32)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(*grads))
+
+
 # Additive masks the MFMA prefill kernel reads itself (no dropout, fp16/bf16,
 # key dimension full, Lk a multiple of four): several tiles, ragged tails.
 MFMA_BIAS = []
