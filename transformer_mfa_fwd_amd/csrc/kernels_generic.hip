@@ -50,18 +50,43 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
     const int64_t q_row_stride = a.q_stride;
     const int64_t kv_row_stride = a.kv_stride;
 
+    // keys any row of this tile can see
+    int lo_first, hi_first, lo_last, hi_last;
+    row_key_range(a, i0, lo_first, hi_first);
+    row_key_range(a, i_end - 1, lo_last, hi_last);
+    const int klo = lo_first, khi = hi_last;
+
+    // K and V of key tile kt into registers (thread tid holds elements tid,
+    // tid + 256, ... of the tile): the next tile's loads are in flight while
+    // the current one is computed, and the first tile's beside Q's.  A masked
+    // key's row stays zero: whatever it holds (NaN in never-written memory)
+    // cannot reach O through its zero weight.
+    constexpr int NPF = GBN * D / 256;
+    float pk[NPF], pv[NPF];
+    auto prefetch = [&](int kt) {
+#pragma unroll
+        for (int n = 0; n < NPF; ++n) {
+            const int x = tid + 256 * n;
+            const int j = x / D, d = x % D;
+            const int key = kt * GBN + j;
+            float kv = 0.0f, vv = 0.0f;
+            if (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) {
+                const int64_t off = ((int64_t)b * a.Lk + key) * kv_row_stride + (int64_t)kvh * D + d;
+                kv = to_f32(k[off]);
+                vv = to_f32(v[off]);
+            }
+            pk[n] = kv;
+            pv[n] = vv;
+        }
+    };
+    if (klo <= khi) prefetch(klo / GBN);
+
     for (int x = tid; x < GBM * D; x += 256) {
         const int r = x / D, d = x % D;
         const int i = i0 + r;
         sQ[r][d] = i < a.Lq ? to_f32(q[((int64_t)b * a.Lq + i) * q_row_stride + (int64_t)hq * D + d])
                             : 0.0f;
     }
-
-    // keys any row of this tile can see
-    int lo_first, hi_first, lo_last, hi_last;
-    row_key_range(a, i0, lo_first, hi_first);
-    row_key_range(a, i_end - 1, lo_last, hi_last);
-    const int klo = lo_first, khi = hi_last;
 
     int rlo[ROWS_PER_WAVE], rhi[ROWS_PER_WAVE];
     float m[ROWS_PER_WAVE], l[ROWS_PER_WAVE], acc[ROWS_PER_WAVE][D / 64];
@@ -79,20 +104,13 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
     if (klo <= khi) {
         for (int kt = klo / GBN; kt <= khi / GBN; ++kt) {
             __syncthreads();  // previous tile fully consumed (and sQ written)
-            for (int x = tid; x < GBN * D; x += 256) {
-                const int j = x / D, d = x % D;
-                const int key = kt * GBN + j;
-                // a masked key's row stays zero: whatever it holds (NaN in
-                // never-written memory) cannot reach O through its zero weight
-                float kv = 0.0f, vv = 0.0f;
-                if (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) {
-                    const int64_t off = ((int64_t)b * a.Lk + key) * kv_row_stride + (int64_t)kvh * D + d;
-                    kv = to_f32(k[off]);
-                    vv = to_f32(v[off]);
-                }
-                sK[j][d] = kv;
-                sV[j][d] = vv;
+#pragma unroll
+            for (int n = 0; n < NPF; ++n) {
+                const int x = tid + 256 * n;
+                sK[x / D][x % D] = pk[n];
+                sV[x / D][x % D] = pv[n];
             }
+            if (kt < khi / GBN) prefetch(kt + 1);
             __syncthreads();
 
             const int key = kt * GBN + lane;
@@ -102,6 +120,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
             float s[ROWS_PER_WAVE];
 #pragma unroll
             for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) s[rr] = 0.0f;
+#pragma unroll 4
             for (int d = 0; d < D; d += 4) {
                 const float4 kk = *reinterpret_cast<const float4*>(&sK[lane][d]);
 #pragma unroll
@@ -144,6 +163,9 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(FwdArgs a) {
             }
             __syncthreads();
 
+            // (unrolled by 8: fully unrolled, the compiler hoists every LDS read
+            // of the loop and runs out of registers)
+#pragma unroll 8
             for (int j = 0; j < GBN; ++j) {
                 float vv[D / 64];
 #pragma unroll
