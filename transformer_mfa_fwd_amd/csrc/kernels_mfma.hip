@@ -161,6 +161,13 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
     constexpr int RPI = 64 / CPR;           // tile rows per DMA instruction
     constexpr int IPW = BN / RPI / 4;       // DMA instructions per wave per tile
     constexpr bool LOGIT = CAP || BIAS;     // scores turned into base-2 logits before the max
+    // With a cap and no additive mask the logit cap*log2e - 2 cap*log2e * r,
+    // r = 1 / (2^(2 log2e s scale / cap) + 1), falls as r grows: the scores
+    // are kept as r (a hidden one as +inf), the row's largest logit comes from
+    // its smallest r, and the last fma of the cap joins the exponential's
+    // argument, 2^(fma(r, -2 cap log2e, cap log2e - m)): one instruction per
+    // score fewer.
+    constexpr bool RDOM = CAP && !BIAS;
     constexpr int NSA = LOGIT ? 13 : 9;     // softmax steps run beside Q.K^T
     constexpr int TRS = NQK - QK_LA;        // slot issuing the first V reads
     static_assert(TRS > 0 && TRS + QK_LA == NQK, "V reads follow the last K read");
@@ -411,6 +418,11 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
         }                                                                                    \
     } while (0)
 
+// the row's extreme over scores (RDOM: the smallest r) and a score's weight
+#define MFA_EXT(X, Y) (RDOM ? fmin_fast((X), (Y)) : fmax_fast((X), (Y)))
+#define MFA_EXP(X) (RDOM ? fast_exp2(fmaf((X), -two_cap_l2, neg_m))                          \
+                         : LOGIT ? fast_exp2((X) + neg_m) : fast_exp2(fmaf((X), c_log2, neg_m)))
+
 // Softmax step U (a constant, 0 .. NSA-1) of the tile whose raw scores are in
 // SC.  With a cap the base-2 logit is
 // cap*log2e - 2 cap*log2e / (2^(2 log2e s scale / cap) + 1); without one it is
@@ -424,7 +436,8 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
             _Pragma("unroll") for (int _e = 0; _e < 8; ++_e) {                               \
                 const float _s = MFA_X(SC, 8 * (U) + _e);                                    \
                 float _x;                                                                    \
-                if constexpr (CAP) _x = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(_s * cap_arg) + 1.0f); \
+                if constexpr (RDOM) _x = fast_rcp(fast_exp2(_s * cap_arg) + 1.0f);             \
+                else if constexpr (CAP) _x = cap_l2 - two_cap_l2 * fast_rcp(fast_exp2(_s * cap_arg) + 1.0f); \
                 else _x = _s * c_log2;                                                       \
                 /* score i = 8 U + e has its bias in group i / 4, component i % 4 */        \
                 if constexpr (BIAS) _x = fmaf(bnx[(8 * (U) + _e) >> 2][(8 * (U) + _e) & 3], LOG2E, _x); \
@@ -441,23 +454,24 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
                     const int _c = (_i >> 4) * 32 + ((_i & 15) >> 2) * 8 + (_i & 3);          \
                     const uint32_t _mw = (uint32_t)__builtin_amdgcn_sbfe(_c < 32 ? _vlo : _vhi, _c & 31, 1); \
                     MFA_X(SC, _i) = __uint_as_float((__float_as_uint(MFA_X(SC, _i)) & _mw) |  \
-                                                    (0xff800000u & ~_mw));                   \
+                                                    ((RDOM ? 0x7f800000u : 0xff800000u) & ~_mw)); \
                 }                                                                            \
             }                                                                                \
         } else if constexpr (_u >= 1 && _u <= 3) {                                           \
             _Pragma("unroll") for (int _d = 0; _d < 4; ++_d) {                               \
                 const int _p = 4 * (_u - 1) + _d;                                            \
                 if (_p < 10)                                                                 \
-                    pm[_p] = fmax_fast(fmax_fast(MFA_X(SC, 3 * _p), MFA_X(SC, 3 * _p + 1)), MFA_X(SC, 3 * _p + 2)); \
+                    pm[_p] = MFA_EXT(MFA_EXT(MFA_X(SC, 3 * _p), MFA_X(SC, 3 * _p + 1)), MFA_X(SC, 3 * _p + 2)); \
             }                                                                                \
-            if (_u == 3) pm[10] = fmax_fast(MFA_X(SC, 30), MFA_X(SC, 31));                  \
+            if (_u == 3) pm[10] = MFA_EXT(MFA_X(SC, 30), MFA_X(SC, 31));                    \
         } else if constexpr (_u == 4) {                                                      \
-            float _t = fmax_fast(fmax_fast(fmax_fast(pm[0], pm[1]), pm[2]),                  \
-                                 fmax_fast(fmax_fast(pm[3], pm[4]), pm[5]));                 \
-            _t = fmax_fast(_t, fmax_fast(fmax_fast(pm[6], pm[7]), pm[8]));                   \
-            _t = fmax_fast(fmax_fast(_t, pm[9]), pm[10]);                                    \
-            _t = xor32_max(_t);                                                              \
-            const float _tl2 = LOGIT ? _t : _t * c_log2;   /* base-2 logit units */         \
+            float _t = MFA_EXT(MFA_EXT(MFA_EXT(pm[0], pm[1]), pm[2]),                        \
+                               MFA_EXT(MFA_EXT(pm[3], pm[4]), pm[5]));                       \
+            _t = MFA_EXT(_t, MFA_EXT(MFA_EXT(pm[6], pm[7]), pm[8]));                         \
+            _t = MFA_EXT(MFA_EXT(_t, pm[9]), pm[10]);                                        \
+            _t = RDOM ? xor32_min(_t) : xor32_max(_t);                                       \
+            /* base-2 logit units (RDOM: the smallest r gives the largest logit) */         \
+            const float _tl2 = RDOM ? fmaf(_t, -two_cap_l2, cap_l2) : (LOGIT ? _t : _t * c_log2); \
             /* Lazy rescale: the running max only moves when a tile's max     */            \
             /* exceeds it by more than 8 (base 2), so every weight 2^(x - m)  */            \
             /* stays <= 256 and the accumulator is rescaled rarely.  Exact    */            \
@@ -471,11 +485,11 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
                     _Pragma("unroll") for (int _e = 0; _e < 16; ++_e) oacc[_db][_e] *= _alpha; \
             }                                                                                \
             neg_m = m == -INFINITY ? 0.0f : -m;                                              \
+            if constexpr (RDOM) neg_m += cap_l2;   /* the exponent's constant: cap log2e - m */ \
         } else {                                                                             \
             _Pragma("unroll") for (int _d = 0; _d < 2; ++_d) {                               \
                 const int _e = 2 * (_u - 5) + _d;                                            \
-                MFA_X(SC, _e) = LOGIT ? fast_exp2(MFA_X(SC, _e) + neg_m)                     \
-                                    : fast_exp2(fmaf(MFA_X(SC, _e), c_log2, neg_m));         \
+                MFA_X(SC, _e) = MFA_EXP(MFA_X(SC, _e));                                      \
             }                                                                                \
             psum0 += MFA_X(SC, 2 * (_u - 5));                                                \
             psum1 += MFA_X(SC, 2 * (_u - 5) + 1);                                            \
@@ -494,8 +508,7 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
         if constexpr ((S4) < 3) {                                                            \
             _Pragma("unroll") for (int _d = 0; _d < 2; ++_d) {                               \
                 const int _e = 8 + 8 * (S4) + 2 * (U) + _d;                                  \
-                MFA_X(SC, _e) = LOGIT ? fast_exp2(MFA_X(SC, _e) + neg_m)                     \
-                                    : fast_exp2(fmaf(MFA_X(SC, _e), c_log2, neg_m));         \
+                MFA_X(SC, _e) = MFA_EXP(MFA_X(SC, _e));                                      \
             }                                                                                \
             psum0 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U));                                      \
             psum1 += MFA_X(SC, 8 + 8 * (S4) + 2 * (U) + 1);                                  \
@@ -678,6 +691,8 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
 #undef MFA_KEEP
 #undef MFA_DROP8
 #undef MFA_SA
+#undef MFA_EXT
+#undef MFA_EXP
 #undef MFA_SB
 #undef MFA_SA_IF
 #undef MFA_SB_IF

@@ -147,15 +147,20 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // IEEE maximum (gfx950 v_maximum3_f32 for chains); unlike fmaxf it needs no
 // canonicalisation of its operands.  Scores are finite or -inf.
 __device__ inline float fmax_fast(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ inline float fmin_fast(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// Max / sum of a value over lanes l and l ^ 32.  v_permlane32_swap exchanges
+// Max / min / sum of a value over lanes l and l ^ 32.  v_permlane32_swap exchanges
 // the upper half of its first operand with the lower half of its second, so
 // with both operands equal each lane ends up holding {v[l], v[l ^ 32]}; this
 // stays on the VALU (no LDS permute).
 __device__ inline float xor32_max(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmax_fast(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_min(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmin_fast(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float xor32_sum(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
