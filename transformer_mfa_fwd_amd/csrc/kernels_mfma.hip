@@ -169,8 +169,13 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
     // score fewer.
     constexpr bool RDOM = CAP && !BIAS;
     constexpr int NSA = LOGIT ? 13 : 9;     // softmax steps run beside Q.K^T
-    constexpr int TRS = NQK - QK_LA;        // slot issuing the first V reads
-    static_assert(TRS > 0 && TRS + QK_LA == NQK, "V reads follow the last K read");
+    // K fragment reads in flight: two with an additive mask (its next tile's
+    // values take 32 registers) or dropout, so that those kernels, at two
+    // workgroups per CU, spill little: a spill's reload in the loop waits for
+    // every copy in flight (vector memory completes in order)
+    constexpr int QKLA = (BIAS || DROP) ? 2 : QK_LA;
+    constexpr int TRS = NQK - QKLA;         // slot issuing the first V reads
+    static_assert(TRS > 0 && TRS + QKLA == NQK, "V reads follow the last K read");
     typedef typename Mfma<T>::v8 v8;
     constexpr float LOG2E = 1.4426950408889634f;
     // CV: P.V on fp16 operands (see cvt_bf16x2_f16x2)
@@ -533,8 +538,8 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
     }
 #define MFA_QK_SLOT(F, SC, SN, SM)                                                           \
     if constexpr ((F) < NQK) {                                                               \
-        mfa_qk_wait<QK_LA, NQK, (SM) ? TRS : NQK, 2 * NDB>(_kf, (F));                        \
-        if constexpr ((F) + QK_LA < NQK) mfa_qk_issue<L::RS, _kb>(_kf, rd_k, (F) + QK_LA);  \
+        mfa_qk_wait<QKLA, NQK, (SM) ? TRS : NQK, 2 * NDB>(_kf, (F));                         \
+        if constexpr ((F) + QKLA < NQK) mfa_qk_issue<L::RS, _kb>(_kf, rd_k, (F) + QKLA);    \
         if constexpr ((SM) && (F) == TRS) MFA_TR_ISSUE(0, vlo[0], vhi[0]);                  \
         if constexpr (SM) {                                                                  \
             MFA_DMA_IF(F, 0) MFA_DMA_IF(F, 1) MFA_DMA_IF(F, 2) MFA_DMA_IF(F, 3)              \
@@ -555,7 +560,7 @@ __device__ __attribute__((always_inline)) inline bool prefill_block(const FwdArg
     do {                                                                                     \
         constexpr int _kb = L::KST + (KSTG) * L::TILE;                                       \
         u32x4_t _kf[NQK];                                                                    \
-        _Pragma("unroll") for (int f = 0; f < QK_LA; ++f) mfa_qk_issue<L::RS, _kb>(_kf, rd_k, f); \
+        _Pragma("unroll") for (int f = 0; f < QKLA; ++f) mfa_qk_issue<L::RS, _kb>(_kf, rd_k, f); \
         _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                     \
             _Pragma("unroll") for (int e = 0; e < 16; ++e) SN[kb][e] = 0.0f;                \
         MFA_QK_SLOT(0, SC, SN, SM) MFA_QK_SLOT(1, SC, SN, SM)                                \
