@@ -761,13 +761,14 @@ __device__ __attribute__((noinline)) void prefill_block_bf16_operands(const void
 
 // BIAS adds an additive score mask read from global memory into registers one
 // tile ahead (32 more VGPRs).  DROP applies attention dropout: the keep bits
-// of a tile's 32 weights per lane come from eight Philox blocks before its
-// softmax, dropped weights are zeroed after they enter the row sum and before
-// they become the P.V operand, and the 1 / (1 - p) factor is folded into the
-// final normalisation.  Either one runs two workgroups per CU: at D = 128 the
-// compiler then spills some 12-28 values, and both still run faster than with
-// one workgroup per CU and no spills; with both, one workgroup per CU.  bf16
-// inputs run P.V on fp16 operands.
+// of a tile's 32 weights per lane come from two Philox blocks (and the two
+// the lane ^ 32 partner evaluates) before its softmax, dropped weights are
+// zeroed after they enter the row sum and before they become the P.V operand,
+// and the 1 / (1 - p) factor is folded into the final normalisation.  Either
+// one runs two workgroups per CU: at D = 128 the compiler then spills a few
+// values (fewer with two K reads in flight), and both still run faster than
+// with one workgroup per CU and no spills; with both, one workgroup per CU.
+// bf16 inputs run P.V on fp16 operands.
 template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP>
 __global__ __launch_bounds__(256, (BIAS && DROP) ? 1 : (BIAS || DROP) ? 2 : (D == 64 ? 3 : 2))
 void prefill_kernel(FwdArgs a, int nqt) {
