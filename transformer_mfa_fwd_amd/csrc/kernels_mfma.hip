@@ -767,10 +767,11 @@ __device__ __attribute__((noinline)) void prefill_block_bf16_operands(const void
 // and the 1 / (1 - p) factor is folded into the final normalisation.  Either
 // one runs two workgroups per CU: at D = 128 the compiler then spills a few
 // values (fewer with two K reads in flight), and both still run faster than
-// with one workgroup per CU and no spills; with both, one workgroup per CU.
+// with one workgroup per CU and no spills.  With both, D = 64 still fits two
+// workgroups per CU without spills; D = 128 takes one (at two it spills ~80).
 // bf16 inputs run P.V on fp16 operands.
 template <typename T, int D, bool CAP, bool MASK, bool SEQ, bool BIAS, bool DROP>
-__global__ __launch_bounds__(256, (BIAS && DROP) ? 1 : (BIAS || DROP) ? 2 : (D == 64 ? 3 : 2))
+__global__ __launch_bounds__(256, (BIAS && DROP) ? (D == 64 ? 2 : 1) : (BIAS || DROP) ? 2 : (D == 64 ? 3 : 2))
 void prefill_kernel(FwdArgs a, int nqt) {
     constexpr bool CVT = std::is_same<T, __bf16>::value;
     __shared__ __attribute__((aligned(1024))) char smem[PfLds<D>::BYTES];
