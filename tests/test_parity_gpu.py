@@ -183,6 +183,30 @@ def test_fully_masked_batch_gives_zero_and_neg_inf():
         assert torch.all(torch.isfinite(lse[1]))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_softcap_rows_without_visible_keys(dtype, D):
+    """Soft-capped prefill (its scores kept as the cap's reciprocal, hidden
+    ones as +inf) with a batch whose keys are all masked and rows whose only
+    keys are masked (a causal window over a key mask with a masked head):
+    those rows get O = 0 and LSE = -inf, every other row the oracle's values."""
+    w = wl.Workload(f"cap_empty_rows_{dtype}_D{D}", dtype, 2, 200, 200, 4, 2, D, True, window=20, softcap=7.0)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    m = torch.ones(2, 200)
+    m[0] = 0.0              # batch 0: no key
+    m[1, :90] = 0.0         # batch 1: rows 0 .. 89 see only masked keys (window 20)
+    md = m.to(DEV)
+    out, lse = mfa.fwd(q, k, v, causal=True, window=w.window, softcap=w.softcap, key_mask=md, scale=w.scale,
+                       path=mfa.PATH_MFMA)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(out[1, :90] == 0) and torch.all(torch.isneginf(lse[1, :, :90]))
+    O, L, _ = default_oracle().full(q, k, v, scale=w.scale, causal=True, window=w.window, q_offset=0,
+                                    softcap=w.softcap, key_mask=m, nthreads=pu.ORACLE_THREADS)
+    pu.compare(dtype, out.double().cpu().numpy().transpose(0, 2, 1, 3), lse.double().cpu().numpy(),
+               O.transpose(0, 2, 1, 3), L, w.name)
+
+
 def test_deterministic_and_no_out_of_bounds_writes():
     w = wl.Workload("canary", "bf16", 2, 190, 190, 4, 2, 128, True, window=50, mask="random_frac",
                     mask_frac=0.2)
