@@ -130,8 +130,15 @@ def test_matrix_core_backward_agrees_with_fp32_kernels(dtype, D):
     f = [x.float() for x in (q, k, v, out, dout)]
     g = mfa.bwd(*f, lse, causal=True, window=200)
     torch.cuda.synchronize()
+    mant = 7 if dtype == "bf16" else 10   # stored fraction bits of the 16-bit outputs
     for name, x, y, zz in zip(("dq", "dk", "dv"), a, g, z):
         scale = max(1.0, float(y.abs().max()))
         err = float((x.float() - y).abs().max())
         assert err <= 1e-2 * scale, (name, err, scale)
-        assert float((zz.float() - x.float()).abs().max()) <= 1e-3 * scale, name
+        # the two instantiations may be different kernels that add the same
+        # products in another order: each element within one unit in the last
+        # place of the 16-bit output, on top of 1e-3 of the tensor's scale
+        xf, zf = x.float(), zz.float()
+        _, e = torch.frexp(torch.maximum(xf.abs(), zf.abs()))
+        ulp = torch.ldexp(torch.ones_like(xf), e - 1 - mant)
+        assert bool(((zf - xf).abs() <= 1e-3 * scale + ulp).all()), name

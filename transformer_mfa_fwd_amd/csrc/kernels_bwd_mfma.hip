@@ -726,6 +726,261 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
     }
 }
 
+// dK and dV at D = 128 without an additive mask or dropout: 16 keys per wave
+// on 16x16x32 MFMAs, eight waves (128 keys) per workgroup.  The accumulators
+// of 16 keys (2 x 32 registers) and their K and V operands (2 x 16) leave two
+// waves per SIMD, where the 32-key kernel above runs one.  Per 32-row step:
+//   S  [32 rows x 16 keys] = Q  . K^T   (A: Q rows from LDS, B: K in registers)
+//   dP [32 rows x 16 keys] = dO . V^T
+//   dV^T [128 x 16 keys] += dO^T . P    (A: transposing LDS reads, B: P itself)
+//   dK^T [128 x 16 keys] += Q^T . dS
+// The products' k index e of lane group g (rows 8 g + e of the MFMA) is tile
+// row 4 g + e for e < 4 and 16 + 4 g + e - 4 after: the rows that score
+// elements (block 0, i) and (block 1, i) of the lane hold, so the packed
+// weights are the B operand as they are, and the transposing reads of dO and
+// Q take the same two groups of four rows.  Two LDS buffers: step u + 1 is
+// stored while step u computes, and its global reads were issued a step
+// earlier.
+template <typename T, bool CAP>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* __restrict__ dout,
+                                                           const float* __restrict__ delta, T* __restrict__ dk,
+                                                           T* __restrict__ dv) {
+    typedef typename Mfma<T>::v8 v8;
+    constexpr int D = 128, NKS = D / 32, NDB = D / 16, CPR = D / 8;
+    typedef BwLds<D> L;
+    // 16-byte chunk c of row r sits at chunk c ^ swz(r), swz(r) = 4 (r % 4) +
+    // the two bits of (r / 4) % 4 swapped: a permutation over any 16
+    // consecutive rows (the row reads), and the transposing reads of lane
+    // groups 0 and 1 (rows 0..7 at two chunks) land on 16 different chunks, as
+    // do those of groups 2 and 3
+    auto swz = [](int r) { return ((r & 3) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1); };
+    constexpr int NBUF = 3;
+    __shared__ __attribute__((aligned(16))) char sQ[NBUF][L::TILE];
+    __shared__ __attribute__((aligned(16))) char sG[NBUF][L::TILE];   // dO rows
+    __shared__ __attribute__((aligned(16))) float sL[NBUF][32];
+    __shared__ __attribute__((aligned(16))) float sD[NBUF][32];
+    __shared__ __attribute__((aligned(16))) int sLo[NBUF][32];
+    __shared__ __attribute__((aligned(16))) int sHi[NBUF][32];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int kvh = blockIdx.x, b = blockIdx.y;
+    const int j0 = blockIdx.z * 128, j_last = min(j0 + 127, a.Lk - 1);
+    const int key = j0 + 16 * wave + col;   // this lane's key (MFMA column)
+    const int keyc = key <= j_last ? key : j_last;
+    const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+    const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
+
+    // B operands: at k-step ks lane l holds K and V of its key at d = 32 g +
+    // 8 ks .. +7 (the A operands read the same d: any order of d within the
+    // products gives the same sums, and this one keeps the row reads free of
+    // LDS bank conflicts); a masked key's rows stay zero (whatever they hold
+    // cannot reach a gradient)
+    const bool mask_ok = !a.key_mask || a.key_mask[(int64_t)b * a.Lk + keyc] > 0.5f;
+    const bool kept = key <= j_last && mask_ok;
+    v8 kop[NKS], vop[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        u32x4_t kx = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)keyc * a.kv_stride + 32 * grp + 8 * ks);
+        u32x4_t vx = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)keyc * a.kv_stride + 32 * grp + 8 * ks);
+        if (!mask_ok) kx = vx = u32x4_t{0u, 0u, 0u, 0u};
+        kop[ks] = bitcast<v8>(kx);
+        vop[ks] = bitcast<v8>(vx);
+    }
+
+    // dka / dva [db] element i: d = 16 db + 4 g + i of this lane's key
+    f32x4_t dka[NDB], dva[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dka[db] = dva[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // the run of 32-row query tiles that can see a key of the block (both ends
+    // of a row's key range are nondecreasing in the row)
+    const int nqt = (a.Lq + 31) / 32;
+    int qt_lo, qt_hi;
+    {
+        int lo = 0, hi = nqt;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            int l0, h0;
+            row_key_range<false>(a, min(32 * mid + 31, a.Lq - 1), l0, h0);
+            if (h0 >= j0) hi = mid; else lo = mid + 1;
+        }
+        qt_lo = lo;
+        hi = nqt;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            int l0, h0;
+            row_key_range<false>(a, 32 * mid, l0, h0);
+            if (l0 > j_last) hi = mid; else lo = mid + 1;
+        }
+        qt_hi = lo - 1;
+    }
+    const int nv = qt_hi >= qt_lo ? qt_hi - qt_lo + 1 : 0, nsteps = a.group * nv;
+
+    // step u's Q and dO rows (thread tid: row tid / 16, 16-byte chunk tid % 16)
+    // and the LSE, Delta and key range of its rows, into registers
+    u32x4_t rq, rg;
+    int rlo_ = 1, rhi_ = 0;
+    float rl_ = 0.0f, rd_ = 0.0f;
+    const int fr = tid / CPR, fk = tid % CPR;
+    auto fetch = [&](int u) {
+        const int hq = kvh * a.group + u / nv, r0 = 32 * (qt_lo + u % nv);
+        const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
+        const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
+        // a row past the end reads the last row and is zeroed: a select, not a branch
+        const int valid = a.Lq - r0, rc = r0 + (fr < valid ? fr : valid - 1);
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + (int64_t)rc * a.q_stride + 8 * fk);
+        const u32x4_t y = *reinterpret_cast<const u32x4_t*>(gb + (int64_t)rc * a.o_stride + 8 * fk);
+        const bool ok = fr < valid;
+        rq = u32x4_t{ok ? x[0] : 0u, ok ? x[1] : 0u, ok ? x[2] : 0u, ok ? x[3] : 0u};
+        rg = u32x4_t{ok ? y[0] : 0u, ok ? y[1] : 0u, ok ? y[2] : 0u, ok ? y[3] : 0u};
+        if (tid < 32) {
+            const int r = r0 + tid;
+            rlo_ = 1; rhi_ = 0; rl_ = 0.0f; rd_ = 0.0f;
+            if (r < a.Lq) {
+                row_key_range<false>(a, r, rlo_, rhi_);
+                const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + r];
+                if (l == -INFINITY) { rlo_ = 1; rhi_ = 0; }
+                rl_ = l == -INFINITY ? 0.0f : l * BW_LOG2E;   // finite: hidden logits are -inf
+                rd_ = delta[((int64_t)b * a.Hq + hq) * a.Lq + r];
+            }
+        }
+    };
+    auto store = [&](int buf) {
+        *reinterpret_cast<u32x4_t*>(sQ[buf] + fr * L::RS + (fk ^ swz(fr)) * 16) = rq;
+        *reinterpret_cast<u32x4_t*>(sG[buf] + fr * L::RS + (fk ^ swz(fr)) * 16) = rg;
+        if (tid < 32) { sLo[buf][tid] = rlo_; sHi[buf][tid] = rhi_; sL[buf][tid] = rl_; sD[buf][tid] = rd_; }
+    };
+    // A operand of S / dP: row 16 blk + (l % 16) at d = 32 g + 8 ks .. +7
+    auto rows16 = [&](const char* tile, int blk, int ks) {
+        const int r = 16 * blk + col;
+        return bitcast<v8>(*reinterpret_cast<const u32x4_t*>(tile + r * L::RS + (((4 * grp + ks) ^ swz(r)) * 16)));
+    };
+    // A operand of dV / dK: the tile transposed, d = 16 db + (l % 16) at rows
+    // 4 g + e and 16 + 4 g + e (e = 0..3); source lane j points at row 4 g +
+    // j / 4 (+ 16), columns 16 db + 4 (j % 4) .. +3
+    const int tr_r0 = 4 * grp + (col >> 2), tr_c = (col & 3) >> 1, tr_h = (col & 1) * 8;
+    auto cols16 = [&](const char* tile, int db) {
+        const int c = 2 * db + tr_c;
+        const i16x4_t lo = lds_read_tr16(tile + tr_r0 * L::RS + ((c ^ swz(tr_r0)) * 16) + tr_h);
+        const i16x4_t hi = lds_read_tr16(tile + (tr_r0 + 16) * L::RS + ((c ^ swz(tr_r0 + 16)) * 16) + tr_h);
+        const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return bitcast<v8>(v);
+    };
+
+    // S and dP of the step in buffer BUF: element (blk, i) of lane l is row
+    // 16 blk + 4 g + i at this lane's key
+    auto sdp_mfma = [&](f32x4_t (&sv)[2], f32x4_t (&dpv)[2], int buf, int blk, int ks) {
+        sv[blk] = Mfma<T>::mma16(rows16(sQ[buf], blk, ks), kop[ks], sv[blk]);
+        dpv[blk] = Mfma<T>::mma16(rows16(sG[buf], blk, ks), vop[ks], dpv[blk]);
+    };
+
+    if (nsteps > 0) {
+        // prologue: steps 0 and 1 stored, step 2 fetched, S and dP of step 0
+        fetch(0);
+        store(0);
+        if (nsteps > 1) { fetch(1); store(1); }
+        if (nsteps > 2) fetch(2);
+        __syncthreads();
+        f32x4_t sc[2], dc[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            sc[blk] = dc[blk] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) sdp_mfma(sc, dc, 0, blk, ks);
+        }
+        int buf = 0;   // buffer of step it
+        for (int it = 0; it < nsteps; ++it) {
+            const int bn = buf == 2 ? 0 : buf + 1, bn2 = bn == 2 ? 0 : bn + 1;   // steps it + 1, it + 2
+            if (it + 2 < nsteps) store(bn2);   // its buffer was last read by step it - 1
+            if (it + 3 < nsteps) fetch(it + 3);
+            // The step in 32 slots of one MFMA each, in a fixed order
+            // (scheduling barriers between them), every LDS operand read LA
+            // slots before its MFMA.  Slots 0..15: S and dP of step it + 1
+            // (after the last step they read a stale buffer and are discarded),
+            // with the softmax of step it, one score per odd slot.  Slots
+            // 16..31: dV and dK of step it.
+            constexpr int LA = 4;
+            // operand m of slots 0..15: block m / 8, k-step (m / 2) % 4, Q (m
+            // even) or dO rows; operand n of slots 16..31: d block n / 2 of dO^T
+            // (n even, dV) or Q^T
+            auto read_a = [&](int m) { return rows16((m & 1) ? sG[bn] : sQ[bn], m >> 3, (m >> 1) & 3); };
+            auto read_c = [&](int n) { return cols16((n & 1) ? sQ[buf] : sG[buf], n >> 1); };
+            v8 opa[16], opc[16];
+            f32x4_t sn[2], dn[2];
+            sn[0] = sn[1] = dn[0] = dn[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            float p[8], ds[8];
+            int los[4], his[4];
+            float ls[4], dd[4];
+            // row data of block BLK of step it: rows 16 blk + 4 g .. +3
+            auto read_rows = [&](int blk) {
+                const int m0 = 16 * blk + 4 * grp;
+                const int4 lo4 = *reinterpret_cast<const int4*>(&sLo[buf][m0]);
+                const int4 hi4 = *reinterpret_cast<const int4*>(&sHi[buf][m0]);
+                const float4 l4 = *reinterpret_cast<const float4*>(&sL[buf][m0]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&sD[buf][m0]);
+                los[0] = lo4.x; los[1] = lo4.y; los[2] = lo4.z; los[3] = lo4.w;
+                his[0] = hi4.x; his[1] = hi4.y; his[2] = hi4.z; his[3] = hi4.w;
+                ls[0] = l4.x; ls[1] = l4.y; ls[2] = l4.z; ls[3] = l4.w;
+                dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
+            };
+            read_rows(0);
+#pragma unroll
+            for (int m = 0; m < LA; ++m) opa[m] = read_a(m);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                if (m + LA < 16) opa[m + LA] = read_a(m + LA);
+                else opc[m + LA - 16] = read_c(m + LA - 16);
+                const int blk = m >> 3, ks = (m >> 1) & 3;
+                if (m & 1) dn[blk] = Mfma<T>::mma16(opa[m], vop[ks], dn[blk]);
+                else sn[blk] = Mfma<T>::mma16(opa[m], kop[ks], sn[blk]);
+                if (m & 1) {
+                    // score e = m / 2: row 16 (e / 4) + 4 g + e % 4 at this lane's key;
+                    // a hidden score's logit becomes -inf, so its weight is exactly 0
+                    const int e = m >> 1, eb = e >> 2, i = e & 3;
+                    float dl;
+                    float x = logit2_minus<CAP>(a, sc[eb][i], ls[i], dl);
+                    x = (kept & (key >= los[i]) & (key <= his[i])) ? x : -INFINITY;   // & : no short circuit
+                    const float pe = fast_exp2(x);
+                    p[e] = pe;
+                    ds[e] = CAP ? pe * (dc[eb][i] - dd[i]) * dl : pe * (dc[eb][i] - dd[i]);
+                }
+                if (m == 7) read_rows(1);   // block 0's row data is used up by this slot's score
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const v8 pop = pack8<T>(p), dop = pack8<T>(ds);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                if (n + LA < 16) opc[n + LA] = read_c(n + LA);
+                if (n & 1) dka[n >> 1] = Mfma<T>::mma16(opc[n], dop, dka[n >> 1]);
+                else dva[n >> 1] = Mfma<T>::mma16(opc[n], pop, dva[n >> 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();   // step it + 2 stored; step it's buffer free for step it + 3
+            sc[0] = sn[0]; sc[1] = sn[1]; dc[0] = dn[0]; dc[1] = dn[1];
+            buf = bn;
+        }
+    }
+    // without a cap the scale (d logit / d dot) is applied to dK here
+    const float oscale = CAP ? 1.0f : a.scale;
+    if (key <= j_last) {
+        T* ko = dk + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
+        T* vo = dv + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            T k4[4], v4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                k4[i] = static_cast<T>(dka[db][i] * oscale);
+                v4[i] = static_cast<T>(dva[db][i]);
+            }
+            *reinterpret_cast<uint2*>(ko + 16 * db + 4 * grp) = *reinterpret_cast<const uint2*>(k4);
+            *reinterpret_cast<uint2*>(vo + 16 * db + 4 * grp) = *reinterpret_cast<const uint2*>(v4);
+        }
+    }
+}
+
 template <typename T, int D, bool CAP, bool EXTRA>
 hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                              hipStream_t s) {
@@ -740,8 +995,12 @@ hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* de
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0,
-                       s, a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
+    if constexpr (D == 128 && !EXTRA)
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, CAP>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(512), 0, s, a, g,
+                           delta, static_cast<T*>(dk), static_cast<T*>(dv));
+    else
+        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0,
+                           s, a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     return hipGetLastError();
 }
 
