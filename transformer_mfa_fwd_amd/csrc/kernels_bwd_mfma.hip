@@ -726,8 +726,8 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
     }
 }
 
-// dK and dV at D = 128 without an additive mask or dropout: 16 keys per wave
-// on 16x16x32 MFMAs, eight waves (128 keys) per workgroup.  The accumulators
+// dK and dV at D = 128: 16 keys per wave on 16x16x32 MFMAs, eight waves (128
+// keys) per workgroup.  The accumulators
 // of 16 keys (2 x 32 registers) and their K and V operands (2 x 16) leave two
 // waves per SIMD, where the 32-key kernel above runs one.  Per 32-row step:
 //   S  [32 rows x 16 keys] = Q  . K^T   (A: Q rows from LDS, B: K in registers)
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
 // Q take the same two groups of four rows.  Two LDS buffers: step u + 1 is
 // stored while step u computes, and its global reads were issued a step
 // earlier.
-template <typename T, bool CAP>
+template <typename T, bool CAP, bool EXTRA>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* __restrict__ dout,
                                                            const float* __restrict__ delta, T* __restrict__ dk,
                                                            T* __restrict__ dv) {
@@ -900,7 +900,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
             // (after the last step they read a stale buffer and are discarded),
             // with the softmax of step it, one score per odd slot.  Slots
             // 16..31: dV and dK of step it.
-            constexpr int LA = 4;
+            constexpr int LA = EXTRA ? 3 : 4;   // (the mask and dropout registers leave room for three)
             // operand m of slots 0..15: block m / 8, k-step (m / 2) % 4, Q (m
             // even) or dO rows; operand n of slots 16..31: d block n / 2 of dO^T
             // (n even, dV) or Q^T
@@ -910,6 +910,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
             f32x4_t sn[2], dn[2];
             sn[0] = sn[1] = dn[0] = dn[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             float p[8], ds[8];
+            // the step's additive mask values and dropout keep bits of this
+            // lane's 8 scores (score e: row 16 (e / 4) + 4 g + e % 4).  The
+            // wave's 16 keys are one 16-key Philox block of each row: lane L
+            // evaluates the block of row L % 32, and each lane takes its key's
+            // bit of its rows' blocks from the lanes that hold them.
+            float bv[EXTRA ? 8 : 1];
+            uint32_t keepm = 0xffu;
+            if constexpr (EXTRA) {
+                const int hq = kvh * a.group + it / nv, r0 = 32 * (qt_lo + it % nv);
+                if (a.bias) {
+                    const float* bk = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] +
+                                      (int64_t)keyc * a.bias_stride[3];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int row = r0 + 16 * (e >> 2) + 4 * grp + (e & 3);
+                        bv[e] = row < a.Lq ? bk[(int64_t)row * a.bias_stride[2]] : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
+                }
+                if (a.drop_scale > 0.0f) {
+                    const uint32_t mrow = dropout_keep16(a, b, hq, r0 + (lane & 31), (j0 + 16 * wave) >> 4);
+                    keepm = 0u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t ms = (uint32_t)__shfl((int)mrow, 16 * (e >> 2) + 4 * grp + (e & 3));
+                        keepm |= ((ms >> col) & 1u) << e;
+                    }
+                }
+            }
+            (void)bv;
             int los[4], his[4];
             float ls[4], dd[4];
             // row data of block BLK of step it: rows 16 blk + 4 g .. +3
@@ -941,10 +973,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
                     const int e = m >> 1, eb = e >> 2, i = e & 3;
                     float dl;
                     float x = logit2_minus<CAP>(a, sc[eb][i], ls[i], dl);
+                    float z = 1.0f;
+                    if constexpr (EXTRA) {
+                        x = fmaf(bv[e], BW_LOG2E, x);
+                        if (a.drop_scale > 0.0f) z = (keepm >> e) & 1u ? a.drop_scale : 0.0f;
+                    }
                     x = (kept & (key >= los[i]) & (key <= his[i])) ? x : -INFINITY;   // & : no short circuit
                     const float pe = fast_exp2(x);
-                    p[e] = pe;
-                    ds[e] = CAP ? pe * (dc[eb][i] - dd[i]) * dl : pe * (dc[eb][i] - dd[i]);
+                    // with dropout dV takes the kept, rescaled weights and dS
+                    // the kept, rescaled dP
+                    p[e] = EXTRA ? pe * z : pe;
+                    const float dz = EXTRA ? dc[eb][i] * z : dc[eb][i];
+                    ds[e] = CAP ? pe * (dz - dd[i]) * dl : pe * (dz - dd[i]);
                 }
                 if (m == 7) read_rows(1);   // block 0's row data is used up by this slot's score
                 __builtin_amdgcn_sched_barrier(0);
@@ -995,9 +1035,10 @@ hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* de
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if constexpr (D == 128 && !EXTRA)
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, CAP>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(512), 0, s, a, g,
-                           delta, static_cast<T*>(dk), static_cast<T*>(dv));
+    // (with both a cap and a mask or dropout the 16-key kernel would spill)
+    if constexpr (D == 128 && !(CAP && EXTRA))
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(512), 0, s,
+                           a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     else
         hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0,
                            s, a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
