@@ -890,6 +890,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
             for (int ks = 0; ks < NKS; ++ks) sdp_mfma(sc, dc, 0, blk, ks);
         }
         int buf = 0;   // buffer of step it
+        uint32_t mpair = 0u;   // dropout keep bits of two steps' rows (EXTRA)
+        (void)mpair;
         for (int it = 0; it < nsteps; ++it) {
             const int bn = buf == 2 ? 0 : buf + 1, bn2 = bn == 2 ? 0 : bn + 1;   // steps it + 1, it + 2
             if (it + 2 < nsteps) store(bn2);   // its buffer was last read by step it - 1
@@ -932,11 +934,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
                     for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
                 }
                 if (a.drop_scale > 0.0f) {
-                    const uint32_t mrow = dropout_keep16(a, b, hq, r0 + (lane & 31), (j0 + 16 * wave) >> 4);
+                    // a step needs 32 blocks: lanes 0..31 evaluate those of an
+                    // even step and lanes 32..63 those of the step after it
+                    if ((it & 1) == 0) {
+                        const int u = min(it + (lane >> 5), nsteps - 1);
+                        mpair = dropout_keep16(a, b, kvh * a.group + u / nv, 32 * (qt_lo + u % nv) + (lane & 31),
+                                               (j0 + 16 * wave) >> 4);
+                    }
                     keepm = 0u;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const uint32_t ms = (uint32_t)__shfl((int)mrow, 16 * (e >> 2) + 4 * grp + (e & 3));
+                        const uint32_t ms =
+                            (uint32_t)__shfl((int)mpair, 32 * (it & 1) + 16 * (e >> 2) + 4 * grp + (e & 3));
                         keepm |= ((ms >> col) & 1u) << e;
                     }
                 }
