@@ -106,6 +106,32 @@ def test_dropout_seed_uses_its_low_32_bits(dtype):
     assert all(torch.equal(x, y) for x, y in zip(*grads))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_backward_dropout_pattern_shared_or_not(dtype, with_bias):
+    """With dropout at D = 128 the dK/dV kernel may store the pattern for the
+    dQ kernel (the pool's workspace, or a caller's with room for it) or each
+    kernel evaluates it (a caller workspace of exactly the Delta size): the
+    gradients are bitwise the same.  Ragged sizes (Lk not a multiple of 16 or
+    of 128, several query heads per kv head)."""
+    w = wl.Workload(f"bd_share_{dtype}", dtype, 2, 150, 203, 4, 2, 128, True, window=120)
+    q, k, v, _ = wl.make_inputs(w, DEV)
+    bias = bias_tensor((1, 1, w.Lq, w.Lk), seed=3).to(DEV) if with_bias else None
+    say(f"{w.name} bias={with_bias} shared vs evaluated dropout pattern")
+    out, lse = mfa.fwd(q, k, v, causal=True, window=120, bias=bias, dropout_p=0.25, seed=11)
+    g = torch.randn(q.shape, generator=torch.Generator().manual_seed(4)).to(q.dtype).to(DEV)
+    need = mfa.bwd_workspace_size(w.B, w.Lq, w.Hq)
+    keep = 2 * w.B * w.Hq * ((w.Lk + 15) // 16) * w.Lq
+    kw = dict(causal=True, window=120, bias=bias, dropout_p=0.25, seed=11)
+    pooled = mfa.bwd(q, k, v, out, g, lse, **kw)
+    small = mfa.bwd(q, k, v, out, g, lse, workspace=torch.empty(need, dtype=torch.uint8, device=DEV), **kw)
+    roomy = mfa.bwd(q, k, v, out, g, lse, workspace=torch.empty(need + keep, dtype=torch.uint8, device=DEV), **kw)
+    torch.cuda.synchronize()
+    for name, x, y, z in zip(("dq", "dk", "dv"), pooled, small, roomy):
+        assert torch.equal(x, y) and torch.equal(x, z), name
+        assert bool(torch.isfinite(x.float()).all()), name
+
+
 # Additive masks the MFMA prefill kernel reads itself (no dropout, fp16/bf16,
 # key dimension full, Lk a multiple of four): several tiles, ragged tails.
 MFMA_BIAS = []

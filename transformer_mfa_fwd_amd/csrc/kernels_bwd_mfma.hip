@@ -260,6 +260,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
     __shared__ __attribute__((aligned(16))) char sK[NBUF][BwLds<D>::TILE];
     __shared__ __attribute__((aligned(16))) char sV[NBUF][BwLds<D>::TILE];
     __shared__ float sM[NBUF][32];   // 1: key kept (in range of the axis and of the key mask)
+    // the additive mask of the tile's 128 rows x 32 keys (EXTRA): read from
+    // global memory 32 keys of a row at a time and from here by each lane's
+    // row; rows padded to 36 floats (16-byte reads of 16 rows hit different banks)
+    constexpr int BRS = 36;
+    __shared__ __attribute__((aligned(16))) float sB[EXTRA ? NBUF : 1][EXTRA ? 128 * BRS : 4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     // grid (Hq, B, query blocks), the latest query block first: under a causal
@@ -291,10 +296,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
     int lo_blk, t0, t1, hi_blk;
     row_key_range<false>(a, i0, lo_blk, t0);
     row_key_range<false>(a, i_last, t1, hi_blk);
-    // additive mask of this lane's row (EXTRA with a mask)
-    const float* brow = nullptr;
-    if (EXTRA && a.bias)
-        brow = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] + (int64_t)rowc * a.bias_stride[2];
+    // additive mask of this (batch, query head) (EXTRA with a mask)
+    const float* bhead = nullptr;
+    if (EXTRA && a.bias) bhead = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1];
 
     f32x16_t acc[NDB];
 #pragma unroll
@@ -306,6 +310,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
         const int t_first = lo_blk / 32, n_t = hi_blk / 32 + 1 - t_first;
         TileRegs<D> rk, rv;
         float rm = 0.0f;
+        float rb[EXTRA ? 16 : 1];   // thread tid: key tid % 32 of rows tid / 32 + 8 j
+        (void)rb;
         // tile t_first + u's K, V and key-kept flags into registers
         auto fetch = [&](int u) {
             const int k0 = 32 * (t_first + u);
@@ -317,11 +323,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
                 const int key = k0 + tid;
                 rm = (key < a.Lk && (!a.key_mask || a.key_mask[(int64_t)b * a.Lk + key] > 0.5f)) ? 1.0f : 0.0f;
             }
+            if constexpr (EXTRA) {
+                if (bhead) {
+                    const int key = k0 + (tid & 31);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int r = i0 + (tid >> 5) + 8 * j;
+                        rb[j] = (r < a.Lq && key < a.Lk)
+                                    ? bhead[(int64_t)r * a.bias_stride[2] + (int64_t)key * a.bias_stride[3]]
+                                    : 0.0f;
+                    }
+                }
+            }
         };
         auto store = [&](int buf) {
             store_tile<D>(sK[buf], rk, tid);
             store_tile<D>(sV[buf], rv, tid);
             if (tid < 32) sM[buf][tid] = rm;
+            if constexpr (EXTRA) {
+                if (bhead) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) sB[buf][((tid >> 5) + 8 * j) * BRS + (tid & 31)] = rb[j];
+                }
+            }
         };
         // A operands of S^T and dP^T (K and V rows) of the tile in buffer BUF
         v8 ka[NKS], va[NKS];
@@ -365,15 +389,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
             float bv[EXTRA ? 16 : 1];
             uint32_t keepm = 0xffffu;
             if constexpr (EXTRA) {
+                if (bhead) {
+                    const float* br = &sB[buf][(32 * wave + (lane & 31)) * BRS + 4 * h];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    bv[r] = (brow && key < a.Lk) ? brow[(int64_t)key * a.bias_stride[3]] : 0.0f;
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const float4 f = *reinterpret_cast<const float4*>(br + 8 * gq);
+                        bv[4 * gq] = f.x; bv[4 * gq + 1] = f.y; bv[4 * gq + 2] = f.z; bv[4 * gq + 3] = f.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) bv[r] = 0.0f;
                 }
                 if (a.drop_scale > 0.0f) {
                     // the tile's 32 keys are two 16-key Philox blocks of this
                     // row, which lanes l and l ^ 32 share: each evaluates one
-                    const uint32_t own = dropout_keep16(a, b, hq, row, (k0 >> 4) + h);
+                    // (from the dK/dV kernel's buffer when it stored them)
+                    const int jb = (k0 >> 4) + h;
+                    const uint32_t own =
+                        a.keep_bits ? (row < a.Lq && 16 * jb < a.Lk
+                                           ? (uint32_t)a.keep_bits[(((int64_t)b * a.Hq + hq) * ((a.Lk + 15) >> 4) + jb) *
+                                                                       a.Lq + row]
+                                           : 0u)
+                                    : dropout_keep16(a, b, hq, row, jb);
                     const uint32_t oth = (uint32_t)__shfl_xor((int)own, 32);
                     const uint32_t m32 = h ? (oth | (own << 16)) : (own | (oth << 16));   // keys 0 .. 31
                     keepm = pack_even_nibbles(m32 >> (4 * h));
@@ -938,8 +975,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
                     // even step and lanes 32..63 those of the step after it
                     if ((it & 1) == 0) {
                         const int u = min(it + (lane >> 5), nsteps - 1);
-                        mpair = dropout_keep16(a, b, kvh * a.group + u / nv, 32 * (qt_lo + u % nv) + (lane & 31),
-                                               (j0 + 16 * wave) >> 4);
+                        const int hqu = kvh * a.group + u / nv, rowu = 32 * (qt_lo + u % nv) + (lane & 31);
+                        const int jb = (j0 + 16 * wave) >> 4;
+                        mpair = dropout_keep16(a, b, hqu, rowu, jb);
+                        // stored for the dQ kernel: every (row, block) with a visible
+                        // weight is written here (its row's tile is in the run)
+                        if (a.keep_bits && it + (lane >> 5) < nsteps && rowu < a.Lq && 16 * jb < a.Lk)
+                            a.keep_bits[(((int64_t)b * a.Hq + hqu) * ((a.Lk + 15) >> 4) + jb) * a.Lq + rowu] =
+                                (uint16_t)mpair;
                     }
                     keepm = 0u;
 #pragma unroll
@@ -1034,23 +1077,23 @@ template <typename T, int D, bool CAP, bool EXTRA>
 hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                              hipStream_t s) {
     const T* g = static_cast<const T*>(dout);
-    if (a.Lq > 0) {
-        if constexpr (EXTRA)
-            hipLaunchKernelGGL((bwd_dq_pipe_mfma_kernel<T, D, CAP, true>), dim3(a.Hq, a.B, (a.Lq + 127) / 128),
-                               dim3(256), 0, s, a, g, delta, static_cast<T*>(dq));
-        else
-            hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0, s,
-                               a, g, delta, static_cast<T*>(dq));
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    // (with both a cap and a mask or dropout the 16-key kernel would spill)
+    // dK/dV first: with dropout its 16-key kernel may store the keep bits that
+    // the dQ kernel then reads (same stream).  With both a cap and a mask or
+    // dropout the 16-key kernel would spill, and the 32-key one runs.
     if constexpr (D == 128 && !(CAP && EXTRA))
         hipLaunchKernelGGL((bwd_dkdv16_kernel<T, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(512), 0, s,
                            a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     else
         hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0,
                            s, a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.Lq <= 0) return e;
+    if constexpr (EXTRA)
+        hipLaunchKernelGGL((bwd_dq_pipe_mfma_kernel<T, D, CAP, true>), dim3(a.Hq, a.B, (a.Lq + 127) / 128),
+                           dim3(256), 0, s, a, g, delta, static_cast<T*>(dq));
+    else
+        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0, s,
+                           a, g, delta, static_cast<T*>(dq));
     return hipGetLastError();
 }
 
@@ -1073,6 +1116,13 @@ hipError_t launch_bwd_mfma_d(const FwdArgs& a, const void* dout, const float* de
 }
 
 }  // namespace
+
+size_t bwd_keep_bits_bytes(const FwdArgs& a, int dtype) {
+    if (!(a.drop_scale > 0.0f) || a.D != 128 || a.softcap > 0.0f || !bwd_mfma_supported(a, dtype) || a.B <= 0 ||
+        a.Lq <= 0 || a.Lk <= 0)
+        return 0;
+    return (size_t)a.B * a.Hq * ((a.Lk + 15) / 16) * a.Lq * sizeof(uint16_t);
+}
 
 bool bwd_mfma_supported(const FwdArgs& a, int dtype) {
     return (dtype == kBF16 || dtype == kF16) && (a.D == 64 || a.D == 128) && !a.seq_bounds && !a.row_pos &&

@@ -802,15 +802,22 @@ int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const 
         if (ws_bytes < need)
             return fail(MFA_ERROR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
     }
-    const mfa::FwdArgs a = make_args(c);
+    mfa::FwdArgs a = make_args(c);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // With dropout the dK/dV kernel can store the keep bits for the dQ kernel,
+    // behind Delta in the workspace: in the pool's, or in a caller's that has
+    // room for them (up to 4 GiB; otherwise each kernel evaluates its own).
+    size_t keep = mfa::bwd_keep_bits_bytes(a, dtype);
+    if (keep > ((size_t)4 << 30) || (!use_pool && ws_bytes < need + keep)) keep = 0;
+    const size_t total = need + keep;
     void* ws = workspace;
-    if (use_pool && need > 0) {
-        const int pst = pool_alloc(&ws, need, s);
+    if (use_pool && total > 0) {
+        const int pst = pool_alloc(&ws, total, s);
         if (pst != MFA_SUCCESS) return pst;
     }
+    if (keep > 0) a.keep_bits = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + need);
     hipError_t e = mfa::launch_backward(a, dout, static_cast<float*>(ws), dq, dk, dv, dtype, s);
-    if (use_pool && need > 0) {
+    if (use_pool && total > 0) {
         hipError_t e2 = hipFreeAsync(ws, s);
         if (e == hipSuccess) e = e2;
     }

@@ -44,6 +44,11 @@ struct FwdArgs {
     uint32_t drop_threshold;
     float drop_scale;
     uint64_t drop_seed;
+    // backward with dropout: the keep bits of every 16-key block, uint16
+    // [B, Hq, ceil(Lk / 16), Lq] (bit f: key 16 jb + f of row i), written by the
+    // dK/dV kernel and read by the dQ kernel that runs after it; null: each
+    // kernel evaluates the blocks it needs
+    uint16_t* keep_bits;
     // MFMA prefill only: each 32-bit word of the Q operand is replaced by
     // (word ^ q_xor) & ~q_clear when it is loaded (sign flip or zeroing of
     // the 16-bit elements), set by its launcher for a scale <= 0
@@ -174,6 +179,10 @@ hipError_t launch_backward(const FwdArgs& a, const void* dout, float* delta, voi
 // The matrix-core backward (fp16/bf16, D 64/128, plain batches, any additive
 // mask and dropout); delta must already hold <dO, O> per row.
 bool bwd_mfma_supported(const FwdArgs& a, int dtype);
+// Bytes of a.keep_bits for this call (0 when its kernels do not share them:
+// no dropout, or not the 16-key dK/dV kernel, which serves D = 128 without a
+// soft-cap on the matrix cores).
+size_t bwd_keep_bits_bytes(const FwdArgs& a, int dtype);
 hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                                 int dtype, hipStream_t s);
 hipError_t launch_mfma_prefill(const FwdArgs& a, int dtype, hipStream_t s);
