@@ -809,12 +809,17 @@ int mfa_bwd(const void* q, const void* k, const void* v, const void* out, const 
     // room for them (up to 4 GiB; otherwise each kernel evaluates its own).
     size_t keep = mfa::bwd_keep_bits_bytes(a, dtype);
     if (keep > ((size_t)4 << 30) || (!use_pool && ws_bytes < need + keep)) keep = 0;
-    const size_t total = need + keep;
     void* ws = workspace;
-    if (use_pool && total > 0) {
-        const int pst = pool_alloc(&ws, total, s);
+    if (use_pool && need + keep > 0) {
+        int pst = pool_alloc(&ws, need + keep, s);
+        if (pst == MFA_ERROR_OUT_OF_MEMORY && keep > 0) {   // without room for the pattern
+            g_last_error.clear();
+            keep = 0;
+            pst = pool_alloc(&ws, need, s);
+        }
         if (pst != MFA_SUCCESS) return pst;
     }
+    const size_t total = need + keep;
     if (keep > 0) a.keep_bits = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + need);
     hipError_t e = mfa::launch_backward(a, dout, static_cast<float*>(ws), dq, dk, dv, dtype, s);
     if (use_pool && total > 0) {
