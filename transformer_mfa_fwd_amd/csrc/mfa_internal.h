@@ -109,13 +109,25 @@ __host__ __device__ inline void row_key_range(const FwdArgs& a, int i, int& lo, 
 // products with the round constants, the halves mixed with the other counter
 // words and the key, the key bumped by the Weyl constants.  c0..c3 in: the
 // counter; out: the block.
+// The 128-bit product of the 64-bit words m and c as four 32 x 32 + 64-bit
+// multiply-adds (each partial sum fits 64 bits) and one 64-bit add.
+__device__ inline void mul64_wide(uint64_t m, uint64_t c, uint64_t& hi, uint64_t& lo) {
+    const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32), cl = (uint32_t)c, ch = (uint32_t)(c >> 32);
+    const uint64_t t0 = (uint64_t)ml * cl;
+    const uint64_t t1 = (uint64_t)ml * ch + (t0 >> 32);
+    const uint64_t t2 = (uint64_t)mh * cl + (uint32_t)t1;
+    hi = (uint64_t)mh * ch + (t1 >> 32) + (t2 >> 32);
+    lo = (t2 << 32) | (uint32_t)t0;
+}
+
 __device__ inline void philox4x64(uint64_t& c0, uint64_t& c1, uint64_t& c2, uint64_t& c3, uint64_t k0,
                                   uint64_t k1) {
     const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        uint64_t hi0, lo0, hi1, lo1;
+        mul64_wide(M0, c0, hi0, lo0);
+        mul64_wide(M1, c2, hi1, lo1);
         c0 = hi1 ^ c1 ^ k0;
         c1 = lo1;
         c2 = hi0 ^ c3 ^ k1;
