@@ -129,9 +129,12 @@ __device__ inline float logit2_minus(const FwdArgs& a, float dot, float lse2, fl
 }
 
 
-// dQ of calls without an additive mask or dropout (two workgroups per CU but
-// with a soft-cap at D = 128).
-template <typename T, int D, bool CAP>
+// dQ (two workgroups per CU but with a soft-cap at D = 128).  EXTRA: with an
+// additive mask whose keys are contiguous (copied into LDS straight from
+// global memory, one 128-row x 32-key tile ahead) and dropout whose pattern
+// the dK/dV kernel stored; other mask or dropout calls take the pipelined
+// kernel below.
+template <typename T, int D, bool CAP, bool EXTRA>
 __global__ __launch_bounds__(256, (CAP && D == 128) ? 1 : 2) void bwd_dq_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
                                                              const float* __restrict__ delta, T* __restrict__ dq) {
     typedef typename Mfma<T>::v8 v8;
@@ -139,6 +142,9 @@ __global__ __launch_bounds__(256, (CAP && D == 128) ? 1 : 2) void bwd_dq_mfma_ke
     __shared__ __attribute__((aligned(16))) char sK[BwLds<D>::TILE];
     __shared__ __attribute__((aligned(16))) char sV[BwLds<D>::TILE];
     __shared__ float sM[32];   // 1: key kept (in range of the axis and of the key mask)
+    // EXTRA: the additive mask of the tile's 128 rows x 32 keys, two buffers;
+    // 16-byte chunk c of row r at chunk c ^ ((r / 2) % 8) of its 128-byte row
+    __shared__ __attribute__((aligned(16))) float sB[EXTRA ? 2 : 1][EXTRA ? 128 * 32 : 4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     // grid (Hq, B, query blocks), the latest query block first: under a causal
@@ -170,6 +176,38 @@ __global__ __launch_bounds__(256, (CAP && D == 128) ? 1 : 2) void bwd_dq_mfma_ke
     int lo_blk, t0, t1, hi_blk;
     row_key_range<false>(a, i0, lo_blk, t0);
     row_key_range<false>(a, i_last, t1, hi_blk);
+    // EXTRA: this (batch, query head)'s additive mask as a buffer of its whole
+    // extent (copies past it read zeros), and the stored dropout pattern
+    const float* bhead = nullptr;
+    int bbytes = 0;
+    if (EXTRA && a.bias) {
+        bhead = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1];
+        bbytes = (int)(((int64_t)(a.Lq - 1) * a.bias_stride[2] + a.Lk) * 4);
+    }
+    const int njb = (a.Lk + 15) >> 4;
+    const uint16_t* keep_row = (EXTRA && a.drop_scale > 0.0f)
+                                   ? a.keep_bits + ((int64_t)b * a.Hq + hq) * njb * a.Lq + rowc
+                                   : nullptr;
+    // copy of tile TL's mask into buffer BB: slot 256 j + tid holds row s / 8,
+    // chunk (s % 8) ^ ((row / 2) % 8)
+    auto bias_copy = [&](int TL, int BB) {
+        if constexpr (EXTRA) {
+            if (bhead) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int sl = 256 * j + tid, r = sl >> 3, c = (sl & 7) ^ ((r >> 1) & 7);
+                    const int64_t off = ((int64_t)(i0 + r) * a.bias_stride[2] + 32 * TL + 4 * c) * 4;
+                    buffer_copy16_to_lds(bhead, bbytes, &sB[BB][(256 * j + 64 * wave) * 4],
+                                         off < bbytes ? (uint32_t)off : (uint32_t)bbytes);
+                }
+            }
+        }
+    };
+    // the pattern words of this lane's row for tile TL: block 2 TL + h
+    auto keep_load = [&](int TL) -> uint32_t {
+        const int jb = 2 * TL + h;
+        return (keep_row && row <= i_last && jb < njb) ? (uint32_t)keep_row[(int64_t)jb * a.Lq] : 0u;
+    };
 
     f32x16_t acc[NDB];
 #pragma unroll
@@ -194,14 +232,46 @@ __global__ __launch_bounds__(256, (CAP && D == 128) ? 1 : 2) void bwd_dq_mfma_ke
             }
         };
         fetch(t_first);
+        bias_copy(t_first, 0);
+        uint32_t kw_next = EXTRA ? keep_load(t_first) : 0u;
         for (int t = t_first; t < t_end; ++t) {
-            const int k0 = 32 * t;
+            const int k0 = 32 * t, bb = (t - t_first) & 1;
             __syncthreads();   // the previous tile is no longer read
             store_tile<D>(sK, rk, tid);
             store_tile<D>(sV, rv, tid);
             if (tid < 32) sM[tid] = rm;
+            if constexpr (EXTRA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's mask copies
             __syncthreads();
-            if (t + 1 < t_end) fetch(t + 1);   // in flight during this tile's products
+            const uint32_t kw = kw_next;
+            if (t + 1 < t_end) {   // in flight during this tile's products
+                fetch(t + 1);
+                bias_copy(t + 1, bb ^ 1);
+                if constexpr (EXTRA) kw_next = keep_load(t + 1);
+            }
+            // EXTRA: mask values and dropout keep bits of this lane's 16 scores
+            // (score 4 G + e is key k0 + 8 G + 4 h + e); the tile's two 16-key
+            // pattern words of this row are shared by lanes l and l ^ 32
+            float bv[EXTRA ? 16 : 1];
+            uint32_t keepm = 0xffffu;
+            if constexpr (EXTRA) {
+                if (bhead) {
+                    const int rr = 32 * wave + (lane & 31);
+#pragma unroll
+                    for (int G = 0; G < 4; ++G) {
+                        const float4 f = *reinterpret_cast<const float4*>(&sB[bb][(rr * 8 + ((2 * G + h) ^ ((rr >> 1) & 7))) * 4]);
+                        bv[4 * G] = f.x; bv[4 * G + 1] = f.y; bv[4 * G + 2] = f.z; bv[4 * G + 3] = f.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) bv[r] = 0.0f;
+                }
+                if (keep_row) {
+                    const uint32_t oth = (uint32_t)__shfl_xor((int)kw, 32);
+                    const uint32_t m32 = h ? (oth | (kw << 16)) : (kw | (oth << 16));   // keys 0 .. 31
+                    keepm = pack_even_nibbles(m32 >> (4 * h));
+                }
+            }
+            (void)bv; (void)kw;
             f32x16_t s = {}, dp = {};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -216,9 +286,14 @@ __global__ __launch_bounds__(256, (CAP && D == 128) ? 1 : 2) void bwd_dq_mfma_ke
                 // (a select on the logit, not a branch around the arithmetic)
                 float dl;
                 float x = logit2_minus<CAP>(a, s[r], lse2, dl);
+                float dpz = dp[r];
+                if constexpr (EXTRA) {
+                    x = fmaf(bv[r], BW_LOG2E, x);
+                    if (a.drop_scale > 0.0f) dpz = (keepm >> r) & 1u ? dpz * a.drop_scale : 0.0f;
+                }
                 x = ((key >= rlo) & (key <= rhi) & (sM[kk] != 0.0f)) ? x : -INFINITY;   // & : no short circuit
                 const float p = fast_exp2(x);
-                s[r] = CAP ? p * (dp[r] - dlt) * dl : p * (dp[r] - dlt);
+                s[r] = CAP ? p * (dpz - dlt) * dl : p * (dpz - dlt);
             }
 #pragma unroll
             for (int sx = 0; sx < 2; ++sx) {
@@ -1088,12 +1163,18 @@ hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* de
                            s, a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.Lq <= 0) return e;
-    if constexpr (EXTRA)
+    // the unpipelined dQ kernel keeps two workgroups per CU; with a mask or
+    // dropout it needs the mask's keys contiguous (copied 16 bytes at a time,
+    // offsets within 32 bits) and the stored dropout pattern
+    const bool direct = !EXTRA || ((!a.bias || (a.bias_stride[3] == 1 &&
+                                                ((int64_t)(a.Lq - 1) * a.bias_stride[2] + a.Lk) * 4 < ((int64_t)1 << 31))) &&
+                                   (!(a.drop_scale > 0.0f) || a.keep_bits));
+    if (EXTRA && !direct)
         hipLaunchKernelGGL((bwd_dq_pipe_mfma_kernel<T, D, CAP, true>), dim3(a.Hq, a.B, (a.Lq + 127) / 128),
                            dim3(256), 0, s, a, g, delta, static_cast<T*>(dq));
     else
-        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0, s,
-                           a, g, delta, static_cast<T*>(dq));
+        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hq, a.B, (a.Lq + 127) / 128), dim3(256), 0,
+                           s, a, g, delta, static_cast<T*>(dq));
     return hipGetLastError();
 }
 
