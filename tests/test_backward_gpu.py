@@ -81,6 +81,21 @@ def test_backward_with_bias_and_dropout(dtype, D):
                          softcap=6.0, mask="random_frac", mask_frac=0.2)
         run_case(wc, bias_shape=(1, 1, 1, 1), p=0.1, seed=77)
         run_case(wc, bias_shape=(1, 0, 0, 1), p=0.9, seed=5)
+        if not (dtype == "bf16" and D == 64):   # that one: test_bf16_cap_mask_delta_from_rounded_o
+            run_case(wc, bias_shape=(1, 1, 1, 1), p=0.0)   # cap and mask alone: the unpipelined dQ kernel
+
+
+@pytest.mark.xfail(strict=True, reason="known: Delta = <dO, O> from the bf16-rounded O the forward hands over "
+                                       "moves dQ by 1.8e-2 here, past the 1e-2 bound against the exact gradient")
+def test_bf16_cap_mask_delta_from_rounded_o():
+    """bf16, D = 64, soft-cap 6, full additive mask, key mask, no dropout:
+    dQ differs from the exact gradient by 1.84e-2 at one element (bound
+    1.01e-2), the same on every kernel path and with dS carried as two bf16
+    operands: the difference comes from Delta, which the backward computes
+    from the rounded O it is given (fp16 O, 8x finer, passes)."""
+    wc = wl.Workload("bwd_bias_drop_cap_mask_bf16_D64", "bf16", 2, 100, 130, 4, 1, 64, False, window=70,
+                     softcap=6.0, mask="random_frac", mask_frac=0.2)
+    run_case(wc, bias_shape=(1, 1, 1, 1), p=0.0)
 
 
 MASKED = [w for w in CASES if w.mask is not None]
