@@ -840,14 +840,14 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
     }
 }
 
-// dK and dV at D = 128: 16 keys per wave on 16x16x32 MFMAs, eight waves (128
-// keys) per workgroup.  The accumulators
-// of 16 keys (2 x 32 registers) and their K and V operands (2 x 16) leave two
-// waves per SIMD, where the 32-key kernel above runs one.  Per 32-row step:
+// dK and dV: 16 keys per wave on 16x16x32 MFMAs, D / 16 waves (D keys) per
+// workgroup.  At D = 128 the accumulators of 16 keys (2 x 32 registers) and
+// their K and V operands (2 x 16) leave two waves per SIMD, where the 32-key
+// kernel above runs one; at D = 64 (half of each) three.  Per 32-row step:
 //   S  [32 rows x 16 keys] = Q  . K^T   (A: Q rows from LDS, B: K in registers)
 //   dP [32 rows x 16 keys] = dO . V^T
-//   dV^T [128 x 16 keys] += dO^T . P    (A: transposing LDS reads, B: P itself)
-//   dK^T [128 x 16 keys] += Q^T . dS
+//   dV^T [D x 16 keys] += dO^T . P      (A: transposing LDS reads, B: P itself)
+//   dK^T [D x 16 keys] += Q^T . dS
 // The products' k index e of lane group g (rows 8 g + e of the MFMA) is tile
 // row 4 g + e for e < 4 and 16 + 4 g + e - 4 after: the rows that score
 // elements (block 0, i) and (block 1, i) of the lane hold, so the packed
@@ -855,19 +855,24 @@ __global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_
 // Q take the same two groups of four rows.  Two LDS buffers: step u + 1 is
 // stored while step u computes, and its global reads were issued a step
 // earlier.
-template <typename T, bool CAP, bool EXTRA>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* __restrict__ dout,
+template <typename T, int D, bool CAP, bool EXTRA>
+__global__ __launch_bounds__(4 * D, D == 128 ? 1 : ((CAP || EXTRA) ? 2 : 3)) void bwd_dkdv16_kernel(FwdArgs a, const T* __restrict__ dout,
                                                            const float* __restrict__ delta, T* __restrict__ dk,
                                                            T* __restrict__ dv) {
     typedef typename Mfma<T>::v8 v8;
-    constexpr int D = 128, NKS = D / 32, NDB = D / 16, CPR = D / 8;
+    constexpr int NKS = D / 32, NDB = D / 16, CPR = D / 8, KW = D;   // KW: keys per workgroup
     typedef BwLds<D> L;
-    // 16-byte chunk c of row r sits at chunk c ^ swz(r), swz(r) = 4 (r % 4) +
-    // the two bits of (r / 4) % 4 swapped: a permutation over any 16
-    // consecutive rows (the row reads), and the transposing reads of lane
+    // where 16-byte chunk c of row r sits.  D = 128: at c ^ swz(r), swz(r) =
+    // 4 (r % 4) + the two bits of (r / 4) % 4 swapped, a permutation over any
+    // 16 consecutive rows (the row reads), and the transposing reads of lane
     // groups 0 and 1 (rows 0..7 at two chunks) land on 16 different chunks, as
-    // do those of groups 2 and 3
-    auto swz = [](int r) { return ((r & 3) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1); };
+    // do those of groups 2 and 3.  D = 64 (8 chunks a row): c rotated right by
+    // one bit, then xor (r / 2) % 8; found, like the D = 128 order, by
+    // counting bank conflicts of both read patterns over candidate layouts
+    auto pch = [](int r, int c) {
+        if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1));
+        else return (((c & 1) << 2) | (c >> 1)) ^ ((r >> 1) & 7);
+    };
     constexpr int NBUF = 3;
     __shared__ __attribute__((aligned(16))) char sQ[NBUF][L::TILE];
     __shared__ __attribute__((aligned(16))) char sG[NBUF][L::TILE];   // dO rows
@@ -879,14 +884,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int kvh = blockIdx.x, b = blockIdx.y;
-    const int j0 = blockIdx.z * 128, j_last = min(j0 + 127, a.Lk - 1);
+    const int j0 = blockIdx.z * KW, j_last = min(j0 + KW - 1, a.Lk - 1);
     const int key = j0 + 16 * wave + col;   // this lane's key (MFMA column)
     const int keyc = key <= j_last ? key : j_last;
     const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
     const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
 
-    // B operands: at k-step ks lane l holds K and V of its key at d = 32 g +
-    // 8 ks .. +7 (the A operands read the same d: any order of d within the
+    // B operands: at k-step ks lane l holds K and V of its key at d = (D / 4) g
+    // + 8 ks .. +7 (the A operands read the same d: any order of d within the
     // products gives the same sums, and this one keeps the row reads free of
     // LDS bank conflicts); a masked key's rows stay zero (whatever they hold
     // cannot reach a gradient)
@@ -895,8 +900,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
     v8 kop[NKS], vop[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-        u32x4_t kx = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)keyc * a.kv_stride + 32 * grp + 8 * ks);
-        u32x4_t vx = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)keyc * a.kv_stride + 32 * grp + 8 * ks);
+        u32x4_t kx = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)keyc * a.kv_stride + (D / 4) * grp + 8 * ks);
+        u32x4_t vx = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)keyc * a.kv_stride + (D / 4) * grp + 8 * ks);
         if (!mask_ok) kx = vx = u32x4_t{0u, 0u, 0u, 0u};
         kop[ks] = bitcast<v8>(kx);
         vop[ks] = bitcast<v8>(vx);
@@ -961,14 +966,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
         }
     };
     auto store = [&](int buf) {
-        *reinterpret_cast<u32x4_t*>(sQ[buf] + fr * L::RS + (fk ^ swz(fr)) * 16) = rq;
-        *reinterpret_cast<u32x4_t*>(sG[buf] + fr * L::RS + (fk ^ swz(fr)) * 16) = rg;
+        *reinterpret_cast<u32x4_t*>(sQ[buf] + fr * L::RS + pch(fr, fk) * 16) = rq;
+        *reinterpret_cast<u32x4_t*>(sG[buf] + fr * L::RS + pch(fr, fk) * 16) = rg;
         if (tid < 32) { sLo[buf][tid] = rlo_; sHi[buf][tid] = rhi_; sL[buf][tid] = rl_; sD[buf][tid] = rd_; }
     };
-    // A operand of S / dP: row 16 blk + (l % 16) at d = 32 g + 8 ks .. +7
+    // A operand of S / dP: row 16 blk + (l % 16) at d = (D / 4) g + 8 ks .. +7
     auto rows16 = [&](const char* tile, int blk, int ks) {
         const int r = 16 * blk + col;
-        return bitcast<v8>(*reinterpret_cast<const u32x4_t*>(tile + r * L::RS + (((4 * grp + ks) ^ swz(r)) * 16)));
+        return bitcast<v8>(*reinterpret_cast<const u32x4_t*>(tile + r * L::RS + pch(r, NKS * grp + ks) * 16));
     };
     // A operand of dV / dK: the tile transposed, d = 16 db + (l % 16) at rows
     // 4 g + e and 16 + 4 g + e (e = 0..3); source lane j points at row 4 g +
@@ -976,8 +981,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
     const int tr_r0 = 4 * grp + (col >> 2), tr_c = (col & 3) >> 1, tr_h = (col & 1) * 8;
     auto cols16 = [&](const char* tile, int db) {
         const int c = 2 * db + tr_c;
-        const i16x4_t lo = lds_read_tr16(tile + tr_r0 * L::RS + ((c ^ swz(tr_r0)) * 16) + tr_h);
-        const i16x4_t hi = lds_read_tr16(tile + (tr_r0 + 16) * L::RS + ((c ^ swz(tr_r0 + 16)) * 16) + tr_h);
+        const i16x4_t lo = lds_read_tr16(tile + tr_r0 * L::RS + pch(tr_r0, c) * 16 + tr_h);
+        const i16x4_t hi = lds_read_tr16(tile + (tr_r0 + 16) * L::RS + pch(tr_r0 + 16, c) * 16 + tr_h);
         const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return bitcast<v8>(v);
     };
@@ -1010,19 +1015,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
             const int bn = buf == 2 ? 0 : buf + 1, bn2 = bn == 2 ? 0 : bn + 1;   // steps it + 1, it + 2
             if (it + 2 < nsteps) store(bn2);   // its buffer was last read by step it - 1
             if (it + 3 < nsteps) fetch(it + 3);
-            // The step in 32 slots of one MFMA each, in a fixed order
+            // The step in NSD + NC slots of one MFMA each, in a fixed order
             // (scheduling barriers between them), every LDS operand read LA
-            // slots before its MFMA.  Slots 0..15: S and dP of step it + 1
+            // slots before its MFMA.  Slots 0..NSD-1: S and dP of step it + 1
             // (after the last step they read a stale buffer and are discarded),
-            // with the softmax of step it, one score per odd slot.  Slots
-            // 16..31: dV and dK of step it.
+            // with the softmax of step it, one score every SPS slots.  The NC
+            // slots after them: dV and dK of step it.
+            constexpr int NSD = 4 * NKS, NC = 2 * NDB, SPS = NSD / 8;
             constexpr int LA = EXTRA ? 3 : 4;   // (the mask and dropout registers leave room for three)
-            // operand m of slots 0..15: block m / 8, k-step (m / 2) % 4, Q (m
-            // even) or dO rows; operand n of slots 16..31: d block n / 2 of dO^T
-            // (n even, dV) or Q^T
-            auto read_a = [&](int m) { return rows16((m & 1) ? sG[bn] : sQ[bn], m >> 3, (m >> 1) & 3); };
+            // operand m of the first slots: block m / (2 NKS), k-step (m / 2) %
+            // NKS, Q (m even) or dO rows; operand n of the others: d block n / 2
+            // of dO^T (n even, dV) or Q^T
+            auto read_a = [&](int m) { return rows16((m & 1) ? sG[bn] : sQ[bn], m / (2 * NKS), (m >> 1) % NKS); };
             auto read_c = [&](int n) { return cols16((n & 1) ? sQ[buf] : sG[buf], n >> 1); };
-            v8 opa[16], opc[16];
+            v8 opa[NSD], opc[NC];
             f32x4_t sn[2], dn[2];
             sn[0] = sn[1] = dn[0] = dn[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             float p[8], ds[8];
@@ -1090,16 +1096,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
             for (int m = 0; m < LA; ++m) opa[m] = read_a(m);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                if (m + LA < 16) opa[m + LA] = read_a(m + LA);
-                else opc[m + LA - 16] = read_c(m + LA - 16);
-                const int blk = m >> 3, ks = (m >> 1) & 3;
+            for (int m = 0; m < NSD; ++m) {
+                if (m + LA < NSD) opa[m + LA] = read_a(m + LA);
+                else opc[m + LA - NSD] = read_c(m + LA - NSD);
+                const int blk = m / (2 * NKS), ks = (m >> 1) % NKS;
                 if (m & 1) dn[blk] = Mfma<T>::mma16(opa[m], vop[ks], dn[blk]);
                 else sn[blk] = Mfma<T>::mma16(opa[m], kop[ks], sn[blk]);
-                if (m & 1) {
-                    // score e = m / 2: row 16 (e / 4) + 4 g + e % 4 at this lane's key;
+                if (m % SPS == SPS - 1) {
+                    // score e = m / SPS: row 16 (e / 4) + 4 g + e % 4 at this lane's key;
                     // a hidden score's logit becomes -inf, so its weight is exactly 0
-                    const int e = m >> 1, eb = e >> 2, i = e & 3;
+                    const int e = m / SPS, eb = e >> 2, i = e & 3;
                     float dl;
                     float x = logit2_minus<CAP>(a, sc[eb][i], ls[i], dl);
                     float z = 1.0f;
@@ -1115,13 +1121,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16_kernel(FwdArgs a, const T* 
                     const float dz = EXTRA ? dc[eb][i] * z : dc[eb][i];
                     ds[e] = CAP ? pe * (dz - dd[i]) * dl : pe * (dz - dd[i]);
                 }
-                if (m == 7) read_rows(1);   // block 0's row data is used up by this slot's score
+                if (m == 4 * SPS - 1) read_rows(1);   // block 0's row data is used up by this slot's score
                 __builtin_amdgcn_sched_barrier(0);
             }
             const v8 pop = pack8<T>(p), dop = pack8<T>(ds);
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                if (n + LA < 16) opc[n + LA] = read_c(n + LA);
+            for (int n = 0; n < NC; ++n) {
+                if (n + LA < NC) opc[n + LA] = read_c(n + LA);
                 if (n & 1) dka[n >> 1] = Mfma<T>::mma16(opc[n], dop, dka[n >> 1]);
                 else dva[n >> 1] = Mfma<T>::mma16(opc[n], pop, dva[n >> 1]);
                 __builtin_amdgcn_sched_barrier(0);
@@ -1158,12 +1164,8 @@ hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* de
     // the dQ kernel then reads (same stream).  (With both a cap and a mask or
     // dropout the 16-key kernel spills a few values and is still faster than
     // the 32-key one: 2.50 -> 2.04 ms on the causal GQA shape.)
-    if constexpr (D == 128)
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(512), 0, s,
-                           a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
-    else
-        hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + 127) / 128), dim3(256), 0,
-                           s, a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + D - 1) / D), dim3(4 * D), 0, s,
+                       a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.Lq <= 0) return e;
     // the unpipelined dQ kernel keeps two workgroups per CU; with a mask or
@@ -1210,7 +1212,7 @@ size_t bwd_keep_bits_bytes(const FwdArgs& a, int dtype) {
 
 bool bwd_mfma_supported(const FwdArgs& a, int dtype) {
     return (dtype == kBF16 || dtype == kF16) && (a.D == 64 || a.D == 128) && !a.seq_bounds && !a.row_pos &&
-           (a.Lq + 127) / 128 <= 65535 && (a.Lk + 127) / 128 <= 65535;   // grid z
+           (a.Lq + 127) / 128 <= 65535 && (a.Lk + a.D - 1) / a.D <= 65535;   // grid z
 }
 
 hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
