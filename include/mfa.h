@@ -173,7 +173,8 @@ int mfa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* out,
  * accumulation); the others in fp32 arithmetic.  The
  * workspace holds Delta: caller-owned (256-byte
  * aligned, at least mfa_bwd_workspace_size bytes) or NULL with ws_bytes = 0
- * for the stream-ordered pool.  With dropout on the matrix cores at D = 128,
+ * for the stream-ordered pool.  With dropout on the matrix cores (fp16 and
+ * bf16, D = 64 or 128),
  * a workspace with room for another
  * 2 * B * Hq * ceil(Lk / 16) * Lq bytes after those (up to 4 GiB; the pool
  * always gives it) also holds the dropout pattern, evaluated once by the

@@ -106,15 +106,16 @@ def test_dropout_seed_uses_its_low_32_bits(dtype):
     assert all(torch.equal(x, y) for x, y in zip(*grads))
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("with_bias", [False, True])
-def test_backward_dropout_pattern_shared_or_not(dtype, with_bias):
-    """With dropout at D = 128 the dK/dV kernel may store the pattern for the
-    dQ kernel (the pool's workspace, or a caller's with room for it) or each
-    kernel evaluates it (a caller workspace of exactly the Delta size): the
-    gradients are bitwise the same.  Ragged sizes (Lk not a multiple of 16 or
-    of 128, several query heads per kv head)."""
-    w = wl.Workload(f"bd_share_{dtype}", dtype, 2, 150, 203, 4, 2, 128, True, window=120)
+def test_backward_dropout_pattern_shared_or_not(dtype, with_bias, D):
+    """With dropout on the matrix cores the dK/dV kernel may store the pattern
+    for the dQ kernel (the pool's workspace, or a caller's with room for it) or
+    each kernel evaluates it (a caller workspace of exactly the Delta size):
+    the gradients are bitwise the same.  Ragged sizes (Lk not a multiple of 16
+    or of the D keys of a dK/dV workgroup, several query heads per kv head)."""
+    w = wl.Workload(f"bd_share_{dtype}_d{D}", dtype, 2, 150, 203, 4, 2, D, True, window=120)
     q, k, v, _ = wl.make_inputs(w, DEV)
     bias = bias_tensor((1, 1, w.Lq, w.Lk), seed=3).to(DEV) if with_bias else None
     say(f"{w.name} bias={with_bias} shared vs evaluated dropout pattern")

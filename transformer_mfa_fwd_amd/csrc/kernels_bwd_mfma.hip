@@ -1204,7 +1204,7 @@ hipError_t launch_bwd_mfma_d(const FwdArgs& a, const void* dout, const float* de
 }  // namespace
 
 size_t bwd_keep_bits_bytes(const FwdArgs& a, int dtype) {
-    if (!(a.drop_scale > 0.0f) || a.D != 128 || !bwd_mfma_supported(a, dtype) || a.B <= 0 ||
+    if (!(a.drop_scale > 0.0f) || !bwd_mfma_supported(a, dtype) || a.B <= 0 ||
         a.Lq <= 0 || a.Lk <= 0)
         return 0;
     return (size_t)a.B * a.Hq * ((a.Lk + 15) / 16) * a.Lq * sizeof(uint16_t);

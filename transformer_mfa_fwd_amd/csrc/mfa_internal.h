@@ -192,8 +192,8 @@ hipError_t launch_backward(const FwdArgs& a, const void* dout, float* delta, voi
 // mask and dropout); delta must already hold <dO, O> per row.
 bool bwd_mfma_supported(const FwdArgs& a, int dtype);
 // Bytes of a.keep_bits for this call (0 when its kernels do not share them:
-// no dropout, or not the 16-key dK/dV kernel, which serves D = 128 on the
-// matrix cores).
+// no dropout, or not the matrix-core backward, whose 16-key dK/dV kernel
+// evaluates the pattern that its dQ kernel then reads).
 size_t bwd_keep_bits_bytes(const FwdArgs& a, int dtype);
 hipError_t launch_backward_mfma(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                                 int dtype, hipStream_t s);
