@@ -6,25 +6,27 @@
 // dS = P (Z dO V^T - Delta) * d s / d<Q, K>, dQ = dS K, dK = dS^T Q,
 // dV = (P Z)^T dO, with Z the dropout factors (keep / (1 - p), or 1) and the
 // additive mask inside s.
-// Every product is a 32x32x16 MFMA with fp32 accumulation; P and dS are
-// rounded to the input type to serve as operands, as the forward rounds P.
+// The dQ products are 32x32x16 MFMAs, the dK/dV products 16x16x32, all with
+// fp32 accumulation; P and dS are rounded to the input type to serve as
+// operands, as the forward rounds P.
 //
 //   bwd_dq_mfma_kernel    one wave per 32 query rows, walking 32-key tiles:
 //       S^T  = K Q^T    (K rows from LDS, Q^T in registers)
 //       dP^T = V dO^T   (V rows from LDS, dO^T in registers)
 //       dQ^T += K^T dS^T (K^T by transposing LDS reads, dS^T straight from the
 //                         accumulator of S^T)
-//   bwd_dkdv_mfma_kernel  one wave per 32 keys, walking the 32-row query tiles
+//   bwd_dkdv16_kernel     one wave per 16 keys, walking the 32-row query tiles
 //                         of every query head of its GQA group:
 //       S  = Q K^T      (Q rows from LDS, K^T in registers)
 //       dP = dO V^T
 //       dV^T += dO^T P,  dK^T += Q^T dS   (transposing LDS reads of dO and Q)
-// An accumulator's 16 elements per lane serve as the B operand of the next
+// An accumulator's elements per lane serve as the B operand of the next
 // product in the order the transposing reads deliver the A operand's rows, so
 // no score crosses lanes.  Each gradient element has one writer (no atomics).
-// The dK/dV kernel, and the dQ kernel of calls with a mask or dropout
-// (bwd_dq_pipe_mfma_kernel), run a software pipeline: the next tile's S and dP
-// MFMAs beside the current tile's softmax, over three LDS buffers.
+// The dK/dV kernel, and the dQ kernel of calls whose mask cannot be copied
+// whole or whose dropout pattern is not stored (bwd_dq_pipe_mfma_kernel), run
+// a software pipeline: the next tile's S and dP MFMAs beside the current
+// tile's softmax, over three LDS buffers.
 #include "mfa_device.h"
 #include "mfa_internal.h"
 
@@ -556,294 +558,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_pipe_mfma_kernel(FwdArgs a, con
     }
 }
 
-// 32 gradient accumulator registers per d block (dK and dV) plus K and V in
-// registers: one workgroup per CU at D = 128.
-template <typename T, int D, bool CAP, bool EXTRA>
-__global__ __launch_bounds__(256, (D == 64 && !EXTRA && !CAP) ? 2 : 1) void bwd_dkdv_mfma_kernel(FwdArgs a, const T* __restrict__ dout,
-                                                               const float* __restrict__ delta, T* __restrict__ dk,
-                                                               T* __restrict__ dv) {
-    typedef typename Mfma<T>::v8 v8;
-    constexpr int NKS = D / 16, NDB = D / 32;
-    // Three buffers of the per-step data: the Q and dO tiles, and the LSE (base
-    // 2), Delta and key range of their rows.  Step u lives in buffer u % 3: it
-    // is stored two steps ahead, its S and dP are formed one step ahead, and its
-    // softmax and dV/dK products run in its own step.
-    constexpr int NBUF = 3;
-    __shared__ __attribute__((aligned(16))) char sQ[NBUF][BwLds<D>::TILE];
-    __shared__ __attribute__((aligned(16))) char sG[NBUF][BwLds<D>::TILE];   // dO rows
-    __shared__ __attribute__((aligned(16))) float sL[NBUF][32];
-    __shared__ __attribute__((aligned(16))) float sD[NBUF][32];
-    __shared__ __attribute__((aligned(16))) int sLo[NBUF][32];
-    __shared__ __attribute__((aligned(16))) int sHi[NBUF][32];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-    // grid (Hkv, B, key blocks), the first key block first: under a causal mask
-    // the most query rows see it
-    const int kvh = blockIdx.x, b = blockIdx.y;
-    const int j0 = blockIdx.z * 128, j_last = min(j0 + 127, a.Lk - 1);
-    const int key = j0 + 32 * wave + (lane & 31);
-    const int keyc = key <= j_last ? key : j_last;
-    const T* kb = static_cast<const T*>(a.k) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
-    const T* vb = static_cast<const T*>(a.v) + (int64_t)b * a.Lk * a.kv_stride + (int64_t)kvh * D;
-
-    // a masked key's K and V rows stay zero (whatever they hold cannot reach a gradient)
-    const bool mask_ok = !a.key_mask || a.key_mask[(int64_t)b * a.Lk + keyc] > 0.5f;
-    const bool kept = key <= j_last && mask_ok;
-    v8 kop[NKS], vop[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        u32x4_t kx = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h);
-        u32x4_t vx = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)keyc * a.kv_stride + 16 * ks + 8 * h);
-        if (!mask_ok) kx = vx = u32x4_t{0u, 0u, 0u, 0u};
-        kop[ks] = bitcast<v8>(kx);
-        vop[ks] = bitcast<v8>(vx);
-    }
-
-    f32x16_t dka[NDB], dva[NDB];
-#pragma unroll
-    for (int mb = 0; mb < NDB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dka[mb][e] = dva[mb][e] = 0.0f;
-
-    // The 32-row query tiles that can see a key of this block form one run
-    // [qt_lo, qt_hi]: both ends of a row's (clipped) key range are
-    // nondecreasing in the row, so "the tile's last row's range ends at or
-    // after j0" turns true once and "its first row's range starts by j_last"
-    // turns false once.  A tile inside the run whose rows see none of the keys
-    // only costs time (every row still applies its own range).  Steps walk
-    // (query head, tile) over the run for every query head of the group.
-    const int nqt = (a.Lq + 31) / 32;
-    int qt_lo, qt_hi;
-    {
-        int lo = 0, hi = nqt;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            int l0, h0;
-            row_key_range<false>(a, min(32 * mid + 31, a.Lq - 1), l0, h0);
-            if (h0 >= j0) hi = mid; else lo = mid + 1;
-        }
-        qt_lo = lo;
-        hi = nqt;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            int l0, h0;
-            row_key_range<false>(a, 32 * mid, l0, h0);
-            if (l0 > j_last) hi = mid; else lo = mid + 1;
-        }
-        qt_hi = lo - 1;
-    }
-    const int nv = qt_hi >= qt_lo ? qt_hi - qt_lo + 1 : 0, nsteps = a.group * nv;
-
-    // step u -> (query head, first row): heads in order, the run's tiles in order
-    auto step_hq = [&](int u) { return kvh * a.group + u / nv; };
-    auto step_r0 = [&](int u) { return 32 * (qt_lo + u % nv); };
-
-    TileRegs<D> rq, rg;
-    int rlo_ = 1, rhi_ = 0;
-    float rl_ = 0.0f, rd_ = 0.0f;
-    // step u's Q and dO rows, and the LSE, Delta and key range of its rows, into registers
-    auto fetch = [&](int u) {
-        const int hq = step_hq(u), r0 = step_r0(u);
-        const T* qb = static_cast<const T*>(a.q) + (int64_t)b * a.Lq * a.q_stride + (int64_t)hq * D;
-        const T* gb = dout + (int64_t)b * a.Lq * a.o_stride + (int64_t)hq * D;
-        fetch_tile<T, D>(rq, qb + (int64_t)r0 * a.q_stride, a.q_stride, a.Lq - r0, tid);
-        fetch_tile<T, D>(rg, gb + (int64_t)r0 * a.o_stride, a.o_stride, a.Lq - r0, tid);
-        if (tid < 32) {
-            const int r = r0 + tid;
-            rlo_ = 1; rhi_ = 0; rl_ = 0.0f; rd_ = 0.0f;
-            if (r < a.Lq) {
-                row_key_range<false>(a, r, rlo_, rhi_);
-                const float l = a.lse[((int64_t)b * a.Hq + hq) * a.Lq + r];
-                if (l == -INFINITY) { rlo_ = 1; rhi_ = 0; }
-                rl_ = l == -INFINITY ? 0.0f : l * BW_LOG2E;   // finite: hidden logits are -inf
-                rd_ = delta[((int64_t)b * a.Hq + hq) * a.Lq + r];
-            }
-        }
-    };
-    // the fetched step into buffer BUF
-    auto store = [&](int buf) {
-        store_tile<D>(sQ[buf], rq, tid);
-        store_tile<D>(sG[buf], rg, tid);
-        if (tid < 32) { sLo[buf][tid] = rlo_; sHi[buf][tid] = rhi_; sL[buf][tid] = rl_; sD[buf][tid] = rd_; }
-    };
-
-    // S and dP of the step in buffer BUF: the MFMAs of k-step ks
-    auto sdp_mfma = [&](f32x16_t& sn, f32x16_t& dn, int buf, int ks) {
-        sn = Mfma<T>::mma32(rows_a<T, D>(sQ[buf], lane, 16 * ks), kop[ks], sn);
-        dn = Mfma<T>::mma32(rows_a<T, D>(sG[buf], lane, 16 * ks), vop[ks], dn);
-    };
-    // A operands of S and dP (Q and dO rows) of the step in buffer BUF, read
-    // early so that their LDS latency hides behind the softmax before them
-    v8 qa[NKS], ga[NKS];
-    auto read_sdp = [&](int buf) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qa[ks] = rows_a<T, D>(sQ[buf], lane, 16 * ks);
-            ga[ks] = rows_a<T, D>(sG[buf], lane, 16 * ks);
-        }
-    };
-
-    if (nsteps > 0) {
-        // prologue: steps 0 and 1 stored, step 2 fetched, S and dP of step 0
-        fetch(0);
-        store(0);
-        if (nsteps > 1) { fetch(1); store(1); }
-        if (nsteps > 2) fetch(2);
-        __syncthreads();
-        f32x16_t sc = {}, dc = {};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sdp_mfma(sc, dc, 0, ks);
-
-        int buf = 0;   // buffer of step it
-        for (int it = 0; it < nsteps; ++it) {
-            const int bn = buf == 2 ? 0 : buf + 1, bn2 = bn == 2 ? 0 : bn + 1;   // steps it + 1, it + 2
-            const int hq = step_hq(it), r0 = step_r0(it);
-            if constexpr (D == 128) read_sdp(bn);   // step it + 1 (stale after the last step; discarded)
-            // A operands of this step's dV and dK products, k-half 0 now and
-            // k-half 1 halfway through the softmax; at use where registers are
-            // short (D = 64 keeps two workgroups per CU without options, and the
-            // D = 128 variant with every option would spill)
-            constexpr bool EARLY = D == 128 && !(EXTRA && CAP);
-            v8 cg[2][NDB], cq[2][NDB];
-            if constexpr (EARLY) {
-#pragma unroll
-                for (int mb = 0; mb < NDB; ++mb) {
-                    cg[0][mb] = cols_a<T, D>(sG[buf], lane, 0, mb);
-                    cq[0][mb] = cols_a<T, D>(sQ[buf], lane, 0, mb);
-                }
-            }
-            if (it + 2 < nsteps) store(bn2);   // its buffer was last read by step it - 1
-            if (it + 3 < nsteps) fetch(it + 3);
-
-            // per-step extras of step it: additive mask values and dropout keep bits
-            float bv[EXTRA ? 16 : 1];
-            uint32_t keepm = 0xffffu;
-            if constexpr (EXTRA) {
-                if (a.bias) {
-                    const float* bk = a.bias + b * a.bias_stride[0] + hq * a.bias_stride[1] + (int64_t)keyc * a.bias_stride[3];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        bv[r] = row < a.Lq ? bk[(int64_t)row * a.bias_stride[2]] : 0.0f;
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) bv[r] = 0.0f;
-                }
-                // keep bits of this lane's 16 scores (rows 8 (r / 4) + 4 h + r % 4
-                // of the step, all at this lane's key).  The step's 32 rows and
-                // the wave's 32 keys make 64 16-key Philox blocks (row, key
-                // half): lane L evaluates the block of row L % 32 and key half
-                // L / 32, and each lane takes its bit of each of its rows' blocks
-                // from the lane that holds it.
-                if (a.drop_scale > 0.0f) {
-                    const int kb0 = (j0 + 32 * wave) >> 4;   // first key block of the wave
-                    const uint32_t m = dropout_keep16(a, b, hq, r0 + (lane & 31), kb0 + (lane >> 5));
-                    const int src_half = ((lane & 31) >> 4) * 32, bit = lane & 15;
-                    keepm = 0u;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int rho = 8 * (r >> 2) + 4 * h + (r & 3);
-                        const uint32_t ms = (uint32_t)__shfl((int)m, rho + src_half);
-                        keepm |= ((ms >> bit) & 1u) << r;
-                    }
-                }
-            }
-            (void)bv;
-
-            // S and dP of step it + 1 on the matrix cores, and beside them the
-            // softmax of step it: element r of lane l is tile row
-            // 8 (r / 4) + 4 h + r % 4 at this lane's key.  After the last step
-            // the products read a stale buffer and are discarded (no branch, so
-            // that the two interleave).
-            f32x16_t sn = {}, dn = {};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (EARLY && j == 2) {
-#pragma unroll
-                    for (int mb = 0; mb < NDB; ++mb) {
-                        cg[1][mb] = cols_a<T, D>(sG[buf], lane, 1, mb);
-                        cq[1][mb] = cols_a<T, D>(sQ[buf], lane, 1, mb);
-                    }
-                }
-                const int m0 = 8 * j + 4 * h;
-                const int4 lo4 = *reinterpret_cast<const int4*>(&sLo[buf][m0]);
-                const int4 hi4 = *reinterpret_cast<const int4*>(&sHi[buf][m0]);
-                const float4 l4 = *reinterpret_cast<const float4*>(&sL[buf][m0]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&sD[buf][m0]);
-                const int los[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, his[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
-                const float ls[4] = {l4.x, l4.y, l4.z, l4.w}, ds4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * j + i;
-                    if ((r & 1) == 0 && NKS == 8) {
-                        sn = Mfma<T>::mma32(qa[r >> 1], kop[r >> 1], sn);
-                        dn = Mfma<T>::mma32(ga[r >> 1], vop[r >> 1], dn);
-                    }
-                    if ((r & 3) == 0 && NKS == 4) sdp_mfma(sn, dn, bn, r >> 2);   // D = 64: read at use
-                    // a hidden score's logit becomes -inf, so its weight is exactly 0
-                    // (a select on the logit, not a branch around the arithmetic)
-                    float dl;
-                    float x = logit2_minus<CAP>(a, sc[r], ls[i], dl);
-                    float z = 1.0f;
-                    if constexpr (EXTRA) {
-                        x = fmaf(bv[r], BW_LOG2E, x);
-                        if (a.drop_scale > 0.0f) z = (keepm >> r) & 1u ? a.drop_scale : 0.0f;
-                    }
-                    x = (kept & (key >= los[i]) & (key <= his[i])) ? x : -INFINITY;   // & : no short circuit
-                    const float p = fast_exp2(x);
-                    if constexpr (EXTRA) dc[r] = CAP ? p * (dc[r] * z - ds4[i]) * dl : p * (dc[r] * z - ds4[i]);
-                    else dc[r] = CAP ? p * (dc[r] - ds4[i]) * dl : p * (dc[r] - ds4[i]);
-                    sc[r] = EXTRA ? p * z : p;
-                }
-            }
-            // dV += dO^T P and dK += Q^T dS of step it
-#pragma unroll
-            for (int sx = 0; sx < 2; ++sx) {
-                const v8 pop = pack8_at<T>(sc, 8 * sx);
-                const v8 dop = pack8_at<T>(dc, 8 * sx);
-#pragma unroll
-                for (int mb = 0; mb < NDB; ++mb) {
-                    if constexpr (!EARLY) {
-                        cg[sx][mb] = cols_a<T, D>(sG[buf], lane, sx, mb);
-                        cq[sx][mb] = cols_a<T, D>(sQ[buf], lane, sx, mb);
-                    }
-                    dva[mb] = Mfma<T>::mma32(cg[sx][mb], pop, dva[mb]);
-                    dka[mb] = Mfma<T>::mma32(cq[sx][mb], dop, dka[mb]);
-                }
-            }
-            __syncthreads();   // step it + 2 stored; step it's buffer free for step it + 3
-            sc = sn;
-            dc = dn;
-            buf = bn;
-        }
-    }
-    // dka / dva [mb] element r: d = 32 mb + 8 (r / 4) + 4 h + r % 4 of this lane's key;
-    // without a cap the scale (d logit / d dot) is applied to dK here
-    const float oscale = CAP ? 1.0f : a.scale;
-    if (key <= j_last) {
-        T* ko = dk + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
-        T* vo = dv + ((int64_t)b * a.Lk + key) * a.kv_stride + (int64_t)kvh * D;
-#pragma unroll
-        for (int mb = 0; mb < NDB; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                T k4[4], v4[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    k4[i] = static_cast<T>(dka[mb][4 * j + i] * oscale);
-                    v4[i] = static_cast<T>(dva[mb][4 * j + i]);
-                }
-                *reinterpret_cast<uint2*>(ko + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(k4);
-                *reinterpret_cast<uint2*>(vo + 32 * mb + 8 * j + 4 * h) = *reinterpret_cast<const uint2*>(v4);
-            }
-    }
-}
-
 // dK and dV: 16 keys per wave on 16x16x32 MFMAs, D / 16 waves (D keys) per
 // workgroup.  At D = 128 the accumulators of 16 keys (2 x 32 registers) and
-// their K and V operands (2 x 16) leave two waves per SIMD, where the 32-key
-// kernel above runs one; at D = 64 (half of each) three.  Per 32-row step:
+// their K and V operands (2 x 16) leave two waves per SIMD, where 32 keys per
+// wave (2 x 64 accumulators) would leave one; at D = 64 (half of each) three.  Per 32-row step:
 //   S  [32 rows x 16 keys] = Q  . K^T   (A: Q rows from LDS, B: K in registers)
 //   dP [32 rows x 16 keys] = dO . V^T
 //   dV^T [D x 16 keys] += dO^T . P      (A: transposing LDS reads, B: P itself)
@@ -1160,10 +878,8 @@ template <typename T, int D, bool CAP, bool EXTRA>
 hipError_t launch_bwd_mfma_t(const FwdArgs& a, const void* dout, const float* delta, void* dq, void* dk, void* dv,
                              hipStream_t s) {
     const T* g = static_cast<const T*>(dout);
-    // dK/dV first: with dropout its 16-key kernel may store the keep bits that
-    // the dQ kernel then reads (same stream).  (With both a cap and a mask or
-    // dropout the 16-key kernel spills a few values and is still faster than
-    // the 32-key one: 2.50 -> 2.04 ms on the causal GQA shape.)
+    // dK/dV first: with dropout its kernel may store the keep bits that the
+    // dQ kernel then reads (same stream)
     hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAP, EXTRA>), dim3(a.Hkv, a.B, (a.Lk + D - 1) / D), dim3(4 * D), 0, s,
                        a, g, delta, static_cast<T*>(dk), static_cast<T*>(dv));
     hipError_t e = hipGetLastError();
